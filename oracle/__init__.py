@@ -1,0 +1,183 @@
+"""Plain CPU oracle for the W4A16 group-quantized linear layer (AWQ inference).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  The HIP library
+and its Python binding never import, link or call anything here, and nothing
+here imports them.
+
+The arithmetic lives in ``oracle.c`` (plain C, single threaded, fp64
+accumulation); this module only compiles it with gcc and wraps it for numpy.
+Readings of the pages that the oracle follows are listed at the top of
+``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "oracle.c")
+LIBRARY = os.path.join(HERE, "liboracle.so")
+
+# Strict IEEE double arithmetic: no fast-math, no contraction into FMA.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off"]
+
+
+def build(source: str = SOURCE, out: str = LIBRARY) -> str:
+    """Compile ``source`` with gcc into the shared library ``out``."""
+    include = os.path.dirname(os.path.abspath(SOURCE))
+    cmd = ["gcc", *CFLAGS, "-I", include, source, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def _ptr(a: np.ndarray | None, ctype):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctype)
+
+
+class Oracle:
+    """numpy-facing wrapper of one compiled oracle library."""
+
+    def __init__(self, path: str = LIBRARY):
+        if not os.path.exists(path):
+            build(out=path)
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.oracle_h2d.restype = ctypes.c_double
+        lib.oracle_h2d.argtypes = [ctypes.c_uint16]
+        lib.oracle_d2h.restype = ctypes.c_uint16
+        lib.oracle_d2h.argtypes = [ctypes.c_double]
+        lib.oracle_h2d_n.argtypes = [_u16p, ctypes.c_size_t, _f64p]
+        lib.oracle_d2h_n.argtypes = [_f64p, ctypes.c_size_t, _u16p]
+        lib.oracle_pack.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, _i32p]
+        lib.oracle_pack_zeros.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, _i32p]
+        lib.oracle_unpack.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, _u8p]
+        lib.oracle_unpack_zeros.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, _u8p]
+        lib.oracle_dequant_one.restype = ctypes.c_uint16
+        lib.oracle_dequant_one.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint16]
+        lib.oracle_dequant.argtypes = [_i32p, _u16p, _i32p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, _u16p]
+        lib.oracle_matmul_w.argtypes = [_u16p, _u16p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, _f64p, _u16p]
+        lib.oracle_linear.restype = ctypes.c_int
+        lib.oracle_linear.argtypes = [_u16p, _i32p, _u16p, _i32p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, _f64p, _u16p]
+        self.lib = lib
+
+    # -- fp16 codec ---------------------------------------------------------
+    def h2d(self, h: int) -> float:
+        return self.lib.oracle_h2d(int(h) & 0xFFFF)
+
+    def d2h(self, x: float) -> int:
+        return int(self.lib.oracle_d2h(float(x)))
+
+    def h2d_array(self, h: np.ndarray) -> np.ndarray:
+        flat = np.ascontiguousarray(h, dtype=np.uint16).ravel()
+        out = np.empty(flat.size, dtype=np.float64)
+        self.lib.oracle_h2d_n(_ptr(flat, _u16p), flat.size, _ptr(out, _f64p))
+        return out.reshape(np.shape(h))
+
+    def d2h_array(self, x: np.ndarray) -> np.ndarray:
+        flat = np.ascontiguousarray(x, dtype=np.float64).ravel()
+        out = np.empty(flat.size, dtype=np.uint16)
+        self.lib.oracle_d2h_n(_ptr(flat, _f64p), flat.size, _ptr(out, _u16p))
+        return out.reshape(np.shape(x))
+
+    # -- packing --------------------------------------------------------------
+    def pack(self, codes: np.ndarray) -> np.ndarray:
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        K, N = codes.shape
+        Q = np.empty((K // 8, N), dtype=np.int32)
+        self.lib.oracle_pack(_ptr(codes, _u8p), K, N, _ptr(Q, _i32p))
+        return Q
+
+    def pack_zeros(self, zeros: np.ndarray) -> np.ndarray:
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+        groups, N = zeros.shape
+        QZ = np.empty((groups, N // 8), dtype=np.int32)
+        self.lib.oracle_pack_zeros(_ptr(zeros, _u8p), groups, N, _ptr(QZ, _i32p))
+        return QZ
+
+    def unpack(self, Q: np.ndarray) -> np.ndarray:
+        Q = np.ascontiguousarray(Q, dtype=np.int32)
+        R, N = Q.shape
+        codes = np.empty((8 * R, N), dtype=np.uint8)
+        self.lib.oracle_unpack(_ptr(Q, _i32p), 8 * R, N, _ptr(codes, _u8p))
+        return codes
+
+    def unpack_zeros(self, QZ: np.ndarray) -> np.ndarray:
+        QZ = np.ascontiguousarray(QZ, dtype=np.int32)
+        groups, C = QZ.shape
+        zeros = np.empty((groups, 8 * C), dtype=np.uint8)
+        self.lib.oracle_unpack_zeros(_ptr(QZ, _i32p), groups, 8 * C, _ptr(zeros, _u8p))
+        return zeros
+
+    # -- dequantization -------------------------------------------------------
+    def dequant_one(self, q: int, z: int, s: int) -> int:
+        return int(self.lib.oracle_dequant_one(int(q), int(z), int(s) & 0xFFFF))
+
+    def dequant(self, Q: np.ndarray, S: np.ndarray, QZ: np.ndarray | None, G: int) -> np.ndarray:
+        Q = np.ascontiguousarray(Q, dtype=np.int32)
+        S = np.ascontiguousarray(S, dtype=np.uint16)
+        if QZ is not None:
+            QZ = np.ascontiguousarray(QZ, dtype=np.int32)
+        K, N = 8 * Q.shape[0], Q.shape[1]
+        W = np.empty((K, N), dtype=np.uint16)
+        self.lib.oracle_dequant(_ptr(Q, _i32p), _ptr(S, _u16p), _ptr(QZ, _i32p), K, N, G,
+                                _ptr(W, _u16p))
+        return W
+
+    # -- the layer ------------------------------------------------------------
+    def matmul_w(self, X: np.ndarray, W: np.ndarray):
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        W = np.ascontiguousarray(W, dtype=np.uint16)
+        M, K = X.shape
+        N = W.shape[1]
+        Y64 = np.empty((M, N), dtype=np.float64)
+        Y16 = np.empty((M, N), dtype=np.uint16)
+        self.lib.oracle_matmul_w(_ptr(X, _u16p), _ptr(W, _u16p), M, K, N, _ptr(Y64, _f64p),
+                                 _ptr(Y16, _u16p))
+        return Y64, Y16
+
+    def linear(self, X: np.ndarray, Q: np.ndarray, S: np.ndarray, QZ: np.ndarray | None,
+               G: int):
+        """Y = X @ dequant(Q, S, QZ); returns (Y64 fp64, Y16 fp16 bit patterns)."""
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        Q = np.ascontiguousarray(Q, dtype=np.int32)
+        S = np.ascontiguousarray(S, dtype=np.uint16)
+        if QZ is not None:
+            QZ = np.ascontiguousarray(QZ, dtype=np.int32)
+        M, K = X.shape
+        N = Q.shape[1]
+        Y64 = np.empty((M, N), dtype=np.float64)
+        Y16 = np.empty((M, N), dtype=np.uint16)
+        rc = self.lib.oracle_linear(_ptr(X, _u16p), _ptr(Q, _i32p), _ptr(S, _u16p),
+                                    _ptr(QZ, _i32p), M, K, N, G, _ptr(Y64, _f64p),
+                                    _ptr(Y16, _u16p))
+        if rc != 0:
+            raise MemoryError("oracle_linear could not allocate the dequantized weight")
+        return Y64, Y16
+
+
+_DEFAULT: Oracle | None = None
+
+
+def load() -> Oracle:
+    """The oracle built from ``oracle.c`` beside this file (built on first use)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle(LIBRARY)
+    return _DEFAULT

@@ -1,0 +1,229 @@
+/*
+ * Plain CPU oracle for the W4A16 group-quantized linear layer (AWQ inference).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file exists to check the HIP library; it is
+ * never part of the product path.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load it.  It shares no code, header, table or
+ * helper with the HIP sources, and it includes nothing from them.
+ *
+ * What it computes, and where that comes from:
+ *   - AWQ keeps weights as 4-bit codes, eight of them inside one INT32 word,
+ *     with floating-point scales and zero points shared by groups of 128
+ *     weights (mbrenndoerfer.com, "AWQ > Implementation", section
+ *     "Understanding the Quantization Structure"; pyshine.com AutoAWQ tour,
+ *     "From Install to Your First Model": zero_point / q_group_size / w_bit).
+ *   - Symmetric dequantization is weight = scale[o] * (code - 8), codes 0..15,
+ *     8 being the symmetric zero point (fak explainer, "Format Specification >
+ *     Dequantization Formula").
+ *   - The kernels dequantize on the fly inside the matrix multiplication and do
+ *     fp16 arithmetic on activations (unfragile.ai AutoAWQ page, the WQLinear
+ *     paragraph; mbrenndoerfer.com, "Loading and Using AWQ Models").
+ *
+ * Readings taken where the pages are silent (each one is a plain choice that
+ * the rest of the pages support):
+ *   R1  nibble order: code j of a word sits in bits 4j..4j+3 (least significant
+ *       nibble first).
+ *   R2  packed axis: the eight codes of one word are eight consecutive k of one
+ *       output column n, so the packed weight is Q[K/8][N].
+ *   R3  group axis: G consecutive k share one scale and one zero for each
+ *       column n, group index g = k / G; scales are S[K/G][N].
+ *   R4  zero points are 4-bit integers 0..15, packed eight per word along n:
+ *       QZ[K/G][N/8]; no zero tensor means the symmetric zero 8.
+ *   R5  asymmetric dequant w = fp16(s * (q - z)): the integer difference is
+ *       exact, then one multiply and one round-to-nearest-even to fp16.
+ *   R6  the layer output is Y = X * W with W[K][N] the dequantized fp16 weight,
+ *       accumulated exactly enough (here fp64, increasing k) and rounded once
+ *       to fp16.
+ *   R7  fp16 is IEEE 754 binary16: subnormals kept, overflow to infinity,
+ *       round to nearest, ties to even.
+ *
+ * Everything is single threaded, unblocked and written for reading, not speed.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------- */
+/* IEEE 754 binary16 codec (R7): 1 sign bit, 5 exponent bits with bias 15,   */
+/* 10 fraction bits.                                                          */
+/* ------------------------------------------------------------------------- */
+
+double oracle_h2d(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);            /* subnormal (or zero): f * 2^-24 */
+    } else if (e == 31) {
+        v = (f == 0) ? INFINITY : NAN;
+    } else {
+        v = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+uint16_t oracle_d2h(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x)) return (uint16_t)(sign | 0x7E00);
+    /* 65504 is the largest finite half; halfway to 65536 (65520) ties to the
+     * even neighbour, which is 65536 and therefore infinity. */
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00);
+    if (a == 0.0) return sign;
+
+    int e2;
+    frexp(a, &e2);           /* a = m * 2^e2 with 0.5 <= m < 1 */
+    int E = e2 - 1;          /* a in [2^E, 2^(E+1)) */
+    int Eq = E < -14 ? -14 : E; /* below 2^-14 the spacing stays 2^-24 */
+    double n = ldexp(a, 10 - Eq); /* a measured in units of the half spacing */
+    double fl = floor(n);
+    double frac = n - fl;
+    double r = fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) r = fl + 1.0;
+
+    uint32_t bits;
+    if (E < -14) {
+        bits = (uint32_t)r;  /* subnormal; r == 1024 lands on the smallest normal */
+    } else {
+        /* r in [1024, 2048]; r == 2048 carries into the exponent field */
+        bits = ((uint32_t)(E + 15) << 10) + (uint32_t)r - 1024u;
+    }
+    return (uint16_t)(sign | bits);
+}
+
+void oracle_h2d_n(const uint16_t *h, size_t count, double *out)
+{
+    for (size_t i = 0; i < count; ++i) out[i] = oracle_h2d(h[i]);
+}
+
+void oracle_d2h_n(const double *x, size_t count, uint16_t *out)
+{
+    for (size_t i = 0; i < count; ++i) out[i] = oracle_d2h(x[i]);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Packing (R1, R2, R4): eight 4-bit codes per 32-bit word.                   */
+/* ------------------------------------------------------------------------- */
+
+void oracle_pack(const uint8_t *codes, int K, int N, int32_t *Q)
+{
+    for (int r = 0; r < K / 8; ++r) {
+        for (int n = 0; n < N; ++n) {
+            uint32_t word = 0;
+            for (int j = 0; j < 8; ++j) {
+                uint32_t c = codes[(size_t)(8 * r + j) * N + n] & 0xFu;
+                word |= c << (4 * j);
+            }
+            Q[(size_t)r * N + n] = (int32_t)word;
+        }
+    }
+}
+
+void oracle_pack_zeros(const uint8_t *zeros, int groups, int N, int32_t *QZ)
+{
+    for (int g = 0; g < groups; ++g) {
+        for (int c = 0; c < N / 8; ++c) {
+            uint32_t word = 0;
+            for (int j = 0; j < 8; ++j) {
+                uint32_t z = zeros[(size_t)g * N + 8 * c + j] & 0xFu;
+                word |= z << (4 * j);
+            }
+            QZ[(size_t)g * (N / 8) + c] = (int32_t)word;
+        }
+    }
+}
+
+int oracle_code(const int32_t *Q, int N, int k, int n)
+{
+    uint32_t word = (uint32_t)Q[(size_t)(k / 8) * N + n];
+    return (int)((word >> (4 * (k % 8))) & 0xFu);
+}
+
+int oracle_zero(const int32_t *QZ, int N, int g, int n)
+{
+    if (QZ == NULL) return 8; /* symmetric zero point */
+    uint32_t word = (uint32_t)QZ[(size_t)g * (N / 8) + n / 8];
+    return (int)((word >> (4 * (n % 8))) & 0xFu);
+}
+
+void oracle_unpack(const int32_t *Q, int K, int N, uint8_t *codes)
+{
+    for (int k = 0; k < K; ++k)
+        for (int n = 0; n < N; ++n)
+            codes[(size_t)k * N + n] = (uint8_t)oracle_code(Q, N, k, n);
+}
+
+void oracle_unpack_zeros(const int32_t *QZ, int groups, int N, uint8_t *zeros)
+{
+    for (int g = 0; g < groups; ++g)
+        for (int n = 0; n < N; ++n)
+            zeros[(size_t)g * N + n] = (uint8_t)oracle_zero(QZ, N, g, n);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Dequantization (R3, R5, and the symmetric formula of the fak explainer).   */
+/* ------------------------------------------------------------------------- */
+
+uint16_t oracle_dequant_one(int q, int z, uint16_t s)
+{
+    /* (q - z) is a small integer and s has 11 significant bits, so the double
+     * product is exact; the only rounding is the final conversion to fp16. */
+    return oracle_d2h((double)(q - z) * oracle_h2d(s));
+}
+
+void oracle_dequant(const int32_t *Q, const uint16_t *S, const int32_t *QZ,
+                    int K, int N, int G, uint16_t *W)
+{
+    for (int k = 0; k < K; ++k) {
+        int g = k / G;
+        for (int n = 0; n < N; ++n) {
+            int q = oracle_code(Q, N, k, n);
+            int z = oracle_zero(QZ, N, g, n);
+            uint16_t s = S[(size_t)g * N + n];
+            W[(size_t)k * N + n] = oracle_dequant_one(q, z, s);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* The layer (R6): Y[M][N] = X[M][K] * W[K][N].                                */
+/* ------------------------------------------------------------------------- */
+
+void oracle_matmul_w(const uint16_t *X, const uint16_t *W, int M, int K, int N,
+                     double *Y64, uint16_t *Y16)
+{
+    /* Every product of two halves is exact in double.  Each output is summed
+     * over k in increasing order; the loop over n sits innermost only so that
+     * W is walked row by row, which leaves each output's order unchanged. */
+    double *acc = (double *)malloc((size_t)N * sizeof(double));
+    for (int m = 0; m < M; ++m) {
+        for (int n = 0; n < N; ++n) acc[n] = 0.0;
+        for (int k = 0; k < K; ++k) {
+            double x = oracle_h2d(X[(size_t)m * K + k]);
+            const uint16_t *wrow = W + (size_t)k * N;
+            for (int n = 0; n < N; ++n) acc[n] += x * oracle_h2d(wrow[n]);
+        }
+        for (int n = 0; n < N; ++n) {
+            if (Y64) Y64[(size_t)m * N + n] = acc[n];
+            if (Y16) Y16[(size_t)m * N + n] = oracle_d2h(acc[n]);
+        }
+    }
+    free(acc);
+}
+
+int oracle_linear(const uint16_t *X, const int32_t *Q, const uint16_t *S,
+                  const int32_t *QZ, int M, int K, int N, int G,
+                  double *Y64, uint16_t *Y16)
+{
+    uint16_t *W = (uint16_t *)malloc((size_t)K * N * sizeof(uint16_t));
+    if (W == NULL) return -1;
+    oracle_dequant(Q, S, QZ, K, N, G, W);
+    oracle_matmul_w(X, W, M, K, N, Y64, Y16);
+    free(W);
+    return 0;
+}

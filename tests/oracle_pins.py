@@ -1,0 +1,398 @@
+"""Pins that tie the CPU oracle to what the pages and the mathematics fix.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError if
+the oracle disagrees with a value or property that does not come from the
+oracle itself:
+
+* hand-worked values stored under ``tests/golden/`` (each file states the
+  passage of the pages it follows and shows the working);
+* closed forms computed by hand (sums of arithmetic series, one-hot inputs,
+  sign and power-of-two symmetries);
+* numpy's own IEEE binary16 conversion, an implementation independent of the
+  oracle's codec, as the library routine that the fp16 special cases reduce to;
+* exact rational brute force (``fractions.Fraction``) on tiny layers, built
+  from the *unpacked* inputs so that it shares no indexing with the oracle.
+
+``tests/test_oracle_pins.py`` runs every pin against the oracle;
+``tests/test_oracle_mutants.py`` compiles copies of ``oracle.c`` with a
+plausible mistake planted and checks that some pin fails for each.
+"""
+from __future__ import annotations
+
+import os
+import sys
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------
+# helpers (numpy only; nothing from the oracle or the HIP library)
+# ----------------------------------------------------------------------------
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line.split()
+
+
+def _np_h2d(h):
+    return np.asarray(h, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _np_d2h(x):
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def _same_halves(a, b):
+    """Bitwise equality of fp16 patterns, NaNs compared by class."""
+    a = np.asarray(a, dtype=np.uint16)
+    b = np.asarray(b, dtype=np.uint16)
+    nan_a = ((a & 0x7C00) == 0x7C00) & ((a & 0x03FF) != 0)
+    nan_b = ((b & 0x7C00) == 0x7C00) & ((b & 0x03FF) != 0)
+    return bool(np.all((a == b) | (nan_a & nan_b)))
+
+
+def _pack_by_hand(codes_col):
+    """One word from eight codes, code j in bits 4j.. (for building inputs only)."""
+    w = 0
+    for j, c in enumerate(codes_col):
+        w |= (int(c) & 0xF) << (4 * j)
+    return w - (1 << 32) if w >= (1 << 31) else w
+
+
+# ----------------------------------------------------------------------------
+# fp16 codec: IEEE 754 binary16, checked against numpy's conversion
+# ----------------------------------------------------------------------------
+
+def pin_h2d_all_halves(o):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = o.h2d_array(h)
+    want = _np_h2d(h)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def pin_d2h_roundtrip_all_halves(o):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = _np_h2d(h)
+    assert _same_halves(o.d2h_array(x), h)
+
+
+def pin_d2h_midpoints(o):
+    """Halfway cases tie to even; a hair either side rounds to the nearer half."""
+    h = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16)  # +0 .. 65504
+    lo = _np_h2d(h)
+    hi = np.append(lo[1:], 65536.0)
+    mid = (lo + hi) / 2.0           # exact in double
+    for x in (mid, np.nextafter(mid, -np.inf), np.nextafter(mid, np.inf)):
+        for sgn in (1.0, -1.0):
+            assert _same_halves(o.d2h_array(sgn * x), _np_d2h(sgn * x))
+    # the even neighbour wins every exact tie (65504 + 16 ties to 65536, infinity)
+    even = np.where(h % 2 == 0, h, h + 1).astype(np.uint16)
+    assert np.array_equal(o.d2h_array(mid), even)
+    assert np.array_equal(o.d2h_array(np.nextafter(mid, -np.inf)), h)
+    assert np.array_equal(o.d2h_array(np.nextafter(mid, np.inf)), (h + 1).astype(np.uint16))
+    # the edges: the largest half, the overflow threshold, the smallest subnormal
+    assert o.d2h(65504.0) == 0x7BFF
+    assert o.d2h(np.nextafter(65520.0, 0.0)) == 0x7BFF
+    assert o.d2h(65520.0) == 0x7C00
+    assert o.d2h(2.0 ** -24) == 0x0001
+    assert o.d2h(2.0 ** -25) == 0x0000            # tie between 0 and 2^-24 goes to 0
+    assert o.d2h(3 * 2.0 ** -26) == 0x0001
+    assert o.d2h(-0.0) == 0x8000
+    assert o.d2h(float("inf")) == 0x7C00 and o.d2h(float("-inf")) == 0xFC00
+    assert (o.d2h(float("nan")) & 0x7C00) == 0x7C00 and (o.d2h(float("nan")) & 0x3FF) != 0
+
+
+def pin_d2h_random(o):
+    rng = np.random.default_rng(12345)
+    x = rng.standard_normal(400_000) * np.exp2(rng.integers(-30, 18, 400_000))
+    assert _same_halves(o.d2h_array(x), _np_d2h(x))
+
+
+# ----------------------------------------------------------------------------
+# packing: eight 4-bit codes per 32-bit word
+# ----------------------------------------------------------------------------
+
+def _golden_pack():
+    codes, words = [], []
+    for f in _rows("pack_words.txt"):
+        codes.append([int(c) for c in f[0].split(",")])
+        words.append(int(f[2]))
+        assert (int(f[1], 16) - (1 << 32) if int(f[1], 16) >= 1 << 31 else int(f[1], 16)) == int(f[2])
+    return codes, words
+
+
+def pin_pack_golden(o):
+    codes, words = _golden_pack()
+    ncol = len(codes)
+    npad = (ncol + 7) // 8 * 8
+    C = np.zeros((8, npad), dtype=np.uint8)
+    for n, col in enumerate(codes):
+        C[:, n] = col
+    Q = o.pack(C)
+    assert Q.shape == (1, npad)
+    assert [int(v) for v in Q[0, :ncol]] == words
+    # the same words unpack to the codes' low nibbles, in order
+    back = o.unpack(Q)
+    for n, col in enumerate(codes):
+        assert [int(v) for v in back[:, n]] == [c & 0xF for c in col]
+
+
+def pin_pack_zeros_golden(o):
+    """Zero points pack eight consecutive columns into one word, column j in bits 4j."""
+    codes, words = _golden_pack()
+    Z = np.array(codes, dtype=np.uint8).reshape(len(codes), 8)  # groups x 8 columns
+    QZ = o.pack_zeros(Z)
+    assert QZ.shape == (len(codes), 1)
+    assert [int(v) for v in QZ[:, 0]] == words
+    assert np.array_equal(o.unpack_zeros(QZ), Z & 0xF)
+
+
+def pin_pack_roundtrip(o):
+    rng = np.random.default_rng(7)
+    c = rng.integers(0, 256, size=(64, 40), dtype=np.uint8)
+    Q = o.pack(c)
+    assert Q.shape == (8, 40)
+    assert np.array_equal(o.unpack(Q), c & 0xF)
+    # packing is a bijection on words: every 32-bit pattern comes back
+    w = rng.integers(-(1 << 31), 1 << 31, size=(5, 48), dtype=np.int64).astype(np.int32)
+    assert np.array_equal(o.pack(o.unpack(w)), w)
+    assert np.array_equal(o.pack_zeros(o.unpack_zeros(w)), w)
+    # a code written at (k, n) by hand is found at (k, n)
+    for k, n in [(0, 0), (7, 3), (13, 39), (63, 1)]:
+        cc = np.zeros((64, 40), dtype=np.uint8)
+        cc[k, n] = 11
+        Qh = np.zeros((8, 40), dtype=np.int32)
+        Qh[k // 8, n] = _pack_by_hand([11 if j == k % 8 else 0 for j in range(8)])
+        assert np.array_equal(o.pack(cc), Qh)
+
+
+def pin_packed_size(o):
+    """qweight is four times smaller than the fp16 weight (8 codes per 4 bytes)."""
+    for K, N in [(8, 8), (128, 64), (512, 512)]:
+        Q = o.pack(np.zeros((K, N), dtype=np.uint8))
+        assert Q.nbytes == K * N // 2 and 2 * K * N == 4 * Q.nbytes
+
+
+# ----------------------------------------------------------------------------
+# dequantization w = fp16(s * (q - z))
+# ----------------------------------------------------------------------------
+
+def pin_dequant_golden(o):
+    for f in _rows("dequant_examples.txt"):
+        q, z, s, w = int(f[0]), int(f[1]), int(f[2], 16), int(f[3], 16)
+        assert o.dequant_one(q, z, s) == w, (q, z, hex(s))
+        assert float(np.uint16(w).view(np.float16)) == float(f[4])
+        # the same example through the tensor path: one column, one group of 8
+        codes = np.full((8, 8), q, dtype=np.uint8)
+        zeros = np.full((1, 8), z, dtype=np.uint8)
+        S = np.full((1, 8), s, dtype=np.uint16)
+        W = o.dequant(o.pack(codes), S, o.pack_zeros(zeros), 8)
+        assert np.all(W == w)
+
+
+def pin_dequant_exhaustive(o):
+    """Every code, every zero and every finite fp16 scale, through the tensor path.
+
+    Layout: group g (G = 16) carries zero point g; inside it, row k carries code
+    k % 16; column n carries the n-th finite fp16 pattern as its scale in every
+    group.  The reference is numpy's rounding of the exact double product.
+    """
+    all_h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = all_h[(all_h & 0x7C00) != 0x7C00]          # 63488 patterns
+    N = finite.size
+    G, groups = 16, 16
+    K = G * groups
+    codes = np.tile((np.arange(K) % 16).astype(np.uint8)[:, None], (1, N))
+    zeros = np.tile(np.arange(groups, dtype=np.uint8)[:, None], (1, N))
+    S = np.tile(finite[None, :], (groups, 1))
+    W = o.dequant(o.pack(codes), S, o.pack_zeros(zeros), G)
+    s64 = _np_h2d(finite)
+    diff = (np.arange(K) % 16 - np.arange(K) // 16).astype(np.float64)
+    want = _np_d2h(diff[:, None] * s64[None, :])
+    assert _same_halves(W, want)
+    # symmetric: no zero tensor means z = 8
+    Ws = o.dequant(o.pack(codes[:16]), S[:1], None, 16)
+    wants = _np_d2h((np.arange(16) - 8).astype(np.float64)[:, None] * s64[None, :])
+    assert _same_halves(Ws, wants)
+
+
+def pin_dequant_invariants(o):
+    s_vals = [0x211F, 0x1419, 0x251F, 0x3C00, 0x0001, 0x7BFF]
+    for s in s_vals:
+        sv = float(np.uint16(s).view(np.float16))
+        for q in range(16):
+            assert o.dequant_one(q, q, s) == 0x0000          # q == z gives +0 for s > 0
+        assert o.dequant_one(8, 8, s) == 0x0000               # symmetric code 8 -> 0
+        assert o.dequant_one(0, 8, s) == int(_np_d2h(-8 * sv))  # code 0 -> -8s
+        assert o.dequant_one(15, 8, s) == int(_np_d2h(7 * sv))  # code 15 -> 7s
+        # (q - z) and (z - q) give results of opposite sign and equal magnitude
+        for q, z in [(3, 8), (15, 0), (1, 2)]:
+            assert o.dequant_one(q, z, s) ^ o.dequant_one(z, q, s) == 0x8000
+
+
+# ----------------------------------------------------------------------------
+# the layer Y = X @ W
+# ----------------------------------------------------------------------------
+
+def pin_tiny_gemv_golden(o):
+    codes = np.array([[(k + n) % 16 for n in range(8)] for k in range(8)], dtype=np.uint8)
+    Q = o.pack(codes)
+    assert [int(v) & 0xFFFFFFFF for v in Q[0]] == [0x76543210 + n * 0x11111111 for n in range(8)]
+    X = np.full((1, 8), 0x3C00, dtype=np.uint16)    # ones
+    for f in _rows("tiny_gemv.txt"):
+        s = int(f[1], 16)
+        QZ = None if f[2] == "none" else o.pack_zeros(
+            np.array([[int(v) for v in f[2].split(",")]], dtype=np.uint8))
+        S = np.full((1, 8), s, dtype=np.uint16)
+        Y64, Y16 = o.linear(X, Q, S, QZ, 8)
+        want = [float(v) for v in f[3].split(",")]
+        assert list(Y64[0]) == want, f[0]
+        assert list(_np_h2d(Y16[0])) == want, f[0]
+
+
+def pin_group_axis(o):
+    """Groups run along K: with q - z = 1, group 0 scaled by 1 and group 1 by 2,
+    rows 0..7 of W are 1 and rows 8..15 are 2 in every column."""
+    K, N, G = 16, 8, 8
+    Q = o.pack(np.full((K, N), 9, dtype=np.uint8))
+    QZ = o.pack_zeros(np.full((2, N), 8, dtype=np.uint8))
+    S = np.array([[0x3C00] * N, [0x4000] * N], dtype=np.uint16)   # 1.0, 2.0
+    one = 0x3C00
+    for x, want in [([one] * 16, 24.0), ([one] * 8 + [0] * 8, 8.0), ([0] * 8 + [one] * 8, 16.0),
+                    ([0] * 15 + [one], 2.0)]:
+        Y64, _ = o.linear(np.array([x], dtype=np.uint16), Q, S, QZ, G)
+        assert np.all(Y64 == want), (x, Y64)
+
+
+def pin_scale_and_zero_columns(o):
+    """Scales and zeros are per column: s[n] = n + 1 and z[n] = 8 - (n % 3) with
+    code 9 give W[k][n] = (n + 1) * (1 + n % 3)."""
+    K, N, G = 8, 16, 8
+    Q = o.pack(np.full((K, N), 9, dtype=np.uint8))
+    zeros = np.array([[8 - (n % 3) for n in range(N)]], dtype=np.uint8)
+    S = _np_d2h(np.arange(1, N + 1, dtype=np.float64))[None, :]
+    X = np.zeros((1, K), dtype=np.uint16)
+    X[0, 3] = 0x3C00
+    Y64, Y16 = o.linear(X, Q, S, o.pack_zeros(zeros), G)
+    assert list(Y64[0]) == [float((n + 1) * (1 + n % 3)) for n in range(N)]
+
+
+def pin_onehot(o):
+    """X = e_k returns row k of the dequantized weight bit for bit."""
+    rng = np.random.default_rng(3)
+    K, N, G = 64, 24, 16
+    codes = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    zeros = rng.integers(0, 16, (K // G, N), dtype=np.uint8)
+    S = _np_d2h(rng.uniform(0.002, 0.02, (K // G, N)))
+    Q, QZ = o.pack(codes), o.pack_zeros(zeros)
+    W = o.dequant(Q, S, QZ, G)
+    X = np.zeros((K, K), dtype=np.uint16)
+    X[np.arange(K), np.arange(K)] = 0x3C00                  # identity: row m = e_m
+    _, Y16 = o.linear(X, Q, S, QZ, G)
+    assert _same_halves(Y16, W)
+
+
+def _exact_layer(X, codes, zeros, S, G):
+    """Exact rational Y from unpacked inputs: w = fp16(s (q - z)) rounded by numpy,
+    then sum of exact products."""
+    M, K = X.shape
+    N = codes.shape[1]
+    xs = [[Fraction(float(v)) for v in row] for row in _np_h2d(X)]
+    W = np.empty((K, N), dtype=np.float64)
+    for k in range(K):
+        g = k // G
+        for n in range(N):
+            z = 8 if zeros is None else int(zeros[g, n])
+            W[k, n] = _np_h2d(_np_d2h((int(codes[k, n]) - z) * float(_np_h2d(S[g, n]))))
+    ws = [[Fraction(float(v)) for v in row] for row in W]
+    exact = [[sum((xs[m][k] * ws[k][n] for k in range(K)), Fraction(0)) for n in range(N)]
+             for m in range(M)]
+    absum = [[sum((abs(xs[m][k] * ws[k][n]) for k in range(K)), Fraction(0)) for n in range(N)]
+             for m in range(M)]
+    return exact, absum
+
+
+def pin_bruteforce_exact(o):
+    rng = np.random.default_rng(11)
+    for M, K, N, G, sym in [(1, 8, 8, 8, False), (3, 16, 24, 8, False), (2, 128, 16, 128, False),
+                            (3, 256, 8, 128, True), (1, 64, 16, 64, True), (16, 32, 8, 16, False)]:
+        codes = rng.integers(0, 16, (K, N), dtype=np.uint8)
+        zeros = None if sym else rng.integers(0, 16, (K // G, N), dtype=np.uint8)
+        S = _np_d2h(rng.uniform(0.002, 0.02, (K // G, N)))
+        X = _np_d2h(rng.standard_normal((M, K)))
+        Y64, Y16 = o.linear(X, o.pack(codes), S, None if sym else o.pack_zeros(zeros), G)
+        exact, absum = _exact_layer(X, codes, zeros, S, G)
+        for m in range(M):
+            for n in range(N):
+                e = exact[m][n]
+                # recursive summation in double: |error| <= (K - 1) u sum|terms|, u = 2^-53
+                assert abs(Fraction(Y64[m, n]) - e) <= K * Fraction(1, 1 << 53) * absum[m][n]
+                assert int(Y16[m, n]) == int(_np_d2h(float(e))), (M, K, N, m, n)
+
+
+def pin_power_of_two(o):
+    """Doubling X or the scales doubles Y exactly (no overflow or underflow here)."""
+    rng = np.random.default_rng(5)
+    K, N, G = 256, 32, 128
+    codes = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    zeros = rng.integers(0, 16, (K // G, N), dtype=np.uint8)
+    S = _np_d2h(rng.uniform(0.002, 0.02, (K // G, N)))
+    X = _np_d2h(rng.standard_normal((4, K)))
+    Q, QZ = o.pack(codes), o.pack_zeros(zeros)
+    Y64, Y16 = o.linear(X, Q, S, QZ, G)
+    Y64x, Y16x = o.linear(_np_d2h(2.0 * _np_h2d(X)), Q, S, QZ, G)
+    Y64s, Y16s = o.linear(X, Q, _np_d2h(4.0 * _np_h2d(S)), QZ, G)
+    assert np.array_equal(Y64x, 2.0 * Y64) and np.array_equal(Y64s, 4.0 * Y64)
+    assert np.array_equal(_np_h2d(Y16x), 2.0 * _np_h2d(Y16))
+    assert np.array_equal(_np_h2d(Y16s), 4.0 * _np_h2d(Y16))
+    # negating X negates Y
+    Yn64, _ = o.linear(X ^ np.uint16(0x8000), Q, S, QZ, G)
+    assert np.array_equal(Yn64, -Y64)
+
+
+def pin_rows_independent(o):
+    """Each output row depends on its own X row only (sampled parity relies on it)."""
+    rng = np.random.default_rng(9)
+    K, N, G = 128, 40, 32
+    codes = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    S = _np_d2h(rng.uniform(0.002, 0.02, (K // G, N)))
+    X = _np_d2h(rng.standard_normal((6, K)))
+    Q = o.pack(codes)
+    Y64, Y16 = o.linear(X, Q, S, None, G)
+    rows = [4, 1]
+    Y64r, Y16r = o.linear(X[rows], Q, S, None, G)
+    assert np.array_equal(Y64r, Y64[rows]) and np.array_equal(Y16r, Y16[rows])
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+def run_all(library_path):
+    """Run every pin against the oracle library at ``library_path``; used by the
+    mutation test in a child process (a planted mistake may crash)."""
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import oracle
+    o = oracle.Oracle(library_path)
+    failed = []
+    for pin in PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            failed.append(pin.__name__)
+    return failed
+
+
+if __name__ == "__main__":
+    bad = run_all(sys.argv[1])
+    print("FAILED:" + ",".join(bad))
+    sys.exit(1 if bad else 0)
