@@ -1,0 +1,124 @@
+/*
+ * awq.h -- C ABI of the MI355X (gfx950) W4A16 group-quantized linear layer.
+ *
+ * The layer is the inference hot path of AWQ (activation-aware 4-bit weight
+ * quantization): Y[M][N] = X[M][K] * W[K][N], where W is kept as 4-bit codes
+ * and dequantized inside the multiplication.  Sources on the AWQ pages:
+ *   - the quantized linear modules perform INT4 weight dequantization and the
+ *     matrix multiplication in one fused kernel, never materializing the fp16
+ *     weight, with a matrix-vector variant for single-token decoding and a
+ *     GEMM variant for batches (unfragile.ai AutoAWQ page, the WQLinear
+ *     paragraph; pyshine.com AutoAWQ tour, the overview bullets on
+ *     WQLinear_GEMM / WQLinear_GEMV);
+ *   - eight 4-bit weights share one INT32 word, with fp16 scales and zero
+ *     points shared by groups of 128 weights (mbrenndoerfer.com,
+ *     "AWQ > Implementation", "Understanding the Quantization Structure");
+ *   - symmetric dequantization weight = scale * (code - 8) (fak explainer,
+ *     "Format Specification > Dequantization Formula"), and one matrix-vector
+ *     plus one batched call over a quantized tensor (fak explainer,
+ *     "Integration with Forward Pass").
+ *
+ * Data layout (row-major, dense; fp16 = IEEE binary16 bit patterns):
+ *   qweight  int32 [K/8][N]    code of (k, n) in bits 4*(k%8)..4*(k%8)+3 of
+ *                              word [k/8][n]: eight consecutive k of one column
+ *   scales   fp16  [K/G][N]    scale of group g = k / G for column n
+ *   qzeros   int32 [K/G][N/8]  zero of (g, n) in bits 4*(n%8).. of word
+ *                              [g][n/8]; NULL selects the symmetric zero 8
+ *   x        fp16  [M][K]      activations;   y  fp16 [M][N]   outputs
+ * Dequantized weight: w(k, n) = fp16_rne(scale(g, n) * (code(k, n) - zero(g, n))).
+ * Layer output: y = fp16_rne(sum_k x(m, k) * w(k, n)), accumulated in fp32.
+ *
+ * Shape rules (AWQ_ERROR_SHAPE otherwise): K, N, G > 0; K % 8 == 0;
+ * N % 8 == 0; G % 8 == 0; K % G == 0; every array below 2^31 elements.
+ * M == 0 is an empty batch: success, nothing launched.  M < 0 is invalid.
+ *
+ * Pointers: every tensor pointer is a DEVICE pointer, 16-byte aligned
+ * (AWQ_ERROR_ALIGNMENT otherwise), owned by the caller, and only read or
+ * written while the launched kernels run; the library keeps none of them,
+ * allocates no memory and holds no state.  Outputs must not overlap inputs.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream).  Every call validates its arguments on the host, returns an error
+ * code with nothing launched if they are wrong, and otherwise enqueues its
+ * kernels and returns without waiting.  A fault inside a kernel surfaces at the
+ * caller's next synchronization, as HIP reports it.  Calls are thread safe.
+ */
+#ifndef AWQ_MI355X_H
+#define AWQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum awq_status {
+    AWQ_SUCCESS = 0,
+    AWQ_ERROR_INVALID_VALUE = 1, /* null pointer, negative M, non-positive K/N/G */
+    AWQ_ERROR_SHAPE = 2,         /* a shape rule above is broken               */
+    AWQ_ERROR_ALIGNMENT = 3,     /* a tensor pointer is not 16-byte aligned    */
+    AWQ_ERROR_UNSUPPORTED = 4,   /* valid layer, but outside this entry point (gemv: M > 16) */
+    AWQ_ERROR_HIP = 5            /* the HIP runtime refused the launch          */
+} awq_status;
+
+/* Non-owning view of one quantized linear layer (logical weight W[K][N]). */
+typedef struct awq_layer {
+    const int32_t *qweight;      /* [K/8][N]                                   */
+    const uint16_t *scales;      /* [K/G][N] fp16                              */
+    const int32_t *qzeros;       /* [K/G][N/8], or NULL for symmetric (zero 8) */
+    int32_t K;
+    int32_t N;
+    int32_t group_size;          /* G; G == K gives one scale per column        */
+} awq_layer;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *awq_status_string(awq_status status);
+
+/*
+ * awq_pack: codes uint8 [K][N] (one 4-bit code per byte; bits above the low
+ * nibble are ignored) -> qweight int32 [K/8][N].  The packing of eight 4-bit
+ * weights into one INT32 word is the mbrenndoerfer.com "Understanding the
+ * Quantization Structure" layout; done once per layer, when it is loaded.
+ */
+awq_status awq_pack(const uint8_t *codes, int32_t *qweight, int32_t K, int32_t N,
+                    void *stream);
+
+/*
+ * awq_pack_zeros: zeros uint8 [groups][N] -> qzeros int32 [groups][N/8],
+ * eight consecutive columns per word (the stored zero points of the pages'
+ * asymmetric, zero_point=True configuration).  groups = K / G.
+ */
+awq_status awq_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int32_t groups,
+                          int32_t N, void *stream);
+
+/*
+ * awq_dequant: materializes W[K][N] fp16 from the layer, bit-exactly
+ * w = fp16_rne(scale * (code - zero)).  Not on the decode path (the fused
+ * kernels never write W); it exposes the exact dequantization the fused
+ * kernels perform.  w_out: device fp16 [K][N].
+ */
+awq_status awq_dequant(const awq_layer *layer, uint16_t *w_out, void *stream);
+
+/*
+ * awq_gemv: fused dequantize-and-multiply for small batches, 1 <= M <= 16 (the
+ * pages' matrix-vector module for single-token decoding).  Streams the packed
+ * weight once.  M > 16 returns AWQ_ERROR_UNSUPPORTED; use awq_gemm.
+ */
+awq_status awq_gemv(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
+                    void *stream);
+
+/*
+ * awq_gemm: fused dequantize-and-multiply for any M >= 0 (the pages' GEMM
+ * module for batched inference): weights are dequantized tile by tile into
+ * on-chip memory and multiplied with fp16 matrix-core instructions, fp32
+ * accumulation.
+ */
+awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_MI355X_H */

@@ -199,14 +199,17 @@ void oracle_matmul_w(const uint16_t *X, const uint16_t *W, int M, int K, int N,
 {
     /* Every product of two halves is exact in double.  Each output is summed
      * over k in increasing order; the loop over n sits innermost only so that
-     * W is walked row by row, which leaves each output's order unchanged. */
+     * W is walked row by row, which leaves each output's order unchanged.
+     * W is decoded to double once (the decoding is exact). */
+    double *Wd = (double *)malloc((size_t)K * N * sizeof(double));
     double *acc = (double *)malloc((size_t)N * sizeof(double));
+    for (size_t i = 0; i < (size_t)K * N; ++i) Wd[i] = oracle_h2d(W[i]);
     for (int m = 0; m < M; ++m) {
         for (int n = 0; n < N; ++n) acc[n] = 0.0;
         for (int k = 0; k < K; ++k) {
             double x = oracle_h2d(X[(size_t)m * K + k]);
-            const uint16_t *wrow = W + (size_t)k * N;
-            for (int n = 0; n < N; ++n) acc[n] += x * oracle_h2d(wrow[n]);
+            const double *wrow = Wd + (size_t)k * N;
+            for (int n = 0; n < N; ++n) acc[n] += x * wrow[n];
         }
         for (int n = 0; n < N; ++n) {
             if (Y64) Y64[(size_t)m * N + n] = acc[n];
@@ -214,6 +217,7 @@ void oracle_matmul_w(const uint16_t *X, const uint16_t *W, int M, int K, int N,
         }
     }
     free(acc);
+    free(Wd);
 }
 
 int oracle_linear(const uint16_t *X, const int32_t *Q, const uint16_t *S,

@@ -1,0 +1,113 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/awq.h declares, and rejects bad arguments before touching a GPU.
+
+Only invalid argument combinations are passed (or M == 0, which returns before
+any launch), so nothing here launches a kernel; the fake device addresses are
+never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from w4a16_group_quantized_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+FAKE = 0x10000000          # 16-byte aligned, never dereferenced
+MISALIGNED = FAKE + 2
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_header_matches_binding():
+    assert header_functions() == sorted(binding.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (awq_\w+)", out))
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for code, name in binding.STATUS_NAMES.items():
+        assert lib.awq_status_string(code).decode().startswith(name)
+    assert lib.awq_status_string(99).decode() == "AWQ_ERROR_UNKNOWN"
+
+
+def layer(K=128, N=64, G=128, qw=FAKE, sc=FAKE, qz=FAKE):
+    return binding.CLayer(qw, sc, qz, K, N, G)
+
+
+@pytest.mark.parametrize("fn", ["awq_gemv", "awq_gemm"])
+@pytest.mark.parametrize("case,want", [
+    (dict(K=0), 1), (dict(N=-8), 1), (dict(G=0), 1),
+    (dict(K=12), 2), (dict(N=20), 2), (dict(G=12, K=24), 2), (dict(K=192, G=128), 2),
+    (dict(K=1 << 16, N=1 << 16, G=128), 2),
+    (dict(qw=None), 1), (dict(sc=None), 1),
+    (dict(qw=MISALIGNED), 3), (dict(sc=MISALIGNED), 3), (dict(qz=MISALIGNED), 3),
+])
+def test_layer_validation(lib, fn, case, want):
+    c = layer(**case)
+    got = getattr(lib, fn)(FAKE, ctypes.byref(c), FAKE, 1, None)
+    assert got == want
+
+
+@pytest.mark.parametrize("fn", ["awq_gemv", "awq_gemm"])
+def test_io_validation(lib, fn):
+    c = layer()
+    f = getattr(lib, fn)
+    assert f(FAKE, None, FAKE, 1, None) == 1               # null layer
+    assert f(None, ctypes.byref(c), FAKE, 1, None) == 1    # null x
+    assert f(FAKE, ctypes.byref(c), None, 1, None) == 1    # null y
+    assert f(FAKE, ctypes.byref(c), FAKE, -1, None) == 1   # negative M
+    assert f(MISALIGNED, ctypes.byref(c), FAKE, 1, None) == 3
+    assert f(FAKE, ctypes.byref(c), MISALIGNED, 1, None) == 3
+    assert f(FAKE, ctypes.byref(c), FAKE, 1 << 30, None) == 2   # M*K beyond 2^31
+    # M == 0 is an empty batch: success, nothing launched
+    assert f(FAKE, ctypes.byref(c), FAKE, 0, None) == 0
+
+
+def test_gemv_rejects_large_batches(lib):
+    c = layer()
+    assert lib.awq_gemv(FAKE, ctypes.byref(c), FAKE, 17, None) == 4
+
+
+def test_pack_validation(lib):
+    assert lib.awq_pack(None, FAKE, 8, 8, None) == 1
+    assert lib.awq_pack(FAKE, FAKE, 0, 8, None) == 1
+    assert lib.awq_pack(FAKE, FAKE, 12, 8, None) == 2
+    assert lib.awq_pack(FAKE, FAKE, 8, 12, None) == 2
+    assert lib.awq_pack(MISALIGNED, FAKE, 8, 8, None) == 3
+    assert lib.awq_pack_zeros(FAKE, None, 1, 8, None) == 1
+    assert lib.awq_pack_zeros(FAKE, FAKE, 1, 4, None) == 2
+    assert lib.awq_pack_zeros(FAKE, MISALIGNED, 1, 8, None) == 3
+
+
+def test_dequant_validation(lib):
+    c = layer()
+    assert lib.awq_dequant(ctypes.byref(c), None, None) == 1
+    assert lib.awq_dequant(ctypes.byref(c), MISALIGNED, None) == 3
+    bad = layer(K=100)
+    assert lib.awq_dequant(ctypes.byref(bad), FAKE, None) == 2
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.load(str(tmp_path / "libawq.so"))

@@ -1,0 +1,155 @@
+"""GPU parity of the fused layer (awq_gemv, awq_gemm) against the oracle.
+
+Y is compared with the oracle's fp16 result under the bar in ``parity``; the
+one-hot and identity cases, where exactly one product reaches each output, are
+compared bit for bit with the oracle's dequantized weight.  Full-size workloads
+run in the launch configuration the benchmark times; for the two large-batch
+GEMMs the oracle computes a seeded sample of rows (all columns), since every
+output row depends on its own row of X only.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_cases import (device_case, device_layer, oracle_case, oracle_weight, random_case,
+                       workload_host)
+from parity import assert_y_close, same_halves_up_to_zero_sign, to_dev, to_host_bits
+from w4a16_group_quantized_amd import binding, synth
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ENTRY = {"gemv": binding.gemv, "gemm": binding.gemm}
+
+
+def _sample_rows(M, count, seed):
+    if M <= count:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    rest = rng.choice(np.arange(1, M - 1), size=count - 2, replace=False)
+    return np.sort(np.concatenate([[0, M - 1], rest]))
+
+
+@pytest.mark.parametrize("entry,name", [
+    ("gemv", "tiny"), ("gemv", "decode_8b_gate"), ("gemv", "gate_up_m16"), ("gemv", "sym70b_m1"),
+    ("gemm", "tiny"), ("gemm", "gate_up_m16"), ("gemm", "prefill_out_proj"),
+    ("gemm", "sym70b_m4096"),
+])
+def test_workload_parity(entry, name):
+    w = synth.WORKLOADS[name]
+    X, _, _, _ = workload_host(name)
+    _, _, W = oracle_weight(name)
+    layer = device_layer(name)
+    y = to_host_bits(ENTRY[entry](to_dev(X), layer))
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.M, 64 if w.K * w.N <= 1 << 25 else 16, w.wid)
+    _, Y16 = oracle.load().matmul_w(np.ascontiguousarray(X[rows]), W)
+    assert_y_close(y[rows], Y16, f"{entry} {name} rows={len(rows)}")
+
+
+RAGGED = [
+    # M, K, N, G, symmetric
+    (1, 8, 8, 8, False), (1, 32, 8, 32, True), (3, 136, 200, 8, False), (5, 256, 72, 64, False),
+    (16, 512, 24, 512, True), (7, 1024, 264, 128, False), (2, 96, 40, 32, False),
+    (1, 520, 8, 8, True), (16, 4096, 136, 128, False), (9, 192, 64, 96, False),
+    (4, 1152, 520, 1152, True),
+]
+
+
+@pytest.mark.parametrize("entry", ["gemv", "gemm"])
+@pytest.mark.parametrize("M,K,N,G,sym", RAGGED)
+def test_ragged_parity(entry, M, K, N, G, sym):
+    seed = 1000 + M * 7 + K * 3 + N + G
+    X, codes, zeros, scales = random_case(seed, M, K, N, G, sym)
+    _, Y16 = oracle_case(X, codes, zeros, scales, G)
+    layer = device_case(codes, zeros, scales, G)
+    y = to_host_bits(ENTRY[entry](to_dev(X), layer))
+    assert_y_close(y, Y16, f"{entry} M={M} K={K} N={N} G={G} sym={sym}")
+
+
+@pytest.mark.parametrize("M,K,N,G", [(37, 200, 136, 8), (130, 1032, 264, 8), (257, 1024, 8, 128),
+                                     (300, 4096, 520, 128)])
+def test_gemm_large_ragged(M, K, N, G):
+    X, codes, zeros, scales = random_case(77 + M, M, K, N, G, False)
+    _, Y16 = oracle_case(X, codes, zeros, scales, G)
+    layer = device_case(codes, zeros, scales, G)
+    assert_y_close(to_host_bits(binding.gemm(to_dev(X), layer)), Y16, f"gemm M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("entry", ["gemv", "gemm"])
+@pytest.mark.parametrize("K,N,G,sym", [(512, 512, 128, False), (256, 200, 8, False),
+                                       (1024, 136, 1024, True)])
+def test_onehot_rows_bit_exact(entry, K, N, G, sym):
+    """X row m = e_k(m): each output is one exact product, rounded once."""
+    _, codes, zeros, scales = random_case(5 + K, 1, K, N, G, sym)
+    W, _ = oracle_case(np.zeros((1, K), np.uint16), codes, zeros, scales, G)
+    ks = np.random.default_rng(K + N).choice(K, size=16, replace=False)
+    X = np.zeros((16, K), dtype=np.uint16)
+    X[np.arange(16), ks] = 0x3C00
+    layer = device_case(codes, zeros, scales, G)
+    y = to_host_bits(ENTRY[entry](to_dev(X), layer))
+    assert same_halves_up_to_zero_sign(y, W[ks])
+
+
+def test_gemm_identity_returns_weight():
+    """X = I_K through awq_gemm gives the whole dequantized matrix."""
+    K, N, G = 256, 136, 64
+    _, codes, zeros, scales = random_case(42, 1, K, N, G, False)
+    W, _ = oracle_case(np.zeros((1, K), np.uint16), codes, zeros, scales, G)
+    X = np.zeros((K, K), dtype=np.uint16)
+    X[np.arange(K), np.arange(K)] = 0x3C00
+    y = to_host_bits(binding.gemm(to_dev(X), device_case(codes, zeros, scales, G)))
+    assert same_halves_up_to_zero_sign(y, W)
+
+
+@pytest.mark.parametrize("entry,name", [("gemv", "decode_8b_gate"), ("gemv", "gate_up_m16"),
+                                        ("gemm", "prefill_out_proj")])
+def test_deterministic_and_power_of_two(entry, name):
+    """Two runs are bit-identical, and doubling X doubles Y bit for bit."""
+    X, _, _, _ = workload_host(name)
+    layer = device_layer(name)
+    xd = to_dev(X)
+    y1 = ENTRY[entry](xd, layer)
+    y2 = ENTRY[entry](xd, layer)
+    y3 = ENTRY[entry](xd * 2, layer)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    # fp16 rounding commutes with doubling except where the doubled value is
+    # still subnormal in fp16 (|Y| below 2^-14), so those outputs are skipped
+    normal = y1.float().abs() >= 2.0 ** -13
+    assert torch.equal((y1.float() * 2).half()[normal].view(torch.int16), y3[normal].view(torch.int16))
+
+
+def test_gemv_equals_gemm_on_decode_shape():
+    """Both entry points compute the same layer (within the bar of each other)."""
+    X, _, _, _ = workload_host("gate_up_m16")
+    layer = device_layer("gate_up_m16")
+    a = to_host_bits(binding.gemv(to_dev(X), layer))
+    b = to_host_bits(binding.gemm(to_dev(X), layer))
+    assert_y_close(a, b, "gemv vs gemm")
+
+
+@pytest.mark.parametrize("entry", ["gemv", "gemm"])
+def test_empty_batch(entry):
+    layer = device_layer("tiny")
+    x = torch.empty((0, 512), dtype=torch.float16, device="cuda")
+    y = ENTRY[entry](x, layer)
+    assert y.shape == (0, 512)
+
+
+def test_gemv_rejects_batches_above_16():
+    layer = device_layer("tiny")
+    x = torch.zeros((17, 512), dtype=torch.float16, device="cuda")
+    with pytest.raises(binding.AwqError) as e:
+        binding.gemv(x, layer)
+    assert e.value.status == 4
+
+
+def test_misaligned_pointer_is_rejected():
+    layer = device_layer("tiny")
+    buf = torch.zeros(512 + 8, dtype=torch.float16, device="cuda")
+    x = buf[1:513].view(1, 512)            # 2 bytes past a 16-byte boundary
+    with pytest.raises(binding.AwqError) as e:
+        binding.gemv(x, layer)
+    assert e.value.status == 3

@@ -39,8 +39,8 @@ MUTANTS = [
     ("matmul_drop_first_k", "for (int k = 0; k < K; ++k) {\n            double x", "for (int k = 1; k < K; ++k) {\n            double x", 0),
     ("matmul_drop_last_k", "for (int k = 0; k < K; ++k) {\n            double x", "for (int k = 0; k < K - 1; ++k) {\n            double x", 0),
     ("matmul_x_transposed", "X[(size_t)m * K + k]", "X[(size_t)k * M + m]", 0),
-    ("matmul_w_transposed", "acc[n] += x * oracle_h2d(wrow[n]);", "acc[n] += x * oracle_h2d(W[((size_t)n * K + k) % ((size_t)K * N)]);", 0),
-    ("matmul_fp32_accumulate", "acc[n] += x * oracle_h2d(wrow[n]);", "acc[n] = (float)(acc[n] + x * oracle_h2d(wrow[n]));", 0),
+    ("matmul_w_transposed", "acc[n] += x * wrow[n];", "acc[n] += x * Wd[((size_t)n * K + k) % ((size_t)K * N)];", 0),
+    ("matmul_fp32_accumulate", "acc[n] += x * wrow[n];", "acc[n] = (float)(acc[n] + x * wrow[n]);", 0),
     ("matmul_y_row_offset", "Y16[(size_t)m * N + n] = oracle_d2h(acc[n]);", "Y16[(size_t)m * N + n] = oracle_d2h(acc[(n + 1) % N]);", 0),
 ]
 

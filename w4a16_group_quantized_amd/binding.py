@@ -1,0 +1,173 @@
+"""Thin Python binding over libawq.so (C ABI of include/awq.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream; tensors must
+be contiguous, on the GPU, and of the dtypes below.  If the library has not
+been built, the first call raises -- there is no fallback path.
+
+Layout (see include/awq.h): qweight int32 [K/8][N], scales fp16 [K/G][N],
+qzeros int32 [K/G][N/8] or None (symmetric), x fp16 [M][K], y fp16 [M][N].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libawq.so")
+
+# Entry points declared in include/awq.h, in declaration order.
+ENTRY_POINTS = ("awq_status_string", "awq_pack", "awq_pack_zeros", "awq_dequant", "awq_gemv",
+                "awq_gemm")
+
+AWQ_SUCCESS = 0
+STATUS_NAMES = {0: "AWQ_SUCCESS", 1: "AWQ_ERROR_INVALID_VALUE", 2: "AWQ_ERROR_SHAPE",
+                3: "AWQ_ERROR_ALIGNMENT", 4: "AWQ_ERROR_UNSUPPORTED", 5: "AWQ_ERROR_HIP"}
+
+
+class AwqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class CLayer(ctypes.Structure):
+    """``awq_layer`` of include/awq.h."""
+
+    _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("qzeros", ctypes.c_void_p), ("K", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("group_size", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libawq.so and declare its signatures (raises if it is missing)."""
+    global _LIB
+    if _LIB is not None and path == LIBRARY:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m w4a16_group_quantized_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.awq_status_string.restype = ctypes.c_char_p
+    lib.awq_status_string.argtypes = [ctypes.c_int]
+    lib.awq_pack.restype = ctypes.c_int
+    lib.awq_pack.argtypes = [vp, vp, i32, i32, vp]
+    lib.awq_pack_zeros.restype = ctypes.c_int
+    lib.awq_pack_zeros.argtypes = [vp, vp, i32, i32, vp]
+    lib.awq_dequant.restype = ctypes.c_int
+    lib.awq_dequant.argtypes = [ctypes.POINTER(CLayer), vp, vp]
+    for name in ("awq_gemv", "awq_gemm"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, ctypes.POINTER(CLayer), vp, i32, vp]
+    if path == LIBRARY:
+        _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().awq_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != AWQ_SUCCESS:
+        raise AwqError(status, status_string(status))
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+@dataclass
+class Layer:
+    """One quantized linear layer resident on the GPU (logical weight W[K][N])."""
+
+    qweight: torch.Tensor            # int32 [K/8][N]
+    scales: torch.Tensor             # fp16  [K/G][N]
+    qzeros: torch.Tensor | None      # int32 [K/G][N/8] or None (symmetric)
+    K: int
+    N: int
+    group_size: int
+
+    def c_struct(self) -> CLayer:
+        return CLayer(_dev(self.qweight, torch.int32, "qweight"),
+                      _dev(self.scales, torch.float16, "scales"),
+                      None if self.qzeros is None else _dev(self.qzeros, torch.int32, "qzeros"),
+                      self.K, self.N, self.group_size)
+
+
+def pack(codes: torch.Tensor, stream=None) -> torch.Tensor:
+    """uint8 codes [K][N] -> int32 qweight [K/8][N]."""
+    K, N = codes.shape
+    out = torch.empty((K // 8, N), dtype=torch.int32, device=codes.device)
+    _check(load().awq_pack(_dev(codes, torch.uint8, "codes"), out.data_ptr(), K, N,
+                           _stream(stream)))
+    return out
+
+
+def pack_zeros(zeros: torch.Tensor, stream=None) -> torch.Tensor:
+    """uint8 zeros [K/G][N] -> int32 qzeros [K/G][N/8]."""
+    groups, N = zeros.shape
+    out = torch.empty((groups, N // 8), dtype=torch.int32, device=zeros.device)
+    _check(load().awq_pack_zeros(_dev(zeros, torch.uint8, "zeros"), out.data_ptr(), groups, N,
+                                 _stream(stream)))
+    return out
+
+
+def make_layer(codes: torch.Tensor, zeros: torch.Tensor | None, scales: torch.Tensor,
+               group_size: int, stream=None) -> Layer:
+    """Packs device codes/zeros (uint8) into a Layer; scales are fp16 [K/G][N]."""
+    K, N = codes.shape
+    qz = None if zeros is None else pack_zeros(zeros, stream)
+    return Layer(pack(codes, stream), scales, qz, K, N, group_size)
+
+
+def dequant(layer: Layer, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Exact fp16 W[K][N]."""
+    if out is None:
+        out = torch.empty((layer.K, layer.N), dtype=torch.float16, device=layer.qweight.device)
+    c = layer.c_struct()
+    _check(load().awq_dequant(ctypes.byref(c), _dev(out, torch.float16, "out"), _stream(stream)))
+    return out
+
+
+def _linear(fn_name: str, x: torch.Tensor, layer: Layer, out: torch.Tensor | None, stream):
+    M = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != layer.K:
+        raise ValueError(f"x must be [M][{layer.K}], got {tuple(x.shape)}")
+    if out is None:
+        out = torch.empty((M, layer.N), dtype=torch.float16, device=x.device)
+    elif tuple(out.shape) != (M, layer.N):
+        raise ValueError(f"out must be [{M}][{layer.N}], got {tuple(out.shape)}")
+    c = layer.c_struct()
+    _check(getattr(load(), fn_name)(_dev(x, torch.float16, "x"), ctypes.byref(c),
+                                    _dev(out, torch.float16, "out"), M, _stream(stream)))
+    return out
+
+
+def gemv(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=None):
+    """y = x @ dequant(layer) for 1 <= M <= 16 (decode)."""
+    return _linear("awq_gemv", x, layer, out, stream)
+
+
+def gemm(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=None):
+    """y = x @ dequant(layer) for any M (prefill / batches)."""
+    return _linear("awq_gemm", x, layer, out, stream)

@@ -1,0 +1,104 @@
+// C ABI of libawq (declared in include/awq.h): argument validation on the
+// host, then one launch on the caller's stream.  Validation runs before any
+// HIP call, so a rejected call touches neither the device nor the stream.
+#include "../../include/awq.h"
+
+#include <hip/hip_runtime.h>
+
+#include "awq_internal.h"
+
+namespace {
+
+constexpr long long kMaxElems = (1LL << 31) - 1;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+awq_status check_layer(const awq_layer *w) {
+    if (w == nullptr || w->qweight == nullptr || w->scales == nullptr)
+        return AWQ_ERROR_INVALID_VALUE;
+    const long long K = w->K, N = w->N, G = w->group_size;
+    if (K <= 0 || N <= 0 || G <= 0) return AWQ_ERROR_INVALID_VALUE;
+    if (K % 8 || N % 8 || G % 8 || K % G) return AWQ_ERROR_SHAPE;
+    if (K * N > kMaxElems) return AWQ_ERROR_SHAPE;  // the dequantized weight's element count
+    if (!aligned16(w->qweight) || !aligned16(w->scales) ||
+        (w->qzeros != nullptr && !aligned16(w->qzeros)))
+        return AWQ_ERROR_ALIGNMENT;
+    return AWQ_SUCCESS;
+}
+
+awq_status check_io(const uint16_t *x, const uint16_t *y, const awq_layer *w, int32_t M) {
+    if (M < 0) return AWQ_ERROR_INVALID_VALUE;
+    if (M == 0) return AWQ_SUCCESS;
+    if (x == nullptr || y == nullptr) return AWQ_ERROR_INVALID_VALUE;
+    if ((long long)M * w->K > kMaxElems || (long long)M * w->N > kMaxElems) return AWQ_ERROR_SHAPE;
+    if (!aligned16(x) || !aligned16(y)) return AWQ_ERROR_ALIGNMENT;
+    return AWQ_SUCCESS;
+}
+
+awq_status from_hip(hipError_t e) { return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char *awq_status_string(awq_status status) {
+    switch (status) {
+    case AWQ_SUCCESS: return "AWQ_SUCCESS";
+    case AWQ_ERROR_INVALID_VALUE: return "AWQ_ERROR_INVALID_VALUE: null pointer or non-positive size";
+    case AWQ_ERROR_SHAPE: return "AWQ_ERROR_SHAPE: K%8, N%8, G%8, K%G must be 0 and arrays below 2^31 elements";
+    case AWQ_ERROR_ALIGNMENT: return "AWQ_ERROR_ALIGNMENT: tensor pointers must be 16-byte aligned";
+    case AWQ_ERROR_UNSUPPORTED: return "AWQ_ERROR_UNSUPPORTED: outside this entry point (awq_gemv takes M <= 16)";
+    case AWQ_ERROR_HIP: return "AWQ_ERROR_HIP: the HIP runtime refused the launch";
+    }
+    return "AWQ_ERROR_UNKNOWN";
+}
+
+awq_status awq_pack(const uint8_t *codes, int32_t *qweight, int32_t K, int32_t N, void *stream) {
+    if (codes == nullptr || qweight == nullptr || K <= 0 || N <= 0) return AWQ_ERROR_INVALID_VALUE;
+    if (K % 8 || N % 8 || (long long)K * N > kMaxElems) return AWQ_ERROR_SHAPE;
+    if (!aligned16(codes) || !aligned16(qweight)) return AWQ_ERROR_ALIGNMENT;
+    return from_hip(awq::launch_pack(codes, qweight, K, N, as_stream(stream)));
+}
+
+awq_status awq_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int32_t groups, int32_t N,
+                          void *stream) {
+    if (zeros == nullptr || qzeros == nullptr || groups <= 0 || N <= 0)
+        return AWQ_ERROR_INVALID_VALUE;
+    if (N % 8 || (long long)groups * N > kMaxElems) return AWQ_ERROR_SHAPE;
+    if (!aligned16(zeros) || !aligned16(qzeros)) return AWQ_ERROR_ALIGNMENT;
+    return from_hip(awq::launch_pack_zeros(zeros, qzeros, groups, N, as_stream(stream)));
+}
+
+awq_status awq_dequant(const awq_layer *layer, uint16_t *w_out, void *stream) {
+    awq_status st = check_layer(layer);
+    if (st != AWQ_SUCCESS) return st;
+    if (w_out == nullptr) return AWQ_ERROR_INVALID_VALUE;
+    if (!aligned16(w_out)) return AWQ_ERROR_ALIGNMENT;
+    return from_hip(awq::launch_dequant(layer->qweight, layer->scales, layer->qzeros, w_out,
+                                        layer->K, layer->N, layer->group_size, as_stream(stream)));
+}
+
+awq_status awq_gemv(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
+                    void *stream) {
+    awq_status st = check_layer(layer);
+    if (st != AWQ_SUCCESS) return st;
+    st = check_io(x, y, layer, M);
+    if (st != AWQ_SUCCESS || M == 0) return st;
+    if (M > 16) return AWQ_ERROR_UNSUPPORTED;
+    return from_hip(awq::launch_gemv(x, layer->qweight, layer->scales, layer->qzeros, y, M,
+                                     layer->K, layer->N, layer->group_size, as_stream(stream)));
+}
+
+awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
+                    void *stream) {
+    awq_status st = check_layer(layer);
+    if (st != AWQ_SUCCESS) return st;
+    st = check_io(x, y, layer, M);
+    if (st != AWQ_SUCCESS || M == 0) return st;
+    return from_hip(awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
+                                     layer->K, layer->N, layer->group_size, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Device-side building blocks shared by the HIP kernels of libawq (gfx950).
+//
+// Packed layout (see include/awq.h): a 32-bit qweight word holds the codes of
+// eight consecutive k of one column, code j in bits 4j..4j+3; a qzeros word
+// holds the zero points of eight consecutive columns of one group.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+// fp16 whose bit pattern is 0x6400 | c has exponent 2^10 and ulp 1, so it is
+// exactly 1024 + c for any 4-bit c.  This turns nibbles into halves with one
+// AND-OR per two codes, no conversion instruction.
+constexpr uint32_t kBias1024x2 = 0x64006400u;
+constexpr uint32_t kNibblePairMask = 0x000F000Fu;
+
+// Splits a qweight word into four half2 registers
+//   p[j] = (1024 + q_j, 1024 + q_{j+4}),  j = 0..3.
+// The pairing (j, j+4) is the one the shift-and-mask yields for free; callers
+// feed the other operand in the same k order.
+__device__ __forceinline__ void unpack_biased(uint32_t w, uint32_t p[4]) {
+    p[0] = (w & kNibblePairMask) | kBias1024x2;
+    p[1] = ((w >> 4) & kNibblePairMask) | kBias1024x2;
+    p[2] = ((w >> 8) & kNibblePairMask) | kBias1024x2;
+    p[3] = ((w >> 12) & kNibblePairMask) | kBias1024x2;
+}
+
+__device__ __forceinline__ half2_t as_half2(uint32_t u) {
+    return __builtin_bit_cast(half2_t, u);
+}
+__device__ __forceinline__ uint32_t as_u32(half2_t h) {
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Exact dequantization of a biased pair: (1024+q) - (1024+z) is the exact small
+// integer q - z, and the single fp16 multiply by s rounds once to nearest even,
+// so each half equals fp16_rne(s * (q - z)).
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t p, half2_t bz2, half2_t s2) {
+    return as_u32((as_half2(p) - bz2) * s2);
+}
+
+// (lo(a), lo(b)) and (hi(a), hi(b)) as one 32-bit half2 each.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+    return (a & 0xFFFFu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+    return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+// Pairs in (j, j+4) order -> eight halves in natural k order (as four dwords).
+__device__ __forceinline__ uint4 pairs_to_natural(const uint32_t d[4]) {
+    uint4 n;
+    n.x = pack_lo(d[0], d[1]);  // (w0, w1)
+    n.y = pack_lo(d[2], d[3]);  // (w2, w3)
+    n.z = pack_hi(d[0], d[1]);  // (w4, w5)
+    n.w = pack_hi(d[2], d[3]);  // (w6, w7)
+    return n;
+}
+
+// Eight halves in natural k order -> (j, j+4) pair order, the inverse of the above.
+__device__ __forceinline__ uint4 natural_to_pairs(uint4 x) {
+    uint4 a;
+    a.x = pack_lo(x.x, x.z);  // (x0, x4)
+    a.y = pack_hi(x.x, x.z);  // (x1, x5)
+    a.z = pack_lo(x.y, x.w);  // (x2, x6)
+    a.w = pack_hi(x.y, x.w);  // (x3, x7)
+    return a;
+}
+
+// Exact dequantization of one qweight word to eight halves in natural k order.
+// bz = 1024 + zero as fp16, s = scale.
+__device__ __forceinline__ uint4 dequant_word_natural(uint32_t w, half_t bz, half_t s) {
+    uint32_t p[4], d[4];
+    unpack_biased(w, p);
+    const half2_t bz2 = {bz, bz};
+    const half2_t s2 = {s, s};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = dequant_pair(p[j], bz2, s2);
+    return pairs_to_natural(d);
+}
+
+// 1024 + z as fp16, from the 4-bit zero point z.
+__device__ __forceinline__ half_t biased_zero(uint32_t z) {
+    return __builtin_bit_cast(half_t, (uint16_t)(0x6400u | (z & 0xFu)));
+}
+
+__device__ __forceinline__ half_t as_half(uint16_t u) {
+    return __builtin_bit_cast(half_t, u);
+}
+__device__ __forceinline__ uint16_t as_u16(half_t h) {
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ half8_t as_half8(uint4 u) {
+    return __builtin_bit_cast(half8_t, u);
+}
+
+}  // namespace awq

@@ -1,0 +1,22 @@
+// Host-side launchers behind the C ABI of include/awq.h.  Arguments reach them
+// already validated (shapes, alignment, non-null pointers, M >= 1).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+hipError_t launch_pack(const uint8_t *codes, int32_t *qweight, int K, int N, hipStream_t s);
+hipError_t launch_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int groups, int N,
+                             hipStream_t s);
+hipError_t launch_dequant(const int32_t *qweight, const uint16_t *scales, const int32_t *qzeros,
+                          uint16_t *w, int K, int N, int G, hipStream_t s);
+hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                       const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
+                       hipStream_t s);
+hipError_t launch_gemm(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                       const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
+                       hipStream_t s);
+
+}  // namespace awq
