@@ -22,15 +22,28 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 constexpr uint32_t kBias1024x2 = 0x64006400u;
 constexpr uint32_t kNibblePairMask = 0x000F000Fu;
 
+// The nibble-pair mask in a vector register that the optimizer cannot see
+// through.  gfx9 VOP3 encodings take no literal constants and read at most one
+// scalar register, so with both constants visible the compiler splits
+// (x & mask) | bias into two literal-carrying VOP2 instructions; with the mask
+// in a vector register it emits a single v_and_or_b32 (bias in a scalar
+// register).  Call once per kernel, outside the loops.
+__device__ __forceinline__ uint32_t nibble_mask_vgpr() {
+    uint32_t v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(kNibblePairMask));
+    return v;
+}
+
 // Splits a qweight word into four half2 registers
-//   p[j] = (1024 + q_j, 1024 + q_{j+4}),  j = 0..3.
-// The pairing (j, j+4) is the one the shift-and-mask yields for free; callers
-// feed the other operand in the same k order.
-__device__ __forceinline__ void unpack_biased(uint32_t w, uint32_t p[4]) {
-    p[0] = (w & kNibblePairMask) | kBias1024x2;
-    p[1] = ((w >> 4) & kNibblePairMask) | kBias1024x2;
-    p[2] = ((w >> 8) & kNibblePairMask) | kBias1024x2;
-    p[3] = ((w >> 12) & kNibblePairMask) | kBias1024x2;
+//   p[j] = (1024 + q_j, 1024 + q_{j+4}),  j = 0..3,
+// with three shifts and four AND-ORs.  The pairing (j, j+4) is the one the
+// shift-and-mask yields for free; callers feed the other operand in the same
+// k order.  `mask` is kNibblePairMask (see nibble_mask_vgpr).
+__device__ __forceinline__ void unpack_biased(uint32_t w, uint32_t mask, uint32_t p[4]) {
+    p[0] = (w & mask) | kBias1024x2;
+    p[1] = ((w >> 4) & mask) | kBias1024x2;
+    p[2] = ((w >> 8) & mask) | kBias1024x2;
+    p[3] = ((w >> 12) & mask) | kBias1024x2;
 }
 
 __device__ __forceinline__ half2_t as_half2(uint32_t u) {
@@ -76,10 +89,11 @@ __device__ __forceinline__ uint4 natural_to_pairs(uint4 x) {
 }
 
 // Exact dequantization of one qweight word to eight halves in natural k order.
-// bz = 1024 + zero as fp16, s = scale.
-__device__ __forceinline__ uint4 dequant_word_natural(uint32_t w, half_t bz, half_t s) {
+// bz = 1024 + zero as fp16, s = scale, mask = kNibblePairMask.
+__device__ __forceinline__ uint4 dequant_word_natural(uint32_t w, uint32_t mask, half_t bz,
+                                                      half_t s) {
     uint32_t p[4], d[4];
-    unpack_biased(w, p);
+    unpack_biased(w, mask, p);
     const half2_t bz2 = {bz, bz};
     const half2_t s2 = {s, s};
 #pragma unroll

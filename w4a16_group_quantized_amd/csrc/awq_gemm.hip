@@ -44,6 +44,7 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const int n0 = (int)(blockIdx.x % tiles_n) * BN;
     const int KR = K / 8;
     const int KT = (K + BK - 1) / BK;
+    const uint32_t nmask = nibble_mask_vgpr();
 
     uint4 a_reg[ACH];
     uint4 q_reg[BCH];
@@ -95,7 +96,7 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
                                     (uint16_t)s_reg[i].y, (uint16_t)(s_reg[i].y >> 16)};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint4 w = b_ok[i] ? dequant_word_natural(qs[j], biased_zero(z_reg[i] >> (4 * j)),
+                const uint4 w = b_ok[i] ? dequant_word_natural(qs[j], nmask, biased_zero(z_reg[i] >> (4 * j)),
                                                                as_half(ss[j]))
                                         : make_uint4(0u, 0u, 0u, 0u);
                 *reinterpret_cast<uint4 *>(&Bs[buf][(nl + j) * LDB + kq * 8]) = w;

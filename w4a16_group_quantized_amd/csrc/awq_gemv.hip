@@ -4,34 +4,41 @@
 // paragraph: INT4 weights dequantized on the fly, fp16 weights never written).
 //
 // Bound: HBM.  Every packed weight byte is read exactly once per call, in
-// 16-byte coalesced loads; scales and zero points once per group; X and Y are
-// small.  Work per packed word must stay below ~20 vector ALU lane-ops for the
-// vector units to keep up with 8 TB/s, so the kernel avoids converting codes to
-// weights one by one:
+// coalesced 16-byte loads; scales and zero points once per group; X and Y are
+// small.  Two things decide the speed:
 //
-//  * nibbles become fp16 (1024 + q) with one AND-OR per two codes;
-//  * the multiply runs on the matrix cores (v_mfma_f32_16x16x32_f16): one
-//    packed word is exactly one lane's B operand (8 k of one column), and the
-//    rows of X (up to 16) fill the A operand, so M = 1 and M = 16 cost the same
-//    ALU work per weight;
-//  * a fifth MFMA against an all-ones B gives sum_k x over the same k, so a
-//    segment of L k (L divides G) yields
-//        C = sum_k x (1024 + q),  Csum = sum_k x
-//    and the segment's contribution is s * (C - (1024 + z) * Csum), i.e.
-//    s * sum_k x (q - z), applied once per segment with two FMAs per output.
-//    Group sizes that are not a multiple of 32 take the exact path instead:
-//    each word is dequantized to fp16 bit-exactly and multiplied directly.
+// 1. Bytes in flight.  A 30 MB weight streams in ~4 us at 8 TB/s, barely more
+//    than a few memory latencies, so each wave issues the loads of all its
+//    packed rows (UNR segments) before it uses any of them, and there is no
+//    branch between the loads (out-of-range lanes read a clamped, in-bounds
+//    address and their results are dropped at the end).
+//
+// 2. ALU work per packed word.  At 8 TB/s the vector units have ~20 lane-ops
+//    per 32-bit word, so codes are never converted to weights one by one:
+//    * nibbles become fp16 (1024 + q) with one AND-OR per two codes;
+//    * the multiply runs on the matrix cores (v_mfma_f32_16x16x32_f16): one
+//      packed word is exactly one lane's B operand (8 k of one column) and the
+//      rows of X fill the A operand, so M = 1 and M = 16 cost the same ALU
+//      work per weight (A rows beyond M repeat row M-1 and are never stored);
+//    * a further MFMA against an all-ones B gives sum_k x over the same k, so
+//      a segment of L consecutive k inside one group yields
+//          C = sum_k x (1024 + q),  Csum = sum_k x,
+//      and adds s * (C - (1024 + z) Csum) = s * sum_k x (q - z) with two FMAs
+//      per output.  Group sizes that are not a multiple of 32 take the exact
+//      path instead, which dequantizes every word bit-exactly first.
 //
 // Tiling: one workgroup owns TN = 16 * WPL output columns and all of K.  Each
-// lane loads WPL consecutive words (columns) of one packed row; lanes 16j..16j+15
-// take packed row 4t + j of step t, so one step covers 32 k.  The NW waves of
-// the workgroup take interleaved segments of K; their fp32 partial sums are
-// added in LDS in a fixed order (deterministic) and written as fp16.
+// lane loads WPL consecutive words (columns) of one packed row; lanes
+// 16j..16j+15 take packed row 4t + j of step t, so a step covers 32 k.  The NW
+// waves split K into contiguous ranges; their fp32 partial sums are added in
+// LDS in a fixed order (deterministic) and written as fp16.  Small X (up to
+// 32 KB) is staged in LDS once per workgroup, already in the (j, j+4) k order
+// of the unpacked pairs; larger X is read from L2 per step.
 #include "awq_device.h"
 #include "awq_internal.h"
 
 namespace awq {
-namespace {
+namespace gemv {
 
 template <int WPL>
 struct Words {
@@ -42,15 +49,17 @@ template <int WPL>
 __device__ __forceinline__ Words<WPL> load_words(const uint32_t *p) {
     Words<WPL> r;
     if constexpr (WPL == 1) {
-        r.w[0] = p[0];
+        r.w[0] = __builtin_nontemporal_load(p);
     } else if constexpr (WPL == 2) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(p);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
         r.w[0] = v.x;
         r.w[1] = v.y;
     } else {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int i = 0; i < WPL / 4; ++i) {
-            const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
             r.w[4 * i + 0] = v.x;
             r.w[4 * i + 1] = v.y;
             r.w[4 * i + 2] = v.z;
@@ -60,137 +69,251 @@ __device__ __forceinline__ Words<WPL> load_words(const uint32_t *p) {
     return r;
 }
 
-// WPL consecutive fp16 scales as floats.
-template <int WPL>
-__device__ __forceinline__ void load_scales(const uint16_t *p, float s[WPL]) {
-#pragma unroll
-    for (int i = 0; i < WPL; ++i) s[i] = (float)as_half(p[i]);
+// Buffer descriptor over [base, base + bytes): raw (unstructured) access, the
+// offsets split into a per-lane part (VGPR) and a wave-uniform part (SGPR), so
+// no per-load 64-bit address arithmetic is needed.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ half8_t mfma_b(const uint32_t p[4]) {
+template <int WPL>
+__device__ __forceinline__ Words<WPL> buffer_words(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    Words<WPL> r;
+    if constexpr (WPL == 1) {
+        r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+    } else if constexpr (WPL == 2) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+        r.w[0] = v.x;
+        r.w[1] = v.y;
+    } else {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int i = 0; i < WPL / 4; ++i) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * i, soff, 0);
+            r.w[4 * i + 0] = v.x;
+            r.w[4 * i + 1] = v.y;
+            r.w[4 * i + 2] = v.z;
+            r.w[4 * i + 3] = v.w;
+        }
+    }
+    return r;
+}
+
+// WPL consecutive fp16 scales, packed two per dword.
+template <int WPL>
+struct Scales {
+    uint32_t h[(WPL + 1) / 2];
+};
+
+template <int WPL>
+__device__ __forceinline__ Scales<WPL> load_scales(const uint16_t *p) {
+    Scales<WPL> r;
+    if constexpr (WPL == 1) {
+        r.h[0] = p[0];
+    } else if constexpr (WPL == 2) {
+        r.h[0] = *reinterpret_cast<const uint32_t *>(p);
+    } else if constexpr (WPL == 4) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(p);
+        r.h[0] = v.x;
+        r.h[1] = v.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < WPL / 8; ++i) {
+            const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+            r.h[4 * i + 0] = v.x;
+            r.h[4 * i + 1] = v.y;
+            r.h[4 * i + 2] = v.z;
+            r.h[4 * i + 3] = v.w;
+        }
+    }
+    return r;
+}
+
+template <int WPL>
+__device__ __forceinline__ Scales<WPL> buffer_scales(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    Scales<WPL> r;
+    if constexpr (WPL == 1) {
+        r.h[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0);
+    } else if constexpr (WPL == 2) {
+        r.h[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+    } else if constexpr (WPL == 4) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+        r.h[0] = v.x;
+        r.h[1] = v.y;
+    } else {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int i = 0; i < WPL / 8; ++i) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * i, soff, 0);
+            r.h[4 * i + 0] = v.x;
+            r.h[4 * i + 1] = v.y;
+            r.h[4 * i + 2] = v.z;
+            r.h[4 * i + 3] = v.w;
+        }
+    }
+    return r;
+}
+
+template <int WPL>
+__device__ __forceinline__ float scale_at(const Scales<WPL> &s, int i) {
+    return (float)as_half((uint16_t)(s.h[i / 2] >> (16 * (i % 2))));
+}
+
+__device__ __forceinline__ half8_t as_b(const uint32_t p[4]) {
     return as_half8(make_uint4(p[0], p[1], p[2], p[3]));
 }
 
-template <int WPL, int NW, bool FOLD>
+// The A operand of one step: row xrow of X, packed row r (k = 8r .. 8r+7).
+template <bool XLDS>
+__device__ __forceinline__ half8_t load_a(const uint16_t *__restrict__ X, const uint4 *xs, int xrow,
+                                         int K, int r) {
+    if constexpr (XLDS) return as_half8(xs[xrow * (K / 8) + r]);
+    else return as_half8(natural_to_pairs(
+             reinterpret_cast<const uint4 *>(X + (size_t)xrow * K)[r]));
+}
+
+// The loads of one segment (SEGR packed rows of WPL columns), held in registers.
+template <int WPL, int STEPS>
+struct Seg {
+    Words<WPL> q[STEPS];
+    Scales<WPL> sc;
+    uint32_t zw;
+};
+
+// X up to this many bytes is staged in LDS (with the reduction buffer the
+// workgroup stays within 64 KB of LDS).
+constexpr size_t kXLdsBytes = 32 * 1024;
+
+// Live rows of the 16x16 MFMA output per lane: lane (kb, c16) holds rows
+// 4 kb + v, v < 4, and rows at or beyond M are never stored, so for M = 1 and
+// M = 2 only v < M needs the per-segment correction.
+constexpr int live_rows(int M) { return M >= 3 ? 4 : M; }
+
+// Folded path: G is a multiple of 32; SEGR packed rows (8 * SEGR k) per segment,
+// SEGR a multiple of 4 dividing G / 8.  The NW waves split the nseg segments of
+// K evenly (the launcher makes nseg a multiple of NW and the per-wave count a
+// multiple of D).  Each wave keeps D segments in flight: the loads of segment
+// s + D are issued right after segment s has been multiplied, into the
+// registers it freed.  Every load is unconditional, so the compiler can count
+// outstanding loads exactly and wait for the oldest segment only.
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool XLDS>
 __global__ void __launch_bounds__(NW * 64)
-gemv_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
+fold_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
-            uint16_t *__restrict__ Y, int M, int K, int N, int G, int seg_rows) {
+            uint16_t *__restrict__ Y, int M, int K, int N, int G) {
     constexpr int TN = 16 * WPL;
-    extern __shared__ float red[];  // [NW][M][TN]
+    constexpr int STEPS = SEGR / 4;
+    constexpr int XMAX = (int)(kXLdsBytes / 16) / (NW * 64);   // X chunks per thread
+    extern __shared__ __attribute__((aligned(16))) uint4 lds[];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int c16 = lane & 15;   // column block (B) / row of X (A) / column of C
-    const int kb = lane >> 4;    // which of the 4 packed rows of a step
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c16 = lane & 15;   // column block of B, row of A, column of C
+    const int kb = lane >> 4;    // which packed row of a step
     const int n0 = blockIdx.x * TN;
     const int ncol = n0 + WPL * c16;
-    const bool col_ok = ncol < N;
-    const bool row_ok = c16 < M;
+    const int ncl = ncol < N ? ncol : N - WPL;   // clamped: in bounds, result dropped
+    const int xrow = c16 < M ? c16 : M - 1;      // clamped: row never stored
     const int KR = K / 8;
+    const int per = KR / SEGR / NW;              // segments per wave, a multiple of D
+    const int s_begin = wave * per;
 
-    const uint32_t *Qc = Q + ncol;
-    const uint16_t *Xr = X + (size_t)c16 * K;
+    // Lane offsets (column, row within the step) in VGPRs; row and group
+    // offsets, which are wave-uniform, in SGPRs.
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, (uint32_t)KR * (uint32_t)N * 4u);
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(S, (uint32_t)(K / G) * (uint32_t)N * 2u);
+    const __amdgpu_buffer_rsrc_t zrs = make_rsrc(QZ, SYM ? 0u : (uint32_t)(K / G) * (uint32_t)N / 2u);
+    const int qvoff = (ncl + kb * N) * 4;
+    const int svoff = ncl * 2;
+    const int zvoff = (ncl / 8) * 4;
+    const int zshift = 4 * (ncl % 8);
+    const int xchunks = XLDS ? M * (K / 8) : 0;
+    float *red = reinterpret_cast<float *>(lds + xchunks);
+    const uint4 *xs = lds;
 
-    float acc[WPL][4];
+    auto load_seg = [&](int seg, Seg<WPL, STEPS> &b) {
+        const int r0 = seg * SEGR;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st)
+            b.q[st] = buffer_words<WPL>(qrs, qvoff, (r0 + 4 * st) * N * 4);
+        const int g = (8 * r0) / G;
+        b.sc = buffer_scales<WPL>(srs, svoff, g * N * 2);
+        if constexpr (!SYM) b.zw = __builtin_amdgcn_raw_buffer_load_b32(zrs, zvoff, g * (N / 8) * 4, 0);
+    };
+
+    const half8_t ones = as_half8(make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
+    const uint32_t nmask = nibble_mask_vgpr();
+    float acc[WPL][VR];
 #pragma unroll
     for (int i = 0; i < WPL; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][v] = 0.f;
+        for (int v = 0; v < VR; ++v) acc[i][v] = 0.f;
 
-    if constexpr (FOLD) {
-        const half8_t ones = as_half8(make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
-        const int nseg = KR / seg_rows;
-        for (int seg = wave; seg < nseg; seg += NW) {
-            const int r0 = seg * seg_rows;
-            const int g = (8 * r0) / G;
-            float s[WPL], bz[WPL];
-            if (col_ok) {
-                load_scales<WPL>(S + (size_t)g * N + ncol, s);
-                const uint32_t zw = QZ ? QZ[(size_t)g * (N / 8) + ncol / 8] >> (4 * (ncol % 8))
-                                       : 0x88888888u;
-#pragma unroll
-                for (int i = 0; i < WPL; ++i) bz[i] = 1024.f + (float)((zw >> (4 * i)) & 0xFu);
-            } else {
-#pragma unroll
-                for (int i = 0; i < WPL; ++i) s[i] = bz[i] = 0.f;
-            }
-            float4_t C[WPL];
-#pragma unroll
-            for (int i = 0; i < WPL; ++i) C[i] = float4_t{0.f, 0.f, 0.f, 0.f};
-            float4_t Cs = {0.f, 0.f, 0.f, 0.f};
-            for (int st = 0; st < seg_rows; st += 4) {
-                const int r = r0 + st + kb;
-                Words<WPL> q;
-                if (col_ok) q = load_words<WPL>(Qc + (size_t)r * N);
-                else
-#pragma unroll
-                    for (int i = 0; i < WPL; ++i) q.w[i] = 0u;
-                uint4 xa = make_uint4(0u, 0u, 0u, 0u);
-                if (row_ok) xa = *reinterpret_cast<const uint4 *>(Xr + 8 * r);
-                const half8_t a = as_half8(natural_to_pairs(xa));
-#pragma unroll
-                for (int i = 0; i < WPL; ++i) {
-                    uint32_t p[4];
-                    unpack_biased(q.w[i], p);
-                    C[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, mfma_b(p), C[i], 0, 0, 0);
-                }
-                Cs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, Cs, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < WPL; ++i)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    acc[i][v] = __builtin_fmaf(s[i], __builtin_fmaf(-bz[i], Cs[v], C[i][v]), acc[i][v]);
-        }
-    } else {
-        // Exact path: each word dequantized bit-exactly, then multiplied.
+    auto compute_seg = [&](int seg, const Seg<WPL, STEPS> &b) {
+        const int r0 = seg * SEGR;
         float4_t C[WPL];
 #pragma unroll
         for (int i = 0; i < WPL; ++i) C[i] = float4_t{0.f, 0.f, 0.f, 0.f};
-        const int nstep = (KR + 3) / 4;
-        for (int st = wave; st < nstep; st += NW) {
-            const int r = 4 * st + kb;
-            const bool r_ok = r < KR;
-            uint4 xa = make_uint4(0u, 0u, 0u, 0u);
-            if (row_ok && r_ok) xa = *reinterpret_cast<const uint4 *>(Xr + 8 * r);
-            const half8_t a = as_half8(natural_to_pairs(xa));
-            uint32_t d[WPL][4];
-            if (col_ok && r_ok) {
-                const Words<WPL> q = load_words<WPL>(Qc + (size_t)r * N);
-                const int g = (8 * r) / G;
-                const uint32_t zw = QZ ? QZ[(size_t)g * (N / 8) + ncol / 8] >> (4 * (ncol % 8))
-                                       : 0x88888888u;
-                const uint16_t *sp = S + (size_t)g * N + ncol;
+        float4_t Cs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < WPL; ++i) {
-                    const half_t bz = biased_zero(zw >> (4 * i));
-                    const half_t sv = as_half(sp[i]);
-                    const half2_t bz2 = {bz, bz}, s2 = {sv, sv};
-                    uint32_t p[4];
-                    unpack_biased(q.w[i], p);
+        for (int st = 0; st < STEPS; ++st) {
+            const half8_t a = load_a<XLDS>(X, xs, xrow, K, r0 + 4 * st + kb);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) d[i][j] = dequant_pair(p[j], bz2, s2);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < WPL; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) d[i][j] = 0u;
+            for (int i = 0; i < WPL; ++i) {
+                uint32_t p[4];
+                unpack_biased(b.q[st].w[i], nmask, p);
+                C[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_b(p), C[i], 0, 0, 0);
             }
-#pragma unroll
-            for (int i = 0; i < WPL; ++i)
-                C[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, mfma_b(d[i]), C[i], 0, 0, 0);
+            Cs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, Cs, 0, 0, 0);
         }
+        const uint32_t zw = SYM ? 0u : b.zw >> zshift;
 #pragma unroll
-        for (int i = 0; i < WPL; ++i)
+        for (int i = 0; i < WPL; ++i) {
+            const float s = scale_at<WPL>(b.sc, i);
+            const float bz = SYM ? 1032.f : 1024.f + (float)((zw >> (4 * i)) & 0xFu);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[i][v] = C[i][v];
+            for (int v = 0; v < VR; ++v)
+                acc[i][v] = __builtin_fmaf(s, __builtin_fmaf(-bz, Cs[v], C[i][v]), acc[i][v]);
+        }
+    };
+
+    // X loads first (clamped, so unconditional), then the first D segments: X
+    // (an L2 hit) arrives while the weight loads are still in flight.
+    Seg<WPL, STEPS> b[D];
+    uint4 xr[XMAX > 0 ? XMAX : 1];
+    if constexpr (XLDS) {
+#pragma unroll
+        for (int j = 0; j < XMAX; ++j) {
+            const int c = threadIdx.x + j * NW * 64;
+            xr[j] = reinterpret_cast<const uint4 *>(X)[c < xchunks ? c : 0];
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_seg(s_begin + d, b[d]);
+    if constexpr (XLDS) {
+#pragma unroll
+        for (int j = 0; j < XMAX; ++j) {
+            const int c = threadIdx.x + j * NW * 64;
+            if (c < xchunks) lds[c] = natural_to_pairs(xr[j]);
+        }
+        __syncthreads();
     }
 
-    // C layout of the 16x16 MFMA: lane (kb, c16) holds rows 4*kb + v, column c16.
+    for (int i = 0; i < per - D; i += D) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+        for (int d = 0; d < D; ++d) {
+            compute_seg(s_begin + i + d, b[d]);
+            load_seg(s_begin + i + d + D, b[d]);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) compute_seg(s_begin + per - D + d, b[d]);
+
+    // C layout of the 16x16 MFMA: lane (kb, c16) holds rows 4 kb + v of column c16.
+#pragma unroll
+    for (int v = 0; v < VR; ++v) {
         const int m = 4 * kb + v;
         if (m < M)
 #pragma unroll
@@ -207,31 +330,439 @@ gemv_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     }
 }
 
-template <int WPL, int NW, bool FOLD>
-hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
-                  uint16_t *y, int M, int K, int N, int G, int seg_rows, hipStream_t s) {
+// ---------------------------------------------------------------------------
+// Small batches (M <= 4), the decode case.
+//
+// Each wave stages the rows of X that its K range needs in its own LDS slice
+// (no workgroup barrier), each 8-k chunk already in the k order of the
+// unpacked weights, with the odd k divided by 16 (exact in fp16 above 2^-10):
+//     A chunk = (x0, x4, x1/16, x5/16, x2, x6, x3/16, x7/16).
+// That lets one shift and four AND-ORs unpack a word:
+//     (w & 0x000F000F)      | bias = (1024 + q0,    1024 + q4)
+//     (w & 0x00F000F0)      | bias = (1024 + 16 q1, 1024 + 16 q5)
+//     (w>>8 & 0x000F000F)   | bias = (1024 + q2,    1024 + q6)
+//     (w>>8 & 0x00F000F0)   | bias = (1024 + 16 q3, 1024 + 16 q7)
+// and the products against A come out as x_j (1024 + q_j) for even k and
+// (x_j / 16)(1024 + 16 q_j) = 64 x_j + x_j q_j for odd k.  With
+//     U = 1024 * sum_k a_k   (a_k the staged A values)
+//     S = sum_even x + 16 * sum_odd (x/16)   (= sum_k x)
+// a group's MFMA sum C gives sum_k x (q - z) = C - U - z S.  U and S per row
+// and segment are computed once, while staging, so no MFMA is spent on them.
+// ---------------------------------------------------------------------------
+
+constexpr uint32_t kSixteenthX2 = 0x2C002C00u;   // (1/16, 1/16) in fp16
+constexpr uint32_t kHighNibblePairMask = 0x00F000F0u;
+
+__device__ __forceinline__ uint32_t high_mask_vgpr() {
+    uint32_t v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(kHighNibblePairMask));
+    return v;
+}
+
+__device__ __forceinline__ void unpack_biased16(uint32_t w, uint32_t lo_mask, uint32_t hi_mask,
+                                                uint32_t p[4]) {
+    const uint32_t w8 = w >> 8;
+    p[0] = (w & lo_mask) | kBias1024x2;
+    p[1] = (w & hi_mask) | kBias1024x2;
+    p[2] = (w8 & lo_mask) | kBias1024x2;
+    p[3] = (w8 & hi_mask) | kBias1024x2;
+}
+
+// Natural-order chunk of X -> staged A chunk (see above).
+__device__ __forceinline__ uint4 stage_chunk(uint4 x) {
+    uint4 a = natural_to_pairs(x);
+    a.y = as_u32(as_half2(a.y) * as_half2(kSixteenthX2));
+    a.w = as_u32(as_half2(a.w) * as_half2(kSixteenthX2));
+    return a;
+}
+
+template <int WPL, int STEPS, bool SYM>
+struct WSeg {
+    Words<WPL> q[STEPS];
+    Scales<WPL> sc;
+    uint32_t zw;
+};
+
+// Chunks of staged X per lane, at most.
+constexpr int kStageChunks = 4;
+
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1>
+__global__ void __launch_bounds__(NW * 64)
+stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
+              const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
+              uint16_t *__restrict__ Y, int M, int K, int N, int G) {
     constexpr int TN = 16 * WPL;
-    const dim3 grid((N + TN - 1) / TN);
-    const size_t lds = (size_t)NW * M * TN * sizeof(float);
-    hipLaunchKernelGGL((gemv_kernel<WPL, NW, FOLD>), grid, dim3(NW * 64), lds, s, x,
-                       reinterpret_cast<const uint32_t *>(qw), sc,
-                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G, seg_rows);
+    constexpr int STEPS = SEGR / 4;
+    extern __shared__ __attribute__((aligned(16))) uint4 lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c16 = lane & 15;   // column block of B, row of A, column of C
+    const int kb = lane >> 4;    // packed row within a step; C rows 4 kb .. 4 kb + 3
+    const int n0 = blockIdx.x * TN;
+    const int ncol = n0 + WPL * c16;
+    const int ncl = ncol < N ? ncol : N - WPL;   // clamped: in bounds, result dropped
+    const int KR = K / 8;
+    const int per = KR / SEGR / NW;              // segments per wave (multiple of D)
+    const int rows_w = per * SEGR;               // packed rows per wave
+    const int r_begin = wave * rows_w;
+    const int spg = G / (8 * SEGR);              // segments per group
+
+    // LDS: staged X slices (all waves), then (U, S) tables, then the reduction.
+    uint4 *xs = lds + wave * (M * rows_w);
+    float2 *tabs = reinterpret_cast<float2 *>(lds + M * KR);
+    float2 *tab = tabs + wave * (M * per);
+    float *red = reinterpret_cast<float *>(tabs + NW * M * per);
+
+    const int xrow = c16 < M ? c16 : M - 1;      // A row of this lane (clamped)
+    const uint32_t lane_q = (uint32_t)(ncl + kb * N);
+
+    // Scale and zero of one segment; loads of one segment.
+    auto load_seg = [&](int seg, WSeg<WPL, STEPS, SYM> &b) {
+        const int r0 = seg * SEGR;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const uint32_t *qrow = Q + (size_t)(r0 + 4 * st) * N;   // wave-uniform
+            b.q[st] = load_words<WPL>(qrow + lane_q);
+        }
+        const int g = (8 * r0) / G;
+        b.sc = load_scales<WPL>(S + (size_t)g * N + ncl);
+        if constexpr (!SYM) b.zw = QZ[(size_t)g * (N / 8) + ncl / 8];
+    };
+
+    // 1. X loads (clamped, unconditional), 2. the first D segments, 3. staging.
+    const int chunks_w = M * rows_w;
+    uint4 xr[kStageChunks];
+#pragma unroll
+    for (int j = 0; j < kStageChunks; ++j) {
+        const int c = lane + 64 * j;
+        const int cc = c < chunks_w ? c : 0;
+        const int m = cc / rows_w;
+        xr[j] = reinterpret_cast<const uint4 *>(X)[(size_t)m * KR + r_begin + cc % rows_w];
+    }
+    WSeg<WPL, STEPS, SYM> b[D];
+    const int s_begin = wave * per;
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_seg(s_begin + d, b[d]);
+
+#pragma unroll
+    for (int j = 0; j < kStageChunks; ++j) {
+        const int c = lane + 64 * j;
+        const uint4 a = stage_chunk(xr[j]);
+        const half2_t one2 = {(half_t)1.0f, (half_t)1.0f};
+        const float lo = __builtin_amdgcn_fdot2(as_half2(a.x), one2,
+                         __builtin_amdgcn_fdot2(as_half2(a.z), one2, 0.f, false), false);
+        const float hi = __builtin_amdgcn_fdot2(as_half2(a.y), one2,
+                         __builtin_amdgcn_fdot2(as_half2(a.w), one2, 0.f, false), false);
+        float t = c < chunks_w ? lo + hi : 0.f;          // sum of the staged values
+        float u = c < chunks_w ? lo + 16.f * hi : 0.f;   // sum of x
+        // segment sums over aligned groups of SEGR lanes (consecutive chunks)
+#pragma unroll
+        for (int o = 1; o < SEGR; o <<= 1) {
+            t += __shfl_xor(t, o, 64);
+            u += __shfl_xor(u, o, 64);
+        }
+        if (c < chunks_w) {
+            xs[c] = a;
+            if (c % SEGR == 0) {
+                const int m = c / rows_w;
+                tab[m * per + (c % rows_w) / SEGR] = make_float2(1024.f * t, u);
+            }
+        }
+    }
+    // Only this wave reads its slice; LDS operations of one wave execute in order.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const uint32_t lo_mask = nibble_mask_vgpr();
+    const uint32_t hi_mask = high_mask_vgpr();
+    float acc[WPL][VR];
+#pragma unroll
+    for (int i = 0; i < WPL; ++i)
+#pragma unroll
+        for (int v = 0; v < VR; ++v) acc[i][v] = 0.f;
+    float4_t C[WPL];
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) C[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+    float Ug[VR], Sg[VR];
+#pragma unroll
+    for (int v = 0; v < VR; ++v) Ug[v] = Sg[v] = 0.f;
+
+    auto compute_seg = [&](int seg, const WSeg<WPL, STEPS, SYM> &bb) {
+        const int rl0 = (seg - s_begin) * SEGR;   // local packed row of the segment
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const half8_t a = as_half8(xs[xrow * rows_w + rl0 + 4 * st + kb]);
+#pragma unroll
+            for (int i = 0; i < WPL; ++i) {
+                uint32_t p[4];
+                unpack_biased16(bb.q[st].w[i], lo_mask, hi_mask, p);
+                C[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_b(p), C[i], 0, 0, 0);
+            }
+        }
+        // (U, S) of this segment for the lane's live C rows 4 kb + v (clamped).
+#pragma unroll
+        for (int v = 0; v < VR; ++v) {
+            const int m = min(4 * kb + v, M - 1);
+            const float2 us = tab[m * per + (seg - s_begin)];
+            Ug[v] += us.x;
+            Sg[v] += us.y;
+        }
+        const bool fold = GRP1 || (seg + 1) % spg == 0 || seg == s_begin + per - 1;   // uniform
+        if (fold) {
+            const uint32_t zw = SYM ? 0u : bb.zw >> (4 * (ncl % 8));
+#pragma unroll
+            for (int i = 0; i < WPL; ++i) {
+                const float sv = scale_at<WPL>(bb.sc, i);
+                const float z = SYM ? 8.f : (float)((zw >> (4 * i)) & 0xFu);
+#pragma unroll
+                for (int v = 0; v < VR; ++v)
+                    acc[i][v] = __builtin_fmaf(sv, __builtin_fmaf(-z, Sg[v], C[i][v] - Ug[v]),
+                                               acc[i][v]);
+                C[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int v = 0; v < VR; ++v) Ug[v] = Sg[v] = 0.f;
+        }
+    };
+
+    for (int i = 0; i < per - D; i += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            compute_seg(s_begin + i + d, b[d]);
+            load_seg(s_begin + i + d + D, b[d]);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) compute_seg(s_begin + per - D + d, b[d]);
+
+    // C layout of the 16x16 MFMA: lane (kb, c16) holds rows 4 kb + v of column c16.
+#pragma unroll
+    for (int v = 0; v < VR; ++v) {
+        const int m = 4 * kb + v;
+        if (m < M)
+#pragma unroll
+            for (int i = 0; i < WPL; ++i) red[(wave * M + m) * TN + WPL * c16 + i] = acc[i][v];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < M * TN; idx += NW * 64) {
+        const int m = idx / TN;
+        const int c = idx % TN;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum += red[(w * M + m) * TN + c];
+        if (n0 + c < N) Y[(size_t)m * N + n0 + c] = as_u16((half_t)sum);
+    }
+}
+
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1>
+hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                         const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                         hipStream_t s) {
+    constexpr int TN = 16 * WPL;
+    const int per = K / 8 / SEGR / NW;
+    const size_t lds = (size_t)M * K * 2 + (size_t)NW * M * per * sizeof(float2) +
+                       (size_t)NW * M * TN * sizeof(float);
+    hipLaunchKernelGGL((stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1>), dim3((N + TN - 1) / TN),
+                       dim3(NW * 64), lds, s, x, reinterpret_cast<const uint32_t *>(qw), sc,
+                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
     return hipGetLastError();
 }
 
-}  // namespace
+// Whether stream_kernel<.., NW, SEGR, D, ..> can take this shape: the segments
+// split evenly over the waves in whole pipelines of D, each wave's X slice fits
+// kStageChunks chunks per lane, and all of LDS stays within 64 KB.
+inline bool stream_fits(int M, int K, int N, int G, int WPL, int NW, int SEGR, int D) {
+    if (M > 4 || G % (8 * SEGR) != 0) return false;
+    const int nseg = K / 8 / SEGR;
+    if (nseg % NW != 0 || (nseg / NW) % D != 0) return false;
+    const int per = nseg / NW;
+    if (M * per * SEGR > 64 * kStageChunks) return false;
+    const size_t lds = (size_t)M * K * 2 + (size_t)NW * M * per * 8 + (size_t)NW * M * 16 * WPL * 4;
+    return lds <= 64 * 1024;
+}
+
+template <int WPL, int NW, int SEGR, int D, int VR>
+hipError_t launch_stream_sg(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                            const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                            hipStream_t s) {
+    const bool grp1 = G == 8 * SEGR;
+    if (qz == nullptr)
+        return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, true, true>(x, qw, sc, qz, y, M, K, N, G, s)
+                    : launch_stream<WPL, NW, SEGR, D, VR, true, false>(x, qw, sc, qz, y, M, K, N, G, s);
+    return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, false, true>(x, qw, sc, qz, y, M, K, N, G, s)
+                : launch_stream<WPL, NW, SEGR, D, VR, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+}
+
+template <int WPL, int NW, int SEGR, int D>
+hipError_t launch_stream_m(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                           hipStream_t s) {
+    switch (live_rows(M)) {
+    case 1: return launch_stream_sg<WPL, NW, SEGR, D, 1>(x, qw, sc, qz, y, M, K, N, G, s);
+    case 2: return launch_stream_sg<WPL, NW, SEGR, D, 2>(x, qw, sc, qz, y, M, K, N, G, s);
+    default: return launch_stream_sg<WPL, NW, SEGR, D, 4>(x, qw, sc, qz, y, M, K, N, G, s);
+    }
+}
+
+// Exact path, any G (multiple of 8): every word is dequantized bit-exactly to
+// fp16 (w = fp16_rne(s (q - z))) and multiplied; no per-segment correction.
+template <int WPL, int NW>
+__global__ void __launch_bounds__(NW * 64)
+exact_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
+             const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
+             uint16_t *__restrict__ Y, int M, int K, int N, int G) {
+    constexpr int TN = 16 * WPL;
+    extern __shared__ __attribute__((aligned(16))) uint4 lds[];
+    float *red = reinterpret_cast<float *>(lds);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c16 = lane & 15;
+    const int kb = lane >> 4;
+    const int n0 = blockIdx.x * TN;
+    const int ncol = n0 + WPL * c16;
+    const int ncl = ncol < N ? ncol : N - WPL;
+    const int xrow = c16 < M ? c16 : M - 1;
+    const int KR = K / 8;
+    const uint32_t nmask = nibble_mask_vgpr();
+
+    float4_t C[WPL];
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) C[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const int nstep = (KR + 3) / 4;
+    for (int st = wave; st < nstep; st += NW) {
+        const int r = 4 * st + kb;
+        uint32_t d[WPL][4];
+        uint4 xa = make_uint4(0u, 0u, 0u, 0u);
+        if (r < KR) {
+            xa = reinterpret_cast<const uint4 *>(X + (size_t)xrow * K)[r];
+            const Words<WPL> q = load_words<WPL>(Q + (size_t)r * N + ncl);
+            const int g = (8 * r) / G;
+            const uint32_t zw = QZ ? QZ[(size_t)g * (N / 8) + ncl / 8] >> (4 * (ncl % 8))
+                                   : 0x88888888u;
+            const uint16_t *sp = S + (size_t)g * N + ncl;
+#pragma unroll
+            for (int i = 0; i < WPL; ++i) {
+                const half_t bz = biased_zero(zw >> (4 * i));
+                const half_t sv = as_half(sp[i]);
+                const half2_t bz2 = {bz, bz}, s2 = {sv, sv};
+                uint32_t p[4];
+                unpack_biased(q.w[i], nmask, p);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d[i][j] = dequant_pair(p[j], bz2, s2);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < WPL; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d[i][j] = 0u;
+        }
+        const half8_t a = as_half8(natural_to_pairs(xa));
+#pragma unroll
+        for (int i = 0; i < WPL; ++i)
+            C[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_b(d[i]), C[i], 0, 0, 0);
+    }
+
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int m = 4 * kb + v;
+        if (m < M)
+#pragma unroll
+            for (int i = 0; i < WPL; ++i) red[(wave * M + m) * TN + WPL * c16 + i] = C[i][v];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < M * TN; idx += NW * 64) {
+        const int m = idx / TN;
+        const int c = idx % TN;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum += red[(w * M + m) * TN + c];
+        if (n0 + c < N) Y[(size_t)m * N + n0 + c] = as_u16((half_t)sum);
+    }
+}
+
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool XLDS>
+hipError_t launch_fold(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
+                       uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
+    constexpr int TN = 16 * WPL;
+    const size_t lds = (XLDS ? (size_t)M * K * 2 : 0) + (size_t)NW * M * TN * sizeof(float);
+    hipLaunchKernelGGL((fold_kernel<WPL, NW, SEGR, D, VR, SYM, XLDS>), dim3((N + TN - 1) / TN),
+                       dim3(NW * 64), lds, s, x, reinterpret_cast<const uint32_t *>(qw), sc,
+                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
+    return hipGetLastError();
+}
+
+template <int WPL, int NW, int SEGR, int D, int VR>
+hipError_t launch_fold_vr(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                          hipStream_t s) {
+    const bool xlds = (size_t)M * K * 2 <= kXLdsBytes;
+    if (qz == nullptr)
+        return xlds ? launch_fold<WPL, NW, SEGR, D, VR, true, true>(x, qw, sc, qz, y, M, K, N, G, s)
+                    : launch_fold<WPL, NW, SEGR, D, VR, true, false>(x, qw, sc, qz, y, M, K, N, G, s);
+    return xlds ? launch_fold<WPL, NW, SEGR, D, VR, false, true>(x, qw, sc, qz, y, M, K, N, G, s)
+                : launch_fold<WPL, NW, SEGR, D, VR, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+}
+
+template <int WPL, int NW, int SEGR, int D>
+hipError_t launch_fold_m(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                         const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                         hipStream_t s) {
+    switch (live_rows(M)) {
+    case 1: return launch_fold_vr<WPL, NW, SEGR, D, 1>(x, qw, sc, qz, y, M, K, N, G, s);
+    case 2: return launch_fold_vr<WPL, NW, SEGR, D, 2>(x, qw, sc, qz, y, M, K, N, G, s);
+    default: return launch_fold_vr<WPL, NW, SEGR, D, 4>(x, qw, sc, qz, y, M, K, N, G, s);
+    }
+}
+
+// Picks the wave count (a divisor of the segment count, at most 8) and the
+// pipeline depth (the largest of 4, 2, 1 dividing the segments per wave).
+template <int WPL, int SEGR>
+hipError_t launch_fold_any(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                           hipStream_t s) {
+    const int nseg = K / 8 / SEGR;
+    if (nseg % 8 == 0) {
+        const int per = nseg / 8;
+        if (per % 4 == 0) return launch_fold_m<WPL, 8, SEGR, 4>(x, qw, sc, qz, y, M, K, N, G, s);
+        if (per % 2 == 0) return launch_fold_m<WPL, 8, SEGR, 2>(x, qw, sc, qz, y, M, K, N, G, s);
+        return launch_fold_m<WPL, 8, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
+    }
+    if (nseg % 4 == 0) return launch_fold_m<WPL, 4, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (nseg % 2 == 0) return launch_fold_m<WPL, 2, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
+    return launch_fold_m<WPL, 1, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
+}
+
+template <int WPL, int NW>
+hipError_t launch_exact(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                        const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                        hipStream_t s) {
+    constexpr int TN = 16 * WPL;
+    hipLaunchKernelGGL((exact_kernel<WPL, NW>), dim3((N + TN - 1) / TN), dim3(NW * 64),
+                       (size_t)NW * M * TN * sizeof(float), s, x,
+                       reinterpret_cast<const uint32_t *>(qw), sc,
+                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
+    return hipGetLastError();
+}
+
+}  // namespace gemv
 
 hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
                        hipStream_t s) {
-    // Segment length (in packed rows of 8 k) must divide G / 8 and be a whole
-    // number of 32-k steps.
-    int seg_rows = 0;
-    if (G % 128 == 0) seg_rows = 16;
-    else if (G % 64 == 0) seg_rows = 8;
-    else if (G % 32 == 0) seg_rows = 4;
-    if (seg_rows) return launch<4, 8, true>(x, qweight, scales, qzeros, y, M, K, N, G, seg_rows, s);
-    return launch<4, 8, false>(x, qweight, scales, qzeros, y, M, K, N, G, 0, s);
+    using namespace gemv;
+    // Decode shapes: per-wave staged X, D-deep load pipeline.
+    if (stream_fits(M, K, N, G, 4, 8, 16, 2))
+        return launch_stream_m<4, 8, 16, 2>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    if (stream_fits(M, K, N, G, 4, 8, 16, 1))
+        return launch_stream_m<4, 8, 16, 1>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    // A segment (SEGR packed rows) must sit inside one group and be whole 32-k steps.
+    if (G % 128 == 0) return launch_fold_any<4, 16>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    if (G % 64 == 0) return launch_fold_any<4, 8>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    if (G % 32 == 0) return launch_fold_any<4, 4>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    return launch_exact<4, 8>(x, qweight, scales, qzeros, y, M, K, N, G, s);
 }
 
 }  // namespace awq

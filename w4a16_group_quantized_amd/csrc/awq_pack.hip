@@ -60,6 +60,7 @@ dequant_kernel(const uint32_t *__restrict__ qweight, const uint16_t *__restrict_
                int G) {
     const int n4 = N / 4;
     const long long total = (long long)(K / 8) * n4;
+    const uint32_t nmask = nibble_mask_vgpr();
     for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
          t += (long long)gridDim.x * blockDim.x) {
         const int r = (int)(t / n4);
@@ -75,7 +76,7 @@ dequant_kernel(const uint32_t *__restrict__ qweight, const uint16_t *__restrict_
         uint4 col[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            col[i] = dequant_word_natural(qs[i], biased_zero(zw >> (4 * i)), as_half(ss[i]));
+            col[i] = dequant_word_natural(qs[i], nmask, biased_zero(zw >> (4 * i)), as_half(ss[i]));
         // col[i] holds k = 8r..8r+7 of column n+i; write row by row, 4 columns at a time.
         const uint32_t *c = reinterpret_cast<const uint32_t *>(col);
 #pragma unroll
