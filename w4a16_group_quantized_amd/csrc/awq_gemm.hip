@@ -3,172 +3,249 @@
 // paragraph; pyshine.com AutoAWQ tour, overview bullets).  At M in the
 // thousands this is a dense contraction, bound by the matrix cores.
 //
-// Per workgroup (256 threads, four waves in a 2 x 2 grid): a BM x BN tile of Y,
-// K walked in BK steps.  Each step
-//   * loads the BM x BK slice of X (16-byte loads) and the BK/8 x BN packed
-//     words of the weight, one 16-byte load (four columns) per thread;
-//   * dequantizes the words bit-exactly (w = fp16_rne(s (q - z))) and stores
-//     them in LDS column-major (eight consecutive k of one column = 16 bytes),
-//     which is the B operand layout of v_mfma_f32_32x32x16_f16;
-//   * runs the wave's (BM/2) x (BN/2) sub-tile of MFMAs with fp32 accumulators.
-// The next step's global loads are issued before the current step's MFMAs and
-// land in the other half of a double-buffered LDS.
+// Workgroup: 256 threads = 4 waves, output tile BM x 256.  Wave w owns the 64
+// columns [64 w, 64 w + 64) of the tile for all BM rows, so every packed
+// weight is loaded and dequantized by exactly one wave, straight into
+// registers: one 16-byte load of a packed row gives a lane four words (four
+// consecutive columns, 8 k each), and each word, dequantized, is that lane's B
+// operand of one v_mfma_f32_16x16x32_f16 (8 k of one column).  The four words
+// feed four MFMA column sets {4 c + i}.  Dequantization is exact:
+// w = fp16_rne(s (q - z)), the same bits awq_dequant writes.
+//
+// X is the shared operand: each K step of BK = 64 loads the BM x 64 slice of X
+// once per workgroup into LDS (16-byte chunks, each reordered to the (j, j+4)
+// k pairing of the unpacked words, XOR-swizzled per row so that the 16 rows an
+// A-operand read touches fall in different banks), and all four waves read
+// their A operands from there.  The next step's X and packed words
+// are loaded while the current step multiplies (double-buffered LDS).
+//
+// Tiles are assigned so that the workgroups one XCD runs (workgroup ids are
+// dealt to the 8 XCDs round-robin) cover a compact block of output tiles:
+// their X rows and weight columns then stay in that XCD's L2.
 #include "awq_device.h"
 #include "awq_internal.h"
 
 namespace awq {
-namespace {
+namespace gemm {
 
-template <int BM, int BN, int BK>
+constexpr int kBN = 256;      // tile columns (4 waves x 64)
+constexpr int kBK = 64;       // k per step
+constexpr int kXcds = 8;      // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr int kGroupM = 4;    // tile rows per band of the tile order
+
+// Workgroup id -> output tile (tm, tn).  Ids are dealt to XCDs round-robin, so
+// id -> (xcd, slot); each XCD takes a contiguous range of the tile order, which
+// walks bands of kGroupM tile rows column by column.
+__device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int &tm, int &tn) {
+    const int T = tiles_m * tiles_n;
+    const int xcd = id % kXcds, slot = id / kXcds;
+    const int base = T / kXcds, extra = T % kXcds;
+    const int t = xcd * base + min(xcd, extra) + slot;
+    const int band = t / (kGroupM * tiles_n);
+    const int rows = min(kGroupM, tiles_m - band * kGroupM);
+    const int in = t - band * kGroupM * tiles_n;
+    tm = band * kGroupM + in % rows;
+    tn = in / rows;
+}
+
+// LDS chunk index of (row, 16-byte k chunk kc) in a tile of 8 chunks per row.
+__device__ __forceinline__ int swz(int row, int kc) { return row * 8 + (kc ^ (row & 7)); }
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// The packed words of one K step for one lane: rows 8 kt + 4 s + kb (s = 0, 1),
+// four consecutive columns, with their scales and zero points.
+struct BStep {
+    uint4 q[2];
+    uint2 sc[2];
+    uint32_t zw[2];
+};
+
+// Workgroup barrier without the memory fence of __syncthreads (which would wait
+// for every outstanding load, including the ones prefetching later steps).
+// LDS data written by direct-to-LDS loads is covered by the explicit vmcnt wait
+// that precedes it; the memory clobber keeps the compiler from moving LDS reads
+// above it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// Four LDS ring buffers as separate objects, so that the compiler can tell an
+// LDS read of one buffer from a direct-to-LDS load into another and need not
+// wait for the latter.
+constexpr int kRing = 4;
+
+template <int BM, bool SYM>
 __global__ void __launch_bounds__(256)
 gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
             uint16_t *__restrict__ Y, int M, int K, int N, int G) {
-    constexpr int LDA = BK + 8;  // halves per LDS row (16-byte pad against bank conflicts)
-    constexpr int LDB = BK + 8;
-    constexpr int WTM = BM / 2, WTN = BN / 2;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int ACH = BM * BK / 8 / 256;         // 16-byte X chunks per thread per step
-    constexpr int BCH = (BK / 8) * (BN / 4) / 256; // 4-word packed chunks per thread per step
-    static_assert(ACH >= 1 && BCH >= 1, "tile too small for 256 threads");
-
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDB];
+    constexpr int MT = BM / 16;                    // 16-row MFMA tiles per wave
+    constexpr int ACH = BM * kBK / 8 / 256;        // X chunks per thread per step
+    constexpr int P = kRing - 1;                   // steps loaded ahead
+    constexpr int LOADS = ACH + (SYM ? 4 : 6);     // vector-memory loads per step per thread
+    __shared__ __attribute__((aligned(16))) uint4 ring0[BM * 8];
+    __shared__ __attribute__((aligned(16))) uint4 ring1[BM * 8];
+    __shared__ __attribute__((aligned(16))) uint4 ring2[BM * 8];
+    __shared__ __attribute__((aligned(16))) uint4 ring3[BM * 8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_n = (N + BN - 1) / BN;
-    const int m0 = (int)(blockIdx.x / tiles_n) * BM;
-    const int n0 = (int)(blockIdx.x % tiles_n) * BN;
+    const int c16 = lane & 15;
+    const int kb = lane >> 4;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + kBN - 1) / kBN;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * kBN + 64 * wave;           // this wave's first column
+    const int ncol = n0 + 4 * c16;                 // this lane's 4 columns
+    const bool col_ok = ncol < N;
+    const int ncl = col_ok ? ncol : N - 4;         // clamped load column
     const int KR = K / 8;
-    const int KT = (K + BK - 1) / BK;
+    const int KT = (K + kBK - 1) / kBK;
+    const int KTP = (KT + kRing - 1) / kRing * kRing;   // steps, padded to whole rings
     const uint32_t nmask = nibble_mask_vgpr();
 
-    uint4 a_reg[ACH];
-    uint4 q_reg[BCH];
-    uint2 s_reg[BCH];
-    uint32_t z_reg[BCH];
-    bool b_ok[BCH];
-
-    auto gload = [&](int kt) {
+    // X: chunk p of a tile (16 bytes) is written by lane p % 64 of one wave's
+    // direct-to-LDS load; the swizzle is undone on the global side, so chunk p
+    // holds (row p / 8, k chunk (p % 8) ^ (row & 7)).  Rows past M read row
+    // M - 1 (their outputs are dropped); k past K, and padding steps, read
+    // valid addresses whose weights are zeroed below.
+    auto load_x = [&](int kt, uint4 *buf) {
 #pragma unroll
         for (int i = 0; i < ACH; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c / (BK / 8);
-            const int gk = kt * BK + (c % (BK / 8)) * 8;
-            const int gm = m0 + row;
-            a_reg[i] = (gm < M && gk < K)
-                           ? *reinterpret_cast<const uint4 *>(X + (size_t)gm * K + gk)
-                           : make_uint4(0u, 0u, 0u, 0u);
+            const int blk = i * 4 + wave;                  // 64-chunk block of the tile
+            const int p = blk * 64 + lane;
+            const int row = p >> 3;
+            const int kc = (p & 7) ^ (row & 7);
+            const int gm = min(m0 + row, M - 1);
+            int gk = kt * kBK + kc * 8;
+            gk = gk < K ? gk : 0;
+            __builtin_amdgcn_global_load_lds(X + (size_t)gm * K + gk, buf + blk * 64, 16, 0, 0);
+        }
+    };
+    auto load_b = [&](int kt, BStep &b) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int r0 = kt * (kBK / 8) + 4 * s + kb;
+            const int r = r0 < KR ? r0 : KR - 1;
+            const int g = (8 * r) / G;
+            b.q[s] = *reinterpret_cast<const uint4 *>(Q + (size_t)r * N + ncl);
+            b.sc[s] = *reinterpret_cast<const uint2 *>(S + (size_t)g * N + ncl);
+            if constexpr (SYM) b.zw[s] = 0x88888888u;
+            else b.zw[s] = QZ[(size_t)g * (N / 8) + ncl / 8];
+        }
+    };
+
+    float4_t acc[MT][4];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][i] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    BStep bq[kRing];
+    // One step: wait for its loads (issued P steps earlier; P - 1 later steps
+    // may still be in flight), barrier (every wave's X tile is in LDS and every
+    // wave is done reading the buffer reloaded next), issue step kt + P, then
+    // dequantize and multiply step kt.
+    auto step = [&](int kt, uint4 *cur_buf, BStep &cur, uint4 *next_buf, BStep &next) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(P - 1) * LOADS>();
+        barrier_no_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        half8_t b[2][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const bool k_ok = kt * (kBK / 8) + 4 * s + kb < KR;
+            const uint32_t q4[4] = {cur.q[s].x, cur.q[s].y, cur.q[s].z, cur.q[s].w};
+            const uint16_t s4[4] = {(uint16_t)cur.sc[s].x, (uint16_t)(cur.sc[s].x >> 16),
+                                    (uint16_t)cur.sc[s].y, (uint16_t)(cur.sc[s].y >> 16)};
+            const uint32_t z4 = cur.zw[s] >> (4 * (ncl % 8));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 w = dequant_word_natural(q4[i], nmask, biased_zero(z4 >> (4 * i)),
+                                                     as_half(s4[i]));
+                b[s][i] = as_half8(k_ok ? w : make_uint4(0u, 0u, 0u, 0u));
+            }
+        }
+        {
+            const int kn = min(kt + P, KT - 1);
+            load_x(kn, next_buf);
+            load_b(kn, next);
         }
 #pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int c = tid + 256 * i;
-            const int r = kt * (BK / 8) + c / (BN / 4);
-            const int n = n0 + (c % (BN / 4)) * 4;
-            b_ok[i] = r < KR && n < N;
-            if (b_ok[i]) {
-                const int g = (8 * r) / G;
-                q_reg[i] = *reinterpret_cast<const uint4 *>(Q + (size_t)r * N + n);
-                s_reg[i] = *reinterpret_cast<const uint2 *>(S + (size_t)g * N + n);
-                z_reg[i] = QZ ? QZ[(size_t)g * (N / 8) + n / 8] >> (4 * (n % 8)) : 0x8888u;
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                // A operand: row 16 t + c16, k chunk 4 s + kb, natural k order.
+                const half8_t a = as_half8(cur_buf[swz(16 * t + c16, 4 * s + kb)]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[s][i], acc[t][i], 0, 0, 0);
             }
         }
     };
 
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c / (BK / 8);
-            const int kc = c % (BK / 8);
-            *reinterpret_cast<uint4 *>(&As[buf][row * LDA + kc * 8]) = a_reg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int c = tid + 256 * i;
-            const int kq = c / (BN / 4);
-            const int nl = (c % (BN / 4)) * 4;
-            const uint32_t qs[4] = {q_reg[i].x, q_reg[i].y, q_reg[i].z, q_reg[i].w};
-            const uint16_t ss[4] = {(uint16_t)s_reg[i].x, (uint16_t)(s_reg[i].x >> 16),
-                                    (uint16_t)s_reg[i].y, (uint16_t)(s_reg[i].y >> 16)};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint4 w = b_ok[i] ? dequant_word_natural(qs[j], nmask, biased_zero(z_reg[i] >> (4 * j)),
-                                                               as_half(ss[j]))
-                                        : make_uint4(0u, 0u, 0u, 0u);
-                *reinterpret_cast<uint4 *>(&Bs[buf][(nl + j) * LDB + kq * 8]) = w;
-            }
-        }
-    };
-
-    float16_t acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
-    const int lrow = lane & 31;
-    const int lk = 8 * (lane >> 5);
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            half8_t a[FM], b[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                a[i] = as_half8(*reinterpret_cast<const uint4 *>(
-                    &As[buf][(wm * WTM + 32 * i + lrow) * LDA + kk + lk]));
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                b[j] = as_half8(*reinterpret_cast<const uint4 *>(
-                    &Bs[buf][(wn * WTN + 32 * j + lrow) * LDB + kk + lk]));
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < KT) sstore(buf ^ 1);
-        __syncthreads();
+    // Prologue: steps 0 .. P-1 in flight.
+    load_x(0, ring0);
+    load_b(0, bq[0]);
+    load_x(min(1, KT - 1), ring1);
+    load_b(min(1, KT - 1), bq[1]);
+    load_x(min(2, KT - 1), ring2);
+    load_b(min(2, KT - 1), bq[2]);
+    for (int kt = 0; kt < KTP; kt += kRing) {
+        step(kt + 0, ring0, bq[0], ring3, bq[3]);
+        step(kt + 1, ring1, bq[1], ring0, bq[0]);
+        step(kt + 2, ring2, bq[2], ring1, bq[1]);
+        step(kt + 3, ring3, bq[3], ring2, bq[2]);
     }
 
-    // C layout of the 32x32 MFMA: lane l holds column l % 32 and, for register
-    // v, row 8 * (v / 4) + 4 * (l / 32) + v % 4.
+    // C layout of the 16x16 MFMA: lane (kb, c16) of column set i holds rows
+    // 4 kb + v of column 4 c16 + i: four consecutive columns per row.
+    if (!col_ok) return;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn * WTN + 32 * j + lrow;
-            if (col >= N) continue;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm * WTM + 32 * i + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
-                if (row < M) Y[(size_t)row * N + col] = as_u16((half_t)acc[i][j][v]);
+        for (int v = 0; v < 4; ++v) {
+            const int row = m0 + 16 * t + 4 * kb + v;
+            if (row < M) {
+                const uint32_t lo = (uint32_t)as_u16((half_t)acc[t][0][v]) |
+                                    ((uint32_t)as_u16((half_t)acc[t][1][v]) << 16);
+                const uint32_t hi = (uint32_t)as_u16((half_t)acc[t][2][v]) |
+                                    ((uint32_t)as_u16((half_t)acc[t][3][v]) << 16);
+                *reinterpret_cast<uint2 *>(Y + (size_t)row * N + ncol) = make_uint2(lo, hi);
             }
         }
 }
 
-}  // namespace
+template <int BM, bool SYM>
+hipError_t launch_sym(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
+                      uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
+    const long long tiles = (long long)((M + BM - 1) / BM) * ((N + kBN - 1) / kBN);
+    hipLaunchKernelGGL((gemm_kernel<BM, SYM>), dim3((unsigned)tiles), dim3(256), 0, s, x,
+                       reinterpret_cast<const uint32_t *>(qw), sc,
+                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
+    return hipGetLastError();
+}
+
+template <int BM>
+hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
+                  uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
+    return qz == nullptr ? launch_sym<BM, true>(x, qw, sc, qz, y, M, K, N, G, s)
+                         : launch_sym<BM, false>(x, qw, sc, qz, y, M, K, N, G, s);
+}
+
+}  // namespace gemm
 
 hipError_t launch_gemm(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
                        hipStream_t s) {
-    constexpr int BM = 128, BN = 128, BK = 64;
-    const dim3 grid((unsigned)(((N + BN - 1) / BN) * (long long)((M + BM - 1) / BM)));
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK>), grid, dim3(256), 0, s, x,
-                       reinterpret_cast<const uint32_t *>(qweight), scales,
-                       reinterpret_cast<const uint32_t *>(qzeros), y, M, K, N, G);
-    return hipGetLastError();
+    return gemm::launch<128>(x, qweight, scales, qzeros, y, M, K, N, G, s);
 }
 
 }  // namespace awq

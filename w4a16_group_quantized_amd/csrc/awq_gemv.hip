@@ -386,7 +386,8 @@ struct WSeg {
 // Chunks of staged X per lane, at most.
 constexpr int kStageChunks = 4;
 
-template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1>
+// XCH: 16-byte chunks of X each lane stages (M * K / 8 / NW <= 64 * XCH).
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH>
 __global__ void __launch_bounds__(NW * 64)
 stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
@@ -432,13 +433,14 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 
     // 1. X loads (clamped, unconditional), 2. the first D segments, 3. staging.
     const int chunks_w = M * rows_w;
-    uint4 xr[kStageChunks];
+    uint4 xr[XCH];
 #pragma unroll
-    for (int j = 0; j < kStageChunks; ++j) {
+    for (int j = 0; j < XCH; ++j) {
         const int c = lane + 64 * j;
         const int cc = c < chunks_w ? c : 0;
-        const int m = cc / rows_w;
-        xr[j] = reinterpret_cast<const uint4 *>(X)[(size_t)m * KR + r_begin + cc % rows_w];
+        const int m = VR == 1 ? 0 : cc / rows_w;             // VR == 1 means M == 1
+        const int rr = VR == 1 ? cc : cc - m * rows_w;
+        xr[j] = reinterpret_cast<const uint4 *>(X)[(size_t)m * KR + r_begin + rr];
     }
     WSeg<WPL, STEPS, SYM> b[D];
     const int s_begin = wave * per;
@@ -446,7 +448,7 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     for (int d = 0; d < D; ++d) load_seg(s_begin + d, b[d]);
 
 #pragma unroll
-    for (int j = 0; j < kStageChunks; ++j) {
+    for (int j = 0; j < XCH; ++j) {
         const int c = lane + 64 * j;
         const uint4 a = stage_chunk(xr[j]);
         const half2_t one2 = {(half_t)1.0f, (half_t)1.0f};
@@ -465,8 +467,8 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         if (c < chunks_w) {
             xs[c] = a;
             if (c % SEGR == 0) {
-                const int m = c / rows_w;
-                tab[m * per + (c % rows_w) / SEGR] = make_float2(1024.f * t, u);
+                const int m = VR == 1 ? 0 : c / rows_w;
+                tab[m * per + (c - m * rows_w) / SEGR] = make_float2(1024.f * t, u);
             }
         }
     }
@@ -556,7 +558,7 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     }
 }
 
-template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1>
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH>
 hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                          hipStream_t s) {
@@ -564,7 +566,7 @@ hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *s
     const int per = K / 8 / SEGR / NW;
     const size_t lds = (size_t)M * K * 2 + (size_t)NW * M * per * sizeof(float2) +
                        (size_t)NW * M * TN * sizeof(float);
-    hipLaunchKernelGGL((stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1>), dim3((N + TN - 1) / TN),
+    hipLaunchKernelGGL((stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH>), dim3((N + TN - 1) / TN),
                        dim3(NW * 64), lds, s, x, reinterpret_cast<const uint32_t *>(qw), sc,
                        reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
     return hipGetLastError();
@@ -583,16 +585,26 @@ inline bool stream_fits(int M, int K, int N, int G, int WPL, int NW, int SEGR, i
     return lds <= 64 * 1024;
 }
 
-template <int WPL, int NW, int SEGR, int D, int VR>
+template <int WPL, int NW, int SEGR, int D, int VR, int XCH>
 hipError_t launch_stream_sg(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                             const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                             hipStream_t s) {
     const bool grp1 = G == 8 * SEGR;
     if (qz == nullptr)
-        return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, true, true>(x, qw, sc, qz, y, M, K, N, G, s)
-                    : launch_stream<WPL, NW, SEGR, D, VR, true, false>(x, qw, sc, qz, y, M, K, N, G, s);
-    return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, false, true>(x, qw, sc, qz, y, M, K, N, G, s)
-                : launch_stream<WPL, NW, SEGR, D, VR, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+        return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, true, true, XCH>(x, qw, sc, qz, y, M, K, N, G, s)
+                    : launch_stream<WPL, NW, SEGR, D, VR, true, false, XCH>(x, qw, sc, qz, y, M, K, N, G, s);
+    return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, false, true, XCH>(x, qw, sc, qz, y, M, K, N, G, s)
+                : launch_stream<WPL, NW, SEGR, D, VR, false, false, XCH>(x, qw, sc, qz, y, M, K, N, G, s);
+}
+
+template <int WPL, int NW, int SEGR, int D, int VR>
+hipError_t launch_stream_x(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                           hipStream_t s) {
+    const int chunks_w = M * (K / 8 / NW);
+    if (chunks_w <= 64) return launch_stream_sg<WPL, NW, SEGR, D, VR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (chunks_w <= 128) return launch_stream_sg<WPL, NW, SEGR, D, VR, 2>(x, qw, sc, qz, y, M, K, N, G, s);
+    return launch_stream_sg<WPL, NW, SEGR, D, VR, kStageChunks>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
 template <int WPL, int NW, int SEGR, int D>
@@ -600,9 +612,9 @@ hipError_t launch_stream_m(const uint16_t *x, const int32_t *qw, const uint16_t 
                            const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                            hipStream_t s) {
     switch (live_rows(M)) {
-    case 1: return launch_stream_sg<WPL, NW, SEGR, D, 1>(x, qw, sc, qz, y, M, K, N, G, s);
-    case 2: return launch_stream_sg<WPL, NW, SEGR, D, 2>(x, qw, sc, qz, y, M, K, N, G, s);
-    default: return launch_stream_sg<WPL, NW, SEGR, D, 4>(x, qw, sc, qz, y, M, K, N, G, s);
+    case 1: return launch_stream_x<WPL, NW, SEGR, D, 1>(x, qw, sc, qz, y, M, K, N, G, s);
+    case 2: return launch_stream_x<WPL, NW, SEGR, D, 2>(x, qw, sc, qz, y, M, K, N, G, s);
+    default: return launch_stream_x<WPL, NW, SEGR, D, 4>(x, qw, sc, qz, y, M, K, N, G, s);
     }
 }
 
