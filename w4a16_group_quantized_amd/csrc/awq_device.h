@@ -60,12 +60,13 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t p, half2_t bz2, half2_
     return as_u32((as_half2(p) - bz2) * s2);
 }
 
-// (lo(a), lo(b)) and (hi(a), hi(b)) as one 32-bit half2 each.
+// (lo(a), lo(b)) and (hi(a), hi(b)) as one 32-bit half2 each, one v_perm_b32
+// apiece (selector bytes 0-3 pick bytes of the second operand, 4-7 of the first).
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-    return (a & 0xFFFFu) | (b << 16);
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-    return (a >> 16) | (b & 0xFFFF0000u);
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 // Pairs in (j, j+4) order -> eight halves in natural k order (as four dwords).
