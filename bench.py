@@ -16,13 +16,33 @@ Prints one JSON line: value = algorithmic bytes per step / time per step, in
 GB/s.  Also reported: the roofline of the dominant kernel (awq_gemv), the
 batched GEMM (awq_gemm, prefill shape M=2048) in TFLOP/s, and the CPU oracle
 timed on a bounded sample of the same workload.
+
+Profiling helpers (the figures under profiles/ come from these):
+
+    python bench.py --profile gemv|gemm
+        a short fixed sequence for rocprofv3 counter passes: 20 calls of the
+        kernel on its workload, each its own dispatch, then 5 device copies of
+        64 MiB -- the plain copy kernel that calibrates FETCH_SIZE/WRITE_SIZE
+    python bench.py --summarize-pmc OUT DIR...
+        folds the counter CSVs of rocprofv3 --pmc runs into a text summary with
+        per-dispatch medians, the copy calibration, the HBM traffic per launch
+        and the hash of the kernel's sources
+    python bench.py --summarize-stats OUT DIR
+        the same for a rocprofv3 --kernel-trace --stats run
+
+The roofline's "traffic" is read from the committed counter summary of the
+GEMV kernel, and only while the hash of its sources still matches.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -35,6 +55,25 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_F16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU, dense fp16
 METRIC = "W4A16 GEMV HBM GB/s (% of peak) at M=1; GEMM TFLOP/s (% MFMA peak) at M=2048"
 ROTATE_BYTES = 1 << 30
+CALIBRATION_COPY_BYTES = 64 << 20
+PROFILE_CALLS = 20
+CSRC = os.path.join(ROOT, "w4a16_group_quantized_amd", "csrc")
+# Sources each profiled kernel is built from: a counter summary is valid only for them.
+KERNEL_SOURCES = {
+    "gemv": ["awq_gemv.hip", "awq_device.h", "awq_internal.h"],
+    "gemm": ["awq_gemm.hip", "awq_device.h", "awq_internal.h"],
+}
+KERNEL_NAMES = {"gemv": ("stream_kernel", "fold_kernel", "exact_kernel"), "gemm": ("gemm_kernel",)}
+PROFILE_WORKLOAD = {"gemv": "decode_8b_gate", "gemm": "prefill_out_proj"}
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "awq_gemv_decode_8b_gate_counters.txt")
+
+
+def source_hash(kind):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def alg_bytes(w, M):
@@ -156,6 +195,127 @@ def cpu_baseline(name, budget_s=10.0):
                       f"unpack + exact dequant + fp64 matmul, {per:.2f} s each"}
 
 
+def profile_run(kind):
+    """Fixed dispatch sequence for counter passes (see the module docstring)."""
+    import torch
+    from w4a16_group_quantized_amd import binding, synth
+    binding.load()
+    name = PROFILE_WORKLOAD[kind]
+    w = synth.WORKLOADS[name]
+    copies = max(2, math.ceil(ROTATE_BYTES / alg_bytes(w, 0))) if kind == "gemv" else 1
+    layers = build_layers(w, copies)
+    X = to_dev(synth.make_x(w.M, w.K, w.wid, w.n_outliers, w.outlier_gain))
+    y = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    fn = getattr(binding, kind)
+    for i in range(PROFILE_CALLS):
+        fn(X, layers[i % copies], out=y)
+    torch.cuda.synchronize()
+    a = torch.ones(CALIBRATION_COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"profiled {PROFILE_CALLS} x awq_{kind} on {name}, then 5 copies of "
+          f"{CALIBRATION_COPY_BYTES} bytes", flush=True)
+
+
+def _per_dispatch(dirs):
+    """{kernel: {counter: [value per dispatch]}} from rocprofv3 --pmc CSVs."""
+    out = {}
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            acc = {}
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    k = row["Kernel_Name"]
+                    key = (k, row["Counter_Name"], row["Dispatch_Id"])
+                    acc[key] = acc.get(key, 0.0) + float(row["Counter_Value"])
+            for (k, c, did), v in acc.items():
+                out.setdefault(k, {}).setdefault(c, []).append((int(did), v))
+    for per in out.values():
+        for c in per:
+            per[c].sort()
+    return out
+
+
+def _short(kernel):
+    k = kernel.replace("void ", "").replace("(anonymous namespace)", "anon")
+    return k.split("(")[0][:90]
+
+
+def summarize_pmc(out_path, dirs, kind, commands):
+    data = _per_dispatch(dirs)
+    kern = [k for k in data if any(n in k for n in KERNEL_NAMES[kind])]
+    copyk = [k for k in data if "copyBuffer" in k]
+    lines = [f"# rocprofv3 --pmc counters: awq_{kind} on {PROFILE_WORKLOAD[kind]}",
+             "# commands (each a run of its own):"]
+    lines += [f"#   {c}" for c in commands]
+    lines.append(f"# source_sha256: {source_hash(kind)}")
+    lines.append("# per kernel and counter: median over dispatches of the per-dispatch sum")
+    lines.append(f"{'kernel':90s} {'counter':28s} {'median':>14s} {'dispatches':>10s}")
+    med = {}
+    for k in kern + copyk:
+        for c, vals in sorted(data[k].items()):
+            if k in copyk:
+                vals = vals[-5:]     # the calibration copies end the profiled sequence
+            m = statistics.median(v for _, v in vals)
+            med[(k, c)] = m
+            lines.append(f"{_short(k):90s} {c:28s} {m:14.1f} {len(vals):10d}")
+    traffic = None
+    if kern and copyk:
+        ck = copyk[0]
+        facs = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if (ck, c) in med and med[(ck, c)] > 0:
+                facs[c] = CALIBRATION_COPY_BYTES / (med[(ck, c)] * 1024.0)
+        if len(facs) == 2 and all((kern[0], c) in med for c in facs):
+            for c, f in facs.items():
+                lines.append(f"calibration {c}: copy of {CALIBRATION_COPY_BYTES} bytes reads "
+                             f"{med[(ck, c)]:.1f} KiB -> factor {f:.4f}")
+            traffic = sum(med[(kern[0], c)] * 1024.0 * f for c, f in facs.items())
+            lines.append(f"traffic_bytes_per_launch: {traffic:.0f}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_stats(out_path, d, command):
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    lines = ["# rocprofv3 --kernel-trace --stats summary", f"# command: {command}",
+             f"# source_sha256 gemv: {source_hash('gemv')}",
+             f"# source_sha256 gemm: {source_hash('gemm')}",
+             f"{'kernel':90s} {'calls':>7s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for r in rows:
+        lines.append(f"{_short(r['Name']):90s} {int(r['Calls']):7d} {float(r['AverageNs'])/1e3:10.3f} "
+                     f"{float(r['MinNs'])/1e3:10.3f} {float(r['MaxNs'])/1e3:10.3f} "
+                     f"{float(r['Percentage']):6.2f}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def committed_traffic():
+    """HBM bytes per launch of awq_gemv from the committed counter summary, or
+    None if there is none or the kernel's sources have changed since."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    sha = traffic = None
+    for line in text.splitlines():
+        if line.startswith("# source_sha256:"):
+            sha = line.split(":", 1)[1].strip()
+        elif line.startswith("traffic_bytes_per_launch:"):
+            traffic = float(line.split(":", 1)[1])
+    if sha != source_hash("gemv"):
+        return None
+    return traffic
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,7 +323,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--profile", choices=["gemv", "gemm"], help="dispatch sequence for counter passes")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar=("OUT", "DIR"),
+                    help="fold rocprofv3 --pmc CSV directories into a summary file")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("OUT", "DIR"),
+                    help="fold a rocprofv3 --kernel-trace --stats directory into a summary file")
+    ap.add_argument("--kind", choices=["gemv", "gemm"], default="gemv", help="kernel of --summarize-pmc")
+    ap.add_argument("--command", action="append", default=[],
+                    help="command line(s) that produced the profiled data, recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1:], args.kind, args.command)
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], " ; ".join(args.command))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer shards by output columns with no exchange; see the design notes)",
@@ -173,11 +347,14 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.profile:
+        profile_run(args.profile)
+        return
     from w4a16_group_quantized_amd import binding
     binding.load()
 
     head = bench_gemv("decode_8b_gate", args.steps, args.warmup)
-    gemm = bench_gemm("prefill_out_proj", max(10, args.steps // 10), max(2, args.warmup // 10))
+    gemm = bench_gemm("prefill_out_proj", args.steps, args.warmup)
     extra = []
     if args.all:
         extra.append(bench_gemv("gate_up_m16", args.steps, args.warmup))
@@ -185,6 +362,7 @@ def main():
         extra.append(bench_gemm("gate_up_m16", args.steps, args.warmup))
         extra.append(bench_gemm("sym70b_m4096", max(5, args.steps // 40), 2))
 
+    traffic = committed_traffic()
     out = {
         "metric": METRIC,
         "value": round(head["gbs"], 1),
@@ -202,7 +380,7 @@ def main():
                    "symmetric": False, "entry": "awq_gemv", "weight_copies": head["weight_copies"],
                    "launch": "hip_graph"},
         "roofline": {"bound": "hbm", "achieved": round(head["gbs"], 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(head["hbm_frac"], 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(head["hbm_frac"], 4), "traffic": traffic},
         "gemm": {"workload": gemm["workload"], "M": gemm["M"], "K": gemm["K"], "N": gemm["N"],
                  "tflops": round(gemm["tflops"], 1), "peak": MFMA_F16_PEAK_TFLOPS,
                  "frac": round(gemm["mfma_frac"], 4), "us_per_call": round(gemm["us_per_call"], 2)},
