@@ -78,6 +78,9 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 // LDS read of one buffer from a direct-to-LDS load into another and need not
 // wait for the latter.
 constexpr int kRing = 4;
+#ifndef AWQ_GEMM_M32
+#define AWQ_GEMM_M32 1
+#endif
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
@@ -87,6 +90,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, uint4 *dst,
                                                 uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, soff, 0, 0);
+}
+
+// 4 bytes per lane from a buffer straight into LDS: lane i writes word i of dst.
+__device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rs, uint4 *dst,
+                                               uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, soff, 0, 0);
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane i writes dst + i.
@@ -295,6 +304,290 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         }
 }
 
+// ---------------------------------------------------------------------------
+// Fast path on 32x32x16 MFMAs: G % 64 == 0 and K % 256 == 0.
+//
+// A v_mfma_f32_32x32x16_f16 keeps the matrix core busy for 32 cycles, twice as
+// long as the 16x16x32 form for the same operand registers, so one wave per
+// SIMD can issue the whole dequantization of the next step's weights between
+// its MFMAs without slowing them.  Wave w still owns the 64 columns
+// [64 w, 64 w + 64) of the 128 x 256 tile, now as 4 row tiles x 2 column tiles
+// of 32 x 32: the lane with column slot j (lane % 32) owns the adjacent columns
+// 2 j and 2 j + 1 (column tiles 0 and 1), and half h = lane / 32 of the 16 k of
+// an MFMA, i.e. packed row 2 kb + h of k block kb.
+//
+// Every load of the loop is a direct-to-LDS buffer load -- X, packed words,
+// scales and zero points -- so all waits are the explicit counts below:
+// the compiler tracks no vector-memory result in registers.  A step kt:
+//   wait for X(kt) and the weights of kt + 1, barrier;
+//   issue the loads of step kt + 3 into the ring slot of kt - 1;
+//   read A(kt) and the packed weights of kt + 1 from LDS;
+//   MFMAs of kt (B dequantized during kt - 1), interleaved with the
+//   dequantization of kt + 1.
+// ---------------------------------------------------------------------------
+namespace m32 {
+
+constexpr int kBM = 128;
+constexpr int kMT = kBM / 32;            // row tiles per wave
+constexpr int kACH = kBM * kBK / 8 / 256; // X chunks per thread per step
+// Per-wave LDS region of one step's weights, in 16-byte chunks: 8 packed rows
+// x 64 columns (row r, column n0 + c at word 64 r + c), 64 scale words (word i:
+// columns n0 + 2 (i % 32), +1), 64 zero words (word i: zero word n0 / 8 + i % 8).
+constexpr int kWave = 8 * 64 / 4 + 16 + 16;
+constexpr int kScale = 8 * 64 / 4;
+constexpr int kZero = kScale + 16;
+
+typedef float float16x_t __attribute__((ext_vector_type(16)));
+
+// Natural-order unpack of one packed word: pair b = (k 2b, 2b+1) as the fp16
+// pair (1024 + q_2b, 64 + q_2b+1).  v_perm copies byte b of the word into
+// bytes 0 and 2 next to the exponent bytes 0x64 and 0x54; the mask keeps the
+// low nibble in the low half (units at bit 0 of a 1024-based half) and the high
+// nibble in the high half (units at bit 4 of a 64-based half).
+__device__ __forceinline__ void unpack_natural(uint32_t w, uint32_t exps, uint32_t p[4]) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        p[b] = __builtin_amdgcn_perm(exps, w, (7u << 24) | ((uint32_t)b << 16) | (5u << 8) | (uint32_t)b) &
+               0xFFF0FF0Fu;
+}
+
+template <bool SYM>
+__global__ void __launch_bounds__(256)
+mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
+              const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
+              uint16_t *__restrict__ Y, int M, int K, int N, int G) {
+    constexpr int BLOADS = SYM ? 3 : 4;   // per step: 2 packed-row loads, scales, zeros
+    constexpr int LOADS = kACH + BLOADS;
+    __shared__ __attribute__((aligned(16))) uint4 ring0[kBM * 8];
+    __shared__ __attribute__((aligned(16))) uint4 ring1[kBM * 8];
+    __shared__ __attribute__((aligned(16))) uint4 ring2[kBM * 8];
+    __shared__ __attribute__((aligned(16))) uint4 ring3[kBM * 8];
+    __shared__ __attribute__((aligned(16))) uint4 bring0[4 * kWave];
+    __shared__ __attribute__((aligned(16))) uint4 bring1[4 * kWave];
+    __shared__ __attribute__((aligned(16))) uint4 bring2[4 * kWave];
+    __shared__ __attribute__((aligned(16))) uint4 bring3[4 * kWave];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31;
+    const int h = lane >> 5;
+    const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * kBM;
+    const int n0 = tn * kBN + 64 * wave;
+    const int KR = K / 8;
+    const int KT = K / kBK;
+
+    // Buffer loads past a buffer's end return zeros; columns at or past N read
+    // the next packed row (in bounds) and their outputs are dropped.
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, (uint32_t)KR * (uint32_t)N * 4u);
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(S, (uint32_t)(K / G) * (uint32_t)N * 2u);
+    const __amdgpu_buffer_rsrc_t zrs = make_rsrc(QZ, SYM ? 0u : (uint32_t)(K / G) * (uint32_t)N / 2u);
+    uint32_t xvoff[kACH];
+#pragma unroll
+    for (int i = 0; i < kACH; ++i) {
+        const int p = (i * 4 + wave) * 64 + lane;
+        const int row = p >> 3;
+        const int xr = min(m0 + row, M - 1);
+        const int xkc = (p & 7) ^ (row & 7);
+        xvoff[i] = ((uint32_t)xr * (uint32_t)K + (uint32_t)xkc * 8u) * 2u;
+    }
+    // packed rows: load d (0, 1) of a step, lane i -> row 4 d + i / 16, columns n0 + 4 (i % 16) ..
+    const uint32_t qvoff = ((uint32_t)(lane >> 4) * (uint32_t)N + (uint32_t)(n0 + 4 * (lane & 15))) * 4u;
+    const uint32_t svoff = (uint32_t)(n0 + 2 * (lane & 31)) * 2u;
+    const uint32_t zvoff = (uint32_t)(n0 / 8 + (lane & 7)) * 4u;
+
+    auto load_step = [&](int kt, uint4 *xbuf, uint4 *bbuf) {
+        uint4 *dst = bbuf + wave * kWave;
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+            buffer_to_lds16(qrs, dst + 64 * d, qvoff, (kt * (kBK / 8) + 4 * d) * N * 4);
+        const int g = (kt * kBK) / G;
+        buffer_to_lds4(srs, dst + kScale, svoff, g * N * 2);
+        if constexpr (!SYM) buffer_to_lds4(zrs, dst + kZero, zvoff, g * (N / 8) * 4);
+#pragma unroll
+        for (int i = 0; i < kACH; ++i)
+            buffer_to_lds16(xrs, xbuf + (i * 4 + wave) * 64, xvoff[i], kt * kBK * 2);
+    };
+
+    // Raw weights of one step for this lane: packed rows 2 kb + h, columns
+    // n0 + 2 j, +1; the scale pair and the zero word of those columns.
+    struct Raw {
+        uint2 q[4];
+        uint32_t sc, zw;
+    };
+    auto read_raw = [&](const uint4 *bbuf) {
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(bbuf + wave * kWave);
+        Raw r;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            r.q[kb] = *reinterpret_cast<const uint2 *>(w + 64 * (2 * kb + h) + 2 * j);
+        r.sc = w[4 * kScale + j];
+        r.zw = SYM ? 0x88888888u : w[4 * kZero + (j >> 2)];
+        return r;
+    };
+    const uint32_t exps = 0x54006400u;
+    half8_t bA[4][2], bB[4][2];
+    // Biased zero pairs (1024 + z, 64 + z) and scale pairs of the two columns.
+    struct Dq {
+        half2_t bz2[2], s2[2];
+    };
+    auto decode = [&](const Raw &r) {
+        Dq dq;
+        const uint32_t z2 = r.zw >> (8 * (j & 3));
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const uint32_t z = (z2 >> (4 * ct)) & 0xFu;
+            dq.bz2[ct] = as_half2(0x54006400u | (z << 20) | z);
+            const half_t sv = as_half((uint16_t)(r.sc >> (16 * ct)));
+            dq.s2[ct] = half2_t{sv, sv};
+        }
+        return dq;
+    };
+
+    float16x_t acc[kMT][2];
+#pragma unroll
+    for (int t = 0; t < kMT; ++t)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[t][ct][v] = 0.f;
+
+    // A operands of k block kb of a step: row tiles t = 0..3.
+    auto read_a = [&](const uint4 *xbuf, int kb, half8_t (&a)[kMT]) {
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) a[t] = as_half8(xbuf[swz(32 * t + j, 2 * kb + h)]);
+    };
+    auto mfma_kb = [&](const half8_t (&a)[kMT], const half8_t (&b)[2]) {
+#pragma unroll
+        for (int t = 0; t < kMT; ++t)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                acc[t][ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[t], b[ct], acc[t][ct], 0, 0, 0);
+    };
+    auto dequant_kb = [&](const Raw &r, const Dq &dq, int kb, half8_t (&b)[2]) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            uint32_t p[4], d[4];
+            unpack_natural(ct ? r.q[kb].y : r.q[kb].x, exps, p);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = dequant_pair(p[e], dq.bz2[ct], dq.s2[ct]);
+            b[ct] = as_half8(make_uint4(d[0], d[1], d[2], d[3]));
+        }
+    };
+
+    // Step kt, software-pipelined inside its 32 MFMAs (4 k blocks x 4 row tiles
+    // x 2 column tiles).  On entry: b_cur = weights of kt (dequantized), a0 =
+    // A(kt, kb 0), r = the packed weights of kt + 1 (read from LDS).  Each k
+    // block's MFMAs run while the next block's A operands are read and one
+    // block of step kt + 1's weights is dequantized.  Between blocks 2 and 3
+    // the wave waits until everything up to step kt + 2 has landed (and its own
+    // LDS reads of slot kt are done) and meets the other waves at a barrier.  After it, X(kt + 1) is visible to all waves, so block 3 reads
+    // A(kt + 1, kb 0) and the packed weights of kt + 2, and the loads of step
+    // kt + 4 go into the ring slots of kt.  Neither LDS latency nor the
+    // barrier reaches the matrix cores by more than a block's lead.
+    half8_t a0[kMT], a1[kMT];
+    Raw r;
+    auto step = [&](int kt, const uint4 *xcur, half8_t (&b_cur)[4][2], half8_t (&b_nxt)[4][2],
+                    const uint4 *xnxt, const uint4 *bnn, uint4 *xload, uint4 *bload) {
+        __builtin_amdgcn_sched_barrier(0);
+        const Raw rc = r;
+        const Dq dq = decode(rc);
+        read_a(xcur, 1, a1);
+        dequant_kb(rc, dq, 0, b_nxt[0]);
+        mfma_kb(a0, b_cur[0]);
+        read_a(xcur, 2, a0);
+        dequant_kb(rc, dq, 1, b_nxt[1]);
+        mfma_kb(a1, b_cur[1]);
+        read_a(xcur, 3, a1);
+        dequant_kb(rc, dq, 2, b_nxt[2]);
+        mfma_kb(a0, b_cur[2]);
+#pragma unroll
+        for (int i = 0; i < 24; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads are done
+        wait_vmcnt<LOADS>();                  // every batch but the last (step kt + 3) is in
+        barrier_no_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(min(kt + kRing, KT - 1), xload, bload);
+        read_a(xnxt, 0, a0);
+        r = read_raw(bnn);
+        mfma_kb(a1, b_cur[3]);
+        dequant_kb(rc, dq, 3, b_nxt[3]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+        }
+    };
+
+    // Prologue: steps 0 .. 3 in flight; step 0 needs steps 0 and 1 landed.
+    load_step(0, ring0, bring0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(min(1, KT - 1), ring1, bring1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(min(2, KT - 1), ring2, bring2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(min(3, KT - 1), ring3, bring3);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<2 * LOADS>();
+    barrier_no_fence();
+    __builtin_amdgcn_sched_barrier(0);
+    r = read_raw(bring0);
+    {
+        const Dq dq = decode(r);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) dequant_kb(r, dq, kb, bA[kb]);
+    }
+    r = read_raw(bring1);
+    read_a(ring0, 0, a0);
+    for (int kt = 0; kt < KT; kt += kRing) {
+        step(kt + 0, ring0, bA, bB, ring1, bring2, ring0, bring0);
+        step(kt + 1, ring1, bB, bA, ring2, bring3, ring1, bring1);
+        step(kt + 2, ring2, bA, bB, ring3, bring0, ring2, bring2);
+        step(kt + 3, ring3, bB, bA, ring0, bring1, ring3, bring3);
+    }
+    wait_vmcnt<0>();   // no load into LDS may outlive the workgroup
+
+    // C layout of the 32x32 MFMA: lane (h, j) holds, in register v, row
+    // 8 (v / 4) + 4 h + v % 4 of column slot j; column tiles 0 and 1 are the
+    // adjacent columns n0 + 2 j and n0 + 2 j + 1, stored as one 4-byte word.
+    const int col = n0 + 2 * j;
+    if (col >= N) return;
+#pragma unroll
+    for (int t = 0; t < kMT; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = m0 + 32 * t + 8 * (v / 4) + 4 * h + (v % 4);
+            if (row < M) {
+                const uint32_t w = (uint32_t)as_u16((half_t)acc[t][0][v]) |
+                                   ((uint32_t)as_u16((half_t)acc[t][1][v]) << 16);
+                *reinterpret_cast<uint32_t *>(Y + (size_t)row * N + col) = w;
+            }
+        }
+}
+
+template <bool SYM>
+hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
+                  uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
+    const long long tiles = (long long)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    hipLaunchKernelGGL((mfma32_kernel<SYM>), dim3((unsigned)tiles), dim3(256), 0, s, x,
+                       reinterpret_cast<const uint32_t *>(qw), sc,
+                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
+    return hipGetLastError();
+}
+
+}  // namespace m32
+
 template <int BM, bool SYM, bool FAST>
 hipError_t launch_sym(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                       uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
@@ -309,6 +602,9 @@ template <int BM>
 hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                   uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
     const bool fast = G % kBK == 0 && K % (kRing * kBK) == 0;
+    if (fast && AWQ_GEMM_M32)
+        return qz == nullptr ? m32::launch<true>(x, qw, sc, qz, y, M, K, N, G, s)
+                             : m32::launch<false>(x, qw, sc, qz, y, M, K, N, G, s);
     if (qz == nullptr)
         return fast ? launch_sym<BM, true, true>(x, qw, sc, qz, y, M, K, N, G, s)
                     : launch_sym<BM, true, false>(x, qw, sc, qz, y, M, K, N, G, s);
