@@ -351,11 +351,13 @@ __device__ __forceinline__ void unpack_natural(uint32_t w, uint32_t exps, uint32
                0xFFF0FF0Fu;
 }
 
-template <bool SYM>
+// GSHIFT: the group of step kt is kt >> gshift (G / 64 a power of two, or
+// gshift = 31 when G == K: one group); otherwise kt / (G / 64).
+template <bool SYM, bool GSHIFT>
 __global__ void __launch_bounds__(256)
 mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
-              uint16_t *__restrict__ Y, int M, int K, int N, int G) {
+              uint16_t *__restrict__ Y, int M, int K, int N, int G, int gshift) {
     constexpr int BLOADS = SYM ? 3 : 4;   // per step: 2 packed-row loads, scales, zeros
     constexpr int LOADS = kACH + BLOADS;
     __shared__ __attribute__((aligned(16))) uint4 ring0[kBM * 8];
@@ -400,14 +402,17 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const uint32_t svoff = (uint32_t)(n0 + 2 * (lane & 31)) * 2u;
     const uint32_t zvoff = (uint32_t)(n0 / 8 + (lane & 7)) * 4u;
 
+    // Byte strides: a step of packed rows, half of it, a scale row, a zero row.
+    const int qstep = 32 * N, qhalf = 16 * N, srow = 2 * N, zrow = N / 2;
+    const int gsteps = G / kBK;
     auto load_step = [&](int kt, uint4 *xbuf, uint4 *bbuf) {
         uint4 *dst = bbuf + wave * kWave;
-#pragma unroll
-        for (int d = 0; d < 2; ++d)
-            buffer_to_lds16(qrs, dst + 64 * d, qvoff, (kt * (kBK / 8) + 4 * d) * N * 4);
-        const int g = (kt * kBK) / G;
-        buffer_to_lds4(srs, dst + kScale, svoff, g * N * 2);
-        if constexpr (!SYM) buffer_to_lds4(zrs, dst + kZero, zvoff, g * (N / 8) * 4);
+        const int qo = kt * qstep;
+        buffer_to_lds16(qrs, dst, qvoff, qo);
+        buffer_to_lds16(qrs, dst + 64, qvoff, qo + qhalf);
+        const int g = GSHIFT ? (kt >> gshift) : kt / gsteps;
+        buffer_to_lds4(srs, dst + kScale, svoff, g * srow);
+        if constexpr (!SYM) buffer_to_lds4(zrs, dst + kZero, zvoff, g * zrow);
 #pragma unroll
         for (int i = 0; i < kACH; ++i)
             buffer_to_lds16(xrs, xbuf + (i * 4 + wave) * 64, xvoff[i], kt * kBK * 2);
@@ -580,9 +585,18 @@ template <bool SYM>
 hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                   uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
     const long long tiles = (long long)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    hipLaunchKernelGGL((mfma32_kernel<SYM>), dim3((unsigned)tiles), dim3(256), 0, s, x,
-                       reinterpret_cast<const uint32_t *>(qw), sc,
-                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
+    const int gsteps = G / kBK;
+    int gshift = -1;
+    if (G == K) gshift = 31;
+    else if ((gsteps & (gsteps - 1)) == 0) gshift = __builtin_ctz((unsigned)gsteps);
+    const auto *q = reinterpret_cast<const uint32_t *>(qw);
+    const auto *z = reinterpret_cast<const uint32_t *>(qz);
+    if (gshift >= 0)
+        hipLaunchKernelGGL((mfma32_kernel<SYM, true>), dim3((unsigned)tiles), dim3(256), 0, s, x, q,
+                           sc, z, y, M, K, N, G, gshift);
+    else
+        hipLaunchKernelGGL((mfma32_kernel<SYM, false>), dim3((unsigned)tiles), dim3(256), 0, s, x, q,
+                           sc, z, y, M, K, N, G, 0);
     return hipGetLastError();
 }
 
