@@ -312,6 +312,7 @@ fold_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     for (int d = 0; d < D; ++d) compute_seg(s_begin + per - D + d, b[d]);
 
     // C layout of the 16x16 MFMA: lane (kb, c16) holds rows 4 kb + v of column c16.
+    __syncthreads();   // every wave is done with the staged X and the tables
 #pragma unroll
     for (int v = 0; v < VR; ++v) {
         const int m = 4 * kb + v;
@@ -331,7 +332,7 @@ fold_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 }
 
 // ---------------------------------------------------------------------------
-// Small batches (M <= 4), the decode case.
+// Small batches (M <= 16, X staged in LDS), the decode case.
 //
 // Each wave stages the rows of X that its K range needs in its own LDS slice
 // (no workgroup barrier), each 8-k chunk already in the k order of the
@@ -384,7 +385,9 @@ struct WSeg {
 };
 
 // Chunks of staged X per lane, at most.
-constexpr int kStageChunks = 4;
+constexpr int kStageChunks = 16;
+// LDS of one workgroup, at most (gfx950: 160 KB per workgroup).
+constexpr size_t kLdsMax = 160 * 1024;
 
 // XCH: 16-byte chunks of X each lane stages (M * K / 8 / NW <= 64 * XCH).
 template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH>
@@ -409,11 +412,12 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const int r_begin = wave * rows_w;
     const int spg = G / (8 * SEGR);              // segments per group
 
-    // LDS: staged X slices (all waves), then (U, S) tables, then the reduction.
+    // LDS: staged X slices (all waves), then (U, S) tables; once every wave is
+    // done with them, the reduction buffer takes their place.
     uint4 *xs = lds + wave * (M * rows_w);
     float2 *tabs = reinterpret_cast<float2 *>(lds + M * KR);
     float2 *tab = tabs + wave * (M * per);
-    float *red = reinterpret_cast<float *>(tabs + NW * M * per);
+    float *red = reinterpret_cast<float *>(lds);
 
     const int xrow = c16 < M ? c16 : M - 1;      // A row of this lane (clamped)
     const uint32_t lane_q = (uint32_t)(ncl + kb * N);
@@ -540,6 +544,7 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     for (int d = 0; d < D; ++d) compute_seg(s_begin + per - D + d, b[d]);
 
     // C layout of the 16x16 MFMA: lane (kb, c16) holds rows 4 kb + v of column c16.
+    __syncthreads();   // every wave is done with the staged X and the tables
 #pragma unroll
     for (int v = 0; v < VR; ++v) {
         const int m = 4 * kb + v;
@@ -558,31 +563,45 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     }
 }
 
+// Dynamic LDS of stream_kernel: staged X and tables, or the reduction buffer
+// that replaces them at the end, whichever is larger.
+inline size_t stream_lds(int M, int K, int WPL, int NW, int SEGR) {
+    const int per = K / 8 / SEGR / NW;
+    const size_t staged = (size_t)M * K * 2 + (size_t)NW * M * per * 8;
+    const size_t red = (size_t)NW * M * 16 * WPL * 4;
+    return staged > red ? staged : red;
+}
+
 template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH>
 hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                          hipStream_t s) {
     constexpr int TN = 16 * WPL;
-    const int per = K / 8 / SEGR / NW;
-    const size_t lds = (size_t)M * K * 2 + (size_t)NW * M * per * sizeof(float2) +
-                       (size_t)NW * M * TN * sizeof(float);
-    hipLaunchKernelGGL((stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH>), dim3((N + TN - 1) / TN),
-                       dim3(NW * 64), lds, s, x, reinterpret_cast<const uint32_t *>(qw), sc,
+    auto kernel = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH>;
+    const size_t lds = stream_lds(M, K, WPL, NW, SEGR);
+    if (lds > 64 * 1024) {
+        // Beyond 64 KB the kernel must be allowed the larger allocation (once).
+        static const hipError_t raised = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+            (int)kLdsMax);
+        if (raised != hipSuccess) return raised;
+    }
+    hipLaunchKernelGGL(kernel, dim3((N + TN - 1) / TN), dim3(NW * 64), lds, s, x,
+                       reinterpret_cast<const uint32_t *>(qw), sc,
                        reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
     return hipGetLastError();
 }
 
 // Whether stream_kernel<.., NW, SEGR, D, ..> can take this shape: the segments
 // split evenly over the waves in whole pipelines of D, each wave's X slice fits
-// kStageChunks chunks per lane, and all of LDS stays within 64 KB.
+// kStageChunks chunks per lane, and LDS stays within the workgroup maximum.
 inline bool stream_fits(int M, int K, int N, int G, int WPL, int NW, int SEGR, int D) {
-    if (M > 4 || G % (8 * SEGR) != 0) return false;
+    if (M > 16 || G % (8 * SEGR) != 0) return false;
     const int nseg = K / 8 / SEGR;
     if (nseg % NW != 0 || (nseg / NW) % D != 0) return false;
     const int per = nseg / NW;
     if (M * per * SEGR > 64 * kStageChunks) return false;
-    const size_t lds = (size_t)M * K * 2 + (size_t)NW * M * per * 8 + (size_t)NW * M * 16 * WPL * 4;
-    return lds <= 64 * 1024;
+    return stream_lds(M, K, WPL, NW, SEGR) <= kLdsMax;
 }
 
 template <int WPL, int NW, int SEGR, int D, int VR, int XCH>
@@ -604,6 +623,8 @@ hipError_t launch_stream_x(const uint16_t *x, const int32_t *qw, const uint16_t 
     const int chunks_w = M * (K / 8 / NW);
     if (chunks_w <= 64) return launch_stream_sg<WPL, NW, SEGR, D, VR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
     if (chunks_w <= 128) return launch_stream_sg<WPL, NW, SEGR, D, VR, 2>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (chunks_w <= 256) return launch_stream_sg<WPL, NW, SEGR, D, VR, 4>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (chunks_w <= 512) return launch_stream_sg<WPL, NW, SEGR, D, VR, 8>(x, qw, sc, qz, y, M, K, N, G, s);
     return launch_stream_sg<WPL, NW, SEGR, D, VR, kStageChunks>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
@@ -765,7 +786,11 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
                        hipStream_t s) {
     using namespace gemv;
-    // Decode shapes: per-wave staged X, D-deep load pipeline.
+    // Per-wave staged X (up to 160 KB of LDS), D-deep load pipeline.  Beyond
+    // four rows, X fills most of LDS (one workgroup per CU), so each workgroup
+    // takes a twice wider strip: fewer workgroups, each staging X once.
+    if (M > 4 && stream_fits(M, K, N, G, 8, 8, 16, 2))
+        return launch_stream_m<8, 8, 16, 2>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 2))
         return launch_stream_m<4, 8, 16, 2>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 1))
