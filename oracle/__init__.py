@@ -72,6 +72,9 @@ class Oracle:
                                        ctypes.c_int, _u16p]
         lib.oracle_matmul_w.argtypes = [_u16p, _u16p, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, _f64p, _u16p]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_gate_up.argtypes = [_f64p, ctypes.c_int, ctypes.c_int, _u16p]
         lib.oracle_linear.restype = ctypes.c_int
         lib.oracle_linear.argtypes = [_u16p, _i32p, _u16p, _i32p, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, _f64p, _u16p]
@@ -170,6 +173,20 @@ class Oracle:
         if rc != 0:
             raise MemoryError("oracle_linear could not allocate the dequantized weight")
         return Y64, Y16
+
+
+    # -- fused gate/up epilogue ---------------------------------------------
+    def silu(self, t: float) -> float:
+        return self.lib.oracle_silu(float(t))
+
+    def gate_up(self, Y64: np.ndarray) -> np.ndarray:
+        """h = fp16(SiLU(Y64[:, :I]) * Y64[:, I:]) from the layer's fp64 sums."""
+        Y64 = np.ascontiguousarray(Y64, dtype=np.float64)
+        M, N = Y64.shape
+        assert N % 2 == 0
+        H16 = np.empty((M, N // 2), dtype=np.uint16)
+        self.lib.oracle_gate_up(_ptr(Y64, _f64p), M, N // 2, _ptr(H16, _u16p))
+        return H16
 
 
 _DEFAULT: Oracle | None = None

@@ -19,6 +19,12 @@
  *     fp16 arithmetic on activations (unfragile.ai AutoAWQ page, the WQLinear
  *     paragraph; mbrenndoerfer.com, "Loading and Using AWQ Models").
  *
+ *   - The fused inference stack merges a layer's gate and up projections into
+ *     one concatenated MLP module (pyshine.com AutoAWQ tour, the introduction
+ *     and "The Quantization Flow Up Close": QuantFusedMLP); the models it
+ *     serves are Llama-family (unfragile.ai AutoAWQ page, the Llama/Mistral
+ *     paragraph), whose MLP multiplies SiLU(gate) by up.
+ *
  * Readings taken where the pages are silent (each one is a plain choice that
  * the rest of the pages support):
  *   R1  nibble order: code j of a word sits in bits 4j..4j+3 (least significant
@@ -36,6 +42,10 @@
  *       to fp16.
  *   R7  fp16 is IEEE 754 binary16: subnormals kept, overflow to infinity,
  *       round to nearest, ties to even.
+ *   R8  fused gate/up: the layer's N = 2I columns are [gate | up]; the output
+ *       is h[m][n] = fp16(SiLU(y(m, n)) * y(m, I + n)), n < I, with y the
+ *       layer's exact (unrounded) sums and SiLU(t) = t / (1 + e^-t), rounded
+ *       once.
  *
  * Everything is single threaded, unblocked and written for reading, not speed.
  */
@@ -230,4 +240,24 @@ int oracle_linear(const uint16_t *X, const int32_t *Q, const uint16_t *S,
     oracle_matmul_w(X, W, M, K, N, Y64, Y16);
     free(W);
     return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Fused gate/up epilogue (R8).                                               */
+/* ------------------------------------------------------------------------- */
+
+double oracle_silu(double t)
+{
+    /* t * sigmoid(t); for t far below zero exp(-t) overflows to infinity and
+     * the quotient is the correctly signed zero. */
+    return t / (1.0 + exp(-t));
+}
+
+void oracle_gate_up(const double *Y64, int M, int I, uint16_t *H16)
+{
+    for (int m = 0; m < M; ++m) {
+        const double *row = Y64 + (size_t)m * 2 * I;
+        for (int n = 0; n < I; ++n)
+            H16[(size_t)m * I + n] = oracle_d2h(oracle_silu(row[n]) * row[I + n]);
+    }
 }

@@ -14,6 +14,7 @@
  *   X      fp16  [M][K]       activations
  *   W      fp16  [K][N]       dequantized weight
  *   Y64    fp64  [M][N]       exact-order fp64 sum; Y16 its fp16 rounding
+ *   H16    fp16  [M][N/2]     fused gate/up output, columns [gate | up] of Y
  */
 #ifndef W4A16_ORACLE_H
 #define W4A16_ORACLE_H
@@ -46,6 +47,9 @@ void oracle_matmul_w(const uint16_t *X, const uint16_t *W, int M, int K, int N,
 int  oracle_linear(const uint16_t *X, const int32_t *Q, const uint16_t *S,
                    const int32_t *QZ, int M, int K, int N, int G,
                    double *Y64, uint16_t *Y16);
+
+double oracle_silu(double t);
+void   oracle_gate_up(const double *Y64, int M, int I, uint16_t *H16);
 
 #ifdef __cplusplus
 }

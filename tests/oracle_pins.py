@@ -23,6 +23,8 @@ import os
 import sys
 from fractions import Fraction
 
+import math
+
 import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -372,6 +374,83 @@ def pin_rows_independent(o):
     rows = [4, 1]
     Y64r, Y16r = o.linear(X[rows], Q, S, None, G)
     assert np.array_equal(Y64r, Y64[rows]) and np.array_equal(Y16r, Y16[rows])
+
+
+def _lambert_w_inv_e():
+    """W(1/e): the root of w e^w = 1/e, by Newton's method in plain floats."""
+    w = 0.25
+    for _ in range(60):
+        f = w * math.exp(w) - math.exp(-1.0)
+        w -= f / (math.exp(w) * (w + 1.0))
+    return w
+
+
+def pin_silu_closed_forms(o):
+    """SiLU(t) = t sigmoid(t): values the definition fixes in closed form."""
+    ln3 = math.log(3.0)
+    assert o.silu(0.0) == 0.0
+    # sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4
+    assert abs(o.silu(ln3) - 0.75 * ln3) <= 4e-16 * ln3
+    assert abs(o.silu(-ln3) + 0.25 * ln3) <= 4e-16 * ln3
+    # sigmoid(t) + sigmoid(-t) = 1, hence SiLU(t) - SiLU(-t) = t
+    rng = np.random.default_rng(21)
+    for t in rng.uniform(-30.0, 30.0, 200):
+        assert abs(o.silu(t) - o.silu(-t) - t) <= 1e-14 * max(1.0, abs(t))
+    # saturation: SiLU(t) = t once e^-t is below half an ulp of 1; tiny and
+    # negative far below zero, and the correctly signed zero past overflow
+    assert o.silu(60.0) == 60.0
+    assert -1e-24 < o.silu(-60.0) < 0.0
+    assert o.silu(-800.0) == 0.0 and math.copysign(1.0, o.silu(-800.0)) < 0
+    # the global minimum: at t* = -1 - W(1/e), SiLU(t*) = t* + 1 = -W(1/e)
+    w = _lambert_w_inv_e()
+    t_star = -1.0 - w
+    assert abs(o.silu(t_star) + w) <= 1e-15
+    grid = np.linspace(t_star - 0.01, t_star + 0.01, 2001)
+    assert min(o.silu(t) for t in grid) >= -w - 1e-15
+
+
+def pin_gate_up_composition(o):
+    """Fused gate/up on a hand-built layer: columns [gate | up], h = SiLU(gate) up.
+
+    K = G = 8, X = ones (twos in row 2), s = 1, z = 0, so each output is its
+    column's code sum (doubled in row 2).  Gate sums of 0 give h = 0 whatever
+    the up column; gate sums of 16 and 32 saturate SiLU to within 1.2e-7
+    relative, so h = fp16(gate * up) there; gate sums of 1, 2 and 4 are where
+    SiLU bends: there sigmoid(t) = e^t / (1 + e^t), evaluated with the constant
+    e, and h is that times t and up, rounded to fp16 (numpy's conversion).
+    """
+    I = 10
+    gate = [0, 16, 16, 0, 16, 0, 16, 16, 1, 2]
+    up = [40, 3, 0, 120, 1, 8, 6, 2, 7, 9]
+    codes = np.zeros((8, 2 * I), dtype=np.uint8)
+    for n in range(I):
+        for c, total in ((n, gate[n]), (I + n, up[n])):
+            left = total
+            for k in range(8):          # spread each sum over the 8 codes
+                codes[k, c] = min(15, left)
+                left -= codes[k, c]
+            assert left == 0
+    Q = o.pack(codes)
+    S = np.full((1, 2 * I), 0x3C00, dtype=np.uint16)
+    QZ = o.pack_zeros(np.zeros((1, 2 * I), dtype=np.uint8))
+    X = np.array([[0x3C00] * 8, [0x4000] * 8], dtype=np.uint16)   # ones, twos
+    Y64, _ = o.linear(X, Q, S, QZ, 8)
+    assert list(Y64[0, :I]) == gate and list(Y64[0, I:]) == up
+    H = o.gate_up(Y64)
+
+    def sig(t):
+        return math.e ** t / (1.0 + math.e ** t)
+
+    for row, f in ((0, 1), (1, 2)):
+        for n in range(I):
+            g, u = f * gate[n], f * up[n]
+            if g == 0:
+                want = 0.0
+            elif g >= 16:
+                want = float(g * u)
+            else:
+                want = g * sig(g) * u
+            assert H[row, n] == _np_d2h(np.array([want]))[0], (row, n, _np_h2d(H[row, n]), want)
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

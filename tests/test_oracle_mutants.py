@@ -42,6 +42,11 @@ MUTANTS = [
     ("matmul_w_transposed", "acc[n] += x * wrow[n];", "acc[n] += x * Wd[((size_t)n * K + k) % ((size_t)K * N)];", 0),
     ("matmul_fp32_accumulate", "acc[n] += x * wrow[n];", "acc[n] = (float)(acc[n] + x * wrow[n]);", 0),
     ("matmul_y_row_offset", "Y16[(size_t)m * N + n] = oracle_d2h(acc[n]);", "Y16[(size_t)m * N + n] = oracle_d2h(acc[(n + 1) % N]);", 0),
+    ("silu_is_sigmoid", "return t / (1.0 + exp(-t));", "return 1.0 / (1.0 + exp(-t));", 0),
+    ("silu_exp_sign", "return t / (1.0 + exp(-t));", "return t / (1.0 + exp(t));", 0),
+    ("gate_up_swapped", "oracle_silu(row[n]) * row[I + n]", "oracle_silu(row[I + n]) * row[n]", 0),
+    ("gate_up_no_silu", "oracle_silu(row[n]) * row[I + n]", "row[n] * row[I + n]", 0),
+    ("gate_up_row_stride", "const double *row = Y64 + (size_t)m * 2 * I;", "const double *row = Y64 + (size_t)m * I;", 0),
 ]
 
 
