@@ -157,6 +157,49 @@ def bench_gemv(name, steps, warmup):
             "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_gate_up(name, M, steps, warmup):
+    """awq_gemv_gate_up on a concatenated [gate | up] layer: h = SiLU(gate) * up."""
+    import torch
+    from w4a16_group_quantized_amd import synth
+    w = synth.WORKLOADS[name]
+    copies = max(2, math.ceil(ROTATE_BYTES / alg_bytes(w, 0)))
+    layers = build_layers(w, copies)
+    X = synth.make_x(max(M, w.M), w.K, w.wid, w.n_outliers, w.outlier_gain)[:M]
+    X = to_dev(np.ascontiguousarray(X))
+    h = torch.empty((M, w.N // 2), dtype=torch.float16, device="cuda")
+    t = time_calls("gemv_gate_up", X, layers, h, steps, warmup)
+    b = alg_bytes(w, M) - 2 * M * w.N + 2 * M * (w.N // 2)   # h replaces Y
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": name, "M": M, "K": w.K, "N": w.N, "group_size": w.G,
+            "symmetric": w.symmetric, "entry": "awq_gemv_gate_up", "weight_copies": copies,
+            "us_per_call": t * 1e6, "alg_bytes": b, "gbs": b / t / 1e9,
+            "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS}
+
+
+def torch_matmul_context(name, steps):
+    """Not the metric: torch.matmul (the vendor fp16 GEMM) on the dequantized
+    weight of the same shape, for context on what a plain fp16 GEMM reaches."""
+    import torch
+    from w4a16_group_quantized_amd import synth
+    w = synth.WORKLOADS[name]
+    a = torch.randn(w.M, w.K, dtype=torch.float16, device="cuda")
+    b = torch.randn(w.K, w.N, dtype=torch.float16, device="cuda") * 0.01
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        a @ b
+    e1.record()
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    flops = 2.0 * w.M * w.N * w.K
+    return {"workload": name, "entry": "torch.matmul fp16 (context, not the metric)",
+            "us_per_call": t * 1e6, "tflops": flops / t / 1e12}
+
+
 def bench_gemm(name, steps, warmup):
     import torch
     from w4a16_group_quantized_amd import synth
@@ -361,6 +404,10 @@ def main():
         extra.append(bench_gemv("sym70b_m1", args.steps, args.warmup))
         extra.append(bench_gemm("gate_up_m16", args.steps, args.warmup))
         extra.append(bench_gemm("sym70b_m4096", max(5, args.steps // 40), 2))
+        extra.append(bench_gate_up("gate_up_m16", 16, args.steps, args.warmup))
+        extra.append(bench_gate_up("gate_up_m16", 1, args.steps, args.warmup))
+        extra.append(torch_matmul_context("prefill_out_proj", 50))
+        extra.append(torch_matmul_context("sym70b_m4096", 5))
 
     traffic = committed_traffic()
     out = {

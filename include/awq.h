@@ -117,6 +117,30 @@ awq_status awq_gemv(const uint16_t *x, const awq_layer *layer, uint16_t *y, int3
 awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
                     void *stream);
 
+/*
+ * awq_gemv_gate_up: the fused MLP front of a Llama-style block in one pass.
+ * The inference stack concatenates the gate and up projections into one
+ * quantized MLP module (pyshine.com AutoAWQ tour, the introduction and "The
+ * Quantization Flow Up Close": QuantFusedMLP); the Llama-family MLP then
+ * multiplies SiLU(gate) by up (unfragile.ai AutoAWQ page, the Llama/Mistral
+ * paragraph).
+ *
+ * The layer holds the concatenation: its N = 2I columns are [gate | up]
+ * (columns n < I the gate projection, I + n the up projection of the same
+ * output n), packed, scaled and zeroed like any layer.  The output is
+ *     h[m][n] = fp16_rne(SiLU(y(m, n)) * y(m, I + n)),   n < I,
+ * with y the layer's fp32 sums (never rounded to fp16 on the way) and
+ * SiLU(t) = t / (1 + e^-t) in fp32.  Y is never written.
+ *   x: device fp16 [M][K];  h: device fp16 [M][I], 16-byte aligned.
+ * Rules beyond the layer's: 1 <= M <= 16 (M == 0 is a no-op); N % 16 == 0
+ * (I a multiple of 8).  Shapes the fused kernel does not cover return
+ * AWQ_ERROR_UNSUPPORTED with nothing launched: G must be a multiple of 128,
+ * K a multiple of 128, and M * K * 2 bytes of X must fit next to the kernel's
+ * tables in the 160 KB of LDS of one workgroup (e.g. M = 16 at K = 4096).
+ */
+awq_status awq_gemv_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t *h, int32_t M,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ LIBRARY = os.path.join(HERE, "libawq.so")
 
 # Entry points declared in include/awq.h, in declaration order.
 ENTRY_POINTS = ("awq_status_string", "awq_pack", "awq_pack_zeros", "awq_dequant", "awq_gemv",
-                "awq_gemm")
+                "awq_gemm", "awq_gemv_gate_up")
 
 AWQ_SUCCESS = 0
 STATUS_NAMES = {0: "AWQ_SUCCESS", 1: "AWQ_ERROR_INVALID_VALUE", 2: "AWQ_ERROR_SHAPE",
@@ -63,7 +63,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.awq_pack_zeros.argtypes = [vp, vp, i32, i32, vp]
     lib.awq_dequant.restype = ctypes.c_int
     lib.awq_dequant.argtypes = [ctypes.POINTER(CLayer), vp, vp]
-    for name in ("awq_gemv", "awq_gemm"):
+    for name in ("awq_gemv", "awq_gemm", "awq_gemv_gate_up"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.POINTER(CLayer), vp, i32, vp]
@@ -149,14 +149,16 @@ def dequant(layer: Layer, out: torch.Tensor | None = None, stream=None) -> torch
     return out
 
 
-def _linear(fn_name: str, x: torch.Tensor, layer: Layer, out: torch.Tensor | None, stream):
+def _linear(fn_name: str, x: torch.Tensor, layer: Layer, out: torch.Tensor | None, stream,
+            width: int | None = None):
     M = x.shape[0]
+    width = layer.N if width is None else width
     if x.dim() != 2 or x.shape[1] != layer.K:
         raise ValueError(f"x must be [M][{layer.K}], got {tuple(x.shape)}")
     if out is None:
-        out = torch.empty((M, layer.N), dtype=torch.float16, device=x.device)
-    elif tuple(out.shape) != (M, layer.N):
-        raise ValueError(f"out must be [{M}][{layer.N}], got {tuple(out.shape)}")
+        out = torch.empty((M, width), dtype=torch.float16, device=x.device)
+    elif tuple(out.shape) != (M, width):
+        raise ValueError(f"out must be [{M}][{width}], got {tuple(out.shape)}")
     c = layer.c_struct()
     _check(getattr(load(), fn_name)(_dev(x, torch.float16, "x"), ctypes.byref(c),
                                     _dev(out, torch.float16, "out"), M, _stream(stream)))
@@ -171,3 +173,9 @@ def gemv(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=
 def gemm(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=None):
     """y = x @ dequant(layer) for any M (prefill / batches)."""
     return _linear("awq_gemm", x, layer, out, stream)
+
+
+def gemv_gate_up(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=None):
+    """h = SiLU(y[:, :N/2]) * y[:, N/2:] with y = x @ dequant(layer), 1 <= M <= 16; the
+    layer's columns are the concatenation [gate | up]."""
+    return _linear("awq_gemv_gate_up", x, layer, out, stream, width=layer.N // 2)

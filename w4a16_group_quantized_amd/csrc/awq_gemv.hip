@@ -381,8 +381,33 @@ template <int WPL, int STEPS, bool SYM>
 struct WSeg {
     Words<WPL> q[STEPS];
     Scales<WPL> sc;
-    uint32_t zw;
+    uint32_t zw, zw2;   // zw2: zero word of the up columns (fused gate/up only)
 };
+
+// Two half-width loads side by side (fused gate/up: gate columns, up columns).
+template <int WPL>
+__device__ __forceinline__ Words<WPL> join(const Words<WPL / 2> &a, const Words<WPL / 2> &b) {
+    Words<WPL> r;
+#pragma unroll
+    for (int i = 0; i < WPL / 2; ++i) {
+        r.w[i] = a.w[i];
+        r.w[WPL / 2 + i] = b.w[i];
+    }
+    return r;
+}
+template <int WPL>
+__device__ __forceinline__ Scales<WPL> join(const Scales<WPL / 2> &a, const Scales<WPL / 2> &b) {
+    Scales<WPL> r;
+#pragma unroll
+    for (int i = 0; i < WPL / 4; ++i) {
+        r.h[i] = a.h[i];
+        r.h[WPL / 4 + i] = b.h[i];
+    }
+    return r;
+}
+
+// SiLU in fp32: t / (1 + e^-t); far below zero the quotient is a signed zero.
+__device__ __forceinline__ float silu(float t) { return t / (1.0f + __expf(-t)); }
 
 // Chunks of staged X per lane, at most.
 constexpr int kStageChunks = 16;
@@ -390,12 +415,17 @@ constexpr int kStageChunks = 16;
 constexpr size_t kLdsMax = 160 * 1024;
 
 // XCH: 16-byte chunks of X each lane stages (M * K / 8 / NW <= 64 * XCH).
-template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH>
+// GU (fused gate/up): the layer's N columns are [gate | up]; a lane's WPL words
+// are WPL / 2 gate columns and the same WPL / 2 columns of the up half, and the
+// output is h = fp16(SiLU(gate) * up), N / 2 columns wide.
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false>
 __global__ void __launch_bounds__(NW * 64)
 stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
               uint16_t *__restrict__ Y, int M, int K, int N, int G) {
-    constexpr int TN = 16 * WPL;
+    constexpr int TN = 16 * WPL;              // weight columns (MFMA column slots) per workgroup
+    constexpr int WO = GU ? WPL / 2 : WPL;    // output columns per lane
+    constexpr int TO = 16 * WO;               // output columns per workgroup
     constexpr int STEPS = SEGR / 4;
     extern __shared__ __attribute__((aligned(16))) uint4 lds[];
 
@@ -403,9 +433,10 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c16 = lane & 15;   // column block of B, row of A, column of C
     const int kb = lane >> 4;    // packed row within a step; C rows 4 kb .. 4 kb + 3
-    const int n0 = blockIdx.x * TN;
-    const int ncol = n0 + WPL * c16;
-    const int ncl = ncol < N ? ncol : N - WPL;   // clamped: in bounds, result dropped
+    const int NO = GU ? N / 2 : N;               // output width
+    const int n0 = blockIdx.x * TO;
+    const int ncol = n0 + WO * c16;
+    const int ncl = ncol < NO ? ncol : NO - WO;  // clamped: in bounds, result dropped
     const int KR = K / 8;
     const int per = KR / SEGR / NW;              // segments per wave (multiple of D)
     const int rows_w = per * SEGR;               // packed rows per wave
@@ -428,11 +459,19 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             const uint32_t *qrow = Q + (size_t)(r0 + 4 * st) * N;   // wave-uniform
-            b.q[st] = load_words<WPL>(qrow + lane_q);
+            if constexpr (GU)
+                b.q[st] = join<WPL>(load_words<WO>(qrow + lane_q), load_words<WO>(qrow + lane_q + NO));
+            else
+                b.q[st] = load_words<WPL>(qrow + lane_q);
         }
         const int g = (8 * r0) / G;
-        b.sc = load_scales<WPL>(S + (size_t)g * N + ncl);
-        if constexpr (!SYM) b.zw = QZ[(size_t)g * (N / 8) + ncl / 8];
+        const uint16_t *srow = S + (size_t)g * N;
+        if constexpr (GU) b.sc = join<WPL>(load_scales<WO>(srow + ncl), load_scales<WO>(srow + NO + ncl));
+        else b.sc = load_scales<WPL>(srow + ncl);
+        if constexpr (!SYM) {
+            b.zw = QZ[(size_t)g * (N / 8) + ncl / 8];
+            if constexpr (GU) b.zw2 = QZ[(size_t)g * (N / 8) + (NO + ncl) / 8];
+        }
     };
 
     // 1. X loads (clamped, unconditional), 2. the first D segments, 3. staging.
@@ -518,10 +557,12 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         const bool fold = GRP1 || (seg + 1) % spg == 0 || seg == s_begin + per - 1;   // uniform
         if (fold) {
             const uint32_t zw = SYM ? 0u : bb.zw >> (4 * (ncl % 8));
+            const uint32_t zw2 = SYM || !GU ? 0u : bb.zw2 >> (4 * (ncl % 8));   // NO % 8 == 0
 #pragma unroll
             for (int i = 0; i < WPL; ++i) {
                 const float sv = scale_at<WPL>(bb.sc, i);
-                const float z = SYM ? 8.f : (float)((zw >> (4 * i)) & 0xFu);
+                const uint32_t zi = GU && i >= WO ? zw2 >> (4 * (i - WO)) : zw >> (4 * i);
+                const float z = SYM ? 8.f : (float)(zi & 0xFu);
 #pragma unroll
                 for (int v = 0; v < VR; ++v)
                     acc[i][v] = __builtin_fmaf(sv, __builtin_fmaf(-z, Sg[v], C[i][v] - Ug[v]),
@@ -553,13 +594,28 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             for (int i = 0; i < WPL; ++i) red[(wave * M + m) * TN + WPL * c16 + i] = acc[i][v];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < M * TN; idx += NW * 64) {
-        const int m = idx / TN;
-        const int c = idx % TN;
-        float sum = 0.f;
+    if constexpr (GU) {
+        for (int idx = threadIdx.x; idx < M * TO; idx += NW * 64) {
+            const int m = idx / TO;
+            const int c = idx % TO;
+            const int slot = WPL * (c / WO) + c % WO;   // gate slot; up is WO further
+            float gs = 0.f, us = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) sum += red[(w * M + m) * TN + c];
-        if (n0 + c < N) Y[(size_t)m * N + n0 + c] = as_u16((half_t)sum);
+            for (int w = 0; w < NW; ++w) {
+                gs += red[(w * M + m) * TN + slot];
+                us += red[(w * M + m) * TN + slot + WO];
+            }
+            if (n0 + c < NO) Y[(size_t)m * NO + n0 + c] = as_u16((half_t)(silu(gs) * us));
+        }
+    } else {
+        for (int idx = threadIdx.x; idx < M * TN; idx += NW * 64) {
+            const int m = idx / TN;
+            const int c = idx % TN;
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) sum += red[(w * M + m) * TN + c];
+            if (n0 + c < N) Y[(size_t)m * N + n0 + c] = as_u16((half_t)sum);
+        }
     }
 }
 
@@ -572,12 +628,13 @@ inline size_t stream_lds(int M, int K, int WPL, int NW, int SEGR) {
     return staged > red ? staged : red;
 }
 
-template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH>
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false>
 hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                          hipStream_t s) {
-    constexpr int TN = 16 * WPL;
-    auto kernel = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH>;
+    constexpr int TO = GU ? 8 * WPL : 16 * WPL;   // output columns per workgroup
+    const int NO = GU ? N / 2 : N;
+    auto kernel = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU>;
     const size_t lds = stream_lds(M, K, WPL, NW, SEGR);
     if (lds > 64 * 1024) {
         // Beyond 64 KB the kernel must be allowed the larger allocation (once).
@@ -586,7 +643,7 @@ hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *s
             (int)kLdsMax);
         if (raised != hipSuccess) return raised;
     }
-    hipLaunchKernelGGL(kernel, dim3((N + TN - 1) / TN), dim3(NW * 64), lds, s, x,
+    hipLaunchKernelGGL(kernel, dim3((NO + TO - 1) / TO), dim3(NW * 64), lds, s, x,
                        reinterpret_cast<const uint32_t *>(qw), sc,
                        reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
     return hipGetLastError();
@@ -780,7 +837,48 @@ hipError_t launch_exact(const uint16_t *x, const int32_t *qw, const uint16_t *sc
     return hipGetLastError();
 }
 
+// Fused gate/up: 8 words per lane (4 gate + 4 up columns), all live rows, X
+// staged in LDS; the shape must fit stream_kernel.
+template <int NW, int D>
+hipError_t launch_gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                          hipStream_t s) {
+    const bool sym = qz == nullptr, grp1 = G == 8 * 16;
+    const bool big = M * (K / 8 / NW) > 128;
+#define AWQ_GU(SYMV, GRPV, XCHV) \
+    launch_stream<8, NW, 16, D, 4, SYMV, GRPV, XCHV, true>(x, qw, sc, qz, y, M, K, N, G, s)
+    if (big) {
+        if (sym) return grp1 ? AWQ_GU(true, true, kStageChunks) : AWQ_GU(true, false, kStageChunks);
+        return grp1 ? AWQ_GU(false, true, kStageChunks) : AWQ_GU(false, false, kStageChunks);
+    }
+    if (sym) return grp1 ? AWQ_GU(true, true, 2) : AWQ_GU(true, false, 2);
+    return grp1 ? AWQ_GU(false, true, 2) : AWQ_GU(false, false, 2);
+#undef AWQ_GU
+}
+
 }  // namespace gemv
+
+bool gemv_gate_up_supported(int M, int K, int N, int G) {
+    using namespace gemv;
+    return M >= 1 && M <= 16 && N % 16 == 0 &&
+           (stream_fits(M, K, N, G, 8, 8, 16, 2) || stream_fits(M, K, N, G, 8, 8, 16, 1) ||
+            stream_fits(M, K, N, G, 8, 2, 16, 1) || stream_fits(M, K, N, G, 8, 1, 16, 1));
+}
+
+hipError_t launch_gemv_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                               const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
+                               hipStream_t s) {
+    using namespace gemv;
+    if (stream_fits(M, K, N, G, 8, 8, 16, 2))
+        return launch_gate_up<8, 2>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    if (stream_fits(M, K, N, G, 8, 8, 16, 1))
+        return launch_gate_up<8, 1>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    if (stream_fits(M, K, N, G, 8, 2, 16, 1))
+        return launch_gate_up<2, 1>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    if (stream_fits(M, K, N, G, 8, 1, 16, 1))
+        return launch_gate_up<1, 1>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    return hipErrorNotSupported;
+}
 
 hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
