@@ -63,7 +63,7 @@ KERNEL_SOURCES = {
     "gemv": ["awq_gemv.hip", "awq_device.h", "awq_internal.h"],
     "gemm": ["awq_gemm.hip", "awq_device.h", "awq_internal.h"],
 }
-KERNEL_NAMES = {"gemv": ("stream_kernel", "fold_kernel", "exact_kernel"), "gemm": ("gemm_kernel",)}
+KERNEL_NAMES = {"gemv": ("stream_kernel", "fold_kernel", "exact_kernel"), "gemm": ("gemm_kernel", "mfma32_kernel")}
 PROFILE_WORKLOAD = {"gemv": "decode_8b_gate", "gemm": "prefill_out_proj"}
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "awq_gemv_decode_8b_gate_counters.txt")
 
