@@ -72,6 +72,8 @@ class Oracle:
                                        ctypes.c_int, _u16p]
         lib.oracle_matmul_w.argtypes = [_u16p, _u16p, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, _f64p, _u16p]
+        lib.oracle_quantize.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, _u8p, _u16p, _u8p]
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_gate_up.argtypes = [_f64p, ctypes.c_int, ctypes.c_int, _u16p]
@@ -174,6 +176,19 @@ class Oracle:
             raise MemoryError("oracle_linear could not allocate the dequantized weight")
         return Y64, Y16
 
+
+    # -- quantizer ------------------------------------------------------------
+    def quantize(self, W: np.ndarray, G: int, symmetric: bool):
+        """fp16 W[K][N] -> (codes u8 [K][N], scales fp16 [K/G][N], zeros u8 [K/G][N] or None)."""
+        W = np.ascontiguousarray(W, dtype=np.uint16)
+        K, N = W.shape
+        assert K % G == 0
+        codes = np.empty((K, N), dtype=np.uint8)
+        S = np.empty((K // G, N), dtype=np.uint16)
+        Z = None if symmetric else np.empty((K // G, N), dtype=np.uint8)
+        self.lib.oracle_quantize(_ptr(W, _u16p), K, N, G, int(symmetric), _ptr(codes, _u8p),
+                                 _ptr(S, _u16p), _ptr(Z, _u8p))
+        return codes, S, Z
 
     # -- fused gate/up epilogue ---------------------------------------------
     def silu(self, t: float) -> float:

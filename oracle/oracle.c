@@ -42,6 +42,18 @@
  *       to fp16.
  *   R7  fp16 is IEEE 754 binary16: subnormals kept, overflow to infinity,
  *       round to nearest, ties to even.
+ *   R9  quantizer (the step before the layer): each group of G weights of a
+ *       column is rounded to integer levels against a scale and zero point
+ *       (pyshine.com AutoAWQ tour, "The Quantization Flow Up Close": the
+ *       pseudo-quantization pass; "From Install to Your First Model":
+ *       zero_point, q_group_size, w_bit).  The pages give no formula; this is
+ *       textbook min-max, with every decision that yields an integer taken in
+ *       fp32 (IEEE, round to nearest even), the precision the GPU kernel uses:
+ *         asymmetric: r = hi - lo (r = |hi| if hi == lo), s = fp16(r / 15),
+ *                     z = clamp(rint(-lo / s), 0, 15)
+ *         symmetric:  r = max |w|, s = fp16(r / 7), z = 8
+ *         both:       s = 1 if it rounds to 0; q = clamp(rint(w / s) + z, 0, 15)
+ *       with lo, hi the group's minimum and maximum.
  *   R8  fused gate/up: the layer's N = 2I columns are [gate | up]; the output
  *       is h[m][n] = fp16(SiLU(y(m, n)) * y(m, I + n)), n < I, with y the
  *       layer's exact (unrounded) sums and SiLU(t) = t / (1 + e^-t), rounded
@@ -259,5 +271,50 @@ void oracle_gate_up(const double *Y64, int M, int I, uint16_t *H16)
         const double *row = Y64 + (size_t)m * 2 * I;
         for (int n = 0; n < I; ++n)
             H16[(size_t)m * I + n] = oracle_d2h(oracle_silu(row[n]) * row[I + n]);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Quantizer (R9).  float arithmetic is IEEE single precision here (SSE, no  */
+/* contraction), the same precision the GPU kernel decides in.               */
+/* ------------------------------------------------------------------------- */
+
+static float clamp_code(float v)
+{
+    return v < 0.0f ? 0.0f : (v > 15.0f ? 15.0f : v);
+}
+
+void oracle_quantize(const uint16_t *W, int K, int N, int G, int symmetric,
+                     uint8_t *codes, uint16_t *S, uint8_t *zeros)
+{
+    for (int g = 0; g < K / G; ++g) {
+        for (int n = 0; n < N; ++n) {
+            float lo = INFINITY, hi = -INFINITY, amax = 0.0f;
+            for (int k = g * G; k < (g + 1) * G; ++k) {
+                float w = (float)oracle_h2d(W[(size_t)k * N + n]);
+                if (w < lo) lo = w;
+                if (w > hi) hi = w;
+                if (fabsf(w) > amax) amax = fabsf(w);
+            }
+            float r, z;
+            if (symmetric) {
+                r = amax / 7.0f;
+                z = 8.0f;
+            } else {
+                float range = hi - lo;
+                if (range == 0.0f) range = fabsf(hi);
+                r = range / 15.0f;
+            }
+            uint16_t sh = oracle_d2h((double)r);
+            if ((sh & 0x7FFF) == 0) sh = 0x3C00;            /* 1.0 */
+            float sv = (float)oracle_h2d(sh);
+            if (!symmetric) z = clamp_code(rintf(-lo / sv));
+            S[(size_t)g * N + n] = sh;
+            if (zeros) zeros[(size_t)g * N + n] = (uint8_t)z;
+            for (int k = g * G; k < (g + 1) * G; ++k) {
+                float w = (float)oracle_h2d(W[(size_t)k * N + n]);
+                codes[(size_t)k * N + n] = (uint8_t)clamp_code(rintf(w / sv) + z);
+            }
+        }
     }
 }

@@ -48,6 +48,8 @@ int  oracle_linear(const uint16_t *X, const int32_t *Q, const uint16_t *S,
                    const int32_t *QZ, int M, int K, int N, int G,
                    double *Y64, uint16_t *Y16);
 
+void   oracle_quantize(const uint16_t *W, int K, int N, int G, int symmetric,
+                       uint8_t *codes, uint16_t *S, uint8_t *zeros);
 double oracle_silu(double t);
 void   oracle_gate_up(const double *Y64, int M, int I, uint16_t *H16);
 

@@ -453,6 +453,100 @@ def pin_gate_up_composition(o):
             assert H[row, n] == _np_d2h(np.array([want]))[0], (row, n, _np_h2d(H[row, n]), want)
 
 
+def _grid_layer(rng, K, N, G, symmetric):
+    """Weights that are exactly s (q - z) on a per-group grid with power-of-two
+    scales (exact in fp16), every group reaching both ends of its range."""
+    groups = K // G
+    # symmetric: s = max|w| / 7 maps the grid to codes 1..15 (-7 s .. 7 s)
+    codes = rng.integers(1 if symmetric else 0, 16, (K, N)).astype(np.uint8)
+    exps = rng.integers(-12, -2, (groups, N))
+    S = np.ldexp(1.0, exps)
+    if symmetric:
+        Z = np.full((groups, N), 8)
+        ends = (1, 15)                       # +-7 s: the symmetric scale is max|w| / 7
+    else:
+        Z = rng.integers(0, 16, (groups, N))
+        ends = (0, 15)
+    for g in range(groups):
+        codes[g * G, :] = ends[0]
+        codes[g * G + 1, :] = ends[1]
+    Zk = np.repeat(Z, G, axis=0)
+    Sk = np.repeat(S, G, axis=0)
+    W = (codes.astype(np.float64) - Zk) * Sk
+    return _np_d2h(W), codes, _np_d2h(S), Z.astype(np.uint8)
+
+
+def pin_quantize_recovers_grid(o):
+    """Min-max over a group spanning its whole grid recovers that grid exactly:
+    lo = -z s and hi = (15 - z) s give s = range / 15 and z = -lo / s."""
+    rng = np.random.default_rng(31)
+    for sym in (False, True):
+        W, codes, S, Z = _grid_layer(rng, 256, 24, 64, sym)
+        c2, S2, Z2 = o.quantize(W, 64, sym)
+        assert np.array_equal(S2, S), sym
+        assert np.array_equal(c2, codes), sym
+        if not sym:
+            assert np.array_equal(Z2, Z)
+
+
+def pin_quantize_nearest_code(o):
+    """Given its scale and zero point, every code is the nearest of the 16 levels
+    (brute force over all codes), and the scale is range / 15 (or max|w| / 7)
+    rounded once to fp16."""
+    rng = np.random.default_rng(32)
+    K, N, G = 64, 12, 16
+    for sym in (False, True):
+        W = _np_d2h(rng.standard_normal((K, N)) * rng.uniform(0.001, 0.1, (1, N)))
+        codes, S, Z = o.quantize(W, G, sym)
+        w = _np_h2d(W)
+        for g in range(K // G):
+            blk = w[g * G:(g + 1) * G]
+            r = (blk.max(0) - blk.min(0)) / 15.0 if not sym else np.abs(blk).max(0) / 7.0
+            assert np.array_equal(S[g], _np_d2h(r.astype(np.float32).astype(np.float64))), sym
+            s = _np_h2d(S[g])
+            z = np.full(N, 8) if sym else Z[g].astype(np.int64)
+            levels = (np.arange(16)[:, None] - z[None, :]) * s[None, :]      # [16][N]
+            for k in range(g * G, (g + 1) * G):
+                err = np.abs(w[k][None, :] - levels)                            # [16][N]
+                best = err.min(0)
+                got = err[codes[k], np.arange(N)]
+                assert np.all(got <= best * (1 + 1e-6) + 1e-12), (sym, k)
+
+
+def pin_quantize_round_trip_bound(o):
+    """|w - dequant(quantize(w))| <= s / 2 (plus the fp16 rounding of the
+    dequantized weight) wherever the code is not clamped, and <= s at a clamp."""
+    rng = np.random.default_rng(33)
+    K, N, G = 512, 40, 128
+    for sym in (False, True):
+        W = _np_d2h(rng.standard_normal((K, N)) * 0.02)
+        codes, S, Z = o.quantize(W, G, sym)
+        QZ = None if sym else o.pack_zeros(Z)
+        Wq = _np_h2d(o.dequant(o.pack(codes), S, QZ, G))
+        w = _np_h2d(W)
+        s = np.repeat(_np_h2d(S), G, axis=0)
+        err = np.abs(w - Wq)
+        slack = 2.0 ** -11 * np.abs(Wq) + 1e-12
+        clamped = (codes == 0) | (codes == 15)
+        assert np.all(err[~clamped] <= s[~clamped] / 2 + slack[~clamped]), sym
+        assert np.all(err <= s + slack), sym
+
+
+def pin_quantize_degenerate_groups(o):
+    """A constant group c is reproduced (range |c|); an all-zero group gives
+    codes equal to the zero point, scale 1."""
+    K, N, G = 32, 8, 16
+    c = np.array([0.5, -0.25, 3.0, -7.0, 0.0, 0.0, 1e-3, -2.0])
+    W = _np_d2h(np.repeat(c[None, :], K, axis=0))
+    for sym in (False, True):
+        codes, S, Z = o.quantize(W, G, sym)
+        QZ = None if sym else o.pack_zeros(Z)
+        Wq = _np_h2d(o.dequant(o.pack(codes), S, QZ, G))
+        w = _np_h2d(W)
+        assert np.all(np.abs(Wq - w) <= 2.0 ** -9 * np.abs(w)), (sym, Wq[0], w[0])
+        assert np.all(_np_h2d(S[:, 4]) == 1.0) and np.all(_np_h2d(S[:, 5]) == 1.0)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

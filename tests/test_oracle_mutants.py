@@ -42,6 +42,12 @@ MUTANTS = [
     ("matmul_w_transposed", "acc[n] += x * wrow[n];", "acc[n] += x * Wd[((size_t)n * K + k) % ((size_t)K * N)];", 0),
     ("matmul_fp32_accumulate", "acc[n] += x * wrow[n];", "acc[n] = (float)(acc[n] + x * wrow[n]);", 0),
     ("matmul_y_row_offset", "Y16[(size_t)m * N + n] = oracle_d2h(acc[n]);", "Y16[(size_t)m * N + n] = oracle_d2h(acc[(n + 1) % N]);", 0),
+    ("quant_range_16", "r = range / 15.0f;", "r = range / 16.0f;", 0),
+    ("quant_sym_8", "r = amax / 7.0f;", "r = amax / 8.0f;", 0),
+    ("quant_zero_sign", "z = clamp_code(rintf(-lo / sv));", "z = clamp_code(rintf(lo / sv));", 0),
+    ("quant_truncate", "clamp_code(rintf(w / sv) + z)", "clamp_code(truncf(w / sv) + z)", 0),
+    ("quant_no_clamp_low", "return v < 0.0f ? 0.0f : (v > 15.0f ? 15.0f : v);", "return v > 15.0f ? 15.0f : v;", 0),
+    ("quant_group_rows", "for (int k = g * G; k < (g + 1) * G; ++k) {\n                float w = (float)oracle_h2d(W[(size_t)k * N + n]);\n                if (w < lo)", "for (int k = g * G; k < (g + 1) * G - 1; ++k) {\n                float w = (float)oracle_h2d(W[(size_t)k * N + n]);\n                if (w < lo)", 0),
     ("silu_is_sigmoid", "return t / (1.0 + exp(-t));", "return 1.0 / (1.0 + exp(-t));", 0),
     ("silu_exp_sign", "return t / (1.0 + exp(-t));", "return t / (1.0 + exp(t));", 0),
     ("gate_up_swapped", "oracle_silu(row[n]) * row[I + n]", "oracle_silu(row[I + n]) * row[n]", 0),
