@@ -177,6 +177,30 @@ def bench_gate_up(name, M, steps, warmup):
             "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_quantize(name, steps, warmup):
+    """awq_quantize on a layer of the workload's shape: fp16 W -> packed codes,
+    scales, zero points.  Algorithmic bytes: W read once, the layer written."""
+    import torch
+    from w4a16_group_quantized_amd import binding, synth
+    w = synth.WORKLOADS[name]
+    rng = np.random.default_rng(w.wid)
+    W = torch.from_numpy((rng.standard_normal((w.K, w.N)) * 0.02).astype(np.float16)).cuda()
+    for _ in range(max(warmup, 1)):
+        binding.quantize(W, w.G, w.symmetric)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        binding.quantize(W, w.G, w.symmetric)
+    e1.record()
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    b = 2 * w.K * w.N + alg_bytes(w, 0)
+    return {"workload": name, "entry": "awq_quantize", "K": w.K, "N": w.N, "group_size": w.G,
+            "us_per_call": t * 1e6, "alg_bytes": b, "gbs": b / t / 1e9,
+            "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS}
+
+
 def torch_matmul_context(name, steps):
     """Not the metric: torch.matmul (the vendor fp16 GEMM) on the dequantized
     weight of the same shape, for context on what a plain fp16 GEMM reaches."""
@@ -406,6 +430,7 @@ def main():
         extra.append(bench_gemm("sym70b_m4096", max(5, args.steps // 40), 2))
         extra.append(bench_gate_up("gate_up_m16", 16, args.steps, args.warmup))
         extra.append(bench_gate_up("gate_up_m16", 1, args.steps, args.warmup))
+        extra.append(bench_quantize("decode_8b_gate", 20, 3))
         extra.append(torch_matmul_context("prefill_out_proj", 50))
         extra.append(torch_matmul_context("sym70b_m4096", 5))
 

@@ -118,6 +118,27 @@ awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int3
                     void *stream);
 
 /*
+ * awq_quantize: produces a layer from fp16 weights, the step before the fused
+ * kernels (the pages' pseudo-quantization pass rounds each group of weights to
+ * integer levels against a scale and zero point: pyshine.com AutoAWQ tour,
+ * "The Quantization Flow Up Close"; zero_point / q_group_size / w_bit in
+ * "From Install to Your First Model").  Per group of G rows and column n,
+ * textbook min-max with every integer decision in fp32 (round to nearest
+ * even, correctly rounded division):
+ *   asymmetric (symmetric == 0): r = hi - lo (|hi| for a constant group),
+ *       s = fp16(r / 15), z = clamp(rint(-lo / s), 0, 15)
+ *   symmetric (symmetric != 0): s = fp16(max|w| / 7), zero point 8
+ *   both: s = 1 if it rounds to 0; code = clamp(rint(w / s) + z, 0, 15)
+ * lo, hi: the group's minimum and maximum.  Weights must be finite.
+ *   w: device fp16 [K][N].  Outputs as in awq_layer: qweight int32 [K/8][N],
+ *   scales fp16 [K/G][N], qzeros int32 [K/G][N/8] (not written, and may be
+ *   NULL, when symmetric).  Shape and alignment rules are the layer's.
+ */
+awq_status awq_quantize(const uint16_t *w, int32_t K, int32_t N, int32_t group_size,
+                        int32_t symmetric, int32_t *qweight, uint16_t *scales, int32_t *qzeros,
+                        void *stream);
+
+/*
  * awq_gemv_gate_up: the fused MLP front of a Llama-style block in one pass.
  * The inference stack concatenates the gate and up projections into one
  * quantized MLP module (pyshine.com AutoAWQ tour, the introduction and "The

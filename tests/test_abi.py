@@ -89,6 +89,20 @@ def test_gemv_rejects_large_batches(lib):
     assert lib.awq_gemv(FAKE, ctypes.byref(c), FAKE, 17, None) == 4
 
 
+def test_quantize_validation(lib):
+    """Arguments the quantizer rejects before any launch."""
+    f = lib.awq_quantize
+    assert f(None, 128, 64, 128, 0, FAKE, FAKE, FAKE, None) == 1          # null w
+    assert f(FAKE, 128, 64, 128, 0, FAKE, FAKE, None, None) == 1          # asymmetric needs qzeros
+    assert f(FAKE, 0, 64, 128, 0, FAKE, FAKE, FAKE, None) == 1            # K = 0
+    assert f(FAKE, 128, 64, 0, 1, FAKE, FAKE, None, None) == 1            # G = 0
+    assert f(FAKE, 120, 64, 128, 1, FAKE, FAKE, None, None) == 2          # K % G
+    assert f(FAKE, 128, 60, 128, 1, FAKE, FAKE, None, None) == 2          # N % 8
+    assert f(FAKE, 128, 64, 12, 1, FAKE, FAKE, None, None) == 2           # G % 8
+    assert f(MISALIGNED, 128, 64, 128, 1, FAKE, FAKE, None, None) == 3
+    assert f(FAKE, 128, 64, 128, 0, FAKE, FAKE, MISALIGNED, None) == 3
+
+
 def test_gate_up_validation(lib):
     """Shapes the fused gate/up entry rejects before any launch."""
     f = lib.awq_gemv_gate_up

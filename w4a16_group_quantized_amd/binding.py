@@ -21,7 +21,7 @@ LIBRARY = os.path.join(HERE, "libawq.so")
 
 # Entry points declared in include/awq.h, in declaration order.
 ENTRY_POINTS = ("awq_status_string", "awq_pack", "awq_pack_zeros", "awq_dequant", "awq_gemv",
-                "awq_gemm", "awq_gemv_gate_up")
+                "awq_gemm", "awq_gemv_gate_up", "awq_quantize")
 
 AWQ_SUCCESS = 0
 STATUS_NAMES = {0: "AWQ_SUCCESS", 1: "AWQ_ERROR_INVALID_VALUE", 2: "AWQ_ERROR_SHAPE",
@@ -63,6 +63,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.awq_pack_zeros.argtypes = [vp, vp, i32, i32, vp]
     lib.awq_dequant.restype = ctypes.c_int
     lib.awq_dequant.argtypes = [ctypes.POINTER(CLayer), vp, vp]
+    lib.awq_quantize.restype = ctypes.c_int
+    lib.awq_quantize.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
     for name in ("awq_gemv", "awq_gemm", "awq_gemv_gate_up"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -138,6 +140,21 @@ def make_layer(codes: torch.Tensor, zeros: torch.Tensor | None, scales: torch.Te
     K, N = codes.shape
     qz = None if zeros is None else pack_zeros(zeros, stream)
     return Layer(pack(codes, stream), scales, qz, K, N, group_size)
+
+
+def quantize(w: torch.Tensor, group_size: int, symmetric: bool = False, stream=None) -> Layer:
+    """fp16 W[K][N] -> a Layer (packed codes, scales, zero points or None), by
+    per-group min-max."""
+    K, N = w.shape
+    dev = w.device
+    qweight = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
+    scales = torch.empty((K // group_size, N), dtype=torch.float16, device=dev)
+    qzeros = None if symmetric else torch.empty((K // group_size, N // 8), dtype=torch.int32,
+                                                 device=dev)
+    _check(load().awq_quantize(_dev(w, torch.float16, "w"), K, N, group_size, int(symmetric),
+                               qweight.data_ptr(), scales.data_ptr(),
+                               None if qzeros is None else qzeros.data_ptr(), _stream(stream)))
+    return Layer(qweight, scales, qzeros, K, N, group_size)
 
 
 def dequant(layer: Layer, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

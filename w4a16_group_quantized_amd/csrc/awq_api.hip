@@ -101,6 +101,21 @@ awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int3
                                      layer->K, layer->N, layer->group_size, as_stream(stream)));
 }
 
+awq_status awq_quantize(const uint16_t *w, int32_t K, int32_t N, int32_t group_size,
+                        int32_t symmetric, int32_t *qweight, uint16_t *scales, int32_t *qzeros,
+                        void *stream) {
+    if (w == nullptr || qweight == nullptr || scales == nullptr || (!symmetric && qzeros == nullptr))
+        return AWQ_ERROR_INVALID_VALUE;
+    if (K <= 0 || N <= 0 || group_size <= 0) return AWQ_ERROR_INVALID_VALUE;
+    if (K % 8 || N % 8 || group_size % 8 || K % group_size || (long long)K * N > kMaxElems)
+        return AWQ_ERROR_SHAPE;
+    if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) ||
+        (!symmetric && !aligned16(qzeros)))
+        return AWQ_ERROR_ALIGNMENT;
+    return from_hip(awq::launch_quantize(w, qweight, scales, qzeros, K, N, group_size,
+                                         symmetric != 0, as_stream(stream)));
+}
+
 awq_status awq_gemv_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t *h, int32_t M,
                             void *stream) {
     awq_status st = check_layer(layer);

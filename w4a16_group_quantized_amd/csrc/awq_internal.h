@@ -15,6 +15,8 @@ hipError_t launch_dequant(const int32_t *qweight, const uint16_t *scales, const 
 hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
                        hipStream_t s);
+hipError_t launch_quantize(const uint16_t *w, int32_t *qweight, uint16_t *scales, int32_t *qzeros,
+                           int K, int N, int G, bool symmetric, hipStream_t s);
 // Fused gate/up (layer columns [gate | up], h = fp16(SiLU(gate) * up)).
 bool gemv_gate_up_supported(int M, int K, int N, int G);
 hipError_t launch_gemv_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
