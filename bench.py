@@ -177,6 +177,23 @@ def bench_gate_up(name, M, steps, warmup):
             "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_gemm_gate_up(name, M, steps, warmup):
+    """awq_gemm_gate_up at batch M on a concatenated [gate | up] layer."""
+    import torch
+    from w4a16_group_quantized_amd import synth
+    w = synth.WORKLOADS[name]
+    layers = build_layers(w, 1)
+    X = to_dev(synth.make_x(M, w.K, w.wid, w.n_outliers, w.outlier_gain))
+    h = torch.empty((M, w.N // 2), dtype=torch.float16, device="cuda")
+    t = time_calls("gemm_gate_up", X, layers, h, steps, warmup)
+    flops = 2.0 * M * w.N * w.K
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": name, "M": M, "K": w.K, "N": w.N, "group_size": w.G,
+            "symmetric": w.symmetric, "entry": "awq_gemm_gate_up", "us_per_call": t * 1e6,
+            "tflops": flops / t / 1e12, "mfma_frac": flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS}
+
+
 def bench_quantize(name, steps, warmup):
     """awq_quantize on a layer of the workload's shape: fp16 W -> packed codes,
     scales, zero points.  Algorithmic bytes: W read once, the layer written."""
@@ -430,6 +447,7 @@ def main():
         extra.append(bench_gemm("sym70b_m4096", max(5, args.steps // 40), 2))
         extra.append(bench_gate_up("gate_up_m16", 16, args.steps, args.warmup))
         extra.append(bench_gate_up("gate_up_m16", 1, args.steps, args.warmup))
+        extra.append(bench_gemm_gate_up("gate_up_m16", 2048, 20, 3))
         extra.append(bench_quantize("decode_8b_gate", 20, 3))
         extra.append(torch_matmul_context("prefill_out_proj", 50))
         extra.append(torch_matmul_context("sym70b_m4096", 5))

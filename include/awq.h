@@ -162,6 +162,19 @@ awq_status awq_quantize(const uint16_t *w, int32_t K, int32_t N, int32_t group_s
 awq_status awq_gemv_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t *h, int32_t M,
                             void *stream);
 
+/*
+ * awq_gemm_gate_up: the same fused gate/up output as awq_gemv_gate_up, for any
+ * batch (M >= 0), on the batched GEMM path: the layer's N = 2I columns are
+ * [gate | up] and h[m][n] = fp16_rne(SiLU(y(m, n)) * y(m, I + n)), n < I, from
+ * the fp32 sums, with each weight dequantized exactly as awq_dequant does.
+ *   x: device fp16 [M][K];  h: device fp16 [M][I], 16-byte aligned.
+ * Rules beyond the layer's: N % 16 == 0.  Shapes outside the fused GEMM
+ * kernel return AWQ_ERROR_UNSUPPORTED before any launch: G must be a multiple
+ * of 64 and K a multiple of 256.
+ */
+awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t *h, int32_t M,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,7 +55,7 @@ def layer(K=128, N=64, G=128, qw=FAKE, sc=FAKE, qz=FAKE):
     return binding.CLayer(qw, sc, qz, K, N, G)
 
 
-@pytest.mark.parametrize("fn", ["awq_gemv", "awq_gemm", "awq_gemv_gate_up"])
+@pytest.mark.parametrize("fn", ["awq_gemv", "awq_gemm", "awq_gemv_gate_up", "awq_gemm_gate_up"])
 @pytest.mark.parametrize("case,want", [
     (dict(K=0), 1), (dict(N=-8), 1), (dict(G=0), 1),
     (dict(K=12), 2), (dict(N=20), 2), (dict(G=12, K=24), 2), (dict(K=192, G=128), 2),
@@ -69,7 +69,7 @@ def test_layer_validation(lib, fn, case, want):
     assert got == want
 
 
-@pytest.mark.parametrize("fn", ["awq_gemv", "awq_gemm", "awq_gemv_gate_up"])
+@pytest.mark.parametrize("fn", ["awq_gemv", "awq_gemm", "awq_gemv_gate_up", "awq_gemm_gate_up"])
 def test_io_validation(lib, fn):
     c = layer()
     f = getattr(lib, fn)
@@ -87,6 +87,15 @@ def test_io_validation(lib, fn):
 def test_gemv_rejects_large_batches(lib):
     c = layer()
     assert lib.awq_gemv(FAKE, ctypes.byref(c), FAKE, 17, None) == 4
+
+
+def test_gemm_gate_up_validation(lib):
+    """Shapes the batched fused gate/up entry rejects before any launch."""
+    f = lib.awq_gemm_gate_up
+    assert f(FAKE, ctypes.byref(layer(N=24)), FAKE, 64, None) == 2                 # I not a multiple of 8
+    assert f(FAKE, ctypes.byref(layer(K=128, G=32)), FAKE, 64, None) == 4          # G % 64
+    assert f(FAKE, ctypes.byref(layer(K=384, G=128)), FAKE, 64, None) == 4         # K % 256
+    assert f(FAKE, ctypes.byref(layer()), FAKE, 0, None) == 0                      # empty batch
 
 
 def test_quantize_validation(lib):

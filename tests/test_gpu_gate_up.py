@@ -93,3 +93,59 @@ def test_gate_up_empty_batch():
     x = torch.empty((0, layer.K), dtype=torch.float16, device="cuda")
     out = binding.gemv_gate_up(x, layer)
     assert tuple(out.shape) == (0, layer.N // 2)
+
+
+# --- the batched entry: awq_gemm_gate_up -------------------------------------
+
+def _sample(M, count, seed):
+    if M <= count:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    rest = rng.choice(np.arange(1, M - 1), size=count - 2, replace=False)
+    return np.sort(np.concatenate([[0, M - 1], rest]))
+
+
+@pytest.mark.parametrize("name,M", [("gate_up_m16", 16), ("gate_up_m16", 300), ("gate_up_m16", 2048),
+                                    ("sym70b_m1", 64)])
+def test_gemm_gate_up_workload(name, M):
+    from w4a16_group_quantized_amd import synth
+    w = synth.WORKLOADS[name]
+    X = synth.make_x(M, w.K, 1000 + M, w.n_outliers, w.outlier_gain)
+    _, _, W = oracle_weight(name)
+    h = to_host_bits(binding.gemm_gate_up(to_dev(X), device_layer(name)))
+    torch.cuda.synchronize()
+    rows = _sample(M, 24, M)
+    assert_y_close(h[rows], _oracle_h(np.ascontiguousarray(X[rows]), W),
+                   f"gemm gate_up {name} M={M} rows={len(rows)}")
+
+
+@pytest.mark.parametrize("M,K,I,G,sym", [
+    (37, 512, 200, 64, False), (130, 256, 8, 128, True), (1, 1024, 264, 256, False),
+    (257, 768, 136, 768, True),
+])
+def test_gemm_gate_up_ragged(M, K, I, G, sym):
+    X, codes, zeros, scales = random_case(1300 + M + I, M, K, 2 * I, G, sym)
+    o = oracle.load()
+    W = o.dequant(o.pack(codes), scales, None if zeros is None else o.pack_zeros(zeros), G)
+    h = to_host_bits(binding.gemm_gate_up(to_dev(X), device_case(codes, zeros, scales, G)))
+    torch.cuda.synchronize()
+    assert_y_close(h, _oracle_h(X, W), f"gemm gate_up M={M} K={K} I={I} G={G} sym={sym}")
+
+
+def test_gemm_gate_up_onehot_saturated():
+    """One-hot rows of X pick one dequantized weight row, so the gate and up sums
+    are exactly w(k, n) and w(k, I + n) and h = fp16(SiLU(w_g) w_u) with an fp32
+    SiLU; checked against the oracle's fp64 SiLU within the bar, and exactly 0
+    where the gate weight is 0."""
+    M, K, I, G = 64, 256, 64, 64
+    X, codes, zeros, scales = random_case(4242, M, K, 2 * I, G, False)
+    X = np.zeros((M, K), dtype=np.uint16)
+    X[np.arange(M), np.arange(M) * 3 % K] = 0x3C00
+    o = oracle.load()
+    W = o.dequant(o.pack(codes), scales, o.pack_zeros(zeros), G)
+    h = to_host_bits(binding.gemm_gate_up(to_dev(X), device_case(codes, zeros, scales, G)))
+    torch.cuda.synchronize()
+    ref = _oracle_h(X, W)
+    assert_y_close(h, ref, "gemm gate_up one-hot")
+    gate_zero = (W[np.arange(M) * 3 % K][:, :I] & 0x7FFF) == 0
+    assert np.all((h[gate_zero] & 0x7FFF) == 0)

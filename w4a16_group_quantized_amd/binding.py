@@ -21,7 +21,7 @@ LIBRARY = os.path.join(HERE, "libawq.so")
 
 # Entry points declared in include/awq.h, in declaration order.
 ENTRY_POINTS = ("awq_status_string", "awq_pack", "awq_pack_zeros", "awq_dequant", "awq_gemv",
-                "awq_gemm", "awq_gemv_gate_up", "awq_quantize")
+                "awq_gemm", "awq_gemv_gate_up", "awq_quantize", "awq_gemm_gate_up")
 
 AWQ_SUCCESS = 0
 STATUS_NAMES = {0: "AWQ_SUCCESS", 1: "AWQ_ERROR_INVALID_VALUE", 2: "AWQ_ERROR_SHAPE",
@@ -65,7 +65,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.awq_dequant.argtypes = [ctypes.POINTER(CLayer), vp, vp]
     lib.awq_quantize.restype = ctypes.c_int
     lib.awq_quantize.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
-    for name in ("awq_gemv", "awq_gemm", "awq_gemv_gate_up"):
+    for name in ("awq_gemv", "awq_gemm", "awq_gemv_gate_up", "awq_gemm_gate_up"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.POINTER(CLayer), vp, i32, vp]
@@ -140,6 +140,12 @@ def make_layer(codes: torch.Tensor, zeros: torch.Tensor | None, scales: torch.Te
     K, N = codes.shape
     qz = None if zeros is None else pack_zeros(zeros, stream)
     return Layer(pack(codes, stream), scales, qz, K, N, group_size)
+
+
+def gemm_gate_up(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=None):
+    """h = SiLU(y[:, :N/2]) * y[:, N/2:] with y = x @ dequant(layer), any M; the layer's
+    columns are the concatenation [gate | up]."""
+    return _linear("awq_gemm_gate_up", x, layer, out, stream, width=layer.N // 2)
 
 
 def quantize(w: torch.Tensor, group_size: int, symmetric: bool = False, stream=None) -> Layer:

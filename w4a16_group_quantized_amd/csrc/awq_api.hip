@@ -49,7 +49,7 @@ const char *awq_status_string(awq_status status) {
     case AWQ_ERROR_INVALID_VALUE: return "AWQ_ERROR_INVALID_VALUE: null pointer or non-positive size";
     case AWQ_ERROR_SHAPE: return "AWQ_ERROR_SHAPE: K%8, N%8, G%8, K%G must be 0 and arrays below 2^31 elements";
     case AWQ_ERROR_ALIGNMENT: return "AWQ_ERROR_ALIGNMENT: tensor pointers must be 16-byte aligned";
-    case AWQ_ERROR_UNSUPPORTED: return "AWQ_ERROR_UNSUPPORTED: outside this entry point (awq_gemv takes M <= 16; awq_gemv_gate_up also needs G % 128 == 0 and X in LDS)";
+    case AWQ_ERROR_UNSUPPORTED: return "AWQ_ERROR_UNSUPPORTED: outside this entry point (awq_gemv takes M <= 16; awq_gemv_gate_up also needs G % 128 == 0 and X in LDS; awq_gemm_gate_up needs G % 64 == 0 and K % 256 == 0)";
     case AWQ_ERROR_HIP: return "AWQ_ERROR_HIP: the HIP runtime refused the launch";
     }
     return "AWQ_ERROR_UNKNOWN";
@@ -126,6 +126,20 @@ awq_status awq_gemv_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
     if (!awq::gemv_gate_up_supported(M, layer->K, layer->N, layer->group_size))
         return AWQ_ERROR_UNSUPPORTED;
     return from_hip(awq::launch_gemv_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
+                                             layer->K, layer->N, layer->group_size,
+                                             as_stream(stream)));
+}
+
+awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t *h, int32_t M,
+                            void *stream) {
+    awq_status st = check_layer(layer);
+    if (st != AWQ_SUCCESS) return st;
+    if (layer->N % 16) return AWQ_ERROR_SHAPE;
+    st = check_io(x, h, layer, M);
+    if (st != AWQ_SUCCESS || M == 0) return st;
+    if (!awq::gemm_gate_up_supported(layer->K, layer->N, layer->group_size))
+        return AWQ_ERROR_UNSUPPORTED;
+    return from_hip(awq::launch_gemm_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
                                              layer->K, layer->N, layer->group_size,
                                              as_stream(stream)));
 }

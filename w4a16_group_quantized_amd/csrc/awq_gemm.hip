@@ -353,7 +353,11 @@ __device__ __forceinline__ void unpack_natural(uint32_t w, uint32_t exps, uint32
 
 // GSHIFT: the group of step kt is kt >> gshift (G / 64 a power of two, or
 // gshift = 31 when G == K: one group); otherwise kt / (G / 64).
-template <bool SYM, bool GSHIFT>
+// GU (fused gate/up): the layer's N = 2I columns are [gate | up].  A wave's 64
+// MFMA columns are then 32 gate columns and the same 32 columns of the up half
+// (column tile 0: gate, tile 1: up, for the same output column), and the
+// output is h[M][I] = fp16(SiLU(gate) * up), 32 columns per wave.
+template <bool SYM, bool GSHIFT, bool GU>
 __global__ void __launch_bounds__(256)
 mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
@@ -374,11 +378,16 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 31;
     const int h = lane >> 5;
-    const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+    const int I = N / 2;                          // GU: output width
+    const int tiles_m = (M + kBM - 1) / kBM;
+    const int tiles_n = GU ? (I + kBN / 2 - 1) / (kBN / 2) : (N + kBN - 1) / kBN;
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * kBM;
-    const int n0 = tn * kBN + 64 * wave;
+    const int n0 = tn * kBN + 64 * wave;          // first weight column of the wave
+    const int hw0 = tn * (kBN / 2) + 32 * wave;   // GU: first output column of the wave
+    // Layer column of slot c (0..63) of the wave's weight tile.
+    auto src_col = [&](int c) { return GU ? (c < 32 ? hw0 + c : I + hw0 + c - 32) : n0 + c; };
     const int KR = K / 8;
     const int KT = K / kBK;
 
@@ -398,9 +407,9 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         xvoff[i] = ((uint32_t)xr * (uint32_t)K + (uint32_t)xkc * 8u) * 2u;
     }
     // packed rows: load d (0, 1) of a step, lane i -> row 4 d + i / 16, columns n0 + 4 (i % 16) ..
-    const uint32_t qvoff = ((uint32_t)(lane >> 4) * (uint32_t)N + (uint32_t)(n0 + 4 * (lane & 15))) * 4u;
-    const uint32_t svoff = (uint32_t)(n0 + 2 * (lane & 31)) * 2u;
-    const uint32_t zvoff = (uint32_t)(n0 / 8 + (lane & 7)) * 4u;
+    const uint32_t qvoff = ((uint32_t)(lane >> 4) * (uint32_t)N + (uint32_t)src_col(4 * (lane & 15))) * 4u;
+    const uint32_t svoff = (uint32_t)src_col(2 * (lane & 31)) * 2u;
+    const uint32_t zvoff = (uint32_t)(src_col(8 * (lane & 7)) / 8) * 4u;
 
     // Byte strides: a step of packed rows, half of it, a scale row, a zero row.
     const int qstep = 32 * N, qhalf = 16 * N, srow = 2 * N, zrow = N / 2;
@@ -424,14 +433,32 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         uint2 q[4];
         uint32_t sc, zw;
     };
+    // GU: slots j (gate) and 32 + j (up); sc = gate | up << 16, zw = the two
+    // zero nibbles (gate in bits 0..3, up in 4..7).
     auto read_raw = [&](const uint4 *bbuf) {
         const uint32_t *w = reinterpret_cast<const uint32_t *>(bbuf + wave * kWave);
         Raw r;
+        if constexpr (GU) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-            r.q[kb] = *reinterpret_cast<const uint2 *>(w + 64 * (2 * kb + h) + 2 * j);
-        r.sc = w[4 * kScale + j];
-        r.zw = SYM ? 0x88888888u : w[4 * kZero + (j >> 2)];
+            for (int kb = 0; kb < 4; ++kb)
+                r.q[kb] = make_uint2(w[64 * (2 * kb + h) + j], w[64 * (2 * kb + h) + 32 + j]);
+            const uint32_t sg = w[4 * kScale + (j >> 1)] >> (16 * (j & 1));
+            const uint32_t su = w[4 * kScale + 16 + (j >> 1)] >> (16 * (j & 1));
+            r.sc = (sg & 0xFFFFu) | (su << 16);
+            if constexpr (SYM) {
+                r.zw = 0x88u;
+            } else {
+                const uint32_t zg = w[4 * kZero + (j >> 3)] >> (4 * (j & 7));
+                const uint32_t zu = w[4 * kZero + 4 + (j >> 3)] >> (4 * (j & 7));
+                r.zw = (zg & 0xFu) | ((zu & 0xFu) << 4);
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                r.q[kb] = *reinterpret_cast<const uint2 *>(w + 64 * (2 * kb + h) + 2 * j);
+            r.sc = w[4 * kScale + j];
+            r.zw = SYM ? 0x88888888u : w[4 * kZero + (j >> 2)];
+        }
         return r;
     };
     const uint32_t exps = 0x54006400u;
@@ -442,7 +469,7 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     };
     auto decode = [&](const Raw &r) {
         Dq dq;
-        const uint32_t z2 = r.zw >> (8 * (j & 3));
+        const uint32_t z2 = GU ? r.zw : r.zw >> (8 * (j & 3));
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             const uint32_t z = (z2 >> (4 * ct)) & 0xFu;
@@ -564,8 +591,25 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     wait_vmcnt<0>();   // no load into LDS may outlive the workgroup
 
     // C layout of the 32x32 MFMA: lane (h, j) holds, in register v, row
-    // 8 (v / 4) + 4 h + v % 4 of column slot j; column tiles 0 and 1 are the
-    // adjacent columns n0 + 2 j and n0 + 2 j + 1, stored as one 4-byte word.
+    // 8 (v / 4) + 4 h + v % 4 of column slot j.
+    if constexpr (GU) {
+        // column tiles 0 and 1 are gate and up of output column hw0 + j
+        const int col = hw0 + j;
+        if (col >= I) return;
+#pragma unroll
+        for (int t = 0; t < kMT; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + 32 * t + 8 * (v / 4) + 4 * h + (v % 4);
+                if (row < M) {
+                    const float g = acc[t][0][v];
+                    Y[(size_t)row * I + col] = as_u16((half_t)(g / (1.0f + __expf(-g)) * acc[t][1][v]));
+                }
+            }
+        return;
+    }
+    // column tiles 0 and 1 are the adjacent columns n0 + 2 j and n0 + 2 j + 1,
+    // stored as one 4-byte word.
     const int col = n0 + 2 * j;
     if (col >= N) return;
 #pragma unroll
@@ -581,10 +625,11 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         }
 }
 
-template <bool SYM>
+template <bool SYM, bool GU>
 hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                   uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
-    const long long tiles = (long long)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    const int tn = GU ? (N / 2 + kBN / 2 - 1) / (kBN / 2) : (N + kBN - 1) / kBN;
+    const long long tiles = (long long)((M + kBM - 1) / kBM) * tn;
     const int gsteps = G / kBK;
     int gshift = -1;
     if (G == K) gshift = 31;
@@ -592,10 +637,10 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
     const auto *q = reinterpret_cast<const uint32_t *>(qw);
     const auto *z = reinterpret_cast<const uint32_t *>(qz);
     if (gshift >= 0)
-        hipLaunchKernelGGL((mfma32_kernel<SYM, true>), dim3((unsigned)tiles), dim3(256), 0, s, x, q,
+        hipLaunchKernelGGL((mfma32_kernel<SYM, true, GU>), dim3((unsigned)tiles), dim3(256), 0, s, x, q,
                            sc, z, y, M, K, N, G, gshift);
     else
-        hipLaunchKernelGGL((mfma32_kernel<SYM, false>), dim3((unsigned)tiles), dim3(256), 0, s, x, q,
+        hipLaunchKernelGGL((mfma32_kernel<SYM, false, GU>), dim3((unsigned)tiles), dim3(256), 0, s, x, q,
                            sc, z, y, M, K, N, G, 0);
     return hipGetLastError();
 }
@@ -617,8 +662,8 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
                   uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
     const bool fast = G % kBK == 0 && K % (kRing * kBK) == 0;
     if (fast && AWQ_GEMM_M32)
-        return qz == nullptr ? m32::launch<true>(x, qw, sc, qz, y, M, K, N, G, s)
-                             : m32::launch<false>(x, qw, sc, qz, y, M, K, N, G, s);
+        return qz == nullptr ? m32::launch<true, false>(x, qw, sc, qz, y, M, K, N, G, s)
+                             : m32::launch<false, false>(x, qw, sc, qz, y, M, K, N, G, s);
     if (qz == nullptr)
         return fast ? launch_sym<BM, true, true>(x, qw, sc, qz, y, M, K, N, G, s)
                     : launch_sym<BM, true, false>(x, qw, sc, qz, y, M, K, N, G, s);
@@ -627,6 +672,18 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
 }
 
 }  // namespace gemm
+
+bool gemm_gate_up_supported(int K, int N, int G) {
+    return N % 16 == 0 && G % gemm::kBK == 0 && K % (gemm::kRing * gemm::kBK) == 0;
+}
+
+hipError_t launch_gemm_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                               const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
+                               hipStream_t s) {
+    return qzeros == nullptr
+               ? gemm::m32::launch<true, true>(x, qweight, scales, qzeros, h, M, K, N, G, s)
+               : gemm::m32::launch<false, true>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+}
 
 hipError_t launch_gemm(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,

@@ -22,6 +22,10 @@ bool gemv_gate_up_supported(int M, int K, int N, int G);
 hipError_t launch_gemv_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                                const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
                                hipStream_t s);
+bool gemm_gate_up_supported(int K, int N, int G);
+hipError_t launch_gemm_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                               const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
+                               hipStream_t s);
 hipError_t launch_gemm(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
                        hipStream_t s);
