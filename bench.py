@@ -58,10 +58,11 @@ ROTATE_BYTES = 1 << 30
 CALIBRATION_COPY_BYTES = 64 << 20
 PROFILE_CALLS = 20
 CSRC = os.path.join(ROOT, "w4a16_group_quantized_amd", "csrc")
-# Sources each profiled kernel is built from: a counter summary is valid only for them.
+# Sources that define each profiled kernel (the launcher declarations in
+# awq_internal.h generate no code): a counter summary is valid only for them.
 KERNEL_SOURCES = {
-    "gemv": ["awq_gemv.hip", "awq_device.h", "awq_internal.h"],
-    "gemm": ["awq_gemm.hip", "awq_device.h", "awq_internal.h"],
+    "gemv": ["awq_gemv.hip", "awq_device.h"],
+    "gemm": ["awq_gemm.hip", "awq_device.h"],
 }
 KERNEL_NAMES = {"gemv": ("stream_kernel", "fold_kernel", "exact_kernel"), "gemm": ("gemm_kernel", "mfma32_kernel")}
 PROFILE_WORKLOAD = {"gemv": "decode_8b_gate", "gemm": "prefill_out_proj"}
