@@ -77,6 +77,21 @@ def test_gemm_large_ragged(M, K, N, G):
     assert_y_close(to_host_bits(binding.gemm(to_dev(X), layer)), Y16, f"gemm M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N,G,sym", [
+    (2200, 384, 14584, 128, False),    # 256-row tiles (>= 512 of them), ragged M and N
+    (2304, 384, 14592, 96, True),      # group of 3 steps: index by division
+    (2200, 512, 14584, 512, False),    # one group per column
+])
+def test_gemm_wide_tiles(M, K, N, G, sym):
+    """Shapes large enough for the 256-row-tile path, checked on sampled rows."""
+    X, codes, zeros, scales = random_case(5000 + M + G, M, K, N, G, sym)
+    rows = _sample_rows(M, 16, M + N)
+    _, Y16 = oracle_case(X, codes, zeros, scales, G, rows=rows)
+    y = to_host_bits(binding.gemm(to_dev(X), device_case(codes, zeros, scales, G)))
+    torch.cuda.synchronize()
+    assert_y_close(y[rows], Y16, f"gemm wide M={M} K={K} N={N} G={G} sym={sym}")
+
+
 @pytest.mark.parametrize("entry", ["gemv", "gemm"])
 @pytest.mark.parametrize("K,N,G,sym", [(512, 512, 128, False), (256, 200, 8, False),
                                        (1024, 136, 1024, True)])

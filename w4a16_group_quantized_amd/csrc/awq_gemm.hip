@@ -327,15 +327,32 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 // ---------------------------------------------------------------------------
 namespace m32 {
 
-constexpr int kBM = 128;
-constexpr int kMT = kBM / 32;            // row tiles per wave
-constexpr int kACH = kBM * kBK / 8 / 256; // X chunks per thread per step
-// Per-wave LDS region of one step's weights, in 16-byte chunks: 8 packed rows
-// x 64 columns (row r, column n0 + c at word 64 r + c), 64 scale words (word i:
-// columns n0 + 2 (i % 32), +1), 64 zero words (word i: zero word n0 / 8 + i % 8).
-constexpr int kWave = 8 * 64 / 4 + 16 + 16;
-constexpr int kScale = 8 * 64 / 4;
-constexpr int kZero = kScale + 16;
+// Geometry of one kernel variant: KB k blocks of 16 per step (BK = 16 KB k),
+// MT row tiles of 32 per wave (BM = 32 MT rows per workgroup).
+template <int KB, int MT>
+struct Geom {
+    static constexpr int BK = 16 * KB;
+    static constexpr int BM = 32 * MT;
+    static constexpr int XCH = BK / 8;               // 16-byte chunks per X row
+    static constexpr int ACH = BM * XCH / 256;       // X chunks per thread per step
+    static constexpr int QROWS = 2 * KB;             // packed rows per step
+    static constexpr int QD = QROWS / 4;             // 16-byte packed-row loads per lane per step
+    // Per-wave LDS region of one step's weights, in 16-byte chunks: QROWS
+    // packed rows x 64 columns (row r, slot c at word 64 r + c), then 64 scale
+    // words (word i: the scales of slots 2 (i % 32), +1), then 64 zero words
+    // (word i: the zero word of slots 8 (i % 8) ..).
+    static constexpr int SCALE = QROWS * 64 / 4;
+    static constexpr int ZERO = SCALE + 16;
+    static constexpr int WAVE = ZERO + 16;
+};
+
+// LDS chunk of (row, 16-byte k chunk kc) in an X tile of XCH chunks per row,
+// XOR-swizzled so that the 16 rows one A-operand read touches in a 16-lane
+// phase fall in different bank groups.
+template <int XCH>
+__device__ __forceinline__ int xswz(int row, int kc) {
+    return row * XCH + (kc ^ (XCH == 8 ? (row & 7) : ((row >> 2) & 3)));
+}
 
 typedef float float16x_t __attribute__((ext_vector_type(16)));
 
@@ -357,17 +374,20 @@ __device__ __forceinline__ void unpack_natural(uint32_t w, uint32_t exps, uint32
 // MFMA columns are then 32 gate columns and the same 32 columns of the up half
 // (column tile 0: gate, tile 1: up, for the same output column), and the
 // output is h[M][I] = fp16(SiLU(gate) * up), 32 columns per wave.
-template <bool SYM, bool GSHIFT, bool GU>
+template <int KB, int MT, bool SYM, bool GSHIFT, bool GU>
 __global__ void __launch_bounds__(256)
 mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
               uint16_t *__restrict__ Y, int M, int K, int N, int G, int gshift) {
-    constexpr int BLOADS = SYM ? 3 : 4;   // per step: 2 packed-row loads, scales, zeros
+    using Gm = Geom<KB, MT>;
+    constexpr int kBM = Gm::BM, kMT = MT, kACH = Gm::ACH, kWave = Gm::WAVE;
+    constexpr int kScale = Gm::SCALE, kZero = Gm::ZERO, kBKs = Gm::BK, kXCH = Gm::XCH;
+    constexpr int BLOADS = Gm::QD + (SYM ? 1 : 2);   // per step: packed rows, scales, zeros
     constexpr int LOADS = kACH + BLOADS;
-    __shared__ __attribute__((aligned(16))) uint4 ring0[kBM * 8];
-    __shared__ __attribute__((aligned(16))) uint4 ring1[kBM * 8];
-    __shared__ __attribute__((aligned(16))) uint4 ring2[kBM * 8];
-    __shared__ __attribute__((aligned(16))) uint4 ring3[kBM * 8];
+    __shared__ __attribute__((aligned(16))) uint4 ring0[kBM * kXCH];
+    __shared__ __attribute__((aligned(16))) uint4 ring1[kBM * kXCH];
+    __shared__ __attribute__((aligned(16))) uint4 ring2[kBM * kXCH];
+    __shared__ __attribute__((aligned(16))) uint4 ring3[kBM * kXCH];
     __shared__ __attribute__((aligned(16))) uint4 bring0[4 * kWave];
     __shared__ __attribute__((aligned(16))) uint4 bring1[4 * kWave];
     __shared__ __attribute__((aligned(16))) uint4 bring2[4 * kWave];
@@ -389,7 +409,7 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     // Layer column of slot c (0..63) of the wave's weight tile.
     auto src_col = [&](int c) { return GU ? (c < 32 ? hw0 + c : I + hw0 + c - 32) : n0 + c; };
     const int KR = K / 8;
-    const int KT = K / kBK;
+    const int KT = K / kBKs;
 
     // Buffer loads past a buffer's end return zeros; columns at or past N read
     // the next packed row (in bounds) and their outputs are dropped.
@@ -401,9 +421,9 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #pragma unroll
     for (int i = 0; i < kACH; ++i) {
         const int p = (i * 4 + wave) * 64 + lane;
-        const int row = p >> 3;
+        const int row = p / kXCH;
         const int xr = min(m0 + row, M - 1);
-        const int xkc = (p & 7) ^ (row & 7);
+        const int xkc = (p % kXCH) ^ (xswz<kXCH>(row, 0) - row * kXCH);
         xvoff[i] = ((uint32_t)xr * (uint32_t)K + (uint32_t)xkc * 8u) * 2u;
     }
     // packed rows: load d (0, 1) of a step, lane i -> row 4 d + i / 16, columns n0 + 4 (i % 16) ..
@@ -412,25 +432,25 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const uint32_t zvoff = (uint32_t)(src_col(8 * (lane & 7)) / 8) * 4u;
 
     // Byte strides: a step of packed rows, half of it, a scale row, a zero row.
-    const int qstep = 32 * N, qhalf = 16 * N, srow = 2 * N, zrow = N / 2;
-    const int gsteps = G / kBK;
+    const int qstep = Gm::QROWS * 4 * N, qhalf = 16 * N, srow = 2 * N, zrow = N / 2;
+    const int gsteps = G / kBKs;
     auto load_step = [&](int kt, uint4 *xbuf, uint4 *bbuf) {
         uint4 *dst = bbuf + wave * kWave;
         const int qo = kt * qstep;
-        buffer_to_lds16(qrs, dst, qvoff, qo);
-        buffer_to_lds16(qrs, dst + 64, qvoff, qo + qhalf);
+#pragma unroll
+        for (int d = 0; d < Gm::QD; ++d) buffer_to_lds16(qrs, dst + 64 * d, qvoff, qo + d * qhalf);
         const int g = GSHIFT ? (kt >> gshift) : kt / gsteps;
         buffer_to_lds4(srs, dst + kScale, svoff, g * srow);
         if constexpr (!SYM) buffer_to_lds4(zrs, dst + kZero, zvoff, g * zrow);
 #pragma unroll
         for (int i = 0; i < kACH; ++i)
-            buffer_to_lds16(xrs, xbuf + (i * 4 + wave) * 64, xvoff[i], kt * kBK * 2);
+            buffer_to_lds16(xrs, xbuf + (i * 4 + wave) * 64, xvoff[i], kt * kBKs * 2);
     };
 
     // Raw weights of one step for this lane: packed rows 2 kb + h, columns
     // n0 + 2 j, +1; the scale pair and the zero word of those columns.
     struct Raw {
-        uint2 q[4];
+        uint2 q[KB];
         uint32_t sc, zw;
     };
     // GU: slots j (gate) and 32 + j (up); sc = gate | up << 16, zw = the two
@@ -440,7 +460,7 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         Raw r;
         if constexpr (GU) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
                 r.q[kb] = make_uint2(w[64 * (2 * kb + h) + j], w[64 * (2 * kb + h) + 32 + j]);
             const uint32_t sg = w[4 * kScale + (j >> 1)] >> (16 * (j & 1));
             const uint32_t su = w[4 * kScale + 16 + (j >> 1)] >> (16 * (j & 1));
@@ -454,7 +474,7 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             }
         } else {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
                 r.q[kb] = *reinterpret_cast<const uint2 *>(w + 64 * (2 * kb + h) + 2 * j);
             r.sc = w[4 * kScale + j];
             r.zw = SYM ? 0x88888888u : w[4 * kZero + (j >> 2)];
@@ -462,7 +482,7 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         return r;
     };
     const uint32_t exps = 0x54006400u;
-    half8_t bA[4][2], bB[4][2];
+    half8_t bA[KB][2], bB[KB][2];
     // Biased zero pairs (1024 + z, 64 + z) and scale pairs of the two columns.
     struct Dq {
         half2_t bz2[2], s2[2];
@@ -488,10 +508,10 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[t][ct][v] = 0.f;
 
-    // A operands of k block kb of a step: row tiles t = 0..3.
+    // A operands of k block kb of a step: row tiles t = 0 .. MT - 1.
     auto read_a = [&](const uint4 *xbuf, int kb, half8_t (&a)[kMT]) {
 #pragma unroll
-        for (int t = 0; t < kMT; ++t) a[t] = as_half8(xbuf[swz(32 * t + j, 2 * kb + h)]);
+        for (int t = 0; t < kMT; ++t) a[t] = as_half8(xbuf[xswz<kXCH>(32 * t + j, 2 * kb + h)]);
     };
     auto mfma_kb = [&](const half8_t (&a)[kMT], const half8_t (&b)[2]) {
 #pragma unroll
@@ -511,37 +531,37 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         }
     };
 
-    // Step kt, software-pipelined inside its 32 MFMAs (4 k blocks x 4 row tiles
+    // Step kt, software-pipelined inside its MFMAs (KB k blocks x MT row tiles
     // x 2 column tiles).  On entry: b_cur = weights of kt (dequantized), a0 =
     // A(kt, kb 0), r = the packed weights of kt + 1 (read from LDS).  Each k
     // block's MFMAs run while the next block's A operands are read and one
-    // block of step kt + 1's weights is dequantized.  Between blocks 2 and 3
+    // block of step kt + 1's weights is dequantized.  Before the last block
     // the wave waits until everything up to step kt + 2 has landed (and its own
-    // LDS reads of slot kt are done) and meets the other waves at a barrier.  After it, X(kt + 1) is visible to all waves, so block 3 reads
+    // LDS reads of slot kt are done) and meets the other waves at a barrier.
+    // After it, X(kt + 1) is visible to all waves, so the last block reads
     // A(kt + 1, kb 0) and the packed weights of kt + 2, and the loads of step
     // kt + 4 go into the ring slots of kt.  Neither LDS latency nor the
     // barrier reaches the matrix cores by more than a block's lead.
+    constexpr int VG = KB == 2 ? 2 : 4;   // dequantization VALU per MFMA (about)
     half8_t a0[kMT], a1[kMT];
     Raw r;
-    auto step = [&](int kt, const uint4 *xcur, half8_t (&b_cur)[4][2], half8_t (&b_nxt)[4][2],
+    auto step = [&](int kt, const uint4 *xcur, half8_t (&b_cur)[KB][2], half8_t (&b_nxt)[KB][2],
                     const uint4 *xnxt, const uint4 *bnn, uint4 *xload, uint4 *bload) {
         __builtin_amdgcn_sched_barrier(0);
         const Raw rc = r;
         const Dq dq = decode(rc);
         read_a(xcur, 1, a1);
-        dequant_kb(rc, dq, 0, b_nxt[0]);
-        mfma_kb(a0, b_cur[0]);
-        read_a(xcur, 2, a0);
-        dequant_kb(rc, dq, 1, b_nxt[1]);
-        mfma_kb(a1, b_cur[1]);
-        read_a(xcur, 3, a1);
-        dequant_kb(rc, dq, 2, b_nxt[2]);
-        mfma_kb(a0, b_cur[2]);
 #pragma unroll
-        for (int i = 0; i < 24; ++i) {
+        for (int kb = 0; kb < KB - 1; ++kb) {
+            dequant_kb(rc, dq, kb, b_nxt[kb]);
+            mfma_kb(kb % 2 ? a1 : a0, b_cur[kb]);
+            if (kb + 2 < KB) read_a(xcur, kb + 2, kb % 2 ? a1 : a0);
+        }
+#pragma unroll
+        for (int i = 0; i < (KB - 1) * kMT * 2; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x002, VG, 0);  // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads are done
@@ -551,14 +571,14 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         load_step(min(kt + kRing, KT - 1), xload, bload);
         read_a(xnxt, 0, a0);
         r = read_raw(bnn);
-        mfma_kb(a1, b_cur[3]);
-        dequant_kb(rc, dq, 3, b_nxt[3]);
+        mfma_kb(a1, b_cur[KB - 1]);            // KB is even: the last block's A is in a1
+        dequant_kb(rc, dq, KB - 1, b_nxt[KB - 1]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kMT * 2; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
             __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x002, VG, 0);  // VALU
         }
     };
 
@@ -578,7 +598,7 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     {
         const Dq dq = decode(r);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) dequant_kb(r, dq, kb, bA[kb]);
+        for (int kb = 0; kb < KB; ++kb) dequant_kb(r, dq, kb, bA[kb]);
     }
     r = read_raw(bring1);
     read_a(ring0, 0, a0);
@@ -625,23 +645,24 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         }
 }
 
-template <bool SYM, bool GU>
+template <int KB, int MT, bool SYM, bool GU>
 hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                   uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
+    using Gm = Geom<KB, MT>;
     const int tn = GU ? (N / 2 + kBN / 2 - 1) / (kBN / 2) : (N + kBN - 1) / kBN;
-    const long long tiles = (long long)((M + kBM - 1) / kBM) * tn;
-    const int gsteps = G / kBK;
+    const long long tiles = (long long)((M + Gm::BM - 1) / Gm::BM) * tn;
+    const int gsteps = G / Gm::BK;
     int gshift = -1;
     if (G == K) gshift = 31;
     else if ((gsteps & (gsteps - 1)) == 0) gshift = __builtin_ctz((unsigned)gsteps);
     const auto *q = reinterpret_cast<const uint32_t *>(qw);
     const auto *z = reinterpret_cast<const uint32_t *>(qz);
     if (gshift >= 0)
-        hipLaunchKernelGGL((mfma32_kernel<SYM, true, GU>), dim3((unsigned)tiles), dim3(256), 0, s, x, q,
-                           sc, z, y, M, K, N, G, gshift);
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, true, GU>), dim3((unsigned)tiles), dim3(256), 0,
+                           s, x, q, sc, z, y, M, K, N, G, gshift);
     else
-        hipLaunchKernelGGL((mfma32_kernel<SYM, false, GU>), dim3((unsigned)tiles), dim3(256), 0, s, x, q,
-                           sc, z, y, M, K, N, G, 0);
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, false, GU>), dim3((unsigned)tiles), dim3(256), 0,
+                           s, x, q, sc, z, y, M, K, N, G, 0);
     return hipGetLastError();
 }
 
@@ -661,9 +682,16 @@ template <int BM>
 hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                   uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
     const bool fast = G % kBK == 0 && K % (kRing * kBK) == 0;
+    // Large batches: 256-row tiles (half the dequantization per MFMA) once they
+    // still fill the GPU twice over; otherwise 128-row tiles.
+    const long long wide_tiles = (long long)((M + 255) / 256) * ((N + kBN - 1) / kBN);
+    const bool wide = G % 32 == 0 && K % (kRing * 32) == 0 && wide_tiles >= 512;
+    if (wide && AWQ_GEMM_M32)
+        return qz == nullptr ? m32::launch<2, 8, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
+                             : m32::launch<2, 8, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
     if (fast && AWQ_GEMM_M32)
-        return qz == nullptr ? m32::launch<true, false>(x, qw, sc, qz, y, M, K, N, G, s)
-                             : m32::launch<false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+        return qz == nullptr ? m32::launch<4, 4, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
+                             : m32::launch<4, 4, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
     if (qz == nullptr)
         return fast ? launch_sym<BM, true, true>(x, qw, sc, qz, y, M, K, N, G, s)
                     : launch_sym<BM, true, false>(x, qw, sc, qz, y, M, K, N, G, s);
@@ -681,8 +709,8 @@ hipError_t launch_gemm_gate_up(const uint16_t *x, const int32_t *qweight, const 
                                const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
                                hipStream_t s) {
     return qzeros == nullptr
-               ? gemm::m32::launch<true, true>(x, qweight, scales, qzeros, h, M, K, N, G, s)
-               : gemm::m32::launch<false, true>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+               ? gemm::m32::launch<4, 4, true, true>(x, qweight, scales, qzeros, h, M, K, N, G, s)
+               : gemm::m32::launch<4, 4, false, true>(x, qweight, scales, qzeros, h, M, K, N, G, s);
 }
 
 hipError_t launch_gemm(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
