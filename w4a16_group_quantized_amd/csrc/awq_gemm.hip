@@ -78,9 +78,6 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 // LDS read of one buffer from a direct-to-LDS load into another and need not
 // wait for the latter.
 constexpr int kRing = 4;
-#ifndef AWQ_GEMM_M32
-#define AWQ_GEMM_M32 1
-#endif
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
@@ -103,13 +100,10 @@ __device__ __forceinline__ void global_to_lds16(const void *src, uint4 *dst) {
     __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
-// FAST: G % 64 == 0 and K % (4 * 64) == 0 -- every step lies in one group and
-// the steps fill whole rings, so all loads are buffer loads with a per-lane
-// offset fixed for the kernel and a per-step offset in a scalar register (no
-// address arithmetic in the loop), scales and zero points are decoded once per
-// step, and no step needs masking.  Other shapes take the general path, which
-// clamps addresses and zeroes the weights of k past K.
-template <int BM, bool SYM, bool FAST>
+// General path, for the shapes the 32x32 kernels below do not take (G not a
+// multiple of 32 or K not a multiple of 128): 16x16x32 MFMAs, packed words in
+// registers, clamped addresses, and the weights of k past K zeroed.
+template <int BM, bool SYM>
 __global__ void __launch_bounds__(256)
 gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
@@ -117,7 +111,7 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     constexpr int MT = BM / 16;                    // 16-row MFMA tiles per wave
     constexpr int ACH = BM * kBK / 8 / 256;        // X chunks per thread per step
     constexpr int P = kRing - 1;                   // steps loaded ahead
-    constexpr int BLOADS = FAST ? (SYM ? 3 : 4) : (SYM ? 4 : 6);
+    constexpr int BLOADS = SYM ? 4 : 6;
     constexpr int LOADS = ACH + BLOADS;            // vector-memory loads per step per thread
     __shared__ __attribute__((aligned(16))) uint4 ring0[BM * 8];
     __shared__ __attribute__((aligned(16))) uint4 ring1[BM * 8];
@@ -146,63 +140,34 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     // direct-to-LDS load; the swizzle is undone on the global side, so chunk p
     // holds (row p / 8, k chunk (p % 8) ^ (row & 7)).  Rows past M read row
     // M - 1 (their outputs are dropped).
-    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, (uint32_t)KR * (uint32_t)N * 4u);
-    const __amdgpu_buffer_rsrc_t srs = make_rsrc(S, (uint32_t)(K / G) * (uint32_t)N * 2u);
-    const __amdgpu_buffer_rsrc_t zrs = make_rsrc(QZ, SYM ? 0u : (uint32_t)(K / G) * (uint32_t)N / 2u);
     int xrow[ACH], xkc[ACH];
-    uint32_t xvoff[ACH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
         const int p = (i * 4 + wave) * 64 + lane;
         const int row = p >> 3;
         xrow[i] = min(m0 + row, M - 1);
         xkc[i] = (p & 7) ^ (row & 7);
-        xvoff[i] = ((uint32_t)xrow[i] * (uint32_t)K + (uint32_t)xkc[i] * 8u) * 2u;
     }
-    const uint32_t qvoff = ((uint32_t)kb * (uint32_t)N + (uint32_t)ncl) * 4u;
-    const uint32_t svoff = (uint32_t)ncl * 2u;
-    const uint32_t zvoff = (uint32_t)(ncl / 8) * 4u;
 
     auto load_x = [&](int kt, uint4 *buf) {
 #pragma unroll
         for (int i = 0; i < ACH; ++i) {
             uint4 *dst = buf + (i * 4 + wave) * 64;
-            if constexpr (FAST) {
-                buffer_to_lds16(xrs, dst, xvoff[i], kt * kBK * 2);
-            } else {
-                int gk = kt * kBK + xkc[i] * 8;
-                gk = gk < K ? gk : 0;     // k past K: any valid address, weights are zeroed
-                global_to_lds16(X + (size_t)xrow[i] * K + gk, dst);
-            }
+            int gk = kt * kBK + xkc[i] * 8;
+            gk = gk < K ? gk : 0;     // k past K: any valid address, weights are zeroed
+            global_to_lds16(X + (size_t)xrow[i] * K + gk, dst);
         }
     };
     auto load_b = [&](int kt, BStep &b) {
-        if constexpr (FAST) {
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-                    qrs, qvoff, (kt * (kBK / 8) + 4 * s) * N * 4, 0);
-                b.q[s] = make_uint4(v.x, v.y, v.z, v.w);
-            }
-            const int g = (kt * kBK) / G;
-            const u32x2 sv = __builtin_amdgcn_raw_buffer_load_b64(srs, svoff, g * N * 2, 0);
-            b.sc[0] = make_uint2(sv.x, sv.y);
-            if constexpr (SYM) b.zw[0] = 0x88888888u;
-            else b.zw[0] = __builtin_amdgcn_raw_buffer_load_b32(zrs, zvoff, g * (N / 8) * 4, 0);
-        } else {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int r0 = kt * (kBK / 8) + 4 * s + kb;
-                const int r = r0 < KR ? r0 : KR - 1;
-                const int g = (8 * r) / G;
-                b.q[s] = *reinterpret_cast<const uint4 *>(Q + (size_t)r * N + ncl);
-                b.sc[s] = *reinterpret_cast<const uint2 *>(S + (size_t)g * N + ncl);
-                if constexpr (SYM) b.zw[s] = 0x88888888u;
-                else b.zw[s] = QZ[(size_t)g * (N / 8) + ncl / 8];
-            }
+        for (int s = 0; s < 2; ++s) {
+            const int r0 = kt * (kBK / 8) + 4 * s + kb;
+            const int r = r0 < KR ? r0 : KR - 1;
+            const int g = (8 * r) / G;
+            b.q[s] = *reinterpret_cast<const uint4 *>(Q + (size_t)r * N + ncl);
+            b.sc[s] = *reinterpret_cast<const uint2 *>(S + (size_t)g * N + ncl);
+            if constexpr (SYM) b.zw[s] = 0x88888888u;
+            else b.zw[s] = QZ[(size_t)g * (N / 8) + ncl / 8];
         }
     };
 
@@ -236,10 +201,9 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
                 s2[i] = half2_t{sv, sv};
             }
         };
-        if constexpr (FAST) decode(cur.sc[0], cur.zw[0]);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            if constexpr (!FAST) decode(cur.sc[s], cur.zw[s]);
+            decode(cur.sc[s], cur.zw[s]);
             const uint32_t q4[4] = {cur.q[s].x, cur.q[s].y, cur.q[s].z, cur.q[s].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -248,9 +212,7 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #pragma unroll
                 for (int j = 0; j < 4; ++j) d[j] = dequant_pair(p[j], bz2[i], s2[i]);
                 uint4 w = pairs_to_natural(d);
-                if constexpr (!FAST) {
-                    if (kt * (kBK / 8) + 4 * s + kb >= KR) w = make_uint4(0u, 0u, 0u, 0u);
-                }
+                if (kt * (kBK / 8) + 4 * s + kb >= KR) w = make_uint4(0u, 0u, 0u, 0u);
                 b[s][i] = as_half8(w);
             }
         }
@@ -668,35 +630,37 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
 
 }  // namespace m32
 
-template <int BM, bool SYM, bool FAST>
-hipError_t launch_sym(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
-                      uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
+template <int BM, bool SYM>
+hipError_t launch_general(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
     const long long tiles = (long long)((M + BM - 1) / BM) * ((N + kBN - 1) / kBN);
-    hipLaunchKernelGGL((gemm_kernel<BM, SYM, FAST>), dim3((unsigned)tiles), dim3(256), 0, s, x,
+    hipLaunchKernelGGL((gemm_kernel<BM, SYM>), dim3((unsigned)tiles), dim3(256), 0, s, x,
                        reinterpret_cast<const uint32_t *>(qw), sc,
                        reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
     return hipGetLastError();
 }
 
-template <int BM>
+// Kernel choice: 256-row tiles with 32-k steps for large batches (half the
+// dequantization per MFMA), as long as they fill the GPU twice over; 128-row
+// tiles with 64-k steps otherwise; 32-k steps when G or K only allow those;
+// the general kernel for the rest.
 hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                   uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
-    const bool fast = G % kBK == 0 && K % (kRing * kBK) == 0;
-    // Large batches: 256-row tiles (half the dequantization per MFMA) once they
-    // still fill the GPU twice over; otherwise 128-row tiles.
+    const bool sym = qz == nullptr;
+    const bool k32 = G % 32 == 0 && K % (kRing * 32) == 0;
+    const bool k64 = G % 64 == 0 && K % (kRing * 64) == 0;
     const long long wide_tiles = (long long)((M + 255) / 256) * ((N + kBN - 1) / kBN);
-    const bool wide = G % 32 == 0 && K % (kRing * 32) == 0 && wide_tiles >= 512;
-    if (wide && AWQ_GEMM_M32)
-        return qz == nullptr ? m32::launch<2, 8, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
-                             : m32::launch<2, 8, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (fast && AWQ_GEMM_M32)
-        return qz == nullptr ? m32::launch<4, 4, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
-                             : m32::launch<4, 4, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (qz == nullptr)
-        return fast ? launch_sym<BM, true, true>(x, qw, sc, qz, y, M, K, N, G, s)
-                    : launch_sym<BM, true, false>(x, qw, sc, qz, y, M, K, N, G, s);
-    return fast ? launch_sym<BM, false, true>(x, qw, sc, qz, y, M, K, N, G, s)
-                : launch_sym<BM, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (k32 && wide_tiles >= 512)
+        return sym ? m32::launch<2, 8, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
+                   : m32::launch<2, 8, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (k64)
+        return sym ? m32::launch<4, 4, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
+                   : m32::launch<4, 4, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (k32)
+        return sym ? m32::launch<2, 4, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
+                   : m32::launch<2, 4, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+    return sym ? launch_general<128, true>(x, qw, sc, qz, y, M, K, N, G, s)
+               : launch_general<128, false>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
 }  // namespace gemm
@@ -716,7 +680,7 @@ hipError_t launch_gemm_gate_up(const uint16_t *x, const int32_t *qweight, const 
 hipError_t launch_gemm(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
                        hipStream_t s) {
-    return gemm::launch<128>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    return gemm::launch(x, qweight, scales, qzeros, y, M, K, N, G, s);
 }
 
 }  // namespace awq
