@@ -1,6 +1,6 @@
 """Plain CPU oracle for the W4A16 group-quantized linear layer (AWQ inference).
 
-TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the repository's smoke check and
 the CPU-baseline leg of ``bench.py`` may import this package.  The HIP library
 and its Python binding never import, link or call anything here, and nothing
 here imports them.
@@ -46,6 +46,17 @@ def _ptr(a: np.ndarray | None, ctype):
         return None
     assert a.flags["C_CONTIGUOUS"]
     return a.ctypes.data_as(ctype)
+
+
+def _check_layer(K: int, N: int, G: int, S: np.ndarray, QZ) -> None:
+    """Shapes the packed layout fixes: eight codes per qweight word along K,
+    eight zero points per qzeros word along N, one scale row per group of G."""
+    if G <= 0 or K % G != 0:
+        raise ValueError(f"group size {G} must divide K={K}")
+    if S.shape != (K // G, N):
+        raise ValueError(f"scales shape {S.shape} != {(K // G, N)}")
+    if QZ is not None and (N % 8 != 0 or QZ.shape != (K // G, N // 8)):
+        raise ValueError(f"qzeros shape {QZ.shape} does not pack N={N} columns in groups of 8")
 
 
 class Oracle:
@@ -105,6 +116,8 @@ class Oracle:
     def pack(self, codes: np.ndarray) -> np.ndarray:
         codes = np.ascontiguousarray(codes, dtype=np.uint8)
         K, N = codes.shape
+        if K % 8 != 0:
+            raise ValueError(f"K={K} is not a multiple of 8 codes per word")
         Q = np.empty((K // 8, N), dtype=np.int32)
         self.lib.oracle_pack(_ptr(codes, _u8p), K, N, _ptr(Q, _i32p))
         return Q
@@ -112,6 +125,8 @@ class Oracle:
     def pack_zeros(self, zeros: np.ndarray) -> np.ndarray:
         zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
         groups, N = zeros.shape
+        if N % 8 != 0:
+            raise ValueError(f"N={N} is not a multiple of 8 zero points per word")
         QZ = np.empty((groups, N // 8), dtype=np.int32)
         self.lib.oracle_pack_zeros(_ptr(zeros, _u8p), groups, N, _ptr(QZ, _i32p))
         return QZ
@@ -140,6 +155,7 @@ class Oracle:
         if QZ is not None:
             QZ = np.ascontiguousarray(QZ, dtype=np.int32)
         K, N = 8 * Q.shape[0], Q.shape[1]
+        _check_layer(K, N, G, S, QZ)
         W = np.empty((K, N), dtype=np.uint16)
         self.lib.oracle_dequant(_ptr(Q, _i32p), _ptr(S, _u16p), _ptr(QZ, _i32p), K, N, G,
                                 _ptr(W, _u16p))
@@ -167,6 +183,9 @@ class Oracle:
             QZ = np.ascontiguousarray(QZ, dtype=np.int32)
         M, K = X.shape
         N = Q.shape[1]
+        if Q.shape[0] * 8 != K:
+            raise ValueError(f"qweight has {Q.shape[0]} packed rows for K={K}")
+        _check_layer(K, N, G, S, QZ)
         Y64 = np.empty((M, N), dtype=np.float64)
         Y16 = np.empty((M, N), dtype=np.uint16)
         rc = self.lib.oracle_linear(_ptr(X, _u16p), _ptr(Q, _i32p), _ptr(S, _u16p),
@@ -182,7 +201,8 @@ class Oracle:
         """fp16 W[K][N] -> (codes u8 [K][N], scales fp16 [K/G][N], zeros u8 [K/G][N] or None)."""
         W = np.ascontiguousarray(W, dtype=np.uint16)
         K, N = W.shape
-        assert K % G == 0
+        if G <= 0 or K % G != 0:
+            raise ValueError(f"group size {G} must divide K={K}")
         codes = np.empty((K, N), dtype=np.uint8)
         S = np.empty((K // G, N), dtype=np.uint16)
         Z = None if symmetric else np.empty((K // G, N), dtype=np.uint8)
@@ -198,7 +218,8 @@ class Oracle:
         """h = fp16(SiLU(Y64[:, :I]) * Y64[:, I:]) from the layer's fp64 sums."""
         Y64 = np.ascontiguousarray(Y64, dtype=np.float64)
         M, N = Y64.shape
-        assert N % 2 == 0
+        if N % 2 != 0:
+            raise ValueError(f"N={N} is not [gate | up] with equal halves")
         H16 = np.empty((M, N // 2), dtype=np.uint16)
         self.lib.oracle_gate_up(_ptr(Y64, _f64p), M, N // 2, _ptr(H16, _u16p))
         return H16

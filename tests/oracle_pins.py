@@ -415,13 +415,14 @@ def pin_gate_up_composition(o):
     K = G = 8, X = ones (twos in row 2), s = 1, z = 0, so each output is its
     column's code sum (doubled in row 2).  Gate sums of 0 give h = 0 whatever
     the up column; gate sums of 16 and 32 saturate SiLU to within 1.2e-7
-    relative, so h = fp16(gate * up) there; gate sums of 1, 2 and 4 are where
+    relative, so h = fp16(gate * up) there; gate sums from 1 to 10 are where
     SiLU bends: there sigmoid(t) = e^t / (1 + e^t), evaluated with the constant
     e, and h is that times t and up, rounded to fp16 (numpy's conversion).
+    N = 2I = 32 keeps whole words of packed zero points.
     """
-    I = 10
-    gate = [0, 16, 16, 0, 16, 0, 16, 16, 1, 2]
-    up = [40, 3, 0, 120, 1, 8, 6, 2, 7, 9]
+    I = 16
+    gate = [0, 16, 16, 0, 16, 0, 16, 16, 1, 2, 3, 5, 1, 0, 2, 16]
+    up = [40, 3, 0, 120, 1, 8, 6, 2, 7, 9, 11, 5, 30, 4, 13, 0]
     codes = np.zeros((8, 2 * I), dtype=np.uint8)
     for n in range(I):
         for c, total in ((n, gate[n]), (I + n, up[n])):
