@@ -32,6 +32,18 @@ Profiling helpers (the figures under profiles/ come from these):
 
 The roofline's "traffic" is read from the committed counter summary of the
 GEMV kernel, and only while the hash of its sources still matches.
+
+    python bench.py --ceilings
+        only the two ceilings below, as one JSON line
+
+"ceilings" in the JSON line (context, not the metric) are what this part
+sustains on the two bound resources, measured live by the probes in
+w4a16_group_quantized_amd/probes: a plain streaming read of the decode layer's
+byte count from the same number of cold copies (the floor for any kernel that
+must read those bytes once), and fp16 MFMA chains on operands that change every
+instruction (the matrix cores' rate once the clock has dropped to the power
+budget, which data-free peaks hide).  Each kernel's fraction of its ceiling is
+reported beside the fraction of the vendor peak.
 """
 from __future__ import annotations
 
@@ -242,6 +254,97 @@ def torch_matmul_context(name, steps):
             "us_per_call": t * 1e6, "tflops": flops / t / 1e12}
 
 
+def _probes():
+    import ctypes
+    from w4a16_group_quantized_amd import build as hip_build
+    if not os.path.exists(hip_build.PROBE_LIBRARY):
+        raise RuntimeError(f"{hip_build.PROBE_LIBRARY} is not built (run the package build first)")
+    lib = ctypes.CDLL(hip_build.PROBE_LIBRARY)
+    lib.awq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    lib.awq_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    return lib
+
+
+def ceiling_read(name, steps=200):
+    """A plain streaming read of the workload's weight bytes, cycling through
+    as many copies as the GEMV bench uses, launched as one HIP graph; the best
+    of three grid sizes."""
+    import torch
+    from w4a16_group_quantized_amd import synth
+    lib = _probes()
+    w = synth.WORKLOADS[name]
+    nbytes = alg_bytes(w, 0) // 16 * 16
+    copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+    bufs = [torch.full((nbytes,), i, dtype=torch.uint8, device="cuda") for i in range(copies)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    best = None
+    for blocks in (1024, 2048, 4096):
+        stream = torch.cuda.Stream()
+
+        def call(i):
+            rc = lib.awq_probe_stream_read(bufs[i % copies].data_ptr(), nbytes, blocks,
+                                           sink.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"awq_probe_stream_read failed: hip error {rc}")
+        with torch.cuda.stream(stream):
+            for i in range(20):
+                call(i)
+        stream.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                call(i)
+        with torch.cuda.stream(stream):
+            graph.replay()
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        e1.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / steps
+        if best is None or t < best[0]:
+            best = (t, blocks)
+        del graph
+    del bufs
+    torch.cuda.empty_cache()
+    t, blocks = best
+    return {"kernel": "streaming read, 16-byte non-temporal loads, grid-stride",
+            "bytes": nbytes, "copies": copies, "blocks": blocks, "us_per_call": round(t * 1e6, 3),
+            "gbs": round(nbytes / t / 1e9, 1)}
+
+
+def ceiling_mfma(blocks=1024, iters=4000, reps=5):
+    """v_mfma_f32_32x32x16_f16 chains on seeded random operands, all CUs busy."""
+    import torch
+    lib = _probes()
+    rng = np.random.default_rng(2024)
+    ops = to_dev(rng.uniform(-1.0, 1.0, 512).astype(np.float16).view(np.uint16))
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call():
+        rc = lib.awq_probe_mfma(ops.data_ptr(), out.data_ptr(), blocks, iters, stream)
+        if rc != 0:
+            raise RuntimeError(f"awq_probe_mfma failed: hip error {rc}")
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    flops = blocks * 4.0 * iters * 8 * 32768.0
+    return {"kernel": "32x32x16 fp16 MFMA chains, random operands changing every instruction",
+            "blocks": blocks, "tflops": round(flops / t / 1e12, 1),
+            "frac_of_peak": round(flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+
+
 def bench_gemm(name, steps, warmup):
     import torch
     from w4a16_group_quantized_amd import synth
@@ -408,6 +511,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--ceilings", action="store_true", help="only measure the two ceilings")
     ap.add_argument("--profile", choices=["gemv", "gemm"], help="dispatch sequence for counter passes")
     ap.add_argument("--summarize-pmc", nargs="+", metavar=("OUT", "DIR"),
                     help="fold rocprofv3 --pmc CSV directories into a summary file")
@@ -434,6 +538,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile:
         profile_run(args.profile)
+        return
+    if args.ceilings:
+        print(json.dumps({"hbm_read": ceiling_read("decode_8b_gate"), "mfma_f16": ceiling_mfma()}))
         return
     from w4a16_group_quantized_amd import binding
     binding.load()
@@ -476,6 +583,9 @@ def main():
                  "tflops": round(gemm["tflops"], 1), "peak": MFMA_F16_PEAK_TFLOPS,
                  "frac": round(gemm["mfma_frac"], 4), "us_per_call": round(gemm["us_per_call"], 2)},
     }
+    read, mfma = ceiling_read("decode_8b_gate"), ceiling_mfma()
+    out["ceilings"] = {"hbm_read": read, "gemv_frac_of_read": round(head["gbs"] / read["gbs"], 4),
+                       "mfma_f16": mfma, "gemm_frac_of_mfma": round(gemm["tflops"] / mfma["tflops"], 4)}
     if extra:
         out["extra"] = extra
     if not args.no_cpu:

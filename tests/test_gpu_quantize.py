@@ -43,6 +43,7 @@ def _check(W, G, sym, what):
 @pytest.mark.parametrize("K,N,G,sym", [
     (128, 64, 128, False), (256, 40, 64, False), (512, 136, 128, True), (64, 8, 8, False),
     (1024, 200, 1024, True), (384, 24, 32, False), (4096, 512, 128, False), (96, 72, 96, True),
+    (2048, 136, 2048, False), (8192, 72, 8192, True), (3072, 64, 1536, False),
 ])
 def test_quantize_bit_exact(K, N, G, sym):
     _check(_weights(K * 7 + N, K, N), G, sym, f"K={K} N={N} G={G} sym={sym}")
@@ -73,3 +74,23 @@ def test_quantize_llama_layer_and_run():
     y = to_host_bits(binding.gemv(to_dev(X), lay))
     torch.cuda.synchronize()
     assert_y_close(y, Y16, "gemv on the GPU-quantized layer")
+
+
+def test_quantize_exact_ties():
+    """Every group spans exactly 15 s with s a power of two, and its other
+    weights sit on half steps (j + 1/2) s: each w / s is an exact tie, which the
+    kernel must round like the correctly rounded quotient (ties to even)."""
+    K, N, G = 256, 64, 32
+    rng = np.random.default_rng(31)
+    W = np.zeros((K, N), dtype=np.float64)
+    for g in range(K // G):
+        for n in range(N):
+            s = 2.0 ** -int(rng.integers(3, 12))
+            z = int(rng.integers(0, 16))                       # lo = -z s, hi = (15 - z) s
+            vals = (rng.integers(-z, 15 - z, G) + 0.5) * s     # half steps inside the range
+            vals[0], vals[1] = -z * s, (15 - z) * s
+            W[g * G:(g + 1) * G, n] = vals
+    W16 = W.astype(np.float16)
+    assert np.array_equal(W16.astype(np.float64), W)          # all exact in fp16
+    codes, _, _, _ = _check(W16.view(np.uint16), G, False, "exact ties")
+    assert codes.max() <= 15

@@ -3,7 +3,8 @@
     python -m w4a16_group_quantized_amd.build
 
 Every HIP source under ``csrc/`` goes into one shared library next to this
-file.  Flags: -O3 for gfx950 only; no fast-math and no denormal flushing (the
+file.  The measurement probes under ``probes/`` (a plain streaming read and an
+MFMA rate probe, used only by bench.py) go into ``probes/libawq_probes.so``.  Flags: -O3 for gfx950 only; no fast-math and no denormal flushing (the
 dequantized weights must round exactly as IEEE fp16); packed-fp32 VALU
 instructions disabled.
 """
@@ -17,6 +18,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libawq.so")
+PROBES = os.path.join(HERE, "probes")
+PROBE_LIBRARY = os.path.join(PROBES, "libawq_probes.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -44,9 +47,10 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(out: str = LIBRARY, extra_flags: list[str] | None = None, verbose: bool = False) -> str:
+def build(out: str = LIBRARY, extra_flags: list[str] | None = None, verbose: bool = False,
+          srcs: list[str] | None = None) -> str:
     """Compile every HIP source into ``out`` (always recompiles)."""
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), *sources(), "-o", out + ".tmp"]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), *(srcs or sources()), "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd))
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,5 +60,12 @@ def build(out: str = LIBRARY, extra_flags: list[str] | None = None, verbose: boo
     return out
 
 
+def build_probes(verbose: bool = False) -> str:
+    """Compile the measurement probes into ``probes/libawq_probes.so``."""
+    return build(PROBE_LIBRARY, verbose=verbose,
+                 srcs=sorted(glob.glob(os.path.join(PROBES, "*.hip"))))
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probes(verbose=True))

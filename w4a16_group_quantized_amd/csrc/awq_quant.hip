@@ -11,11 +11,25 @@
 //   symmetric:  s = fp16(max|w| / 7), z = 8
 //   both:       s = 1 if it rounds to 0; q = clamp(rint(w / s) + z, 0, 15)
 //
-// One thread owns eight consecutive columns of one group: a first pass over the
-// group's rows (16-byte loads, coalesced along N) finds the extremes, a second
-// pass (re-reading the rows, mostly from cache) computes the codes and writes
-// eight packed words per packed row as two 16-byte stores.  Bound: HBM, about
-// 2 K N bytes read twice at most, K N / 2 written.
+// A workgroup of WPG waves owns one group of 64 columns: lane (c, r) =
+// (lane / 8, lane % 8) of wave v takes the 8 columns 8 c .. 8 c + 7 and the
+// rows r + 8 v, + 8 WPG, ... of the group.  A first pass (16-byte loads, 8 in
+// flight per lane, 128 contiguous bytes per row across the wave's column
+// chunks) finds each column's extremes; shuffles over the eight row lanes of a
+// chunk, then LDS across the waves, complete them (exactly, in any order).  A
+// second pass takes packed rows p = r + 8 v, + 8 WPG, ...: it re-reads the
+// group's rows 8 p .. 8 p + 7 (from cache), computes the codes and writes the
+// eight packed words of the chunk as two 16-byte stores.  Bound: HBM, 2 K N
+// bytes read, K N / 2 written.  WPG = 4 for layers with few (group, column)
+// tiles and long groups, so that those are read by enough lanes at once.
+//
+// The extremes are taken on the fp16 values themselves (packed min / max,
+// exact).  rint(w / s) is decided from w * (1 / s): that product is within
+// 2^-22 |w / s| of the true quotient, so unless it lies that close to a
+// half-integer its rint equals rint of the correctly rounded quotient; the
+// values that close divide exactly.  With fp16 weights and scales exact ties
+// (w = (k + 1/2) s) are common, so the test is made per value: redoing a
+// whole packed row whenever one of its values is close costs more.
 #include "awq_device.h"
 #include "awq_internal.h"
 
@@ -24,100 +38,172 @@ namespace {
 
 __device__ __forceinline__ float clamp_code(float v) { return fminf(fmaxf(v, 0.0f), 15.0f); }
 
-__device__ __forceinline__ void load8(const uint16_t *p, float w[8]) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        w[2 * i] = (float)as_half((uint16_t)u[i]);
-        w[2 * i + 1] = (float)as_half((uint16_t)(u[i] >> 16));
-    }
+__device__ __forceinline__ uint4 load16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// rint(w / s) with the quotient correctly rounded to fp32 first; inv = 1 / s.
+__device__ __forceinline__ float rint_quotient(float w, float s, float inv) {
+    const float q = w * inv;
+    const float t = __builtin_rintf(q);
+    if (fabsf(q - t) >= 0.5f - fabsf(q) * 0x1p-21f) return __builtin_rintf(w / s);
+    return t;
 }
 
-template <bool SYM>
-__global__ void __launch_bounds__(256)
+// Columns of one column chunk, one chunk per eight lanes.
+constexpr int kRowLanes = 8;
+
+template <bool SYM, int WPG>
+__global__ void __launch_bounds__(64 * WPG)
 quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16_t *__restrict__ S,
-                uint32_t *__restrict__ QZ, int K, int N, int G) {
-    const int n8 = N / 8;
-    const long long total = (long long)(K / G) * n8;
-    for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
-         t += (long long)gridDim.x * blockDim.x) {
-        const int g = (int)(t / n8);
-        const int n = (int)(t % n8) * 8;
-        const uint16_t *wg = W + (size_t)g * G * N + n;
+                uint32_t *__restrict__ QZ, int K, int N, int G, int tiles_n) {
+    constexpr int kStride = kRowLanes * WPG;     // rows between a lane's consecutive rows
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c = lane >> 3, r = lane & 7;
+    const int rr = r + kRowLanes * wave;         // first row of this lane
+    const int g = blockIdx.x / tiles_n;
+    const int n = (blockIdx.x % tiles_n) * 64 + 8 * c;
+    const bool live = n < N;                     // N % 8 == 0: a chunk is all in or all out
+    const uint16_t *wg = W + (size_t)g * G * N + (live ? n : 0);
 
-        float lo[8], hi[8], amax[8];
+    // Column pairs (2 i, 2 i + 1) as half2: minimum, maximum, maximum of |w|.
+    half2_t lo2[4], hi2[4], am2[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            lo[i] = __builtin_huge_valf();
-            hi[i] = -__builtin_huge_valf();
-            amax[i] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+        lo2[i] = as_half2(0x7C007C00u);   // +inf
+        hi2[i] = as_half2(0xFC00FC00u);   // -inf
+        am2[i] = as_half2(0u);
+    }
+    auto take = [&](uint4 v) {
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const half2_t w2 = as_half2(u[i]);
+            lo2[i] = __builtin_elementwise_min(lo2[i], w2);
+            hi2[i] = __builtin_elementwise_max(hi2[i], w2);
+            am2[i] = __builtin_elementwise_max(am2[i], as_half2(u[i] & 0x7FFF7FFFu));
         }
-        for (int k = 0; k < G; ++k) {
-            float w[8];
-            load8(wg + (size_t)k * N, w);
+    };
+    if (live) {
+        int k = rr;
+        for (; k + 7 * kStride < G; k += 8 * kStride) {
+            uint4 v[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                lo[i] = fminf(lo[i], w[i]);
-                hi[i] = fmaxf(hi[i], w[i]);
-                amax[i] = fmaxf(amax[i], fabsf(w[i]));
+            for (int u = 0; u < 8; ++u) v[u] = load16(wg + (size_t)(k + u * kStride) * N);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) take(v[u]);
+        }
+        for (; k < G; k += kStride) take(load16(wg + (size_t)k * N));
+    }
+    // The chunk's eight row lanes are lanes 8 c .. 8 c + 7 of each wave.
+#pragma unroll
+    for (int o = 1; o < kRowLanes; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo2[i] = __builtin_elementwise_min(lo2[i], as_half2(__shfl_xor(as_u32(lo2[i]), o, 64)));
+            hi2[i] = __builtin_elementwise_max(hi2[i], as_half2(__shfl_xor(as_u32(hi2[i]), o, 64)));
+            am2[i] = __builtin_elementwise_max(am2[i], as_half2(__shfl_xor(as_u32(am2[i]), o, 64)));
+        }
+    if constexpr (WPG > 1) {
+        __shared__ uint32_t part[WPG][8][3][4];   // wave, chunk, quantity, column pair
+        if (r == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                part[wave][c][0][i] = as_u32(lo2[i]);
+                part[wave][c][1][i] = as_u32(hi2[i]);
+                part[wave][c][2][i] = as_u32(am2[i]);
             }
-        }
-        float sv[8], zv[8];
-        uint32_t sh[4] = {0u, 0u, 0u, 0u}, zword = 0u;
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float r;
-            if (SYM) {
-                r = amax[i] / 7.0f;
-            } else {
-                float range = hi[i] - lo[i];
-                if (range == 0.0f) range = fabsf(hi[i]);
-                r = range / 15.0f;
+        for (int v = 0; v < WPG; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo2[i] = __builtin_elementwise_min(lo2[i], as_half2(part[v][c][0][i]));
+                hi2[i] = __builtin_elementwise_max(hi2[i], as_half2(part[v][c][1][i]));
+                am2[i] = __builtin_elementwise_max(am2[i], as_half2(part[v][c][2][i]));
             }
-            uint16_t s16 = as_u16((half_t)r);
-            if ((s16 & 0x7FFFu) == 0u) s16 = 0x3C00u;   // 1.0
-            sv[i] = (float)as_half(s16);
-            zv[i] = SYM ? 8.0f : clamp_code(__builtin_rintf(-lo[i] / sv[i]));
-            sh[i / 2] |= (uint32_t)s16 << (16 * (i % 2));
-            zword |= (uint32_t)zv[i] << (4 * i);
+    }
+    if (!live) return;
+    float lo[8], hi[8], amax[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            lo[2 * i + e] = (float)lo2[i][e];
+            hi[2 * i + e] = (float)hi2[i][e];
+            amax[2 * i + e] = (float)am2[i][e];
         }
+
+    float sv[8], zv[8], inv[8];
+    uint32_t sh[4] = {0u, 0u, 0u, 0u}, zword = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float rg;
+        if (SYM) {
+            rg = amax[i] / 7.0f;
+        } else {
+            float range = hi[i] - lo[i];
+            if (range == 0.0f) range = fabsf(hi[i]);
+            rg = range / 15.0f;
+        }
+        uint16_t s16 = as_u16((half_t)rg);
+        if ((s16 & 0x7FFFu) == 0u) s16 = 0x3C00u;   // 1.0
+        sv[i] = (float)as_half(s16);
+        inv[i] = 1.0f / sv[i];
+        zv[i] = SYM ? 8.0f : clamp_code(__builtin_rintf(-lo[i] / sv[i]));
+        sh[i / 2] |= (uint32_t)s16 << (16 * (i % 2));
+        zword |= (uint32_t)zv[i] << (4 * i);
+    }
+    if (rr == 0) {
         *reinterpret_cast<uint4 *>(S + (size_t)g * N + n) = make_uint4(sh[0], sh[1], sh[2], sh[3]);
-        if (!SYM) QZ[(size_t)g * n8 + n / 8] = zword;
+        if (!SYM) QZ[(size_t)g * (N / 8) + n / 8] = zword;
+    }
 
-        for (int r = 0; r < G / 8; ++r) {
-            uint32_t word[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    for (int p = rr; p < G / 8; p += kStride) {
+        uint4 v[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float w[8];
-                load8(wg + (size_t)(8 * r + j) * N, w);
+        for (int j = 0; j < 8; ++j) v[j] = load16(wg + (size_t)(8 * p + j) * N);
+        // Value of column i in row j of the packed row.
+        auto wat = [&](int j, int i) {
+            const uint32_t u = i < 2 ? v[j].x : i < 4 ? v[j].y : i < 6 ? v[j].z : v[j].w;
+            return (float)as_half((uint16_t)(u >> (16 * (i & 1))));
+        };
+        uint32_t word[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    word[i] |= (uint32_t)clamp_code(__builtin_rintf(w[i] / sv[i]) + zv[i]) << (4 * j);
-            }
-            uint32_t *qrow = Q + (size_t)(g * (G / 8) + r) * N + n;
-            reinterpret_cast<uint4 *>(qrow)[0] = make_uint4(word[0], word[1], word[2], word[3]);
-            reinterpret_cast<uint4 *>(qrow)[1] = make_uint4(word[4], word[5], word[6], word[7]);
-        }
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                word[i] |= (uint32_t)clamp_code(rint_quotient(wat(j, i), sv[i], inv[i]) + zv[i]) << (4 * j);
+        uint32_t *qrow = Q + (size_t)(g * (G / 8) + p) * N + n;
+        reinterpret_cast<uint4 *>(qrow)[0] = make_uint4(word[0], word[1], word[2], word[3]);
+        reinterpret_cast<uint4 *>(qrow)[1] = make_uint4(word[4], word[5], word[6], word[7]);
     }
 }
 
 }  // namespace
 
+template <int WPG>
+hipError_t launch_q(const uint16_t *w, uint32_t *q, uint16_t *scales, uint32_t *z, int K, int N, int G,
+                    int tiles_n, long long blocks, bool symmetric, hipStream_t s) {
+    if (symmetric)
+        hipLaunchKernelGGL((quantize_kernel<true, WPG>), dim3((unsigned)blocks), dim3(64 * WPG), 0, s, w,
+                           q, scales, z, K, N, G, tiles_n);
+    else
+        hipLaunchKernelGGL((quantize_kernel<false, WPG>), dim3((unsigned)blocks), dim3(64 * WPG), 0, s,
+                           w, q, scales, z, K, N, G, tiles_n);
+    return hipGetLastError();
+}
+
+// One wave per (group, 64 columns); four for long groups (1024 rows or more)
+// when there are too few tiles to fill the GPU several times over.
 hipError_t launch_quantize(const uint16_t *w, int32_t *qweight, uint16_t *scales, int32_t *qzeros,
                            int K, int N, int G, bool symmetric, hipStream_t s) {
-    const long long threads = (long long)(K / G) * (N / 8);
-    long long blocks = (threads + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
+    const int tiles_n = (N + 63) / 64;
+    const long long blocks = (long long)(K / G) * tiles_n;
+    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     auto *q = reinterpret_cast<uint32_t *>(qweight);
     auto *z = reinterpret_cast<uint32_t *>(qzeros);
-    if (symmetric)
-        hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, w, q, scales,
-                           z, K, N, G);
-    else
-        hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, w, q,
-                           scales, z, K, N, G);
-    return hipGetLastError();
+    if (blocks >= 4096 || G < 1024) return launch_q<1>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
+    return launch_q<4>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
 }
 
 }  // namespace awq

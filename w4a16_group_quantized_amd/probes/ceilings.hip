@@ -1,0 +1,100 @@
+// Measurement probes, not part of the layer: what this GPU sustains on the two
+// resources the fused kernels are bound by, measured under the same conditions
+// as the kernels themselves.
+//
+//   awq_probe_stream_read: a plain streaming read of `bytes` -- 16-byte
+//   non-temporal loads, grid-stride, four in flight per lane -- with the data
+//   folded into one word so that no load can be removed.  Its time for the
+//   decode layer's byte count, from copies that are not in any cache, is the
+//   floor a kernel that must read those bytes can reach on this part.
+//
+//   awq_probe_mfma: chains of v_mfma_f32_32x32x16_f16 with no memory traffic in
+//   the loop, on operands that change from one instruction to the next (four A
+//   and four B registers of seeded values, rotated).  Under load the part lowers
+//   its clock to stay in its power budget, and how far depends on how much the
+//   operand bits toggle: all-zero operands keep the nominal clock, random ones
+//   do not.  The rate measured here is the matrix cores' sustained fp16 rate on
+//   realistic data.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kUnroll = 4;
+
+__global__ void __launch_bounds__(256)
+stream_read_kernel(const u32x4 *__restrict__ p, long long n16, uint32_t *sink) {
+    uint32_t acc = 0;
+    const long long stride = (long long)gridDim.x * 256;
+    long long i = blockIdx.x * 256LL + threadIdx.x;
+    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(p + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;   // practically never taken; keeps the loads
+}
+
+// Eight independent accumulators per wave, each fed every eighth MFMA, so that
+// no MFMA waits for the previous result.
+__global__ void __launch_bounds__(256)
+mfma_kernel(const half8 *__restrict__ in, float *__restrict__ out, int iters) {
+    const int t = threadIdx.x;
+    half8 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        a[u] = in[(t + 5 * u) & 63];
+        b[u] = in[(t + 11 * u + 7) & 63];
+    }
+    f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i & 3], b[(i + (i >> 2)) & 3], acc[i], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += acc[i][v];
+    out[blockIdx.x * 256 + t] = s;
+}
+
+}  // namespace
+
+// bytes: a multiple of 16; buf: device memory of at least `bytes`; sink: one
+// device word.  Returns the launch's hipError_t.
+extern "C" int awq_probe_stream_read(const void *buf, long long bytes, int blocks, uint32_t *sink,
+                                     hipStream_t stream) {
+    if (buf == nullptr || sink == nullptr || bytes <= 0 || bytes % 16 != 0 || blocks <= 0)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, stream,
+                       static_cast<const u32x4 *>(buf), bytes / 16, sink);
+    return (int)hipGetLastError();
+}
+
+// operands: 512 fp16 values (64 x 8) in device memory; out: blocks * 256
+// floats of device memory.  Flops per launch: blocks * 4 waves * iters * 8 *
+// 32768.  Returns the launch's hipError_t.
+extern "C" int awq_probe_mfma(const uint16_t *operands, float *out, int blocks, int iters,
+                              hipStream_t stream) {
+    if (operands == nullptr || out == nullptr || blocks <= 0 || iters <= 0)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mfma_kernel, dim3(blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const half8 *>(operands), out, iters);
+    return (int)hipGetLastError();
+}
