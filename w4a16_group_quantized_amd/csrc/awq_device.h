@@ -46,6 +46,36 @@ __device__ __forceinline__ void unpack_biased(uint32_t w, uint32_t mask, uint32_
     p[3] = ((w >> 12) & mask) | kBias1024x2;
 }
 
+// All-reduce over aligned groups of L lanes (L = 2, 4, 8 or 16) with DPP lane
+// moves, which stay in the vector ALU (a __shfl_xor is an LDS permute with its
+// latency).  Step s combines each lane with a partner in the other half of its
+// group of 2^(s+1) lanes: xor 1 and xor 2 within a quad, then the mirror lane
+// within 8 and within 16.  After the steps before it the value is uniform
+// within each half, so a mirror partner serves as well as an xor partner.
+// op(a, b) must be commutative and associative (exactly, for the result to be
+// the same in every lane: min and max are; a float sum is the same in every
+// lane of the group but depends on the step order).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+template <int L, typename Op>
+__device__ __forceinline__ uint32_t lane_group_reduce(uint32_t v, Op op) {
+    static_assert(L == 1 || L == 2 || L == 4 || L == 8 || L == 16, "group of 1..16 lanes");
+    if constexpr (L >= 2) v = op(v, dpp_move<0xB1>(v));    // quad_perm [1,0,3,2]: xor 1
+    if constexpr (L >= 4) v = op(v, dpp_move<0x4E>(v));    // quad_perm [2,3,0,1]: xor 2
+    if constexpr (L >= 8) v = op(v, dpp_move<0x141>(v));   // row_half_mirror: 7 - i within 8
+    if constexpr (L >= 16) v = op(v, dpp_move<0x140>(v));  // row_mirror: 15 - i within 16
+    return v;
+}
+template <int L>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    return __builtin_bit_cast(float, lane_group_reduce<L>(__builtin_bit_cast(uint32_t, v),
+        [](uint32_t a, uint32_t b) {
+            return __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+        }));
+}
+
 __device__ __forceinline__ half2_t as_half2(uint32_t u) {
     return __builtin_bit_cast(half2_t, u);
 }

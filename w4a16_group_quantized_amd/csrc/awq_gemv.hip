@@ -165,11 +165,16 @@ __device__ __forceinline__ half8_t as_b(const uint32_t p[4]) {
     return as_half8(make_uint4(p[0], p[1], p[2], p[3]));
 }
 
+// X staged in LDS row-major, K / 8 chunks per row: chunk r of row m sits at
+// r ^ (m % 16) when K / 8 is a multiple of 16, so that one chunk of 16
+// different rows (an A-operand read of 16 lanes) falls in 16 bank groups.
+__device__ __forceinline__ int xlds_swizzle(int m, int K) { return (K & 127) == 0 ? (m & 15) : 0; }
+
 // The A operand of one step: row xrow of X, packed row r (k = 8r .. 8r+7).
 template <bool XLDS>
 __device__ __forceinline__ half8_t load_a(const uint16_t *__restrict__ X, const uint4 *xs, int xrow,
                                          int K, int r) {
-    if constexpr (XLDS) return as_half8(xs[xrow * (K / 8) + r]);
+    if constexpr (XLDS) return as_half8(xs[xrow * (K / 8) + (r ^ xlds_swizzle(xrow, K))]);
     else return as_half8(natural_to_pairs(
              reinterpret_cast<const uint4 *>(X + (size_t)xrow * K)[r]));
 }
@@ -296,7 +301,8 @@ fold_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #pragma unroll
         for (int j = 0; j < XMAX; ++j) {
             const int c = threadIdx.x + j * NW * 64;
-            if (c < xchunks) lds[c] = natural_to_pairs(xr[j]);
+            const int m = c / (K / 8), r = c - m * (K / 8);
+            if (c < xchunks) lds[m * (K / 8) + (r ^ xlds_swizzle(m, K))] = natural_to_pairs(xr[j]);
         }
         __syncthreads();
     }
@@ -444,7 +450,11 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const int spg = G / (8 * SEGR);              // segments per group
 
     // LDS: staged X slices (all waves), then (U, S) tables; once every wave is
-    // done with them, the reduction buffer takes their place.
+    // done with them, the reduction buffer takes their place.  Chunk rr of row
+    // m of a slice sits at rr ^ (m % 16) (rows_w is a multiple of 16, so the
+    // chunk stays in its row): an A-operand read takes one chunk of 16
+    // different rows per 16 lanes, which then fall in 16 different bank groups
+    // instead of one.
     uint4 *xs = lds + wave * (M * rows_w);
     float2 *tabs = reinterpret_cast<float2 *>(lds + M * KR);
     float2 *tab = tabs + wave * (M * per);
@@ -502,17 +512,13 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         float t = c < chunks_w ? lo + hi : 0.f;          // sum of the staged values
         float u = c < chunks_w ? lo + 16.f * hi : 0.f;   // sum of x
         // segment sums over aligned groups of SEGR lanes (consecutive chunks)
-#pragma unroll
-        for (int o = 1; o < SEGR; o <<= 1) {
-            t += __shfl_xor(t, o, 64);
-            u += __shfl_xor(u, o, 64);
-        }
+        t = lane_group_sum<SEGR>(t);
+        u = lane_group_sum<SEGR>(u);
         if (c < chunks_w) {
-            xs[c] = a;
-            if (c % SEGR == 0) {
-                const int m = VR == 1 ? 0 : c / rows_w;
-                tab[m * per + (c - m * rows_w) / SEGR] = make_float2(1024.f * t, u);
-            }
+            const int m = VR == 1 ? 0 : c / rows_w;
+            const int rr = c - m * rows_w;
+            xs[m * rows_w + (rr ^ (m & 15))] = a;
+            if (c % SEGR == 0) tab[m * per + rr / SEGR] = make_float2(1024.f * t, u);
         }
     }
     // Only this wave reads its slice; LDS operations of one wave execute in order.
@@ -538,7 +544,7 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         const int rl0 = (seg - s_begin) * SEGR;   // local packed row of the segment
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            const half8_t a = as_half8(xs[xrow * rows_w + rl0 + 4 * st + kb]);
+            const half8_t a = as_half8(xs[xrow * rows_w + ((rl0 + 4 * st + kb) ^ (xrow & 15))]);
 #pragma unroll
             for (int i = 0; i < WPL; ++i) {
                 uint32_t p[4];
@@ -886,9 +892,11 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
     using namespace gemv;
     // Per-wave staged X (up to 160 KB of LDS), D-deep load pipeline.  Beyond
     // four rows, X fills most of LDS (one workgroup per CU), so each workgroup
-    // takes a twice wider strip: fewer workgroups, each staging X once.
-    if (M > 4 && stream_fits(M, K, N, G, 8, 8, 16, 2))
-        return launch_stream_m<8, 8, 16, 2>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    // takes a twice wider strip: fewer workgroups, each staging X once; and one
+    // segment in flight per wave, so that staging X and the first loads compete
+    // less for the CU's load path (measured faster).
+    if (M > 4 && stream_fits(M, K, N, G, 8, 8, 16, 1))
+        return launch_stream_m<8, 8, 16, 1>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 2))
         return launch_stream_m<4, 8, 16, 2>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 1))

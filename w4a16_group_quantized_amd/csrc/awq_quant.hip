@@ -95,14 +95,14 @@ quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16
         for (; k < G; k += kStride) take(load16(wg + (size_t)k * N));
     }
     // The chunk's eight row lanes are lanes 8 c .. 8 c + 7 of each wave.
+    auto hmin = [](uint32_t a, uint32_t b) { return as_u32(__builtin_elementwise_min(as_half2(a), as_half2(b))); };
+    auto hmax = [](uint32_t a, uint32_t b) { return as_u32(__builtin_elementwise_max(as_half2(a), as_half2(b))); };
 #pragma unroll
-    for (int o = 1; o < kRowLanes; o <<= 1)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            lo2[i] = __builtin_elementwise_min(lo2[i], as_half2(__shfl_xor(as_u32(lo2[i]), o, 64)));
-            hi2[i] = __builtin_elementwise_max(hi2[i], as_half2(__shfl_xor(as_u32(hi2[i]), o, 64)));
-            am2[i] = __builtin_elementwise_max(am2[i], as_half2(__shfl_xor(as_u32(am2[i]), o, 64)));
-        }
+    for (int i = 0; i < 4; ++i) {
+        lo2[i] = as_half2(lane_group_reduce<kRowLanes>(as_u32(lo2[i]), hmin));
+        hi2[i] = as_half2(lane_group_reduce<kRowLanes>(as_u32(hi2[i]), hmax));
+        am2[i] = as_half2(lane_group_reduce<kRowLanes>(as_u32(am2[i]), hmax));
+    }
     if constexpr (WPG > 1) {
         __shared__ uint32_t part[WPG][8][3][4];   // wave, chunk, quantity, column pair
         if (r == 0)
