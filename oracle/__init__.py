@@ -88,6 +88,15 @@ class Oracle:
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_gate_up.argtypes = [_f64p, ctypes.c_int, ctypes.c_int, _u16p]
+        I, D = ctypes.c_int, ctypes.c_double
+        lib.oracle_channel_stats.argtypes = [_u16p, I, _u16p, I, I, I, _f64p, _f64p]
+        lib.oracle_scale_candidate.argtypes = [_f64p, _f64p, I, D, _f64p]
+        lib.oracle_migrate.argtypes = [_u16p, _u16p, I, I, I, _f64p, _u16p, _u16p]
+        lib.oracle_scale_loss.restype = I
+        lib.oracle_scale_loss.argtypes = [_u16p, _u16p, I, I, I, I, I, _f64p,
+                                          ctypes.POINTER(ctypes.c_double)]
+        lib.oracle_scale_search.restype = I
+        lib.oracle_scale_search.argtypes = [_u16p, I, _u16p, I, I, I, I, _f64p, I, _f64p, _f64p]
         lib.oracle_linear.restype = ctypes.c_int
         lib.oracle_linear.argtypes = [_u16p, _i32p, _u16p, _i32p, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, _f64p, _u16p]
@@ -223,6 +232,75 @@ class Oracle:
         H16 = np.empty((M, N // 2), dtype=np.uint16)
         self.lib.oracle_gate_up(_ptr(Y64, _f64p), M, N // 2, _ptr(H16, _u16p))
         return H16
+
+    # -- scale migration and search (R14, R15, R16) ---------------------------
+    def channel_stats(self, X: np.ndarray, W: np.ndarray, G: int):
+        """(xbar, wbar) fp64 [K]: mean |x| per input channel, and the mean over
+        output columns of |w| normalized by its group's largest |w|."""
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        W = np.ascontiguousarray(W, dtype=np.uint16)
+        M, K = X.shape
+        N = W.shape[1]
+        if W.shape[0] != K or G <= 0 or K % G != 0:
+            raise ValueError(f"X {X.shape}, W {W.shape}, G={G} do not fit")
+        xbar, wbar = np.empty(K), np.empty(K)
+        self.lib.oracle_channel_stats(_ptr(X, _u16p), M, _ptr(W, _u16p), K, N, G,
+                                      _ptr(xbar, _f64p), _ptr(wbar, _f64p))
+        return xbar, wbar
+
+    def scale_candidate(self, xbar: np.ndarray, wbar: np.ndarray, alpha: float) -> np.ndarray:
+        xbar = np.ascontiguousarray(xbar, dtype=np.float64)
+        wbar = np.ascontiguousarray(wbar, dtype=np.float64)
+        c = np.empty(xbar.size)
+        self.lib.oracle_scale_candidate(_ptr(xbar, _f64p), _ptr(wbar, _f64p), xbar.size,
+                                        float(alpha), _ptr(c, _f64p))
+        return c
+
+    def migrate(self, X: np.ndarray, W: np.ndarray, c: np.ndarray):
+        """(fp16(X / c), fp16(c * W)), c per input channel."""
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        W = np.ascontiguousarray(W, dtype=np.uint16)
+        c = np.ascontiguousarray(c, dtype=np.float64)
+        M, K = X.shape
+        N = W.shape[1]
+        if W.shape[0] != K or c.size != K:
+            raise ValueError("X, W and c do not fit")
+        Xs, Ws = np.empty_like(X), np.empty_like(W)
+        self.lib.oracle_migrate(_ptr(X, _u16p), _ptr(W, _u16p), M, K, N, _ptr(c, _f64p),
+                                _ptr(Xs, _u16p), _ptr(Ws, _u16p))
+        return Xs, Ws
+
+    def scale_loss(self, X: np.ndarray, W: np.ndarray, G: int, symmetric: bool,
+                   c: np.ndarray) -> float:
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        W = np.ascontiguousarray(W, dtype=np.uint16)
+        c = np.ascontiguousarray(c, dtype=np.float64)
+        M, K = X.shape
+        N = W.shape[1]
+        if W.shape[0] != K or c.size != K or G <= 0 or K % G != 0:
+            raise ValueError("X, W, c and G do not fit")
+        out = ctypes.c_double()
+        if self.lib.oracle_scale_loss(_ptr(X, _u16p), _ptr(W, _u16p), M, K, N, G,
+                                      int(symmetric), _ptr(c, _f64p), ctypes.byref(out)) != 0:
+            raise MemoryError("oracle_scale_loss could not allocate")
+        return out.value
+
+    def scale_search(self, X: np.ndarray, W: np.ndarray, G: int, symmetric: bool, alphas):
+        """(best index, losses fp64 [n_alpha], scales of the best alpha fp64 [K])."""
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        W = np.ascontiguousarray(W, dtype=np.uint16)
+        a = np.ascontiguousarray(alphas, dtype=np.float64)
+        M, K = X.shape
+        N = W.shape[1]
+        if W.shape[0] != K or G <= 0 or K % G != 0 or a.size < 1:
+            raise ValueError("X, W, G and alphas do not fit")
+        losses, c = np.empty(a.size), np.empty(K)
+        best = self.lib.oracle_scale_search(_ptr(X, _u16p), M, _ptr(W, _u16p), K, N, G,
+                                            int(symmetric), _ptr(a, _f64p), a.size,
+                                            _ptr(losses, _f64p), _ptr(c, _f64p))
+        if best < 0:
+            raise MemoryError("oracle_scale_search could not allocate")
+        return best, losses, c
 
 
 _DEFAULT: Oracle | None = None

@@ -42,7 +42,10 @@
  *       to fp16.
  *   R7  fp16 is IEEE 754 binary16: subnormals kept, overflow to infinity,
  *       round to nearest, ties to even.
- *   R9  quantizer (the step before the layer): each group of G weights of a
+ *   R8-R11 (codes above 15 masked when packed; K, N and G multiples of 8 and
+ *       K of G; the synthetic inputs' outlier channels and fp16 draws) concern
+ *       the callers and the input generator, not the arithmetic here.
+ *   R13 quantizer (the step before the layer): each group of G weights of a
  *       column is rounded to integer levels against a scale and zero point
  *       (pyshine.com AutoAWQ tour, "The Quantization Flow Up Close": the
  *       pseudo-quantization pass; "From Install to Your First Model":
@@ -54,10 +57,32 @@
  *         symmetric:  r = max |w|, s = fp16(r / 7), z = 8
  *         both:       s = 1 if it rounds to 0; q = clamp(rint(w / s) + z, 0, 15)
  *       with lo, hi the group's minimum and maximum.
- *   R8  fused gate/up: the layer's N = 2I columns are [gate | up]; the output
+ *   R12 fused gate/up: the layer's N = 2I columns are [gate | up]; the output
  *       is h[m][n] = fp16(SiLU(y(m, n)) * y(m, I + n)), n < I, with y the
  *       layer's exact (unrounded) sums and SiLU(t) = t / (1 + e^-t), rounded
  *       once.
+ *   R14 channel statistics of the scale search (pyshine.com AutoAWQ tour, "The
+ *       Quantization Flow Up Close": a per-channel mean of normalized weights
+ *       and a mean of activations; the AwqQuantizer captures activation
+ *       magnitudes): for input channel k,
+ *         xbar[k] = mean over the calibration rows m of |x(m, k)|,
+ *         wbar[k] = mean over the output columns n of |w(k, n)| / a(g, n),
+ *       with a(g, n) the largest |w| of k's quantization group in column n
+ *       (normalized per group: the pages do not say over what; a column whose
+ *       group is all zero adds 0).
+ *   R15 candidate scales (same passages; "duo_scaling" uses both statistics,
+ *       and the scales come from a grid search): for a grid value alpha in
+ *       [0, 1], c[k] = max(xbar[k], 1e-4)^alpha / max(wbar[k], 1e-4)^(1 - alpha).
+ *       The grid itself is the caller's; the floor keeps c finite and nonzero.
+ *   R16 objective (same passages: the FP16 module is run once as a reference
+ *       and the candidate that minimizes the output error is kept; dividing
+ *       the preceding op's output by c and multiplying the weights by c is
+ *       invisible before rounding, "scale_ln_fcs"): the migrated inputs are
+ *       X'(m, k) = fp16(x(m, k) / c[k]) and W'(k, n) = fp16(c[k] * w(k, n)),
+ *       each rounded once; W' is quantized by R13 and dequantized by R5; the
+ *       candidate's output is Y' = fp16(X' * deq(W')) (R6); the loss is the
+ *       mean over (m, n) of (y - y')^2 with y the exact X * W.  The search
+ *       keeps the first grid value of least loss.
  *
  * Everything is single threaded, unblocked and written for reading, not speed.
  */
@@ -255,7 +280,7 @@ int oracle_linear(const uint16_t *X, const int32_t *Q, const uint16_t *S,
 }
 
 /* ------------------------------------------------------------------------- */
-/* Fused gate/up epilogue (R8).                                               */
+/* Fused gate/up epilogue (R12).                                              */
 /* ------------------------------------------------------------------------- */
 
 double oracle_silu(double t)
@@ -275,7 +300,7 @@ void oracle_gate_up(const double *Y64, int M, int I, uint16_t *H16)
 }
 
 /* ------------------------------------------------------------------------- */
-/* Quantizer (R9).  float arithmetic is IEEE single precision here (SSE, no  */
+/* Quantizer (R13).  float arithmetic is IEEE single precision here (SSE, no */
 /* contraction), the same precision the GPU kernel decides in.               */
 /* ------------------------------------------------------------------------- */
 
@@ -317,4 +342,106 @@ void oracle_quantize(const uint16_t *W, int K, int N, int G, int symmetric,
             }
         }
     }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Scale migration and its search objective (R14, R15, R16).                  */
+/* ------------------------------------------------------------------------- */
+
+void oracle_channel_stats(const uint16_t *X, int M, const uint16_t *W, int K, int N, int G,
+                          double *xbar, double *wbar)
+{
+    for (int k = 0; k < K; ++k) {
+        double sum = 0.0;
+        for (int m = 0; m < M; ++m) sum += fabs(oracle_h2d(X[(size_t)m * K + k]));
+        xbar[k] = sum / M;
+    }
+    for (int k = 0; k < K; ++k) wbar[k] = 0.0;
+    for (int n = 0; n < N; ++n) {
+        for (int g = 0; g < K / G; ++g) {
+            double a = 0.0;
+            for (int k = g * G; k < (g + 1) * G; ++k) {
+                double v = fabs(oracle_h2d(W[(size_t)k * N + n]));
+                if (v > a) a = v;
+            }
+            if (a == 0.0) continue;
+            for (int k = g * G; k < (g + 1) * G; ++k)
+                wbar[k] += fabs(oracle_h2d(W[(size_t)k * N + n])) / a;
+        }
+    }
+    for (int k = 0; k < K; ++k) wbar[k] /= N;
+}
+
+void oracle_scale_candidate(const double *xbar, const double *wbar, int K, double alpha, double *c)
+{
+    for (int k = 0; k < K; ++k) {
+        double xa = xbar[k] > 1e-4 ? xbar[k] : 1e-4;
+        double wa = wbar[k] > 1e-4 ? wbar[k] : 1e-4;
+        c[k] = pow(xa, alpha) / pow(wa, 1.0 - alpha);
+    }
+}
+
+void oracle_migrate(const uint16_t *X, const uint16_t *W, int M, int K, int N, const double *c,
+                    uint16_t *Xs, uint16_t *Ws)
+{
+    for (int m = 0; m < M; ++m)
+        for (int k = 0; k < K; ++k)
+            Xs[(size_t)m * K + k] = oracle_d2h(oracle_h2d(X[(size_t)m * K + k]) / c[k]);
+    for (int k = 0; k < K; ++k)
+        for (int n = 0; n < N; ++n)
+            Ws[(size_t)k * N + n] = oracle_d2h(c[k] * oracle_h2d(W[(size_t)k * N + n]));
+}
+
+int oracle_scale_loss(const uint16_t *X, const uint16_t *W, int M, int K, int N, int G,
+                      int symmetric, const double *c, double *loss)
+{
+    size_t mk = (size_t)M * K, kn = (size_t)K * N, mn = (size_t)M * N;
+    uint16_t *Xs = malloc(mk * 2), *Ws = malloc(kn * 2), *Wq = malloc(kn * 2);
+    uint16_t *S = malloc((size_t)(K / G) * N * 2), *Yh16 = malloc(mn * 2), *Yr16 = malloc(mn * 2);
+    uint8_t *codes = malloc(kn), *zeros = malloc((size_t)(K / G) * N);
+    double *Yr = malloc(mn * 8), *Yh = malloc(mn * 8);
+    int ok = Xs && Ws && Wq && S && Yh16 && Yr16 && codes && zeros && Yr && Yh;
+    if (ok) {
+        oracle_migrate(X, W, M, K, N, c, Xs, Ws);
+        oracle_quantize(Ws, K, N, G, symmetric, codes, S, symmetric ? NULL : zeros);
+        for (int k = 0; k < K; ++k)
+            for (int n = 0; n < N; ++n) {
+                int z = symmetric ? 8 : zeros[(size_t)(k / G) * N + n];
+                Wq[(size_t)k * N + n] =
+                    oracle_dequant_one(codes[(size_t)k * N + n], z, S[(size_t)(k / G) * N + n]);
+            }
+        oracle_matmul_w(X, W, M, K, N, Yr, Yr16);
+        oracle_matmul_w(Xs, Wq, M, K, N, Yh, Yh16);
+        double sum = 0.0;
+        for (size_t i = 0; i < mn; ++i) {
+            double d = Yr[i] - oracle_h2d(Yh16[i]);
+            sum += d * d;
+        }
+        *loss = sum / (double)mn;
+    }
+    free(Xs); free(Ws); free(Wq); free(S); free(Yh16); free(Yr16);
+    free(codes); free(zeros); free(Yr); free(Yh);
+    return ok ? 0 : -1;
+}
+
+int oracle_scale_search(const uint16_t *X, int M, const uint16_t *W, int K, int N, int G,
+                        int symmetric, const double *alphas, int n_alpha, double *losses,
+                        double *c_best)
+{
+    double *xbar = malloc((size_t)K * 8), *wbar = malloc((size_t)K * 8), *c = malloc((size_t)K * 8);
+    int best = -1;
+    if (xbar && wbar && c) {
+        oracle_channel_stats(X, M, W, K, N, G, xbar, wbar);
+        for (int i = 0; i < n_alpha; ++i) {
+            oracle_scale_candidate(xbar, wbar, K, alphas[i], c);
+            if (oracle_scale_loss(X, W, M, K, N, G, symmetric, c, &losses[i]) != 0) {
+                best = -1;
+                break;
+            }
+            if (best < 0 || losses[i] < losses[best]) best = i;
+        }
+        if (best >= 0 && c_best) oracle_scale_candidate(xbar, wbar, K, alphas[best], c_best);
+    }
+    free(xbar); free(wbar); free(c);
+    return best;
 }

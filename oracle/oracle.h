@@ -15,6 +15,7 @@
  *   W      fp16  [K][N]       dequantized weight
  *   Y64    fp64  [M][N]       exact-order fp64 sum; Y16 its fp16 rounding
  *   H16    fp16  [M][N/2]     fused gate/up output, columns [gate | up] of Y
+ *   xbar, wbar, c  fp64 [K]   per-input-channel statistics and scales
  */
 #ifndef W4A16_ORACLE_H
 #define W4A16_ORACLE_H
@@ -52,6 +53,17 @@ void   oracle_quantize(const uint16_t *W, int K, int N, int G, int symmetric,
                        uint8_t *codes, uint16_t *S, uint8_t *zeros);
 double oracle_silu(double t);
 void   oracle_gate_up(const double *Y64, int M, int I, uint16_t *H16);
+
+void oracle_channel_stats(const uint16_t *X, int M, const uint16_t *W, int K, int N, int G,
+                          double *xbar, double *wbar);
+void oracle_scale_candidate(const double *xbar, const double *wbar, int K, double alpha, double *c);
+void oracle_migrate(const uint16_t *X, const uint16_t *W, int M, int K, int N, const double *c,
+                    uint16_t *Xs, uint16_t *Ws);
+int  oracle_scale_loss(const uint16_t *X, const uint16_t *W, int M, int K, int N, int G,
+                       int symmetric, const double *c, double *loss);
+int  oracle_scale_search(const uint16_t *X, int M, const uint16_t *W, int K, int N, int G,
+                         int symmetric, const double *alphas, int n_alpha, double *losses,
+                         double *c_best);
 
 #ifdef __cplusplus
 }

@@ -548,6 +548,94 @@ def pin_quantize_degenerate_groups(o):
         assert np.all(_np_h2d(S[:, 4]) == 1.0) and np.all(_np_h2d(S[:, 5]) == 1.0)
 
 
+# --- scale migration and its search (R14, R15, R16) -----------------------
+
+def pin_channel_stats_hand_worked(o):
+    """A 2 x 8 X and an 8 x 2 W with G = 4, worked by hand: xbar is the mean
+    |x| per channel; wbar the mean over columns of |w| over its group's max |w|
+    (an all-zero group contributes 0)."""
+    X = _np_d2h(np.array([[1, -2, 0.5, 4, -1, 0, 3, -0.25],
+                          [-3, 2, 0.5, -4, 1, 0, -1, 0.75]], dtype=np.float64))
+    W = _np_d2h(np.array([[1, -8], [-2, 8], [4, 2], [0, 1],
+                          [0, 0.5], [0, -0.5], [0, 0.25], [0, 1]], dtype=np.float64))
+    xbar, wbar = o.channel_stats(X, W, 4)
+    assert list(xbar) == [2, 2, 0.5, 4, 1, 0, 2, 0.5]
+    assert list(wbar) == [0.625, 0.75, 0.625, 0.0625, 0.25, 0.25, 0.125, 0.5]
+
+
+def pin_scale_candidate_closed_forms(o):
+    """alpha = 1 gives xbar, alpha = 0 gives 1 / wbar, alpha = 1/2 gives
+    sqrt(xbar / wbar); statistics below 1e-4 count as 1e-4."""
+    xbar = np.array([4.0, 0.25, 1e-6, 2.0])
+    wbar = np.array([0.5, 1.0, 0.5, 1e-8])
+    assert list(o.scale_candidate(xbar, wbar, 1.0)) == [4.0, 0.25, 1e-4, 2.0]
+    assert list(o.scale_candidate(xbar, wbar, 0.0)) == [2.0, 1.0, 2.0, 1e4]
+    half = o.scale_candidate(xbar, wbar, 0.5)
+    want = [math.sqrt(4.0 / 0.5), math.sqrt(0.25), math.sqrt(1e-4 / 0.5), math.sqrt(2.0 / 1e-4)]
+    assert all(abs(a - b) <= 1e-15 * b for a, b in zip(half, want)), (half, want)
+
+
+def _dyadic_x(rng, M, K):
+    """X = +-j / 8, j = 1..16: few significant bits, so products with grid
+    weights and their sums are exact in fp64 in any order."""
+    return _np_d2h(rng.integers(1, 17, (M, K)) / 8.0 * rng.choice([-1.0, 1.0], (M, K)))
+
+
+def pin_migration_invariance_exact(o):
+    """With c a power of two per channel and no value leaving the normal fp16
+    range, X / c and c W are exact, so (X / c)(c W) = X W bit for bit: the
+    migration is invisible before rounding."""
+    rng = np.random.default_rng(41)
+    M, K, N = 6, 64, 24
+    X = _np_d2h(rng.uniform(2.0 ** -4, 4.0, (M, K)) * rng.choice([-1.0, 1.0], (M, K)))
+    W = _np_d2h(rng.uniform(2.0 ** -8, 1.0, (K, N)) * rng.choice([-1.0, 1.0], (K, N)))
+    c = np.ldexp(1.0, rng.integers(-3, 4, K))
+    Xs, Ws = o.migrate(X, W, c)
+    assert np.array_equal(_np_h2d(Xs), _np_h2d(X) / c)
+    assert np.array_equal(_np_h2d(Ws), c[:, None] * _np_h2d(W))
+    Y, _ = o.matmul_w(X, W)
+    Ys, _ = o.matmul_w(Xs, Ws)
+    assert np.array_equal(Y, Ys)
+
+
+def pin_scale_loss_on_a_grid(o):
+    """A weight already on each group's grid, scaled by a power of two constant
+    within each group, stays on a grid that the quantizer recovers exactly; with
+    X / c exact too, the candidate's output is fp16(X W) and the loss is the
+    output rounding alone: mean((y - fp16(y))^2), with y computed in numpy."""
+    rng = np.random.default_rng(42)
+    M, K, N, G = 5, 256, 24, 64
+    for sym in (False, True):
+        W, _, _, _ = _grid_layer(rng, K, N, G, sym)
+        X = _dyadic_x(rng, M, K)
+        c = np.repeat(np.ldexp(1.0, rng.integers(-2, 3, K // G)), G)
+        y = _np_h2d(X) @ _np_h2d(W)
+        want = np.mean((y - _np_h2d(_np_d2h(y))) ** 2)
+        assert want > 0.0
+        assert o.scale_loss(X, W, G, sym, c) == want, sym
+        # the same layer with c varying inside the groups leaves the grid
+        c2 = np.ldexp(1.0, rng.integers(-2, 3, K))
+        assert o.scale_loss(X, W, G, sym, c2) > want, sym
+
+
+def pin_scale_search_first_minimum(o):
+    """|x| = 1 everywhere and |w| constant within each group and column give
+    xbar = wbar = 1, hence c = 1 for every alpha: all losses are equal, equal to
+    the loss at c = 1, and the search keeps the first grid value."""
+    rng = np.random.default_rng(43)
+    M, K, N, G = 4, 128, 16, 32
+    X = _np_d2h(rng.choice([-1.0, 1.0], (M, K)))
+    a = np.repeat(np.ldexp(1.0, rng.integers(-8, -2, (K // G, N))), G, axis=0)
+    W = _np_d2h(a * rng.choice([-1.0, 1.0], (K, N)))
+    xbar, wbar = o.channel_stats(X, W, G)
+    assert np.all(xbar == 1.0) and np.all(wbar == 1.0)
+    alphas = [0.0, 0.3, 0.5, 0.9, 1.0]
+    best, losses, cb = o.scale_search(X, W, G, False, alphas)
+    assert best == 0
+    assert np.all(losses == o.scale_loss(X, W, G, False, np.ones(K)))
+    assert np.all(cb == 1.0)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

@@ -53,6 +53,17 @@ MUTANTS = [
     ("gate_up_swapped", "oracle_silu(row[n]) * row[I + n]", "oracle_silu(row[I + n]) * row[n]", 0),
     ("gate_up_no_silu", "oracle_silu(row[n]) * row[I + n]", "row[n] * row[I + n]", 0),
     ("gate_up_row_stride", "const double *row = Y64 + (size_t)m * 2 * I;", "const double *row = Y64 + (size_t)m * I;", 0),
+    ("stats_x_no_abs", "sum += fabs(oracle_h2d(X[(size_t)m * K + k]));", "sum += oracle_h2d(X[(size_t)m * K + k]);", 0),
+    ("stats_w_not_normalized", "wbar[k] += fabs(oracle_h2d(W[(size_t)k * N + n])) / a;", "wbar[k] += fabs(oracle_h2d(W[(size_t)k * N + n]));", 0),
+    ("stats_w_mean_over_k", "for (int k = 0; k < K; ++k) wbar[k] /= N;", "for (int k = 0; k < K; ++k) wbar[k] /= K;", 0),
+    ("stats_w_group_off_by_one", "for (int k = g * G; k < (g + 1) * G; ++k) {\n                double v", "for (int k = g * G; k < (g + 1) * G - 1; ++k) {\n                double v", 0),
+    ("candidate_exponents_swapped", "c[k] = pow(xa, alpha) / pow(wa, 1.0 - alpha);", "c[k] = pow(xa, 1.0 - alpha) / pow(wa, alpha);", 0),
+    ("candidate_no_floor", "double xa = xbar[k] > 1e-4 ? xbar[k] : 1e-4;", "double xa = xbar[k];", 0),
+    ("migrate_x_times_c", "oracle_d2h(oracle_h2d(X[(size_t)m * K + k]) / c[k])", "oracle_d2h(oracle_h2d(X[(size_t)m * K + k]) * c[k])", 0),
+    ("migrate_w_divided", "oracle_d2h(c[k] * oracle_h2d(W[(size_t)k * N + n]))", "oracle_d2h(oracle_h2d(W[(size_t)k * N + n]) / c[k])", 0),
+    ("loss_unrounded_output", "double d = Yr[i] - oracle_h2d(Yh16[i]);", "double d = Yr[i] - Yh[i];", 0),
+    ("loss_reference_quantized", "oracle_matmul_w(X, W, M, K, N, Yr, Yr16);", "oracle_matmul_w(Xs, Wq, M, K, N, Yr, Yr16);", 0),
+    ("search_last_minimum", "if (best < 0 || losses[i] < losses[best]) best = i;", "if (best < 0 || losses[i] <= losses[best]) best = i;", 0),
 ]
 
 
