@@ -231,6 +231,37 @@ def bench_quantize(name, steps, warmup):
             "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_scale_search(name, M, n_alpha, reps):
+    """awq_scale_search on the workload's layer shape: M calibration rows (X ~ N(0, 1)
+    with the workload's outlier channels), an fp16 W ~ N(0, 0.02), an evenly spaced
+    grid of n_alpha values in [0, 1).  Each candidate quantizes the migrated weight,
+    runs the fused GEMM and reduces the error; the fp16 reference GEMM runs once."""
+    import torch
+    from w4a16_group_quantized_amd import binding, synth
+    w = synth.WORKLOADS[name]
+    x = to_dev(synth.make_x(M, w.K, w.wid, max(w.n_outliers, w.K // 100), 20.0))
+    rng = np.random.default_rng(w.wid)
+    W = torch.from_numpy((rng.standard_normal((w.K, w.N)) * 0.02).astype(np.float16)).cuda()
+    alphas = [i / n_alpha for i in range(n_alpha)]
+    lib = binding.load()
+    ws = torch.empty(lib.awq_scale_search_workspace_bytes(M, w.K, w.N, w.G), dtype=torch.uint8,
+                     device="cuda")
+    binding.scale_search(x, W, w.G, alphas, w.symmetric, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        best, _, _ = binding.scale_search(x, W, w.G, alphas, w.symmetric, workspace=ws)
+    e1.record()
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    flops = 2.0 * M * w.N * w.K * (n_alpha + 1)    # the candidates' GEMMs and the reference
+    return {"workload": name, "entry": "awq_scale_search", "M": M, "K": w.K, "N": w.N,
+            "group_size": w.G, "n_alpha": n_alpha, "ms_per_search": t * 1e3,
+            "us_per_candidate": t * 1e6 / n_alpha, "gemm_tflops": flops / t / 1e12,
+            "best_alpha": alphas[int(best.item())]}
+
+
 def torch_matmul_context(name, steps):
     """Not the metric: torch.matmul (the vendor fp16 GEMM) on the dequantized
     weight of the same shape, for context on what a plain fp16 GEMM reaches."""
@@ -557,6 +588,7 @@ def main():
         extra.append(bench_gate_up("gate_up_m16", 1, args.steps, args.warmup))
         extra.append(bench_gemm_gate_up("gate_up_m16", 2048, 20, 3))
         extra.append(bench_quantize("decode_8b_gate", 20, 3))
+        extra.append(bench_scale_search("decode_8b_gate", 4096, 20, 3))
         extra.append(torch_matmul_context("prefill_out_proj", 50))
         extra.append(torch_matmul_context("sym70b_m4096", 5))
 

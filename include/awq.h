@@ -59,7 +59,8 @@ typedef enum awq_status {
     AWQ_ERROR_SHAPE = 2,         /* a shape rule above is broken               */
     AWQ_ERROR_ALIGNMENT = 3,     /* a tensor pointer is not 16-byte aligned    */
     AWQ_ERROR_UNSUPPORTED = 4,   /* valid layer, but outside this entry point (gemv: M > 16) */
-    AWQ_ERROR_HIP = 5            /* the HIP runtime refused the launch          */
+    AWQ_ERROR_HIP = 5,           /* the HIP runtime refused the launch          */
+    AWQ_ERROR_WORKSPACE = 6      /* workspace NULL, unaligned or too small      */
 } awq_status;
 
 /* Non-owning view of one quantized linear layer (logical weight W[K][N]). */
@@ -174,6 +175,55 @@ awq_status awq_gemv_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
  */
 awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t *h, int32_t M,
                             void *stream);
+
+/*
+ * The scale search of AWQ's calibration (pyshine.com AutoAWQ tour, "The
+ * Quantization Flow Up Close": per-channel means of normalized weights and of
+ * activations, the FP16 module run once as the reference, the candidate
+ * scaling of least output error; scale_ln_fcs: dividing the preceding op's
+ * output by c and multiplying the weights by c leaves the layer unchanged
+ * before rounding).  The pages give no formula for the statistics, the
+ * candidates or the grid; the readings taken are:
+ *   xbar[k] = mean over calibration rows of |x(m, k)|;
+ *   wbar[k] = mean over output columns n of |w(k, n)| / a(g, n), with a(g, n)
+ *             the largest |w| of k's quantization group in column n (an
+ *             all-zero group adds 0);
+ *   c[k]    = max(xbar[k], 1e-4)^alpha / max(wbar[k], 1e-4)^(1 - alpha);
+ *   loss(alpha) = mean over (m, n) of (y - y')^2, with y = x W in fp32 and
+ *             y' the awq_gemm output for fp16(x / c) and the layer that
+ *             awq_quantize makes of fp16(c W); the first alpha of least loss
+ *             is kept.
+ *
+ * Inputs: x device fp16 [M][K] calibration activations (M >= 1), w device fp16
+ * [K][N] the layer's unquantized weight, both 16-byte aligned; the layer's
+ * shape rules apply, and M*K, K*N and M*N must be below 2^31.
+ * Workspace: device memory of at least the *_workspace_bytes query for the
+ * same sizes, 16-byte aligned, owned by the caller; its contents on return are
+ * unspecified.  AWQ_ERROR_WORKSPACE if it is NULL, unaligned or too small.
+ * Both calls enqueue on `stream` and return without waiting.  Results are
+ * deterministic: every reduction runs in a fixed order.
+ */
+size_t awq_channel_stats_workspace_bytes(int32_t M, int32_t K, int32_t N, int32_t group_size);
+
+/* xbar, wbar: device fp32 [K] outputs (4-byte aligned). */
+awq_status awq_channel_stats(const uint16_t *x, int32_t M, const uint16_t *w, int32_t K, int32_t N,
+                             int32_t group_size, float *xbar, float *wbar, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+size_t awq_scale_search_workspace_bytes(int32_t M, int32_t K, int32_t N, int32_t group_size);
+
+/*
+ * alphas: HOST array of n_alpha grid values in [0, 1], 1 <= n_alpha <= 64
+ * (AWQ_ERROR_INVALID_VALUE otherwise, NaN included); read before the call
+ * returns.  losses: device fp64 [n_alpha]; best: device int32, the index of the
+ * first least loss; best_scales: device fp32 [K], the scales c of that alpha,
+ * or NULL.  symmetric != 0 quantizes the migrated weight with the symmetric
+ * zero 8.
+ */
+awq_status awq_scale_search(const uint16_t *x, int32_t M, const uint16_t *w, int32_t K, int32_t N,
+                            int32_t group_size, int32_t symmetric, const float *alphas,
+                            int32_t n_alpha, double *losses, int32_t *best, float *best_scales,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

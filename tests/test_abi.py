@@ -144,3 +144,41 @@ def test_dequant_validation(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         binding.load(str(tmp_path / "libawq.so"))
+
+
+def test_scale_workspace_queries(lib):
+    for fn in (lib.awq_channel_stats_workspace_bytes, lib.awq_scale_search_workspace_bytes):
+        assert fn(64, 256, 128, 64) > 0
+        assert fn(0, 256, 128, 64) == 0 and fn(64, 256, 128, 48) == 0
+    # the search holds at least the migrated X and W, the reference and the output
+    need = 64 * 256 * 2 + 256 * 128 * 2 + 64 * 128 * 4 + 64 * 128 * 2
+    assert lib.awq_scale_search_workspace_bytes(64, 256, 128, 64) >= need
+
+
+def test_channel_stats_validation(lib):
+    ws = lib.awq_channel_stats_workspace_bytes(64, 256, 128, 64)
+
+    def call(x=FAKE, M=64, w=FAKE, K=256, N=128, G=64, xb=FAKE, wb=FAKE, wsp=FAKE, nb=ws):
+        return lib.awq_channel_stats(x, M, w, K, N, G, xb, wb, wsp, nb, None)
+    assert call(x=None) == 1 and call(M=0) == 1 and call(xb=None) == 1 and call(G=0) == 1
+    assert call(K=260) == 2 and call(N=100) == 2 and call(G=48) == 2
+    assert call(x=MISALIGNED) == 3 and call(w=MISALIGNED) == 3
+    assert call(wsp=None) == 6 and call(wsp=MISALIGNED) == 6 and call(nb=ws - 1) == 6
+
+
+def test_scale_search_validation(lib):
+    ws = lib.awq_scale_search_workspace_bytes(64, 256, 128, 64)
+    good = (ctypes.c_float * 3)(0.0, 0.5, 1.0)
+
+    def call(x=FAKE, M=64, K=256, N=128, G=64, alphas=good, n=3, losses=FAKE, best=FAKE,
+             wsp=FAKE, nb=ws):
+        return lib.awq_scale_search(x, M, FAKE, K, N, G, 0, alphas, n, losses, best, None, wsp, nb,
+                                    None)
+    assert call(x=None) == 1 and call(M=-1) == 1 and call(losses=None) == 1 and call(best=None) == 1
+    assert call(alphas=None) == 1 and call(n=0) == 1 and call(n=65) == 1
+    for bad in (-0.1, 1.5, float("nan")):
+        assert call(alphas=(ctypes.c_float * 1)(bad), n=1) == 1, bad
+    assert call(K=260) == 2 and call(G=48) == 2
+    assert call(M=1 << 20, K=4096) == 2          # M * K beyond 2^31
+    assert call(x=MISALIGNED) == 3
+    assert call(wsp=None) == 6 and call(nb=ws - 1) == 6

@@ -21,11 +21,15 @@ LIBRARY = os.path.join(HERE, "libawq.so")
 
 # Entry points declared in include/awq.h, in declaration order.
 ENTRY_POINTS = ("awq_status_string", "awq_pack", "awq_pack_zeros", "awq_dequant", "awq_gemv",
-                "awq_gemm", "awq_gemv_gate_up", "awq_quantize", "awq_gemm_gate_up")
+                "awq_gemm", "awq_gemv_gate_up", "awq_quantize", "awq_gemm_gate_up",
+                "awq_channel_stats_workspace_bytes", "awq_channel_stats",
+                "awq_scale_search_workspace_bytes", "awq_scale_search")
 
 AWQ_SUCCESS = 0
 STATUS_NAMES = {0: "AWQ_SUCCESS", 1: "AWQ_ERROR_INVALID_VALUE", 2: "AWQ_ERROR_SHAPE",
-                3: "AWQ_ERROR_ALIGNMENT", 4: "AWQ_ERROR_UNSUPPORTED", 5: "AWQ_ERROR_HIP"}
+                3: "AWQ_ERROR_ALIGNMENT", 4: "AWQ_ERROR_UNSUPPORTED", 5: "AWQ_ERROR_HIP",
+                6: "AWQ_ERROR_WORKSPACE"}
+SCALE_SEARCH_MAX_ALPHAS = 64
 
 
 class AwqError(RuntimeError):
@@ -69,6 +73,15 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.POINTER(CLayer), vp, i32, vp]
+    for name in ("awq_channel_stats_workspace_bytes", "awq_scale_search_workspace_bytes"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_size_t
+        fn.argtypes = [i32, i32, i32, i32]
+    lib.awq_channel_stats.restype = ctypes.c_int
+    lib.awq_channel_stats.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.awq_scale_search.restype = ctypes.c_int
+    lib.awq_scale_search.argtypes = [vp, i32, vp, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_float),
+                                     i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     if path == LIBRARY:
         _LIB = lib
     return lib
@@ -202,3 +215,48 @@ def gemv_gate_up(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None,
     """h = SiLU(y[:, :N/2]) * y[:, N/2:] with y = x @ dequant(layer), 1 <= M <= 16; the
     layer's columns are the concatenation [gate | up]."""
     return _linear("awq_gemv_gate_up", x, layer, out, stream, width=layer.N // 2)
+
+
+def _calibration(x: torch.Tensor, w: torch.Tensor):
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[0]:
+        raise ValueError(f"x [M][K] and w [K][N] do not fit: {tuple(x.shape)}, {tuple(w.shape)}")
+    return x.shape[0], w.shape[0], w.shape[1]
+
+
+def channel_stats(x: torch.Tensor, w: torch.Tensor, group_size: int, stream=None):
+    """(xbar, wbar) fp32 [K]: mean |x| per input channel over the calibration rows,
+    and the mean over output columns of |w| over its group's largest |w|."""
+    M, K, N = _calibration(x, w)
+    lib = load()
+    xbar = torch.empty(K, dtype=torch.float32, device=x.device)
+    wbar = torch.empty(K, dtype=torch.float32, device=x.device)
+    nbytes = lib.awq_channel_stats_workspace_bytes(M, K, N, group_size)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check(lib.awq_channel_stats(_dev(x, torch.float16, "x"), M, _dev(w, torch.float16, "w"), K, N,
+                                 group_size, xbar.data_ptr(), wbar.data_ptr(), ws.data_ptr(),
+                                 ws.numel(), _stream(stream)))
+    return xbar, wbar
+
+
+def scale_search(x: torch.Tensor, w: torch.Tensor, group_size: int, alphas, symmetric: bool = False,
+                 stream=None, workspace: torch.Tensor | None = None):
+    """AWQ's scale search over the grid ``alphas``: (best index as a device int32
+    tensor, losses fp64 [n_alpha], scales fp32 [K] of the best alpha).  The
+    workspace is allocated here unless one of at least
+    awq_scale_search_workspace_bytes is given."""
+    M, K, N = _calibration(x, w)
+    lib = load()
+    a = (ctypes.c_float * len(alphas))(*[float(v) for v in alphas])
+    losses = torch.empty(len(alphas), dtype=torch.float64, device=x.device)
+    best = torch.empty(1, dtype=torch.int32, device=x.device)
+    scales = torch.empty(K, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        nbytes = lib.awq_scale_search_workspace_bytes(M, K, N, group_size)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check(lib.awq_scale_search(_dev(x, torch.float16, "x"), M, _dev(w, torch.float16, "w"), K, N,
+                                group_size, int(symmetric), a, len(alphas), losses.data_ptr(),
+                                best.data_ptr(), scales.data_ptr(),
+                                _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                _stream(stream)))
+    return best, losses, scales
+

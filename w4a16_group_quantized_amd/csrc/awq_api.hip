@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <math.h>
+
 #include "awq_internal.h"
 
 namespace {
@@ -39,6 +41,18 @@ awq_status from_hip(hipError_t e) { return e == hipSuccess ? AWQ_SUCCESS : AWQ_E
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Calibration X [M][K] and fp16 weight W [K][N] of the scale search.
+awq_status check_calibration(const uint16_t *x, int32_t M, const uint16_t *w, int32_t K, int32_t N,
+                             int32_t G) {
+    if (x == nullptr || w == nullptr || M <= 0 || K <= 0 || N <= 0 || G <= 0)
+        return AWQ_ERROR_INVALID_VALUE;
+    if (K % 8 || N % 8 || G % 8 || K % G) return AWQ_ERROR_SHAPE;
+    if ((long long)M * K > kMaxElems || (long long)K * N > kMaxElems || (long long)M * N > kMaxElems)
+        return AWQ_ERROR_SHAPE;
+    if (!aligned16(x) || !aligned16(w)) return AWQ_ERROR_ALIGNMENT;
+    return AWQ_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -51,6 +65,7 @@ const char *awq_status_string(awq_status status) {
     case AWQ_ERROR_ALIGNMENT: return "AWQ_ERROR_ALIGNMENT: tensor pointers must be 16-byte aligned";
     case AWQ_ERROR_UNSUPPORTED: return "AWQ_ERROR_UNSUPPORTED: outside this entry point (awq_gemv takes M <= 16; awq_gemv_gate_up also needs G % 128 == 0 and X in LDS; awq_gemm_gate_up needs G % 64 == 0 and K % 256 == 0)";
     case AWQ_ERROR_HIP: return "AWQ_ERROR_HIP: the HIP runtime refused the launch";
+    case AWQ_ERROR_WORKSPACE: return "AWQ_ERROR_WORKSPACE: null, unaligned or smaller than the *_workspace_bytes query";
     }
     return "AWQ_ERROR_UNKNOWN";
 }
@@ -141,6 +156,48 @@ awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
         return AWQ_ERROR_UNSUPPORTED;
     return from_hip(awq::launch_gemm_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
                                              layer->K, layer->N, layer->group_size,
+                                             as_stream(stream)));
+}
+
+size_t awq_channel_stats_workspace_bytes(int32_t M, int32_t K, int32_t N, int32_t group_size) {
+    if (M <= 0 || K <= 0 || N <= 0 || group_size <= 0 || K % group_size) return 0;
+    return awq::channel_stats_workspace(M, K, N, group_size);
+}
+
+size_t awq_scale_search_workspace_bytes(int32_t M, int32_t K, int32_t N, int32_t group_size) {
+    if (M <= 0 || K <= 0 || N <= 0 || group_size <= 0 || K % group_size) return 0;
+    return awq::scale_search_workspace(M, K, N, group_size);
+}
+
+awq_status awq_channel_stats(const uint16_t *x, int32_t M, const uint16_t *w, int32_t K, int32_t N,
+                             int32_t group_size, float *xbar, float *wbar, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    awq_status st = check_calibration(x, M, w, K, N, group_size);
+    if (st != AWQ_SUCCESS) return st;
+    if (xbar == nullptr || wbar == nullptr) return AWQ_ERROR_INVALID_VALUE;
+    if (workspace == nullptr || !aligned16(workspace) ||
+        workspace_bytes < awq::channel_stats_workspace(M, K, N, group_size))
+        return AWQ_ERROR_WORKSPACE;
+    return from_hip(awq::launch_channel_stats(x, M, w, K, N, group_size, xbar, wbar, workspace,
+                                              as_stream(stream)));
+}
+
+awq_status awq_scale_search(const uint16_t *x, int32_t M, const uint16_t *w, int32_t K, int32_t N,
+                            int32_t group_size, int32_t symmetric, const float *alphas,
+                            int32_t n_alpha, double *losses, int32_t *best, float *best_scales,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    awq_status st = check_calibration(x, M, w, K, N, group_size);
+    if (st != AWQ_SUCCESS) return st;
+    if (alphas == nullptr || losses == nullptr || best == nullptr || n_alpha < 1 ||
+        n_alpha > awq::kScaleSearchMaxAlphas)
+        return AWQ_ERROR_INVALID_VALUE;
+    for (int i = 0; i < n_alpha; ++i)
+        if (!(alphas[i] >= 0.0f && alphas[i] <= 1.0f)) return AWQ_ERROR_INVALID_VALUE;   // also NaN
+    if (workspace == nullptr || !aligned16(workspace) ||
+        workspace_bytes < awq::scale_search_workspace(M, K, N, group_size))
+        return AWQ_ERROR_WORKSPACE;
+    return from_hip(awq::launch_scale_search(x, M, w, K, N, group_size, symmetric != 0, alphas,
+                                             n_alpha, losses, best, best_scales, workspace,
                                              as_stream(stream)));
 }
 

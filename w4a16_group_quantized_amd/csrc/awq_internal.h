@@ -29,5 +29,15 @@ hipError_t launch_gemm_gate_up(const uint16_t *x, const int32_t *qweight, const 
 hipError_t launch_gemm(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
                        hipStream_t s);
+// Scale search (per-channel statistics, candidates, migrated layer, loss).
+constexpr int kScaleSearchMaxAlphas = 64;
+size_t channel_stats_workspace(int M, int K, int N, int G);
+size_t scale_search_workspace(int M, int K, int N, int G);
+hipError_t launch_channel_stats(const uint16_t *x, int M, const uint16_t *w, int K, int N, int G,
+                                float *xbar, float *wbar, void *workspace, hipStream_t s);
+// alphas: host array of n_alpha values (read during the call).
+hipError_t launch_scale_search(const uint16_t *x, int M, const uint16_t *w, int K, int N, int G,
+                               bool symmetric, const float *alphas, int n_alpha, double *losses,
+                               int32_t *best, float *best_scales, void *workspace, hipStream_t s);
 
 }  // namespace awq
