@@ -25,7 +25,7 @@
 namespace awq {
 namespace scale {
 
-constexpr int kStatRows = 64;       // calibration rows per partial-sum chunk of xbar
+constexpr int kStatRows = 64;       // calibration rows per partial-sum chunk of xbar, at least
 constexpr int kStatCols = 512;      // columns per xbar block (64 lanes x 8)
 constexpr int kLossBlocks = 1024;   // blocks of the squared-error reduction
 constexpr float kFloor = 1e-4f;
@@ -59,13 +59,18 @@ __device__ __forceinline__ double block_sum(double v, double *sh) {
     return sh[0];
 }
 
+// Rows per xbar chunk: kStatRows, or more when M would need more than 65535
+// chunks (the grid's y limit).
+inline int stat_rows(int M) { return max(kStatRows, (M + 65534) / 65535); }
+
 // xbar, pass 1: partial[chunk][k] = sum of |x(m, k)| over the chunk's rows.
-// Block (column block b, chunk r): 64 lanes x 8 columns, kStatRows rows.
+// Block (column block b, chunk r): 64 lanes x 8 columns, `rows` rows.
 __global__ void __launch_bounds__(64)
-act_partial_kernel(const uint16_t *__restrict__ X, int M, int K, double *__restrict__ partial) {
+act_partial_kernel(const uint16_t *__restrict__ X, int M, int K, int rows,
+                   double *__restrict__ partial) {
     const int k0 = blockIdx.x * kStatCols + 8 * threadIdx.x;
     if (k0 >= K) return;
-    const int r0 = blockIdx.y * kStatRows, r1 = min(M, r0 + kStatRows);
+    const int r0 = blockIdx.y * rows, r1 = min(M, r0 + rows);
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int m = r0; m < r1; ++m) {
         float f[8];
@@ -169,7 +174,7 @@ __global__ void migrate_w_kernel(const uint16_t *__restrict__ W, const float *__
 }
 
 // The fp16 layer's output y = X W in fp32, for the reference: a plain 64 x 64
-// tile per workgroup, 32-k steps staged in LDS (W transposed to [n][k] so that
+// tile per workgroup (a 1-D grid, tile rows minor), 32-k steps staged in LDS (W transposed to [n][k] so that
 // a lane's B operand, 8 k of one column, is one 16-byte read), four waves of
 // one 32 x 32 v_mfma_f32_32x32x16_f16 tile each.  Rows past M, columns past N
 // and k past K load zeros and are not stored.
@@ -181,7 +186,8 @@ dense_gemm_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W
     __shared__ __attribute__((aligned(16))) uint16_t As[kDT][kDPad];
     __shared__ __attribute__((aligned(16))) uint16_t Bt[kDT][kDPad];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int m0 = blockIdx.y * kDT, n0 = blockIdx.x * kDT;
+    const int tiles_m = (M + kDT - 1) / kDT;
+    const int m0 = (int)(blockIdx.x % tiles_m) * kDT, n0 = (int)(blockIdx.x / tiles_m) * kDT;
     const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);
     const int ar = t >> 2, akc = (t & 3) * 8;   // X chunk: row, k offset
     const int bk = t >> 3, bnc = (t & 7) * 8;   // W chunk: k row, column offset
@@ -284,7 +290,7 @@ Layout layout(int M, int K, int N, int G, bool search) {
         off += up256(bytes);
         return o;
     };
-    const size_t chunks = (size_t)(M + kStatRows - 1) / kStatRows;
+    const size_t chunks = (size_t)(M + stat_rows(M) - 1) / stat_rows(M);
     L.act = take(chunks * K * sizeof(double));
     L.amax = take((size_t)(K / G) * N * sizeof(float));
     if (search) {
@@ -313,9 +319,9 @@ hipError_t stats(const uint16_t *x, int M, const uint16_t *w, int K, int N, int 
                  float *wbar, char *ws, const Layout &L, hipStream_t s) {
     auto *act = reinterpret_cast<double *>(ws + L.act);
     auto *amax = reinterpret_cast<float *>(ws + L.amax);
-    const int chunks = (M + kStatRows - 1) / kStatRows;
+    const int rows = stat_rows(M), chunks = (M + rows - 1) / rows;
     hipLaunchKernelGGL(act_partial_kernel, dim3((K + kStatCols - 1) / kStatCols, chunks), dim3(64), 0,
-                       s, x, M, K, act);
+                       s, x, M, K, rows, act);
     hipLaunchKernelGGL(act_final_kernel, dim3(grid_for(K, 256)), dim3(256), 0, s, act, chunks, M, K,
                        xbar);
     hipLaunchKernelGGL(group_absmax_kernel, dim3(grid_for((long long)(K / G) * (N / 8), 256)),
@@ -361,8 +367,8 @@ hipError_t launch_scale_search(const uint16_t *x, int M, const uint16_t *w, int 
 
     hipError_t e = stats(x, M, w, K, N, G, xbar, wbar, ws, L, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dense_gemm_kernel, dim3((N + kDT - 1) / kDT, (M + kDT - 1) / kDT), dim3(256), 0,
-                       s, x, w, M, K, N, yref);
+    const long long dtiles = (long long)((M + kDT - 1) / kDT) * ((N + kDT - 1) / kDT);
+    hipLaunchKernelGGL(dense_gemm_kernel, dim3((unsigned)dtiles), dim3(256), 0, s, x, w, M, K, N, yref);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     for (int i = 0; i < n_alpha; ++i) {
         hipLaunchKernelGGL(candidate_kernel, dim3(grid_for(K, 256)), dim3(256), 0, s, xbar, wbar, K,
