@@ -10,7 +10,10 @@ reduces and writes Y.  The weight is replicated into enough copies (>= 1 GiB)
 that successive steps read different copies, so every step streams from HBM
 rather than from the 256 MB last-level cache.  Inputs are resident in HBM before
 the timed region.  The K timed steps are launched as one captured HIP graph on
-one stream and bracketed by events on that stream.
+one stream and bracketed by events on that stream, with the device synchronized
+before and after; that replay gives the value.  Four more replays of the same
+graph give the median, minimum and maximum time per call ("timing"), beside the
+same calls on a single cache-resident copy ("hot_cache_us"), as context.
 
 Prints one JSON line: value = algorithmic bytes per step / time per step, in
 GB/s.  Also reported: the roofline of the dominant kernel (awq_gemv), the
@@ -119,9 +122,12 @@ def build_layers(w, copies):
     return layers
 
 
-def time_calls(fn_name, x, layers, y, steps, warmup):
+def time_calls(fn_name, x, layers, y, steps, warmup, reps=1):
     """Launches ``steps`` calls, cycling through ``layers``, as one HIP graph on
-    one stream; returns seconds per call measured with events on that stream."""
+    one stream; returns seconds per call of the first timed replay, measured
+    with events on that stream between device synchronizations.  With reps > 1
+    the graph is replayed reps times in all and (first, median, min, max) is
+    returned."""
     import torch
     from w4a16_group_quantized_amd import binding
 
@@ -142,16 +148,24 @@ def time_calls(fn_name, x, layers, y, steps, warmup):
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        graph.replay()
-        end.record(stream)
-    end.synchronize()
+    times = []
+    for _ in range(reps):
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            graph.replay()
+            end.record(stream)
+        end.synchronize()
+        times.append(start.elapsed_time(end) * 1e-3 / steps)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e-3 / steps
+    if reps == 1:
+        return times[0]
+    return times[0], statistics.median(times), min(times), max(times)
 
 
-def bench_gemv(name, steps, warmup):
+def bench_gemv(name, steps, warmup, reps=1, hot=False):
+    """awq_gemv on the workload, cycling through enough weight copies that every
+    call reads HBM; ``reps`` replays give the median (and min, max); ``hot``
+    adds the same calls on one copy (cache-resident), as context."""
     import torch
     from w4a16_group_quantized_amd import synth
     w = synth.WORKLOADS[name]
@@ -160,14 +174,22 @@ def bench_gemv(name, steps, warmup):
     layers = build_layers(w, copies)
     X = to_dev(synth.make_x(w.M, w.K, w.wid, w.n_outliers, w.outlier_gain))
     y = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
-    t = time_calls("gemv", X, layers, y, steps, warmup)
+    r = time_calls("gemv", X, layers, y, steps, warmup, reps)
+    t, t_med, t_min, t_max = r if reps > 1 else (r, r, r, r)
+    t_hot = time_calls("gemv", X, layers[:1], y, steps, warmup) if hot else None
     b = alg_bytes(w, w.M)
     del layers
     torch.cuda.empty_cache()
-    return {"workload": name, "M": w.M, "K": w.K, "N": w.N, "group_size": w.G,
-            "symmetric": w.symmetric, "entry": "awq_gemv", "weight_copies": copies,
-            "us_per_call": t * 1e6, "alg_bytes": b, "gbs": b / t / 1e9,
-            "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS}
+    out = {"workload": name, "M": w.M, "K": w.K, "N": w.N, "group_size": w.G,
+           "symmetric": w.symmetric, "entry": "awq_gemv", "weight_copies": copies,
+           "us_per_call": t * 1e6, "alg_bytes": b, "gbs": b / t / 1e9,
+           "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS}
+    if reps > 1:
+        out["reps"] = {"n": reps, "calls_each": steps, "median_us": t_med * 1e6,
+                       "min_us": t_min * 1e6, "max_us": t_max * 1e6}
+    if hot:
+        out["hot_cache_us"] = t_hot * 1e6
+    return out
 
 
 def bench_gate_up(name, M, steps, warmup):
@@ -576,7 +598,7 @@ def main():
     from w4a16_group_quantized_amd import binding
     binding.load()
 
-    head = bench_gemv("decode_8b_gate", args.steps, args.warmup)
+    head = bench_gemv("decode_8b_gate", args.steps, args.warmup, reps=5, hot=True)
     gemm = bench_gemm("prefill_out_proj", args.steps, args.warmup)
     extra = []
     if args.all:
@@ -611,6 +633,11 @@ def main():
                    "launch": "hip_graph"},
         "roofline": {"bound": "hbm", "achieved": round(head["gbs"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(head["hbm_frac"], 4), "traffic": traffic},
+        "timing": {"replays": head["reps"]["n"], "calls_each": head["reps"]["calls_each"],
+                   "median_us": round(head["reps"]["median_us"], 3),
+                   "min_us": round(head["reps"]["min_us"], 3),
+                   "max_us": round(head["reps"]["max_us"], 3),
+                   "hot_cache_us": round(head["hot_cache_us"], 3)},
         "gemm": {"workload": gemm["workload"], "M": gemm["M"], "K": gemm["K"], "N": gemm["N"],
                  "tflops": round(gemm["tflops"], 1), "peak": MFMA_F16_PEAK_TFLOPS,
                  "frac": round(gemm["mfma_frac"], 4), "us_per_call": round(gemm["us_per_call"], 2)},
