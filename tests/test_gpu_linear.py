@@ -176,3 +176,17 @@ def test_misaligned_pointer_is_rejected():
     with pytest.raises(binding.AwqError) as e:
         binding.gemv(x, layer)
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("M,K,N,G,sym", [
+    (37, 768, 200, 768, False), (130, 256, 72, 256, False), (64, 2048, 136, 2048, True),
+    (1, 1024, 264, 1024, False),
+])
+def test_gemm_one_group(M, K, N, G, sym):
+    """One group per column (G == K): scales and zero points are loaded once per
+    lane, past the last column included (ragged N)."""
+    X, codes, zeros, scales = random_case(9000 + M + K, M, K, N, G, sym)
+    _, Y16 = oracle_case(X, codes, zeros, scales, G)
+    y = to_host_bits(binding.gemm(to_dev(X), device_case(codes, zeros, scales, G)))
+    torch.cuda.synchronize()
+    assert_y_close(y, Y16, f"gemm one group M={M} K={K} N={N} sym={sym}")

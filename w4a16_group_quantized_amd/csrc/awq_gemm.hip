@@ -330,21 +330,25 @@ __device__ __forceinline__ void unpack_natural(uint32_t w, uint32_t exps, uint32
                0xFFF0FF0Fu;
 }
 
-// GSHIFT: the group of step kt is kt >> gshift (G / 64 a power of two, or
-// gshift = 31 when G == K: one group); otherwise kt / (G / 64).
+// GMODE, how step kt finds its group: 1, kt >> gshift (G / BK a power of
+// two); 0, kt / (G / BK); 2, one group (G == K): each lane then loads its scale
+// pair and zero word once, into registers, before the loop, and the steps load
+// and decode only packed words.
 // GU (fused gate/up): the layer's N = 2I columns are [gate | up].  A wave's 64
 // MFMA columns are then 32 gate columns and the same 32 columns of the up half
 // (column tile 0: gate, tile 1: up, for the same output column), and the
 // output is h[M][I] = fp16(SiLU(gate) * up), 32 columns per wave.
-template <int KB, int MT, bool SYM, bool GSHIFT, bool GU>
+template <int KB, int MT, bool SYM, int GMODE, bool GU>
 __global__ void __launch_bounds__(256)
 mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
               uint16_t *__restrict__ Y, int M, int K, int N, int G, int gshift) {
+    constexpr bool ONEG = GMODE == 2;
+    static_assert(!(ONEG && GU), "one-group mode is for the plain layer");
     using Gm = Geom<KB, MT>;
     constexpr int kBM = Gm::BM, kMT = MT, kACH = Gm::ACH, kWave = Gm::WAVE;
     constexpr int kScale = Gm::SCALE, kZero = Gm::ZERO, kBKs = Gm::BK, kXCH = Gm::XCH;
-    constexpr int BLOADS = Gm::QD + (SYM ? 1 : 2);   // per step: packed rows, scales, zeros
+    constexpr int BLOADS = Gm::QD + (ONEG ? 0 : (SYM ? 1 : 2));   // per step: packed rows, scales, zeros
     constexpr int LOADS = kACH + BLOADS;
     __shared__ __attribute__((aligned(16))) uint4 ring0[kBM * kXCH];
     __shared__ __attribute__((aligned(16))) uint4 ring1[kBM * kXCH];
@@ -401,9 +405,11 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         const int qo = kt * qstep;
 #pragma unroll
         for (int d = 0; d < Gm::QD; ++d) buffer_to_lds16(qrs, dst + 64 * d, qvoff, qo + d * qhalf);
-        const int g = GSHIFT ? (kt >> gshift) : kt / gsteps;
-        buffer_to_lds4(srs, dst + kScale, svoff, g * srow);
-        if constexpr (!SYM) buffer_to_lds4(zrs, dst + kZero, zvoff, g * zrow);
+        if constexpr (!ONEG) {
+            const int g = GMODE == 1 ? (kt >> gshift) : kt / gsteps;
+            buffer_to_lds4(srs, dst + kScale, svoff, g * srow);
+            if constexpr (!SYM) buffer_to_lds4(zrs, dst + kZero, zvoff, g * zrow);
+        }
 #pragma unroll
         for (int i = 0; i < kACH; ++i)
             buffer_to_lds16(xrs, xbuf + (i * 4 + wave) * 64, xvoff[i], kt * kBKs * 2);
@@ -438,8 +444,13 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
                 r.q[kb] = *reinterpret_cast<const uint2 *>(w + 64 * (2 * kb + h) + 2 * j);
-            r.sc = w[4 * kScale + j];
-            r.zw = SYM ? 0x88888888u : w[4 * kZero + (j >> 2)];
+            if constexpr (ONEG) {
+                r.sc = 0u;        // unused: the hoisted scales serve every step
+                r.zw = 0u;
+            } else {
+                r.sc = w[4 * kScale + j];
+                r.zw = SYM ? 0x88888888u : w[4 * kZero + (j >> 2)];
+            }
         }
         return r;
     };
@@ -507,11 +518,22 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     constexpr int VG = KB == 2 ? 2 : 4;   // dequantization VALU per MFMA (about)
     half8_t a0[kMT], a1[kMT];
     Raw r;
+    // One group: the lane's scale pair (columns n0 + 2 j, +1) and zero word,
+    // loaded once; buffer loads past the end (columns at or past N) give 0.
+    Dq dq_one{};
+    if constexpr (ONEG) {
+        Raw hr{};
+        hr.sc = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, svoff, 0, 0);
+        hr.zw = SYM ? 0x88888888u
+                    : (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                          zrs, (uint32_t)((n0 >> 3) + (j >> 2)) * 4u, 0, 0);
+        dq_one = decode(hr);
+    }
     auto step = [&](int kt, const uint4 *xcur, half8_t (&b_cur)[KB][2], half8_t (&b_nxt)[KB][2],
                     const uint4 *xnxt, const uint4 *bnn, uint4 *xload, uint4 *bload) {
         __builtin_amdgcn_sched_barrier(0);
         const Raw rc = r;
-        const Dq dq = decode(rc);
+        const Dq dq = ONEG ? dq_one : decode(rc);
         read_a(xcur, 1, a1);
 #pragma unroll
         for (int kb = 0; kb < KB - 1; ++kb) {
@@ -558,7 +580,7 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     __builtin_amdgcn_sched_barrier(0);
     r = read_raw(bring0);
     {
-        const Dq dq = decode(r);
+        const Dq dq = ONEG ? dq_one : decode(r);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) dequant_kb(r, dq, kb, bA[kb]);
     }
@@ -619,11 +641,18 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
     else if ((gsteps & (gsteps - 1)) == 0) gshift = __builtin_ctz((unsigned)gsteps);
     const auto *q = reinterpret_cast<const uint32_t *>(qw);
     const auto *z = reinterpret_cast<const uint32_t *>(qz);
+    if constexpr (!GU) {
+        if (G == K) {
+            hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 2, false>), dim3((unsigned)tiles), dim3(256),
+                               0, s, x, q, sc, z, y, M, K, N, G, 0);
+            return hipGetLastError();
+        }
+    }
     if (gshift >= 0)
-        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, true, GU>), dim3((unsigned)tiles), dim3(256), 0,
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 1, GU>), dim3((unsigned)tiles), dim3(256), 0,
                            s, x, q, sc, z, y, M, K, N, G, gshift);
     else
-        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, false, GU>), dim3((unsigned)tiles), dim3(256), 0,
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 0, GU>), dim3((unsigned)tiles), dim3(256), 0,
                            s, x, q, sc, z, y, M, K, N, G, 0);
     return hipGetLastError();
 }
