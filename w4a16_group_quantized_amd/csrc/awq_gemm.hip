@@ -5,19 +5,18 @@
 //
 // Workgroup: 256 threads = 4 waves, output tile BM x 256.  Wave w owns the 64
 // columns [64 w, 64 w + 64) of the tile for all BM rows, so every packed
-// weight is loaded and dequantized by exactly one wave, straight into
-// registers: one 16-byte load of a packed row gives a lane four words (four
-// consecutive columns, 8 k each), and each word, dequantized, is that lane's B
-// operand of one v_mfma_f32_16x16x32_f16 (8 k of one column).  The four words
-// feed four MFMA column sets {4 c + i}.  Dequantization is exact:
-// w = fp16_rne(s (q - z)), the same bits awq_dequant writes.
+// weight is loaded and dequantized by exactly one wave, straight into the
+// registers of an MFMA B operand (a packed word is 8 k of one column: one
+// lane's B operand).  Dequantization is exact: w = fp16_rne(s (q - z)), the
+// same bits awq_dequant writes.  X is the shared operand: each K step loads the
+// BM x BK slice of X once per workgroup into LDS, XOR-swizzled per row, and all
+// four waves read their A operands from there.
 //
-// X is the shared operand: each K step of BK = 64 loads the BM x 64 slice of X
-// once per workgroup into LDS (16-byte chunks, each reordered to the (j, j+4)
-// k pairing of the unpacked words, XOR-swizzled per row so that the 16 rows an
-// A-operand read touches fall in different banks), and all four waves read
-// their A operands from there.  The next step's X and packed words
-// are loaded while the current step multiplies (double-buffered LDS).
+// Two kernels:
+//   m32::mfma32_kernel (G a multiple of 32 and K of 128): v_mfma_f32_32x32x16,
+//     a four-step ring of direct-to-LDS loads, 128- or 256-row tiles;
+//   gemm_kernel (every other shape): v_mfma_f32_16x16x32, packed words loaded
+//     into registers, clamped addresses and the weights of k past K zeroed.
 //
 // Tiles are assigned so that the workgroups one XCD runs (workgroup ids are
 // dealt to the 8 XCDs round-robin) cover a compact block of output tiles:
@@ -267,7 +266,8 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 }
 
 // ---------------------------------------------------------------------------
-// Fast path on 32x32x16 MFMAs: G % 64 == 0 and K % 256 == 0.
+// Fast path on 32x32x16 MFMAs: steps of BK = 64 k (G % 64 == 0, K % 256 == 0)
+// or 32 k (G % 32 == 0, K % 128 == 0), 128- or 256-row tiles.
 //
 // A v_mfma_f32_32x32x16_f16 keeps the matrix core busy for 32 cycles, twice as
 // long as the 16x16x32 form for the same operand registers, so one wave per
@@ -281,11 +281,12 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 // Every load of the loop is a direct-to-LDS buffer load -- X, packed words,
 // scales and zero points -- so all waits are the explicit counts below:
 // the compiler tracks no vector-memory result in registers.  A step kt:
-//   wait for X(kt) and the weights of kt + 1, barrier;
-//   issue the loads of step kt + 3 into the ring slot of kt - 1;
-//   read A(kt) and the packed weights of kt + 1 from LDS;
-//   MFMAs of kt (B dequantized during kt - 1), interleaved with the
-//   dequantization of kt + 1.
+//   MFMAs of kt's k blocks but the last (B dequantized during kt - 1),
+//   interleaved with the A reads of kt and the dequantization of kt + 1;
+//   wait until X(kt + 1) and the weights of kt + 2 have landed, barrier;
+//   issue the loads of step kt + 4 into the ring slots of kt;
+//   read A(kt + 1, block 0) and the packed words of kt + 2 from LDS while the
+//   last block's MFMAs run, and dequantize the last block of kt + 1.
 // ---------------------------------------------------------------------------
 namespace m32 {
 

@@ -8,32 +8,38 @@
 // small.  Two things decide the speed:
 //
 // 1. Bytes in flight.  A 30 MB weight streams in ~4 us at 8 TB/s, barely more
-//    than a few memory latencies, so each wave issues the loads of all its
-//    packed rows (UNR segments) before it uses any of them, and there is no
-//    branch between the loads (out-of-range lanes read a clamped, in-bounds
-//    address and their results are dropped at the end).
+//    than a few memory latencies, so each wave keeps D segments (SEGR packed
+//    rows each) of loads in flight and issues them with no branch between them
+//    (out-of-range lanes read a clamped, in-bounds address and their results
+//    are dropped at the end).
 //
 // 2. ALU work per packed word.  At 8 TB/s the vector units have ~20 lane-ops
 //    per 32-bit word, so codes are never converted to weights one by one:
-//    * nibbles become fp16 (1024 + q) with one AND-OR per two codes;
+//    * nibbles become fp16 biased values (1024 + q, or 64 + q for the upper
+//      nibble of a byte) with one shift and four AND-ORs per word;
 //    * the multiply runs on the matrix cores (v_mfma_f32_16x16x32_f16): one
 //      packed word is exactly one lane's B operand (8 k of one column) and the
 //      rows of X fill the A operand, so M = 1 and M = 16 cost the same ALU
 //      work per weight (A rows beyond M repeat row M-1 and are never stored);
-//    * a further MFMA against an all-ones B gives sum_k x over the same k, so
-//      a segment of L consecutive k inside one group yields
-//          C = sum_k x (1024 + q),  Csum = sum_k x,
-//      and adds s * (C - (1024 + z) Csum) = s * sum_k x (q - z) with two FMAs
-//      per output.  Group sizes that are not a multiple of 32 take the exact
-//      path instead, which dequantizes every word bit-exactly first.
+//    * the bias and zero point are removed once per group segment, not per
+//      weight: with C = sum_k a (biased value) over the segment, the staged or
+//      computed sums U and S give s * (C - U - z S) = s * sum_k x (q - z), two
+//      FMAs per output.
 //
-// Tiling: one workgroup owns TN = 16 * WPL output columns and all of K.  Each
-// lane loads WPL consecutive words (columns) of one packed row; lanes
-// 16j..16j+15 take packed row 4t + j of step t, so a step covers 32 k.  The NW
-// waves split K into contiguous ranges; their fp32 partial sums are added in
-// LDS in a fixed order (deterministic) and written as fp16.  Small X (up to
-// 32 KB) is staged in LDS once per workgroup, already in the (j, j+4) k order
-// of the unpacked pairs; larger X is read from L2 per step.
+// Kernels:
+//   stream_kernel (M <= 16, G a multiple of 128, X in LDS): each wave stages
+//     the slice of X its K range needs into its own LDS region, odd k divided
+//     by 16 so that the 64-biased upper nibbles need no shift, together with
+//     the per-segment sums U and S; no workgroup barrier before the loop;
+//   fold_kernel (G a multiple of 32, or X beyond LDS): the same fold, with X
+//     from LDS or L2 and S from an MFMA against an all-ones B;
+//   exact_kernel (any other G): every word dequantized exactly first.
+//
+// Tiling: one workgroup owns TN = 16 * WPL columns and all of K.  Each lane
+// loads WPL consecutive words (columns) of one packed row; lanes 16j..16j+15
+// take packed row 4t + j of step t, so a step covers 32 k.  The NW waves split
+// K into contiguous ranges; their fp32 partial sums are added in LDS in a fixed
+// order (deterministic) and written as fp16.
 #include "awq_device.h"
 #include "awq_internal.h"
 
