@@ -253,6 +253,45 @@ def bench_quantize(name, steps, warmup):
             "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_gemm_splitk(name, M, steps, warmup):
+    """awq_gemm and awq_gemm_splitk (slices chosen automatically) at batch M on the
+    workload's layer, as one captured graph each."""
+    import dataclasses
+    import torch
+    from w4a16_group_quantized_amd import binding, synth
+    w = dataclasses.replace(synth.WORKLOADS[name], M=M)
+    layers = build_layers(w, 1)
+    x = to_dev(synth.make_x(M, w.K, w.wid, w.n_outliers, w.outlier_gain))
+    y = torch.empty((M, w.N), dtype=torch.float16, device="cuda")
+    t_plain = time_calls("gemm", x, layers, y, steps, warmup)
+    splits = binding.splitk_splits(M, layers[0])
+    ws = torch.empty(max(binding.load().awq_gemm_splitk_workspace_bytes(M, w.N, splits), 16),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(max(warmup, 1)):
+            binding.gemm_splitk(x, layers[0], splits, out=y, stream=stream, workspace=ws)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(steps):
+            binding.gemm_splitk(x, layers[0], splits, out=y, stream=stream, workspace=ws)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    stream.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    flops = 2.0 * M * w.N * w.K
+    return {"workload": name, "entry": "awq_gemm_splitk", "M": M, "K": w.K, "N": w.N,
+            "splits": splits, "us_per_call": t * 1e6, "tflops": flops / t / 1e12,
+            "awq_gemm_us": t_plain * 1e6}
+
+
 def bench_scale_search(name, M, n_alpha, reps):
     """awq_scale_search on the workload's layer shape: M calibration rows (X ~ N(0, 1)
     with the workload's outlier channels), an fp16 W ~ N(0, 0.02), an evenly spaced
@@ -609,6 +648,8 @@ def main():
         extra.append(bench_gate_up("gate_up_m16", 16, args.steps, args.warmup))
         extra.append(bench_gate_up("gate_up_m16", 1, args.steps, args.warmup))
         extra.append(bench_gemm_gate_up("gate_up_m16", 2048, 20, 3))
+        for m in (64, 256, 512):
+            extra.append(bench_gemm_splitk("prefill_out_proj", m, 100, 10))
         extra.append(bench_quantize("decode_8b_gate", 20, 3))
         extra.append(bench_scale_search("decode_8b_gate", 4096, 20, 3))
         extra.append(torch_matmul_context("prefill_out_proj", 50))

@@ -177,6 +177,27 @@ awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
                             void *stream);
 
 /*
+ * awq_gemm_splitk: the same output as awq_gemm, for batches too small to fill
+ * the GPU with output tiles (roughly M up to a few hundred rows at K = 4096):
+ * K is cut into `splits` slices, each summed by its own workgroups with the
+ * weights dequantized exactly as awq_dequant does, into fp32 partial outputs
+ * in `workspace`; the slices are then added in order and rounded once to fp16
+ * (deterministic).  splits == 1 is awq_gemm (workspace ignored).
+ *   x: device fp16 [M][K];  y: device fp16 [M][N], 16-byte aligned.
+ *   splits: 1..16 (AWQ_ERROR_INVALID_VALUE otherwise); K % splits == 0 and each
+ *     slice a whole number of groups (or G == K) and of 256 k (or 128 k with G
+ *     a multiple of 32), else AWQ_ERROR_UNSUPPORTED before any launch.
+ *   workspace: device memory of at least awq_gemm_splitk_workspace_bytes(M, N,
+ *     splits) bytes (splits * M * N fp32), 16-byte aligned, owned by the
+ *     caller (AWQ_ERROR_WORKSPACE otherwise); its contents on return are
+ *     unspecified.
+ */
+size_t awq_gemm_splitk_workspace_bytes(int32_t M, int32_t N, int32_t splits);
+
+awq_status awq_gemm_splitk(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
+                           int32_t splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The scale search of AWQ's calibration (pyshine.com AutoAWQ tour, "The
  * Quantization Flow Up Close": per-channel means of normalized weights and of
  * activations, the FP16 module run once as the reference, the candidate

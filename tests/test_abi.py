@@ -182,3 +182,22 @@ def test_scale_search_validation(lib):
     assert call(M=1 << 20, K=4096) == 2          # M * K beyond 2^31
     assert call(x=MISALIGNED) == 3
     assert call(wsp=None) == 6 and call(nb=ws - 1) == 6
+
+
+def test_gemm_splitk_validation(lib):
+    ws = lib.awq_gemm_splitk_workspace_bytes(64, 256, 4)
+    assert ws == 4 * 64 * 256 * 4
+    assert lib.awq_gemm_splitk_workspace_bytes(64, 256, 0) == 0
+    assert lib.awq_gemm_splitk_workspace_bytes(64, 256, 17) == 0
+
+    def call(M=64, splits=4, wsp=FAKE, nb=ws, **kw):
+        lay = layer(K=1024, N=256, G=128, **kw)
+        return lib.awq_gemm_splitk(FAKE, ctypes.byref(lay), FAKE, M, splits, wsp, nb, None)
+    assert call(splits=0) == 1 and call(splits=17) == 1 and call(M=-1) == 1
+    assert call(M=0) == 0                       # empty batch: nothing launched
+    assert call(splits=3) == 4                  # 1024 / 3 is not whole
+    assert call(splits=16) == 4                 # 64-k slices: less than a 128-k ring turn
+    assert call(wsp=None) == 6 and call(wsp=MISALIGNED) == 6 and call(nb=ws - 1) == 6
+    lay = layer(K=1024, N=256, G=256)
+    assert lib.awq_gemm_splitk(FAKE, ctypes.byref(lay), FAKE, 64, 8, FAKE, 8 * 64 * 256 * 4,
+                               None) == 4       # 128-k slices cut the 256-row groups

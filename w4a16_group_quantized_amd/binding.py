@@ -22,6 +22,7 @@ LIBRARY = os.path.join(HERE, "libawq.so")
 # Entry points declared in include/awq.h, in declaration order.
 ENTRY_POINTS = ("awq_status_string", "awq_pack", "awq_pack_zeros", "awq_dequant", "awq_gemv",
                 "awq_gemm", "awq_gemv_gate_up", "awq_quantize", "awq_gemm_gate_up",
+                "awq_gemm_splitk_workspace_bytes", "awq_gemm_splitk",
                 "awq_channel_stats_workspace_bytes", "awq_channel_stats",
                 "awq_scale_search_workspace_bytes", "awq_scale_search")
 
@@ -73,6 +74,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.POINTER(CLayer), vp, i32, vp]
+    lib.awq_gemm_splitk_workspace_bytes.restype = ctypes.c_size_t
+    lib.awq_gemm_splitk_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.awq_gemm_splitk.restype = ctypes.c_int
+    lib.awq_gemm_splitk.argtypes = [vp, ctypes.POINTER(CLayer), vp, i32, i32, vp, ctypes.c_size_t, vp]
     for name in ("awq_channel_stats_workspace_bytes", "awq_scale_search_workspace_bytes"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_size_t
@@ -209,6 +214,46 @@ def gemv(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=
 def gemm(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=None):
     """y = x @ dequant(layer) for any M (prefill / batches)."""
     return _linear("awq_gemm", x, layer, out, stream)
+
+
+def splitk_splits(M: int, layer: Layer, cus: int = 256) -> int:
+    """Slices of K for awq_gemm_splitk: the fewest (1, 2, 4, 8, 16) that give at
+    least one workgroup per CU (128 x 256 output tiles), among those the layer
+    allows; 1 when the output tiles alone fill the GPU."""
+    tiles = -(-M // 128) * -(-layer.N // 256)
+    best = 1
+    for s in (2, 4, 8, 16):
+        if tiles * best >= cus:
+            break
+        if layer.K % s == 0:
+            ks = layer.K // s
+            whole = layer.group_size == layer.K or ks % layer.group_size == 0
+            if whole and (ks % 256 == 0 or (ks % 128 == 0 and layer.group_size % 32 == 0)):
+                best = s
+    return best
+
+
+def gemm_splitk(x: torch.Tensor, layer: Layer, splits: int | None = None,
+                out: torch.Tensor | None = None, stream=None, workspace: torch.Tensor | None = None):
+    """awq_gemm's output with K split across workgroups (``splits`` slices, chosen by
+    splitk_splits when None); the fp32 partials go to ``workspace`` (allocated here
+    unless given)."""
+    M = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != layer.K:
+        raise ValueError(f"x must be [M][{layer.K}], got {tuple(x.shape)}")
+    splits = splitk_splits(M, layer) if splits is None else splits
+    if out is None:
+        out = torch.empty((M, layer.N), dtype=torch.float16, device=x.device)
+    lib = load()
+    if workspace is None:
+        nbytes = lib.awq_gemm_splitk_workspace_bytes(max(M, 1), layer.N, splits)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    c = layer.c_struct()
+    _check(lib.awq_gemm_splitk(_dev(x, torch.float16, "x"), ctypes.byref(c),
+                               _dev(out, torch.float16, "out"), M, splits,
+                               _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                               _stream(stream)))
+    return out
 
 
 def gemv_gate_up(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=None):

@@ -12,6 +12,7 @@
 namespace {
 
 constexpr long long kMaxElems = (1LL << 31) - 1;
+constexpr int kMaxSplits = 16;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -63,7 +64,7 @@ const char *awq_status_string(awq_status status) {
     case AWQ_ERROR_INVALID_VALUE: return "AWQ_ERROR_INVALID_VALUE: null pointer or non-positive size";
     case AWQ_ERROR_SHAPE: return "AWQ_ERROR_SHAPE: K%8, N%8, G%8, K%G must be 0 and arrays below 2^31 elements";
     case AWQ_ERROR_ALIGNMENT: return "AWQ_ERROR_ALIGNMENT: tensor pointers must be 16-byte aligned";
-    case AWQ_ERROR_UNSUPPORTED: return "AWQ_ERROR_UNSUPPORTED: outside this entry point (awq_gemv takes M <= 16; awq_gemv_gate_up also needs G % 128 == 0 and X in LDS; awq_gemm_gate_up needs G % 64 == 0 and K % 256 == 0)";
+    case AWQ_ERROR_UNSUPPORTED: return "AWQ_ERROR_UNSUPPORTED: outside this entry point (awq_gemv takes M <= 16; awq_gemv_gate_up also needs G % 128 == 0 and X in LDS; awq_gemm_gate_up needs G % 64 == 0 and K % 256 == 0; awq_gemm_splitk needs slices of whole groups (or one group) and whole 128- or 256-k ring turns)";
     case AWQ_ERROR_HIP: return "AWQ_ERROR_HIP: the HIP runtime refused the launch";
     case AWQ_ERROR_WORKSPACE: return "AWQ_ERROR_WORKSPACE: null, unaligned or smaller than the *_workspace_bytes query";
     }
@@ -157,6 +158,31 @@ awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
     return from_hip(awq::launch_gemm_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
                                              layer->K, layer->N, layer->group_size,
                                              as_stream(stream)));
+}
+
+size_t awq_gemm_splitk_workspace_bytes(int32_t M, int32_t N, int32_t splits) {
+    if (M <= 0 || N <= 0 || splits < 1 || splits > kMaxSplits) return 0;
+    return awq::gemm_splitk_workspace(M, N, splits);
+}
+
+awq_status awq_gemm_splitk(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
+                           int32_t splits, void *workspace, size_t workspace_bytes, void *stream) {
+    awq_status st = check_layer(layer);
+    if (st != AWQ_SUCCESS) return st;
+    if (splits < 1 || splits > kMaxSplits) return AWQ_ERROR_INVALID_VALUE;
+    st = check_io(x, y, layer, M);
+    if (st != AWQ_SUCCESS || M == 0) return st;
+    if (splits == 1)
+        return from_hip(awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
+                                         layer->K, layer->N, layer->group_size, as_stream(stream)));
+    if (!awq::gemm_splitk_supported(layer->K, layer->group_size, splits)) return AWQ_ERROR_UNSUPPORTED;
+    if ((long long)splits * M * layer->N > kMaxElems) return AWQ_ERROR_SHAPE;
+    if (workspace == nullptr || !aligned16(workspace) ||
+        workspace_bytes < awq::gemm_splitk_workspace(M, layer->N, splits))
+        return AWQ_ERROR_WORKSPACE;
+    return from_hip(awq::launch_gemm_splitk(x, layer->qweight, layer->scales, layer->qzeros, y, M,
+                                            layer->K, layer->N, layer->group_size, splits, workspace,
+                                            as_stream(stream)));
 }
 
 size_t awq_channel_stats_workspace_bytes(int32_t M, int32_t K, int32_t N, int32_t group_size) {

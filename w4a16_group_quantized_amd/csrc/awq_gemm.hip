@@ -335,17 +335,22 @@ __device__ __forceinline__ void unpack_natural(uint32_t w, uint32_t exps, uint32
 // two); 0, kt / (G / BK); 2, one group (G == K): each lane then loads its scale
 // pair and zero word once, into registers, before the loop, and the steps load
 // and decode only packed words.
+// SPLIT (split K): workgroup row blockIdx.y sums only the k in slice
+// [y kslice, (y + 1) kslice), which starts on a group boundary (or lies in the
+// single group), and writes its fp32 partial tile to Y taken as float
+// [slices][M][N]; a second kernel adds the slices.
 // GU (fused gate/up): the layer's N = 2I columns are [gate | up].  A wave's 64
 // MFMA columns are then 32 gate columns and the same 32 columns of the up half
 // (column tile 0: gate, tile 1: up, for the same output column), and the
 // output is h[M][I] = fp16(SiLU(gate) * up), 32 columns per wave.
-template <int KB, int MT, bool SYM, int GMODE, bool GU>
+template <int KB, int MT, bool SYM, int GMODE, bool GU, bool SPLIT = false>
 __global__ void __launch_bounds__(256)
 mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
-              uint16_t *__restrict__ Y, int M, int K, int N, int G, int gshift) {
+              uint16_t *__restrict__ Y, int M, int K, int N, int G, int gshift, int kslice) {
     constexpr bool ONEG = GMODE == 2;
     static_assert(!(ONEG && GU), "one-group mode is for the plain layer");
+    static_assert(!(SPLIT && GU), "split K is for the plain layer");
     using Gm = Geom<KB, MT>;
     constexpr int kBM = Gm::BM, kMT = MT, kACH = Gm::ACH, kWave = Gm::WAVE;
     constexpr int kScale = Gm::SCALE, kZero = Gm::ZERO, kBKs = Gm::BK, kXCH = Gm::XCH;
@@ -375,15 +380,29 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const int hw0 = tn * (kBN / 2) + 32 * wave;   // GU: first output column of the wave
     // Layer column of slot c (0..63) of the wave's weight tile.
     auto src_col = [&](int c) { return GU ? (c < 32 ? hw0 + c : I + hw0 + c - 32) : n0 + c; };
-    const int KR = K / 8;
-    const int KT = K / kBKs;
+    // The k this workgroup sums: all of K, or its slice under split K.
+    const int k0 = SPLIT ? (int)blockIdx.y * kslice : 0;
+    const int KL = SPLIT ? kslice : K;
+    const int groups = ONEG ? 1 : (K - k0) / G;   // scale rows from the slice's first group on
+    if constexpr (SPLIT) {
+        X += k0;
+        Q += (size_t)(k0 / 8) * N;
+        if constexpr (!ONEG) {
+            S += (size_t)(k0 / G) * N;
+            if constexpr (!SYM) QZ += (size_t)(k0 / G) * (N / 8);
+        }
+    }
+    const int KR = KL / 8;
+    const int KT = KL / kBKs;
 
     // Buffer loads past a buffer's end return zeros; columns at or past N read
-    // the next packed row (in bounds) and their outputs are dropped.
-    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+    // the next packed row (in bounds) and their outputs are dropped.  X rows
+    // keep their stride K; the buffer ends after the slice's part of row M - 1.
+    const __amdgpu_buffer_rsrc_t xrs =
+        make_rsrc(X, ((uint32_t)(M - 1) * (uint32_t)K + (uint32_t)KL) * 2u);
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, (uint32_t)KR * (uint32_t)N * 4u);
-    const __amdgpu_buffer_rsrc_t srs = make_rsrc(S, (uint32_t)(K / G) * (uint32_t)N * 2u);
-    const __amdgpu_buffer_rsrc_t zrs = make_rsrc(QZ, SYM ? 0u : (uint32_t)(K / G) * (uint32_t)N / 2u);
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(S, (uint32_t)groups * (uint32_t)N * 2u);
+    const __amdgpu_buffer_rsrc_t zrs = make_rsrc(QZ, SYM ? 0u : (uint32_t)groups * (uint32_t)N / 2u);
     uint32_t xvoff[kACH];
 #pragma unroll
     for (int i = 0; i < kACH; ++i) {
@@ -614,9 +633,23 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         return;
     }
     // column tiles 0 and 1 are the adjacent columns n0 + 2 j and n0 + 2 j + 1,
-    // stored as one 4-byte word.
+    // stored as one 4-byte word (split K: one 8-byte fp32 pair of the slice's
+    // partial tile).
     const int col = n0 + 2 * j;
     if (col >= N) return;
+    if constexpr (SPLIT) {
+        float *Yf = reinterpret_cast<float *>(Y) + (size_t)blockIdx.y * M * N;
+#pragma unroll
+        for (int t = 0; t < kMT; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + 32 * t + 8 * (v / 4) + 4 * h + (v % 4);
+                if (row < M)
+                    *reinterpret_cast<float2 *>(Yf + (size_t)row * N + col) =
+                        make_float2(acc[t][0][v], acc[t][1][v]);
+            }
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < kMT; ++t)
 #pragma unroll
@@ -645,20 +678,78 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
     if constexpr (!GU) {
         if (G == K) {
             hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 2, false>), dim3((unsigned)tiles), dim3(256),
-                               0, s, x, q, sc, z, y, M, K, N, G, 0);
+                               0, s, x, q, sc, z, y, M, K, N, G, 0, K);
             return hipGetLastError();
         }
     }
     if (gshift >= 0)
         hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 1, GU>), dim3((unsigned)tiles), dim3(256), 0,
-                           s, x, q, sc, z, y, M, K, N, G, gshift);
+                           s, x, q, sc, z, y, M, K, N, G, gshift, K);
     else
         hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 0, GU>), dim3((unsigned)tiles), dim3(256), 0,
-                           s, x, q, sc, z, y, M, K, N, G, 0);
+                           s, x, q, sc, z, y, M, K, N, G, 0, K);
+    return hipGetLastError();
+}
+
+// Split K: `splits` slices of K / splits k, each a whole number of steps and
+// of groups (or inside the single group), as a second grid dimension; fp32
+// partial tiles into part[splits][M][N].
+template <int KB, int MT, bool SYM>
+hipError_t launch_split(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
+                        float *part, int M, int K, int N, int G, int splits, hipStream_t s) {
+    using Gm = Geom<KB, MT>;
+    const int kslice = K / splits;
+    const long long tiles = (long long)((M + Gm::BM - 1) / Gm::BM) * ((N + kBN - 1) / kBN);
+    const dim3 grid((unsigned)tiles, (unsigned)splits);
+    const auto *q = reinterpret_cast<const uint32_t *>(qw);
+    const auto *z = reinterpret_cast<const uint32_t *>(qz);
+    auto *y = reinterpret_cast<uint16_t *>(part);
+    const int gsteps = G / Gm::BK;
+    if (G == K)
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 2, false, true>), grid, dim3(256), 0, s, x, q, sc,
+                           z, y, M, K, N, G, 0, kslice);
+    else if ((gsteps & (gsteps - 1)) == 0)
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 1, false, true>), grid, dim3(256), 0, s, x, q, sc,
+                           z, y, M, K, N, G, __builtin_ctz((unsigned)gsteps), kslice);
+    else
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 0, false, true>), grid, dim3(256), 0, s, x, q, sc,
+                           z, y, M, K, N, G, 0, kslice);
     return hipGetLastError();
 }
 
 }  // namespace m32
+
+// Y = fp16(sum over the slices of part[s]), slices added in order.
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float *__restrict__ part, int splits, long long count,
+                     uint16_t *__restrict__ Y) {
+    const long long quads = count / 4;
+    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < quads; i += (long long)gridDim.x * 256) {
+        float4 a = reinterpret_cast<const float4 *>(part)[i];
+        for (int sl = 1; sl < splits; ++sl) {
+            const float4 b = reinterpret_cast<const float4 *>(part + (size_t)sl * count)[i];
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        reinterpret_cast<uint2 *>(Y)[i] =
+            make_uint2((uint32_t)as_u16((half_t)a.x) | ((uint32_t)as_u16((half_t)a.y) << 16),
+                       (uint32_t)as_u16((half_t)a.z) | ((uint32_t)as_u16((half_t)a.w) << 16));
+    }
+}
+
+// Step size of the split-K kernel for slices of kslice k: 64 (or 32) k steps,
+// whole ring turns, and whole groups unless there is a single group.
+inline int splitk_bk(int K, int G, int splits) {
+    if (splits < 1 || K % splits) return 0;
+    const int kslice = K / splits;
+    const bool groups_ok = G == K || kslice % G == 0;
+    if (!groups_ok) return 0;
+    if ((G == K || G % 64 == 0) && kslice % (kRing * 64) == 0) return 64;
+    if ((G == K || G % 32 == 0) && kslice % (kRing * 32) == 0) return 32;
+    return 0;
+}
 
 template <int BM, bool SYM>
 hipError_t launch_general(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
@@ -694,6 +785,34 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
 }
 
 }  // namespace gemm
+
+bool gemm_splitk_supported(int K, int G, int splits) { return gemm::splitk_bk(K, G, splits) != 0; }
+
+size_t gemm_splitk_workspace(int M, int N, int splits) {
+    return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+}
+
+hipError_t launch_gemm_splitk(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                              const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
+                              int splits, void *workspace, hipStream_t s) {
+    using namespace gemm;
+    const bool sym = qzeros == nullptr;
+    auto *part = static_cast<float *>(workspace);
+    hipError_t e;
+    if (splitk_bk(K, G, splits) == 64)
+        e = sym ? m32::launch_split<4, 4, true>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s)
+                : m32::launch_split<4, 4, false>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s);
+    else
+        e = sym ? m32::launch_split<2, 4, true>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s)
+                : m32::launch_split<2, 4, false>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s);
+    if (e != hipSuccess) return e;
+    const long long count = (long long)M * N;
+    long long blocks = (count / 4 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, part, splits, count,
+                       y);
+    return hipGetLastError();
+}
 
 bool gemm_gate_up_supported(int K, int N, int G) {
     return N % 16 == 0 && G % gemm::kBK == 0 && K % (gemm::kRing * gemm::kBK) == 0;

@@ -29,6 +29,13 @@ hipError_t launch_gemm_gate_up(const uint16_t *x, const int32_t *qweight, const 
 hipError_t launch_gemm(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
                        hipStream_t s);
+// Split K: slices of K / splits summed by separate workgroups into fp32
+// partials (workspace: splits * M * N floats), then added in slice order.
+bool gemm_splitk_supported(int K, int G, int splits);
+size_t gemm_splitk_workspace(int M, int N, int splits);
+hipError_t launch_gemm_splitk(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                              const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
+                              int splits, void *workspace, hipStream_t s);
 // Scale search (per-channel statistics, candidates, migrated layer, loss).
 constexpr int kScaleSearchMaxAlphas = 64;
 size_t channel_stats_workspace(int M, int K, int N, int G);
