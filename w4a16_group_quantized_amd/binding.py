@@ -217,18 +217,32 @@ def gemm(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=
 
 
 def splitk_splits(M: int, layer: Layer, cus: int = 256) -> int:
-    """Slices of K for awq_gemm_splitk: the fewest (1, 2, 4, 8, 16) that give at
-    least one workgroup per CU (128 x 256 output tiles), among those the layer
-    allows; 1 when the output tiles alone fill the GPU."""
+    """Slices of K for awq_gemm_splitk (1, 2, 4, 8 or 16, among those the layer
+    allows), from a cost model fitted to MI355X timings of a 4096 x 4096 and a
+    4096 x 28672 layer at M = 16 to 2048.  Workgroups (128 x 256 output tiles
+    times slices) run in waves of one per CU; a workgroup costs about 3.2 us
+    plus 8.8 ns per k, the per-k cost growing by up to 57% as the wave fills the
+    chip (the MFMA units share the power budget); a split adds about 5.9 us and
+    the partial sums, splits * M * N * 4 bytes written and read again at about
+    7.9 TB/s.  More slices are taken only where the model saves at least 5%."""
     tiles = -(-M // 128) * -(-layer.N // 256)
+
+    def cost(s):
+        active = min(tiles * s, cus)
+        waves = -(-tiles * s // cus)
+        t = waves * (3.2e-6 + (layer.K // s) * 8.8e-9 * (1 + 0.57 * active / cus))
+        if s > 1:
+            t += 5.9e-6 + 2 * s * M * layer.N * 4 / 7.9e12
+        return t
+
     best = 1
     for s in (2, 4, 8, 16):
-        if tiles * best >= cus:
-            break
-        if layer.K % s == 0:
-            ks = layer.K // s
-            whole = layer.group_size == layer.K or ks % layer.group_size == 0
-            if whole and (ks % 256 == 0 or (ks % 128 == 0 and layer.group_size % 32 == 0)):
+        if layer.K % s:
+            continue
+        ks = layer.K // s
+        whole = layer.group_size == layer.K or ks % layer.group_size == 0
+        if whole and (ks % 256 == 0 or (ks % 128 == 0 and layer.group_size % 32 == 0)):
+            if cost(s) < 0.95 * cost(best):
                 best = s
     return best
 
