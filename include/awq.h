@@ -113,7 +113,11 @@ awq_status awq_gemv(const uint16_t *x, const awq_layer *layer, uint16_t *y, int3
  * awq_gemm: fused dequantize-and-multiply for any M >= 0 (the pages' GEMM
  * module for batched inference): weights are dequantized tile by tile into
  * on-chip memory and multiplied with fp16 matrix-core instructions, fp32
- * accumulation.
+ * accumulation.  Each weight is dequantized exactly as awq_dequant does,
+ * except on one-group layers (group_size == K): there the matrix cores take
+ * q - z (exact) and each column's scale multiplies its fp32 sum once, as
+ * awq_gemv does per group (no fp16 rounding of each s (q - z); the difference
+ * is far inside the layer's output tolerance).
  */
 awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
                     void *stream);
@@ -180,7 +184,7 @@ awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
  * awq_gemm_splitk: the same output as awq_gemm, for batches too small to fill
  * the GPU with output tiles (roughly M up to a few hundred rows at K = 4096):
  * K is cut into `splits` slices, each summed by its own workgroups with the
- * weights dequantized exactly as awq_dequant does, into fp32 partial outputs
+ * weights dequantized as awq_gemm does, into fp32 partial outputs
  * in `workspace`; the slices are then added in order and rounded once to fp16
  * (deterministic).  splits == 1 is awq_gemm (workspace ignored).
  *   x: device fp16 [M][K];  y: device fp16 [M][N], 16-byte aligned.

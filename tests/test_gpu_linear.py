@@ -96,9 +96,12 @@ def test_gemm_wide_tiles(M, K, N, G, sym):
 
 @pytest.mark.parametrize("entry", ["gemv", "gemm"])
 @pytest.mark.parametrize("K,N,G,sym", [(512, 512, 128, False), (256, 200, 8, False),
-                                       (1024, 136, 1024, True)])
+                                       (1024, 136, 1024, True), (1024, 136, 1024, False)])
 def test_onehot_rows_bit_exact(entry, K, N, G, sym):
-    """X row m = e_k(m): each output is one exact product, rounded once."""
+    """X row m = e_k(m): each output is one exact product, rounded once.  On
+    one-group layers the GEMM multiplies the sum q - z by the scale after the
+    matrix cores: with x = 1 that product is still exact in fp32, so the output
+    is still the dequantized weight bit for bit."""
     _, codes, zeros, scales = random_case(5 + K, 1, K, N, G, sym)
     W, _ = oracle_case(np.zeros((1, K), np.uint16), codes, zeros, scales, G)
     ks = np.random.default_rng(K + N).choice(K, size=16, replace=False)
@@ -109,9 +112,10 @@ def test_onehot_rows_bit_exact(entry, K, N, G, sym):
     assert same_halves_up_to_zero_sign(y, W[ks])
 
 
-def test_gemm_identity_returns_weight():
-    """X = I_K through awq_gemm gives the whole dequantized matrix."""
-    K, N, G = 256, 136, 64
+@pytest.mark.parametrize("K,N,G", [(256, 136, 64), (256, 136, 256)])
+def test_gemm_identity_returns_weight(K, N, G):
+    """X = I_K through awq_gemm gives the whole dequantized matrix (also with one
+    group per column, where the scale multiplies the fp32 sum)."""
     _, codes, zeros, scales = random_case(42, 1, K, N, G, False)
     W, _ = oracle_case(np.zeros((1, K), np.uint16), codes, zeros, scales, G)
     X = np.zeros((K, K), dtype=np.uint16)
@@ -184,7 +188,9 @@ def test_misaligned_pointer_is_rejected():
 ])
 def test_gemm_one_group(M, K, N, G, sym):
     """One group per column (G == K): scales and zero points are loaded once per
-    lane, past the last column included (ragged N)."""
+    lane, past the last column included (ragged N); the matrix cores take q - z
+    and each column's scale multiplies its fp32 sum, so Y is held to the layer's
+    parity bar like the folded decode path."""
     X, codes, zeros, scales = random_case(9000 + M + K, M, K, N, G, sym)
     _, Y16 = oracle_case(X, codes, zeros, scales, G)
     y = to_host_bits(binding.gemm(to_dev(X), device_case(codes, zeros, scales, G)))

@@ -334,7 +334,10 @@ __device__ __forceinline__ void unpack_natural(uint32_t w, uint32_t exps, uint32
 // GMODE, how step kt finds its group: 1, kt >> gshift (G / BK a power of
 // two); 0, kt / (G / BK); 2, one group (G == K): each lane then loads its scale
 // pair and zero word once, into registers, before the loop, and the steps load
-// and decode only packed words.
+// and decode only packed words.  B is then q - z, exact, and the column's scale
+// multiplies the fp32 sums in the epilogue: one VALU fewer per weight pair, and
+// no rounding of s (q - z) to fp16 (the output differs from x times
+// awq_dequant's weights by that rounding, well inside the layer's tolerance).
 // SPLIT (split K): workgroup row blockIdx.y sums only the k in slice
 // [y kslice, (y + 1) kslice), which starts on a group boundary (or lies in the
 // single group), and writes its fp32 partial tile to Y taken as float
@@ -518,8 +521,12 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         for (int ct = 0; ct < 2; ++ct) {
             uint32_t p[4], d[4];
             unpack_natural(ct ? r.q[kb].y : r.q[kb].x, exps, p);
+            // One group: B is q - z (exact small integers); the column's scale
+            // multiplies the fp32 sums once, in the epilogue.
 #pragma unroll
-            for (int e = 0; e < 4; ++e) d[e] = dequant_pair(p[e], dq.bz2[ct], dq.s2[ct]);
+            for (int e = 0; e < 4; ++e)
+                d[e] = ONEG ? as_u32(as_half2(p[e]) - dq.bz2[ct])
+                            : dequant_pair(p[e], dq.bz2[ct], dq.s2[ct]);
             b[ct] = as_half8(make_uint4(d[0], d[1], d[2], d[3]));
         }
     };
@@ -637,6 +644,16 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     // partial tile).
     const int col = n0 + 2 * j;
     if (col >= N) return;
+    if constexpr (ONEG) {
+        const float s0 = (float)dq_one.s2[0][0], s1 = (float)dq_one.s2[1][0];
+#pragma unroll
+        for (int t = 0; t < kMT; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                acc[t][0][v] *= s0;
+                acc[t][1][v] *= s1;
+            }
+    }
     if constexpr (SPLIT) {
         float *Yf = reinterpret_cast<float *>(Y) + (size_t)blockIdx.y * M * N;
 #pragma unroll
