@@ -30,7 +30,10 @@
 //   stream_kernel (M <= 16, G a multiple of 128, X in LDS): each wave stages
 //     the slice of X its K range needs into its own LDS region, odd k divided
 //     by 16 so that the 64-biased upper nibbles need no shift, together with
-//     the per-segment sums U and S; no workgroup barrier before the loop;
+//     the per-segment sums U and S; no workgroup barrier before the loop.  Up
+//     to four rows the slice is staged before the first multiply; beyond four
+//     (128 KB per workgroup at 16 rows), each segment's part is loaded with
+//     that segment's weights and staged just before it is multiplied;
 //   fold_kernel (G a multiple of 32, or X beyond LDS): the same fold, with X
 //     from LDS or L2 and S from an MFMA against an all-ones B;
 //   exact_kernel (any other G): every word dequantized exactly first.
@@ -430,7 +433,13 @@ constexpr size_t kLdsMax = 160 * 1024;
 // GU (fused gate/up): the layer's N columns are [gate | up]; a lane's WPL words
 // are WPL / 2 gate columns and the same WPL / 2 columns of the up half, and the
 // output is h = fp16(SiLU(gate) * up), N / 2 columns wide.
-template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false>
+// XS > 0 stages X progressively: the XS chunks per lane of a segment's slice
+// of X (M * SEGR <= 64 * XS) are loaded with the segment's weights and staged
+// just before the segment is multiplied, instead of the whole slice up front.
+// With 16 rows the whole slice is 128 KB per workgroup, and every workgroup
+// asking for it at once delays the first multiply by microseconds.
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false,
+          int XS = 0>
 __global__ void __launch_bounds__(NW * 64)
 stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
@@ -490,47 +499,87 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         }
     };
 
-    // 1. X loads (clamped, unconditional), 2. the first D segments, 3. staging.
-    const int chunks_w = M * rows_w;
-    uint4 xr[XCH];
-#pragma unroll
-    for (int j = 0; j < XCH; ++j) {
-        const int c = lane + 64 * j;
-        const int cc = c < chunks_w ? c : 0;
-        const int m = VR == 1 ? 0 : cc / rows_w;             // VR == 1 means M == 1
-        const int rr = VR == 1 ? cc : cc - m * rows_w;
-        xr[j] = reinterpret_cast<const uint4 *>(X)[(size_t)m * KR + r_begin + rr];
-    }
-    WSeg<WPL, STEPS, SYM> b[D];
-    const int s_begin = wave * per;
-#pragma unroll
-    for (int d = 0; d < D; ++d) load_seg(s_begin + d, b[d]);
-
-#pragma unroll
-    for (int j = 0; j < XCH; ++j) {
-        const int c = lane + 64 * j;
-        const uint4 a = stage_chunk(xr[j]);
+    // Staging of one chunk: row m, wave-local packed row rr, `live` false for
+    // the padding lanes.  The segment sums (U, S) of a row are reduced over the
+    // aligned groups of SEGR lanes that hold that row's chunks of one segment.
+    auto stage = [&](const uint4 &raw, bool live, int m, int rr) {
+        const uint4 a = stage_chunk(raw);
         const half2_t one2 = {(half_t)1.0f, (half_t)1.0f};
         const float lo = __builtin_amdgcn_fdot2(as_half2(a.x), one2,
                          __builtin_amdgcn_fdot2(as_half2(a.z), one2, 0.f, false), false);
         const float hi = __builtin_amdgcn_fdot2(as_half2(a.y), one2,
                          __builtin_amdgcn_fdot2(as_half2(a.w), one2, 0.f, false), false);
-        float t = c < chunks_w ? lo + hi : 0.f;          // sum of the staged values
-        float u = c < chunks_w ? lo + 16.f * hi : 0.f;   // sum of x
-        // segment sums over aligned groups of SEGR lanes (consecutive chunks)
+        float t = live ? lo + hi : 0.f;          // sum of the staged values
+        float u = live ? lo + 16.f * hi : 0.f;   // sum of x
         t = lane_group_sum<SEGR>(t);
         u = lane_group_sum<SEGR>(u);
-        if (c < chunks_w) {
-            const int m = VR == 1 ? 0 : c / rows_w;
-            const int rr = c - m * rows_w;
+        if (live) {
             xs[m * rows_w + (rr ^ (m & 15))] = a;
-            if (c % SEGR == 0) tab[m * per + rr / SEGR] = make_float2(1024.f * t, u);
+            if (rr % SEGR == 0) tab[m * per + rr / SEGR] = make_float2(1024.f * t, u);
         }
-    }
+    };
     // Only this wave reads its slice; LDS operations of one wave execute in order.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    auto staged = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    const uint4 *X4 = reinterpret_cast<const uint4 *>(X);
+    WSeg<WPL, STEPS, SYM> b[D];
+    const int s_begin = wave * per;
+    // Progressive staging: chunk c = lane + 64 j of segment sl is row c / SEGR,
+    // packed row sl * SEGR + c % SEGR of the wave's slice (clamped loads).
+    // A segment's swizzled chunks (rr ^ (m % 16)) stay in its own 16 packed rows.
+    static_assert(XS == 0 || SEGR % 16 == 0, "progressive staging needs 16-row segments");
+    constexpr int XSN = XS > 0 ? XS : 1;
+    uint4 xq[D][XSN];
+    auto load_x_seg = [&](int sl, uint4 (&q)[XSN]) {
+#pragma unroll
+        for (int j = 0; j < XSN; ++j) {
+            const int c = lane + 64 * j;
+            const int cc = c < M * SEGR ? c : 0;
+            q[j] = X4[(size_t)(cc / SEGR) * KR + r_begin + sl * SEGR + cc % SEGR];
+        }
+    };
+    auto stage_x_seg = [&](int sl, const uint4 (&q)[XSN]) {
+#pragma unroll
+        for (int j = 0; j < XSN; ++j) {
+            const int c = lane + 64 * j;
+            stage(q[j], c < M * SEGR, c / SEGR, sl * SEGR + c % SEGR);
+        }
+        staged();
+    };
+
+    if constexpr (XS > 0) {
+        // X chunks of a segment first, then its weights: the wait for the
+        // chunks does not wait for the segment's own weights.
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load_x_seg(d, xq[d]);
+            load_seg(s_begin + d, b[d]);
+        }
+    } else {
+        // 1. X loads (clamped, unconditional), 2. the first D segments, 3. staging.
+        const int chunks_w = M * rows_w;
+        uint4 xr[XCH];
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+            const int c = lane + 64 * j;
+            const int cc = c < chunks_w ? c : 0;
+            const int m = VR == 1 ? 0 : cc / rows_w;             // VR == 1 means M == 1
+            const int rr = VR == 1 ? cc : cc - m * rows_w;
+            xr[j] = X4[(size_t)m * KR + r_begin + rr];
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_seg(s_begin + d, b[d]);
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+            const int c = lane + 64 * j;
+            const int m = VR == 1 ? 0 : c / rows_w;
+            stage(xr[j], c < chunks_w, m, c - m * rows_w);
+        }
+        staged();
+    }
 
     const uint32_t lo_mask = nibble_mask_vgpr();
     const uint32_t hi_mask = high_mask_vgpr();
@@ -589,12 +638,17 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     for (int i = 0; i < per - D; i += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
+            if constexpr (XS > 0) stage_x_seg(i + d, xq[d]);
             compute_seg(s_begin + i + d, b[d]);
+            if constexpr (XS > 0) load_x_seg(i + d + D, xq[d]);
             load_seg(s_begin + i + d + D, b[d]);
         }
     }
 #pragma unroll
-    for (int d = 0; d < D; ++d) compute_seg(s_begin + per - D + d, b[d]);
+    for (int d = 0; d < D; ++d) {
+        if constexpr (XS > 0) stage_x_seg(per - D + d, xq[d]);
+        compute_seg(s_begin + per - D + d, b[d]);
+    }
 
     // C layout of the 16x16 MFMA: lane (kb, c16) holds rows 4 kb + v of column c16.
     __syncthreads();   // every wave is done with the staged X and the tables
@@ -640,13 +694,14 @@ inline size_t stream_lds(int M, int K, int WPL, int NW, int SEGR) {
     return staged > red ? staged : red;
 }
 
-template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false>
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false,
+          int XS = 0>
 hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                          hipStream_t s) {
     constexpr int TO = GU ? 8 * WPL : 16 * WPL;   // output columns per workgroup
     const int NO = GU ? N / 2 : N;
-    auto kernel = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU>;
+    auto kernel = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS>;
     const size_t lds = stream_lds(M, K, WPL, NW, SEGR);
     if (lds > 64 * 1024) {
         // Beyond 64 KB the kernel must be allowed the larger allocation (once).
@@ -695,6 +750,29 @@ hipError_t launch_stream_x(const uint16_t *x, const int32_t *qw, const uint16_t 
     if (chunks_w <= 256) return launch_stream_sg<WPL, NW, SEGR, D, VR, 4>(x, qw, sc, qz, y, M, K, N, G, s);
     if (chunks_w <= 512) return launch_stream_sg<WPL, NW, SEGR, D, VR, 8>(x, qw, sc, qz, y, M, K, N, G, s);
     return launch_stream_sg<WPL, NW, SEGR, D, VR, kStageChunks>(x, qw, sc, qz, y, M, K, N, G, s);
+}
+
+// Beyond four rows (all four C rows of a lane live), X staged progressively:
+// XS = ceil(M * 16 / 64) chunks per lane per 16-row segment.
+template <int WPL, int NW, int D, bool GU, int XS>
+hipError_t launch_stream_prog_xs(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                                 const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                                 hipStream_t s) {
+    const bool grp1 = G == 8 * 16;
+#define AWQ_PROG(SYMV, GRPV) \
+    launch_stream<WPL, NW, 16, D, 4, SYMV, GRPV, 1, GU, XS>(x, qw, sc, qz, y, M, K, N, G, s)
+    if (qz == nullptr) return grp1 ? AWQ_PROG(true, true) : AWQ_PROG(true, false);
+    return grp1 ? AWQ_PROG(false, true) : AWQ_PROG(false, false);
+#undef AWQ_PROG
+}
+
+template <int WPL, int NW, int D, bool GU>
+hipError_t launch_stream_prog(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                              const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                              hipStream_t s) {
+    if (M <= 8) return launch_stream_prog_xs<WPL, NW, D, GU, 2>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (M <= 12) return launch_stream_prog_xs<WPL, NW, D, GU, 3>(x, qw, sc, qz, y, M, K, N, G, s);
+    return launch_stream_prog_xs<WPL, NW, D, GU, 4>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
 template <int WPL, int NW, int SEGR, int D>
@@ -855,6 +933,7 @@ template <int NW, int D>
 hipError_t launch_gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                           hipStream_t s) {
+    if (M > 4) return launch_stream_prog<8, NW, D, true>(x, qw, sc, qz, y, M, K, N, G, s);
     const bool sym = qz == nullptr, grp1 = G == 8 * 16;
     const bool big = M * (K / 8 / NW) > 128;
 #define AWQ_GU(SYMV, GRPV, XCHV) \
@@ -902,7 +981,7 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
     // segment in flight per wave, so that staging X and the first loads compete
     // less for the CU's load path (measured faster).
     if (M > 4 && stream_fits(M, K, N, G, 8, 8, 16, 1))
-        return launch_stream_m<8, 8, 16, 1>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        return launch_stream_prog<8, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 2))
         return launch_stream_m<4, 8, 16, 2>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 1))
