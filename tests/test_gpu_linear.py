@@ -54,6 +54,10 @@ RAGGED = [
     (16, 512, 24, 512, True), (7, 1024, 264, 128, False), (2, 96, 40, 32, False),
     (1, 520, 8, 8, True), (16, 4096, 136, 128, False), (9, 192, 64, 96, False),
     (4, 1152, 520, 1152, True),
+    # beyond four rows the decode kernel stages X segment by segment, 2, 3 or 4
+    # chunks per lane: 7, 12 and 13 rows, with groups of one segment, of two, and
+    # one group per column
+    (12, 2048, 264, 128, False), (7, 4096, 200, 256, True), (13, 1024, 72, 1024, False),
 ]
 
 
