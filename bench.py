@@ -240,25 +240,30 @@ def bench_gemm_gate_up(name, M, steps, warmup):
 
 def bench_quantize(name, steps, warmup):
     """awq_quantize on a layer of the workload's shape: fp16 W -> packed codes,
-    scales, zero points.  Algorithmic bytes: W read once, the layer written."""
+    scales, zero points, cycling through enough copies of W (1 GiB) that every
+    call reads HBM.  Algorithmic bytes: W read once, the layer written."""
     import torch
     from w4a16_group_quantized_amd import binding, synth
     w = synth.WORKLOADS[name]
     rng = np.random.default_rng(w.wid)
-    W = torch.from_numpy((rng.standard_normal((w.K, w.N)) * 0.02).astype(np.float16)).cuda()
-    for _ in range(max(warmup, 1)):
-        binding.quantize(W, w.G, w.symmetric)
+    W0 = torch.from_numpy((rng.standard_normal((w.K, w.N)) * 0.02).astype(np.float16)).cuda()
+    copies = max(2, math.ceil(ROTATE_BYTES / (2 * w.K * w.N)))
+    Ws = [W0.clone() for _ in range(copies)]
+    for i in range(max(warmup, 1)):
+        binding.quantize(Ws[i % copies], w.G, w.symmetric)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(steps):
-        binding.quantize(W, w.G, w.symmetric)
+    for i in range(steps):
+        binding.quantize(Ws[i % copies], w.G, w.symmetric)
     e1.record()
     e1.synchronize()
     t = e0.elapsed_time(e1) * 1e-3 / steps
     b = 2 * w.K * w.N + alg_bytes(w, 0)
+    del Ws, W0
+    torch.cuda.empty_cache()
     return {"workload": name, "entry": "awq_quantize", "K": w.K, "N": w.N, "group_size": w.G,
-            "us_per_call": t * 1e6, "alg_bytes": b, "gbs": b / t / 1e9,
+            "w_copies": copies, "us_per_call": t * 1e6, "alg_bytes": b, "gbs": b / t / 1e9,
             "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS}
 
 

@@ -22,6 +22,8 @@
 // eight packed words of the chunk as two 16-byte stores.  Bound: HBM, 2 K N
 // bytes read, K N / 2 written.  WPG = 4 for layers with few (group, column)
 // tiles and long groups, so that those are read by enough lanes at once.
+// Groups of 64 to 256 rows are instead read once: the first pass takes the
+// second pass's packed rows and keeps them in registers.
 //
 // The extremes are taken on the fp16 values themselves (packed min / max,
 // exact).  rint(w / s) is decided from w * (1 / s): that product is within
@@ -51,7 +53,10 @@ __device__ __forceinline__ float rint_quotient(float w, float s, float inv) {
 // Columns of one column chunk, one chunk per eight lanes.
 constexpr int kRowLanes = 8;
 
-template <bool SYM, int WPG>
+// HOLD > 0 (one wave, G = 64 HOLD): the first pass already reads the packed
+// rows the second pass quantizes, p = r, r + 8, ..., and keeps them in
+// registers (HOLD x 8 chunks per lane), so the group is read once.
+template <bool SYM, int WPG, int HOLD = 0>
 __global__ void __launch_bounds__(64 * WPG)
 quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16_t *__restrict__ S,
                 uint32_t *__restrict__ QZ, int K, int N, int G, int tiles_n) {
@@ -83,16 +88,29 @@ quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16
             am2[i] = __builtin_elementwise_max(am2[i], as_half2(u[i] & 0x7FFF7FFFu));
         }
     };
+    static_assert(HOLD == 0 || WPG == 1, "held rows are for one wave per group");
+    uint4 hv[HOLD > 0 ? HOLD : 1][8];
     if (live) {
-        int k = rr;
-        for (; k + 7 * kStride < G; k += 8 * kStride) {
-            uint4 v[8];
+        if constexpr (HOLD > 0) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = load16(wg + (size_t)(k + u * kStride) * N);
+            for (int h = 0; h < HOLD; ++h)
 #pragma unroll
-            for (int u = 0; u < 8; ++u) take(v[u]);
+                for (int j = 0; j < 8; ++j) hv[h][j] = load16(wg + (size_t)(8 * (r + 8 * h) + j) * N);
+#pragma unroll
+            for (int h = 0; h < HOLD; ++h)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) take(hv[h][j]);
+        } else {
+            int k = rr;
+            for (; k + 7 * kStride < G; k += 8 * kStride) {
+                uint4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = load16(wg + (size_t)(k + u * kStride) * N);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) take(v[u]);
+            }
+            for (; k < G; k += kStride) take(load16(wg + (size_t)k * N));
         }
-        for (; k < G; k += kStride) take(load16(wg + (size_t)k * N));
     }
     // The chunk's eight row lanes are lanes 8 c .. 8 c + 7 of each wave.
     auto hmin = [](uint32_t a, uint32_t b) { return as_u32(__builtin_elementwise_min(as_half2(a), as_half2(b))); };
@@ -158,10 +176,8 @@ quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16
         if (!SYM) QZ[(size_t)g * (N / 8) + n / 8] = zword;
     }
 
-    for (int p = rr; p < G / 8; p += kStride) {
-        uint4 v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = load16(wg + (size_t)(8 * p + j) * N);
+    // Codes of packed row p (its eight rows in v) as the chunk's eight words.
+    auto emit = [&](int p, const uint4 (&v)[8]) {
         // Value of column i in row j of the packed row.
         auto wat = [&](int j, int i) {
             const uint32_t u = i < 2 ? v[j].x : i < 4 ? v[j].y : i < 6 ? v[j].z : v[j].w;
@@ -176,20 +192,31 @@ quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16
         uint32_t *qrow = Q + (size_t)(g * (G / 8) + p) * N + n;
         reinterpret_cast<uint4 *>(qrow)[0] = make_uint4(word[0], word[1], word[2], word[3]);
         reinterpret_cast<uint4 *>(qrow)[1] = make_uint4(word[4], word[5], word[6], word[7]);
+    };
+    if constexpr (HOLD > 0) {
+#pragma unroll
+        for (int h = 0; h < HOLD; ++h) emit(r + 8 * h, hv[h]);
+    } else {
+        for (int p = rr; p < G / 8; p += kStride) {
+            uint4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = load16(wg + (size_t)(8 * p + j) * N);
+            emit(p, v);
+        }
     }
 }
 
 }  // namespace
 
-template <int WPG>
+template <int WPG, int HOLD = 0>
 hipError_t launch_q(const uint16_t *w, uint32_t *q, uint16_t *scales, uint32_t *z, int K, int N, int G,
                     int tiles_n, long long blocks, bool symmetric, hipStream_t s) {
     if (symmetric)
-        hipLaunchKernelGGL((quantize_kernel<true, WPG>), dim3((unsigned)blocks), dim3(64 * WPG), 0, s, w,
-                           q, scales, z, K, N, G, tiles_n);
+        hipLaunchKernelGGL((quantize_kernel<true, WPG, HOLD>), dim3((unsigned)blocks), dim3(64 * WPG), 0,
+                           s, w, q, scales, z, K, N, G, tiles_n);
     else
-        hipLaunchKernelGGL((quantize_kernel<false, WPG>), dim3((unsigned)blocks), dim3(64 * WPG), 0, s,
-                           w, q, scales, z, K, N, G, tiles_n);
+        hipLaunchKernelGGL((quantize_kernel<false, WPG, HOLD>), dim3((unsigned)blocks), dim3(64 * WPG), 0,
+                           s, w, q, scales, z, K, N, G, tiles_n);
     return hipGetLastError();
 }
 
@@ -202,6 +229,10 @@ hipError_t launch_quantize(const uint16_t *w, int32_t *qweight, uint16_t *scales
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     auto *q = reinterpret_cast<uint32_t *>(qweight);
     auto *z = reinterpret_cast<uint32_t *>(qzeros);
+    // Groups of 64, 128 or 256 rows: read once, held in registers between the passes.
+    if (G == 64) return launch_q<1, 1>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
+    if (G == 128) return launch_q<1, 2>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
+    if (G == 256) return launch_q<1, 4>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
     if (blocks >= 4096 || G < 1024) return launch_q<1>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
     return launch_q<4>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
 }
