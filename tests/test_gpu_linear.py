@@ -152,6 +152,29 @@ def test_deterministic_and_power_of_two(entry, name):
     assert torch.equal((y1.float() * 2).half()[normal].view(torch.int16), y3[normal].view(torch.int16))
 
 
+SCALE_CASES = [(1, 4096, 264, 128, False), (16, 1024, 136, 128, True), (5, 2048, 200, 2048, False)]
+
+
+@pytest.mark.parametrize("entry,M,K,N,G,sym",
+                         [("gemv",) + c for c in SCALE_CASES] +
+                         [("gemm",) + c for c in SCALE_CASES + [(300, 1024, 264, 1024, True)]])
+def test_doubling_scales_doubles_y(entry, M, K, N, G, sym):
+    """Every scale times 2 (exponent + 1, exact) doubles Y bit for bit: in the
+    exact dequantization fp16(2 s (q - z)) = 2 fp16(s (q - z)), in the folded
+    decode path and in the one-group GEMM the scale multiplies an fp32 sum, and
+    fp32 and fp16 rounding commute with doubling away from the subnormals."""
+    X, codes, zeros, scales = random_case(4400 + M + K + G, M, K, N, G, sym)
+    X = X.copy()
+    X[np.abs(X.view(np.float16).astype(np.float64)) < 2.0 ** -9] = 0   # see the test above
+    xd = to_dev(X)
+    y1 = ENTRY[entry](xd, device_case(codes, zeros, scales, G))
+    y2 = ENTRY[entry](xd, device_case(codes, zeros, (scales + 0x0400).astype(np.uint16), G))
+    torch.cuda.synchronize()
+    normal = y1.float().abs() >= 2.0 ** -13
+    assert normal.float().mean().item() > 0.99
+    assert torch.equal((y1.float() * 2).half()[normal].view(torch.int16), y2[normal].view(torch.int16))
+
+
 def test_gemv_equals_gemm_on_decode_shape():
     """Both entry points compute the same layer (within the bar of each other)."""
     X, _, _, _ = workload_host("gate_up_m16")
