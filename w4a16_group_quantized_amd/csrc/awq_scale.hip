@@ -232,11 +232,27 @@ dense_gemm_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W
 __global__ void __launch_bounds__(256)
 sqerr_kernel(const float *__restrict__ Yref, const uint16_t *__restrict__ Yhat, long long count,
              double *__restrict__ partial) {
+    // Eight outputs per lane and iteration (count = M N is a multiple of 8, both
+    // arrays 16-byte aligned): two 16-byte loads of Yref and one of Yhat.
     __shared__ double sh[256];
     double acc = 0.0;
-    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < count; i += (long long)gridDim.x * 256) {
-        const double d = (double)Yref[i] - (double)(float)as_half(Yhat[i]);
-        acc += d * d;
+    const long long n8 = count / 8;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 *yr = reinterpret_cast<const f32x4 *>(Yref);
+    const u32x4 *yh = reinterpret_cast<const u32x4 *>(Yhat);
+    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n8; i += (long long)gridDim.x * 256) {
+        const f32x4 a = __builtin_nontemporal_load(yr + 2 * i);
+        const f32x4 b = __builtin_nontemporal_load(yr + 2 * i + 1);
+        const u32x4 h = __builtin_nontemporal_load(yh + i);
+        float f[8];
+        halves8(make_uint4(h.x, h.y, h.z, h.w), f);
+        const float r[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double d = (double)r[e] - (double)f[e];
+            acc += d * d;
+        }
     }
     const double s = block_sum(acc, sh);
     if (threadIdx.x == 0) partial[blockIdx.x] = s;
