@@ -17,6 +17,11 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
                        hipStream_t s);
 hipError_t launch_quantize(const uint16_t *w, int32_t *qweight, uint16_t *scales, int32_t *qzeros,
                            int K, int N, int G, bool symmetric, hipStream_t s);
+// The same for W'(k, n) = fp16(c[k] w(k, n)), formed as the rows are read
+// (c: device fp32 [K]); no W' is written.
+hipError_t launch_quantize_migrated(const uint16_t *w, const float *c, int32_t *qweight,
+                                    uint16_t *scales, int32_t *qzeros, int K, int N, int G,
+                                    bool symmetric, hipStream_t s);
 // Fused gate/up (layer columns [gate | up], h = fp16(SiLU(gate) * up)).
 bool gemv_gate_up_supported(int M, int K, int N, int G);
 hipError_t launch_gemv_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,

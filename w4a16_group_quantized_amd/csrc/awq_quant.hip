@@ -56,10 +56,13 @@ constexpr int kRowLanes = 8;
 // HOLD > 0 (one wave, G = 64 HOLD): the first pass already reads the packed
 // rows the second pass quantizes, p = r, r + 8, ..., and keeps them in
 // registers (HOLD x 8 chunks per lane), so the group is read once.
-template <bool SYM, int WPG, int HOLD = 0>
+// MIG: the layer quantized is W'(k, n) = fp16(c[k] w(k, n)) (fp32 product,
+// one rounding), formed from each row as it is loaded; c: fp32 [K].
+template <bool SYM, int WPG, int HOLD = 0, bool MIG = false>
 __global__ void __launch_bounds__(64 * WPG)
 quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16_t *__restrict__ S,
-                uint32_t *__restrict__ QZ, int K, int N, int G, int tiles_n) {
+                uint32_t *__restrict__ QZ, int K, int N, int G, int tiles_n,
+                const float *__restrict__ c_rows) {
     constexpr int kStride = kRowLanes * WPG;     // rows between a lane's consecutive rows
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -69,6 +72,22 @@ quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16
     const int n = (blockIdx.x % tiles_n) * 64 + 8 * c;
     const bool live = n < N;                     // N % 8 == 0: a chunk is all in or all out
     const uint16_t *wg = W + (size_t)g * G * N + (live ? n : 0);
+    // The 8 columns of row k of the group (migrated when MIG).
+    auto row8 = [&](int k) {
+        uint4 v = load16(wg + (size_t)k * N);
+        if constexpr (MIG) {
+            const float ck = c_rows[(size_t)g * G + k];
+            uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = ck * (float)as_half((uint16_t)u[i]);
+                const float hi = ck * (float)as_half((uint16_t)(u[i] >> 16));
+                u[i] = (uint32_t)as_u16((half_t)lo) | ((uint32_t)as_u16((half_t)hi) << 16);
+            }
+            v = make_uint4(u[0], u[1], u[2], u[3]);
+        }
+        return v;
+    };
 
     // Column pairs (2 i, 2 i + 1) as half2: minimum, maximum, maximum of |w|.
     half2_t lo2[4], hi2[4], am2[4];
@@ -95,7 +114,7 @@ quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16
 #pragma unroll
             for (int h = 0; h < HOLD; ++h)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) hv[h][j] = load16(wg + (size_t)(8 * (r + 8 * h) + j) * N);
+                for (int j = 0; j < 8; ++j) hv[h][j] = row8(8 * (r + 8 * h) + j);
 #pragma unroll
             for (int h = 0; h < HOLD; ++h)
 #pragma unroll
@@ -105,11 +124,11 @@ quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16
             for (; k + 7 * kStride < G; k += 8 * kStride) {
                 uint4 v[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = load16(wg + (size_t)(k + u * kStride) * N);
+                for (int u = 0; u < 8; ++u) v[u] = row8(k + u * kStride);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) take(v[u]);
             }
-            for (; k < G; k += kStride) take(load16(wg + (size_t)k * N));
+            for (; k < G; k += kStride) take(row8(k));
         }
     }
     // The chunk's eight row lanes are lanes 8 c .. 8 c + 7 of each wave.
@@ -200,7 +219,7 @@ quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16
         for (int p = rr; p < G / 8; p += kStride) {
             uint4 v[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = load16(wg + (size_t)(8 * p + j) * N);
+            for (int j = 0; j < 8; ++j) v[j] = row8(8 * p + j);
             emit(p, v);
         }
     }
@@ -208,33 +227,46 @@ quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16
 
 }  // namespace
 
-template <int WPG, int HOLD = 0>
-hipError_t launch_q(const uint16_t *w, uint32_t *q, uint16_t *scales, uint32_t *z, int K, int N, int G,
-                    int tiles_n, long long blocks, bool symmetric, hipStream_t s) {
+template <int WPG, int HOLD, bool MIG>
+hipError_t launch_q(const uint16_t *w, const float *c, uint32_t *q, uint16_t *scales, uint32_t *z, int K,
+                    int N, int G, int tiles_n, long long blocks, bool symmetric, hipStream_t s) {
     if (symmetric)
-        hipLaunchKernelGGL((quantize_kernel<true, WPG, HOLD>), dim3((unsigned)blocks), dim3(64 * WPG), 0,
-                           s, w, q, scales, z, K, N, G, tiles_n);
+        hipLaunchKernelGGL((quantize_kernel<true, WPG, HOLD, MIG>), dim3((unsigned)blocks), dim3(64 * WPG),
+                           0, s, w, q, scales, z, K, N, G, tiles_n, c);
     else
-        hipLaunchKernelGGL((quantize_kernel<false, WPG, HOLD>), dim3((unsigned)blocks), dim3(64 * WPG), 0,
-                           s, w, q, scales, z, K, N, G, tiles_n);
+        hipLaunchKernelGGL((quantize_kernel<false, WPG, HOLD, MIG>), dim3((unsigned)blocks), dim3(64 * WPG),
+                           0, s, w, q, scales, z, K, N, G, tiles_n, c);
     return hipGetLastError();
 }
 
-// One wave per (group, 64 columns); four for long groups (1024 rows or more)
-// when there are too few tiles to fill the GPU several times over.
-hipError_t launch_quantize(const uint16_t *w, int32_t *qweight, uint16_t *scales, int32_t *qzeros,
-                           int K, int N, int G, bool symmetric, hipStream_t s) {
+template <bool MIG>
+hipError_t launch_quantize_any(const uint16_t *w, const float *c, int32_t *qweight, uint16_t *scales,
+                               int32_t *qzeros, int K, int N, int G, bool symmetric, hipStream_t s) {
     const int tiles_n = (N + 63) / 64;
     const long long blocks = (long long)(K / G) * tiles_n;
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     auto *q = reinterpret_cast<uint32_t *>(qweight);
     auto *z = reinterpret_cast<uint32_t *>(qzeros);
     // Groups of 64, 128 or 256 rows: read once, held in registers between the passes.
-    if (G == 64) return launch_q<1, 1>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
-    if (G == 128) return launch_q<1, 2>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
-    if (G == 256) return launch_q<1, 4>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
-    if (blocks >= 4096 || G < 1024) return launch_q<1>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
-    return launch_q<4>(w, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
+    if (G == 64) return launch_q<1, 1, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
+    if (G == 128) return launch_q<1, 2, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
+    if (G == 256) return launch_q<1, 4, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
+    // One wave per (group, 64 columns); four for long groups (1024 rows or more)
+    // when there are too few tiles to fill the GPU several times over.
+    if (blocks >= 4096 || G < 1024)
+        return launch_q<1, 0, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
+    return launch_q<4, 0, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
+}
+
+hipError_t launch_quantize(const uint16_t *w, int32_t *qweight, uint16_t *scales, int32_t *qzeros,
+                           int K, int N, int G, bool symmetric, hipStream_t s) {
+    return launch_quantize_any<false>(w, nullptr, qweight, scales, qzeros, K, N, G, symmetric, s);
+}
+
+hipError_t launch_quantize_migrated(const uint16_t *w, const float *c, int32_t *qweight,
+                                    uint16_t *scales, int32_t *qzeros, int K, int N, int G,
+                                    bool symmetric, hipStream_t s) {
+    return launch_quantize_any<true>(w, c, qweight, scales, qzeros, K, N, G, symmetric, s);
 }
 
 }  // namespace awq

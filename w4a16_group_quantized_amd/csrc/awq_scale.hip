@@ -18,7 +18,8 @@
 // All reductions run in a fixed order (fp64 partial sums), so a loss is the
 // same bits on every run.  The search is calibration work, done once per layer:
 // the kernels here are plain, and the time goes to the quantizer and the fused
-// GEMM of each candidate, which are the layer's own kernels.
+// GEMM of each candidate, which are the layer's own kernels.  The quantizer
+// forms fp16(c W) row by row as it reads W, so no migrated weight is written.
 #include "awq_device.h"
 #include "awq_internal.h"
 
@@ -158,21 +159,6 @@ __global__ void migrate_x_kernel(const uint16_t *__restrict__ X, const float *__
     }
 }
 
-// W'(k, n) = fp16(c[k] * w), 8 values per thread.
-__global__ void migrate_w_kernel(const uint16_t *__restrict__ W, const float *__restrict__ c, int K,
-                                 int N, uint16_t *__restrict__ Ws) {
-    const long long total = (long long)K * N / 8;
-    for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
-         t += (long long)gridDim.x * blockDim.x) {
-        const float ck = c[(int)(t * 8 / N)];
-        float f[8];
-        halves8(reinterpret_cast<const uint4 *>(W)[t], f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = ck * f[i];
-        reinterpret_cast<uint4 *>(Ws)[t] = pack8(f);
-    }
-}
-
 // The fp16 layer's output y = X W in fp32, for the reference: a plain 64 x 64
 // tile per workgroup (a 1-D grid, tile rows minor), 32-k steps staged in LDS (W transposed to [n][k] so that
 // a lane's B operand, 8 k of one column, is one 16-byte read), four waves of
@@ -293,7 +279,7 @@ argmin_kernel(const double *__restrict__ losses, int n, Alphas alphas, const flo
 
 // Workspace regions, each 256-byte aligned.
 struct Layout {
-    size_t act, amax, xbar, wbar, c, xs, ws, q, s, qz, yref, yhat, loss, total;
+    size_t act, amax, xbar, wbar, c, xs, q, s, qz, yref, yhat, loss, total;
 };
 
 inline size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -314,7 +300,6 @@ Layout layout(int M, int K, int N, int G, bool search) {
         L.wbar = take((size_t)K * sizeof(float));
         L.c = take((size_t)K * sizeof(float));
         L.xs = take((size_t)M * K * 2);
-        L.ws = take((size_t)K * N * 2);
         L.q = take((size_t)K / 8 * N * 4);
         L.s = take((size_t)(K / G) * N * 2);
         L.qz = take((size_t)(K / G) * (N / 8) * 4);
@@ -372,7 +357,6 @@ hipError_t launch_scale_search(const uint16_t *x, int M, const uint16_t *w, int 
     auto *wbar = reinterpret_cast<float *>(ws + L.wbar);
     auto *c = reinterpret_cast<float *>(ws + L.c);
     auto *xs = reinterpret_cast<uint16_t *>(ws + L.xs);
-    auto *wsc = reinterpret_cast<uint16_t *>(ws + L.ws);
     auto *q = reinterpret_cast<int32_t *>(ws + L.q);
     auto *sc = reinterpret_cast<uint16_t *>(ws + L.s);
     auto *qz = symmetric ? nullptr : reinterpret_cast<int32_t *>(ws + L.qz);
@@ -391,10 +375,10 @@ hipError_t launch_scale_search(const uint16_t *x, int M, const uint16_t *w, int 
                            alphas[i], c);
         hipLaunchKernelGGL(migrate_x_kernel, dim3(grid_for((long long)M * K / 8, 256)), dim3(256), 0,
                            s, x, c, M, K, xs);
-        hipLaunchKernelGGL(migrate_w_kernel, dim3(grid_for((long long)K * N / 8, 256)), dim3(256), 0,
-                           s, w, c, K, N, wsc);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_quantize(wsc, q, sc, qz, K, N, G, symmetric, s)) != hipSuccess) return e;
+        // the migrated weight fp16(c W) is formed row by row inside the quantizer
+        if ((e = launch_quantize_migrated(w, c, q, sc, qz, K, N, G, symmetric, s)) != hipSuccess)
+            return e;
         if ((e = launch_gemm(xs, q, sc, qz, yhat, M, K, N, G, s)) != hipSuccess) return e;
         hipLaunchKernelGGL(sqerr_kernel, dim3(kLossBlocks), dim3(256), 0, s, yref, yhat, mn, part);
         hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, s, part, kLossBlocks, mn,
