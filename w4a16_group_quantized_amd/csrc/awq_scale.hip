@@ -159,57 +159,101 @@ __global__ void migrate_x_kernel(const uint16_t *__restrict__ X, const float *__
     }
 }
 
-// The fp16 layer's output y = X W in fp32, for the reference: a plain 64 x 64
-// tile per workgroup (a 1-D grid, tile rows minor), 32-k steps staged in LDS (W transposed to [n][k] so that
-// a lane's B operand, 8 k of one column, is one 16-byte read), four waves of
-// one 32 x 32 v_mfma_f32_32x32x16_f16 tile each.  Rows past M, columns past N
-// and k past K load zeros and are not stored.
-constexpr int kDT = 64, kDK = 32, kDPad = kDK + 8;   // row stride 40 halves: 80 bytes
+// The fp16 layer's output y = X W in fp32, for the reference: a 128 x 128 tile
+// per workgroup (a 1-D grid, tile rows minor), four waves of 2 x 2
+// v_mfma_f32_32x32x16_f16 tiles each, 32-k steps through a two-slot LDS ring
+// (the next step's loads are in flight during the MFMAs; one barrier a step).
+// W is stored transposed, [n][k], so that a lane's B operand (8 k of one
+// column) is one 16-byte read: each lane loads 8 consecutive k of one column
+// (2-byte loads, coalesced along n across the lanes) and writes them as one
+// 16-byte chunk.  Rows past M, columns past N and k past K load zeros and are
+// not stored.
+constexpr int kDT = 128, kDK = 32, kDPad = kDK + 8;   // row stride 40 halves: 80 bytes
 
 __global__ void __launch_bounds__(256)
 dense_gemm_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, int M, int K,
                   int N, float *__restrict__ Y) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[kDT][kDPad];
-    __shared__ __attribute__((aligned(16))) uint16_t Bt[kDT][kDPad];
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kDT][kDPad];
+    __shared__ __attribute__((aligned(16))) uint16_t Bt[2][kDT][kDPad];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int tiles_m = (M + kDT - 1) / kDT;
     const int m0 = (int)(blockIdx.x % tiles_m) * kDT, n0 = (int)(blockIdx.x / tiles_m) * kDT;
-    const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);
-    const int ar = t >> 2, akc = (t & 3) * 8;   // X chunk: row, k offset
-    const int bk = t >> 3, bnc = (t & 7) * 8;   // W chunk: k row, column offset
-    float16_t acc;
+    const int wr = 64 * (wave >> 1), wc = 64 * (wave & 1);
+    // Chunk i (0, 1) of this thread: X row c / 4, k offset 8 (c % 4); W column
+    // c % 128, k octet c / 128; with c = t + 256 i.
+    uint4 ra[2], rb[2];
+    auto gload = [&](int k0) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-    for (int k0 = 0; k0 < K; k0 += kDK) {
-        uint4 av = make_uint4(0, 0, 0, 0), bv = make_uint4(0, 0, 0, 0);
-        if (m0 + ar < M && k0 + akc < K)
-            av = *reinterpret_cast<const uint4 *>(X + (size_t)(m0 + ar) * K + k0 + akc);
-        if (k0 + bk < K && n0 + bnc < N)
-            bv = *reinterpret_cast<const uint4 *>(W + (size_t)(k0 + bk) * N + n0 + bnc);
-        *reinterpret_cast<uint4 *>(&As[ar][akc]) = av;
-        const uint32_t bu[4] = {bv.x, bv.y, bv.z, bv.w};
+        for (int i = 0; i < 2; ++i) {
+            const int c = t + 256 * i;
+            const int row = c >> 2, kc = (c & 3) * 8;
+            ra[i] = (m0 + row < M && k0 + kc < K)
+                        ? *reinterpret_cast<const uint4 *>(X + (size_t)(m0 + row) * K + k0 + kc)
+                        : make_uint4(0u, 0u, 0u, 0u);
+            const int n = c & (kDT - 1), k8 = k0 + 8 * (c >> 7);
+            uint32_t h[4] = {0u, 0u, 0u, 0u};
+            if (k8 < K && n0 + n < N) {
+                const uint16_t *wp = W + (size_t)k8 * N + n0 + n;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            Bt[bnc + 2 * i][bk] = (uint16_t)bu[i];
-            Bt[bnc + 2 * i + 1][bk] = (uint16_t)(bu[i] >> 16);
+                for (int e = 0; e < 8; ++e) h[e / 2] |= (uint32_t)wp[(size_t)e * N] << (16 * (e % 2));
+            }
+            rb[i] = make_uint4(h[0], h[1], h[2], h[3]);
         }
-        __syncthreads();
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = t + 256 * i;
+            *reinterpret_cast<uint4 *>(&As[buf][c >> 2][(c & 3) * 8]) = ra[i];
+            *reinterpret_cast<uint4 *>(&Bt[buf][c & (kDT - 1)][8 * (c >> 7)]) = rb[i];
+        }
+    };
+    float16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = 0; k0 < K; k0 += kDK) {
+        const bool more = k0 + kDK < K;
+        if (more) gload(k0 + kDK);
 #pragma unroll
         for (int kk = 0; kk < kDK; kk += 16) {
             const int kl = kk + 8 * (lane >> 5);
-            const half8_t a = as_half8(*reinterpret_cast<const uint4 *>(&As[wr + (lane & 31)][kl]));
-            const half8_t b = as_half8(*reinterpret_cast<const uint4 *>(&Bt[wc + (lane & 31)][kl]));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+            half8_t a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                a[i] = as_half8(*reinterpret_cast<const uint4 *>(&As[buf][wr + 32 * i + (lane & 31)][kl]));
+                b[i] = as_half8(*reinterpret_cast<const uint4 *>(&Bt[buf][wc + 32 * i + (lane & 31)][kl]));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
+        // The other slot was last read in the previous step, before its barrier.
+        if (more) sstore(buf ^ 1);
         __syncthreads();
+        buf ^= 1;
     }
     // C layout: lane (h, j) holds in register v row 8 (v / 4) + 4 h + v % 4 of column j.
-    const int col = n0 + wc + (lane & 31);
-    if (col >= N) return;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wr + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
-        if (row < M) Y[(size_t)row * N + col] = acc[v];
+    for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wc + 32 * j + (lane & 31);
+        if (col >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + wr + 32 * i + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+                if (row < M) Y[(size_t)row * N + col] = acc[i][j][v];
+            }
     }
 }
 
