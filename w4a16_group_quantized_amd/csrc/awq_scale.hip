@@ -150,11 +150,14 @@ __global__ void migrate_x_kernel(const uint16_t *__restrict__ X, const float *__
     const long long total = (long long)M * K / 8;
     for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
          t += (long long)gridDim.x * blockDim.x) {
-        const int k0 = (int)((t * 8) % K);
+        const int k0 = (int)((t * 8) % K);   // a multiple of 8: c + k0 is 32-byte aligned
+        const float4 c0 = reinterpret_cast<const float4 *>(c + k0)[0];
+        const float4 c1 = reinterpret_cast<const float4 *>(c + k0)[1];
+        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
         float f[8];
         halves8(reinterpret_cast<const uint4 *>(X)[t], f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = f[i] / c[k0 + i];
+        for (int i = 0; i < 8; ++i) f[i] = f[i] / cv[i];
         reinterpret_cast<uint4 *>(Xs)[t] = pack8(f);
     }
 }
