@@ -8,13 +8,18 @@
 // weight is loaded and dequantized by exactly one wave, straight into the
 // registers of an MFMA B operand (a packed word is 8 k of one column: one
 // lane's B operand).  Dequantization is exact: w = fp16_rne(s (q - z)), the
-// same bits awq_dequant writes.  X is the shared operand: each K step loads the
+// same bits awq_dequant writes; on one-group layers (G = K) the B operand is
+// q - z and each column's scale multiplies its fp32 sums once, in the epilogue.
+// X is the shared operand: each K step loads the
 // BM x BK slice of X once per workgroup into LDS, XOR-swizzled per row, and all
 // four waves read their A operands from there.
 //
 // Two kernels:
 //   m32::mfma32_kernel (G a multiple of 32 and K of 128): v_mfma_f32_32x32x16,
-//     a four-step ring of direct-to-LDS loads, 128- or 256-row tiles;
+//     a four-step ring of direct-to-LDS loads, 128- or 256-row tiles; also
+//     the split-K mode (fp32 partial tiles per K slice, then
+//     splitk_reduce_kernel adds the slices in order) and the fused gate/up
+//     epilogue;
 //   gemm_kernel (every other shape): v_mfma_f32_16x16x32, packed words loaded
 //     into registers, clamped addresses and the weights of k past K zeroed.
 //
