@@ -488,7 +488,20 @@ def cpu_baseline(name, budget_s=10.0):
     per = el / runs
     return {"value": alg_bytes(w, w.M) / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{runs} full passes of the {name} layer (M={w.M} K={w.K} N={w.N}), "
-                      f"unpack + exact dequant + fp64 matmul, {per:.2f} s each"}
+                      f"unpack + exact dequant + fp64 matmul, {per:.2f} s each",
+            "host": {"cpu": host_cpu_model(), "nproc": os.cpu_count()}}
+
+
+def host_cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def profile_run(kind):
