@@ -1,0 +1,79 @@
+"""The largest layer the C ABI takes: K * N just below 2^31 elements.
+
+K = 8192 and N = 262136 give K N = 2,147,418,112 (a 1.07 GB packed weight, a
+4.3 GB dequantized one), so every index and byte offset the kernels form on
+this layer sits near the top of its range: 32-bit buffer sizes, per-step
+offsets, and the dequantized output's 64-bit addressing.  The packed words, the
+scales and the zero points are seeded host draws (uniform words, scales in
+[0.001, 0.01]); the oracle takes the same host arrays, restricted to seeded
+blocks of 8 columns across the whole width (always the first and the last),
+and computes those columns.  Rows of X come from the synthetic generator.
+Each kernel variant the shapes select is covered: the decode kernel (1 row),
+the fold kernel (16 rows: X does not fit LDS at K = 8192), the GEMM, split K
+and the exact dequantization.
+"""
+import numpy as np
+import pytest
+import torch
+
+from parity import assert_y_close, to_dev, to_host_bits
+from w4a16_group_quantized_amd import binding, synth
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+K, N, G = 8192, 262136, 128
+
+
+@pytest.fixture(scope="module")
+def big():
+    rng = np.random.default_rng(20261203)
+    Q = rng.integers(0, 1 << 32, size=(K // 8, N), dtype=np.uint32).view(np.int32)
+    S = rng.uniform(0.001, 0.01, size=(K // G, N)).astype(np.float16).view(np.uint16)
+    QZ = rng.integers(0, 1 << 32, size=(K // G, N // 8), dtype=np.uint32).view(np.int32)
+    layer = binding.Layer(torch.from_numpy(Q).cuda(), torch.from_numpy(S.view(np.float16)).cuda(),
+                          torch.from_numpy(QZ).cuda(), K, N, G)
+    blocks = np.array(sorted({0, N // 8 - 1} | set(rng.choice(N // 8, 30, replace=False).tolist())))
+    cols = (8 * blocks[:, None] + np.arange(8)[None, :]).reshape(-1)
+    sampled = (np.ascontiguousarray(Q[:, cols]), np.ascontiguousarray(S[:, cols]),
+               np.ascontiguousarray(QZ[:, blocks]))
+    yield layer, cols, sampled
+    del layer
+    torch.cuda.empty_cache()
+
+
+def _oracle_y(X, sampled):
+    Qs, Ss, QZs = sampled
+    return oracle.load().linear(X, Qs, Ss, QZs, G)[1]
+
+
+@pytest.mark.parametrize("entry,M", [("gemv", 1), ("gemv", 16), ("gemm", 64)])
+def test_largest_layer(big, entry, M):
+    layer, cols, sampled = big
+    X = synth.make_x(M, K, 500 + M)
+    fn = binding.gemv if entry == "gemv" else binding.gemm
+    y = fn(to_dev(X), layer)
+    torch.cuda.synchronize()
+    got = to_host_bits(y[:, torch.from_numpy(cols).cuda()])
+    assert_y_close(got, _oracle_y(X, sampled), f"{entry} M={M} on the largest layer")
+
+
+def test_largest_layer_splitk(big):
+    layer, cols, sampled = big
+    X = synth.make_x(64, K, 601)
+    y = binding.gemm_splitk(to_dev(X), layer, 4)
+    torch.cuda.synchronize()
+    got = to_host_bits(y[:, torch.from_numpy(cols).cuda()])
+    assert_y_close(got, _oracle_y(X, sampled), "split K on the largest layer")
+
+
+def test_largest_layer_dequant(big):
+    layer, cols, sampled = big
+    W = binding.dequant(layer)                                     # 4.3 GB of fp16
+    torch.cuda.synchronize()
+    got = to_host_bits(W[:, torch.from_numpy(cols).cuda()])
+    del W
+    torch.cuda.empty_cache()
+    Qs, Ss, QZs = sampled
+    assert np.array_equal(got, oracle.load().dequant(Qs, Ss, QZs, G))
