@@ -10,7 +10,8 @@ blocks of 8 columns across the whole width (always the first and the last),
 and computes those columns.  Rows of X come from the synthetic generator.
 Each kernel variant the shapes select is covered: the decode kernel (1 row),
 the fold kernel (16 rows: X does not fit LDS at K = 8192), the GEMM, split K
-and the exact dequantization.
+and the exact dequantization.  A last case takes the largest batch instead:
+M K just below 2^31, a 4.3 GB X through the GEMM.
 """
 import numpy as np
 import pytest
@@ -77,3 +78,31 @@ def test_largest_layer_dequant(big):
     torch.cuda.empty_cache()
     Qs, Ss, QZs = sampled
     assert np.array_equal(got, oracle.load().dequant(Qs, Ss, QZs, G))
+
+
+def test_largest_batch_gemm():
+    """M K just below 2^31 (M = 524287 rows at K = 4096: a 4.3 GB X): the GEMM's
+    X addressing at the top of its 32-bit byte range.  X is a seeded block of 997
+    rows tiled down the batch (997 is prime, so a wrong row offset lands on a
+    different row unless it is a multiple of 997); the oracle computes the first,
+    the last and seeded rows."""
+    Kb, Nb, Gb = 4096, 64, 128
+    M = (2**31 - 1) // Kb
+    _, codes, zeros, scales = synth.workload_inputs(synth.WORKLOADS["decode_8b_gate"])
+    codes, zeros, scales = codes[:, :Nb].copy(), zeros[:, :Nb].copy(), scales[:, :Nb].copy()
+    block = synth.make_x(997, Kb, 4242)
+    X = np.tile(block, (M // 997 + 1, 1))[:M]
+    layer = binding.make_layer(to_dev(codes), to_dev(zeros), to_dev(scales), Gb)
+    x = to_dev(X)
+    del X
+    y = binding.gemm(x, layer)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 1, M - 2, M - 1} |
+                           set(np.random.default_rng(7).choice(M, 60, replace=False).tolist())))
+    got = to_host_bits(y[torch.from_numpy(rows).cuda()])
+    del x, y
+    torch.cuda.empty_cache()
+    o = oracle.load()
+    Xr = np.ascontiguousarray(block[rows % 997])
+    want = o.linear(Xr, o.pack(codes), scales, o.pack_zeros(zeros), Gb)[1]
+    assert_y_close(got, want, "gemm on the largest batch")
