@@ -10,8 +10,9 @@ blocks of 8 columns across the whole width (always the first and the last),
 and computes those columns.  Rows of X come from the synthetic generator.
 Each kernel variant the shapes select is covered: the decode kernel (1 row),
 the fold kernel (16 rows: X does not fit LDS at K = 8192), the GEMM, split K
-and the exact dequantization.  A last case takes the largest batch instead:
-M K just below 2^31, a 4.3 GB X through the GEMM.
+and the exact dequantization.  Two more cases take the largest batch (M K just
+below 2^31, a 4.3 GB X through the GEMM) and the largest fp16 W through the
+quantizer.
 """
 import numpy as np
 import pytest
@@ -106,3 +107,31 @@ def test_largest_batch_gemm():
     Xr = np.ascontiguousarray(block[rows % 997])
     want = o.linear(Xr, o.pack(codes), scales, o.pack_zeros(zeros), Gb)[1]
     assert_y_close(got, want, "gemm on the largest batch")
+
+
+@pytest.mark.parametrize("sym", [False, True])
+def test_largest_layer_quantize(sym):
+    """awq_quantize on a 4.3 GB fp16 W (K N just below 2^31): a seeded block of
+    1009 columns (prime, as above) tiled across the width, W ~ N(0, 0.02); the
+    codes, scales and zero points of sampled column blocks are the oracle's bit
+    for bit."""
+    rng = np.random.default_rng(1009 + sym)
+    block = (rng.standard_normal((K, 1009)) * 0.02).astype(np.float16)
+    blocks = np.array(sorted({0, N // 8 - 1} | set(rng.choice(N // 8, 30, replace=False).tolist())))
+    cols = (8 * blocks[:, None] + np.arange(8)[None, :]).reshape(-1)
+    w = torch.from_numpy(np.tile(block, (1, N // 1009 + 1))[:, :N].copy()).cuda()
+    layer = binding.quantize(w, G, sym)
+    torch.cuda.synchronize()
+    del w
+    ci = torch.from_numpy(cols).cuda()
+    q = layer.qweight[:, ci].cpu().numpy()
+    s = to_host_bits(layer.scales[:, ci])
+    z = None if sym else layer.qzeros[:, torch.from_numpy(blocks).cuda()].cpu().numpy()
+    del layer
+    torch.cuda.empty_cache()
+    o = oracle.load()
+    codes, S, Z = o.quantize(np.ascontiguousarray(block[:, cols % 1009]).view(np.uint16), G, sym)
+    assert np.array_equal(q, o.pack(codes))
+    assert np.array_equal(s, S)
+    if not sym:
+        assert np.array_equal(z, o.pack_zeros(Z))
