@@ -752,6 +752,18 @@ hipError_t launch_stream_x(const uint16_t *x, const int32_t *qw, const uint16_t 
     return launch_stream_sg<WPL, NW, SEGR, D, VR, kStageChunks>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
+// Compute units of the current device (queried once per process).
+inline int device_cus() {
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return 256;
+        return n;
+    }();
+    return cus;
+}
+
 // Beyond four rows (all four C rows of a lane live), X staged progressively:
 // XS = ceil(M * 16 / 64) chunks per lane per 16-row segment.
 template <int WPL, int NW, int D, bool GU, int XS>
@@ -976,12 +988,21 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
                        hipStream_t s) {
     using namespace gemv;
     // Per-wave staged X (up to 160 KB of LDS), D-deep load pipeline.  Beyond
-    // four rows, X fills most of LDS (one workgroup per CU), so each workgroup
-    // takes a twice wider strip: fewer workgroups, each staging X once; and one
-    // segment in flight per wave, so that staging X and the first loads compete
-    // less for the CU's load path (measured faster).
-    if (M > 4 && stream_fits(M, K, N, G, 8, 8, 16, 1))
-        return launch_stream_prog<8, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    // four rows X is staged segment by segment, one segment in flight per wave,
+    // and the strip width depends on the layer: 64-column strips whenever all
+    // of them run in one round (the CUs times the workgroups one CU's LDS
+    // holds), since every CU then streams; else 128-column strips, fewer
+    // workgroups each staging X once.  (Measured: 4096 x 14336 at 16 rows,
+    // 10.5 against 15.5 us; 4096 x 28672 at 16 rows, one workgroup per CU,
+    // 17.3 against 18.6 us the other way round.)
+    if (M > 4) {
+        const size_t lds = stream_lds(M, K, 4, 8, 16);
+        const long long per_round = (long long)device_cus() * (long long)(kLdsMax / lds);
+        if ((N + 63) / 64 <= per_round && stream_fits(M, K, N, G, 4, 8, 16, 1))
+            return launch_stream_prog<4, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        if (stream_fits(M, K, N, G, 8, 8, 16, 1))
+            return launch_stream_prog<8, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    }
     if (stream_fits(M, K, N, G, 4, 8, 16, 2))
         return launch_stream_m<4, 8, 16, 2>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 1))
