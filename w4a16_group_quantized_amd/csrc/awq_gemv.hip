@@ -995,14 +995,22 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
     // workgroups each staging X once.  (Measured: 4096 x 14336 at 16 rows,
     // 10.5 against 15.5 us; 4096 x 28672 at 16 rows, one workgroup per CU,
     // 17.3 against 18.6 us the other way round.)
+    // On narrow layers, where 64-column strips would leave half the CUs or
+    // more idle, 32-column strips (measured: 4096 x 4096 at 1 row 5.9 ->
+    // 4.7 us, at 16 rows 9.6 -> 8.5 us; 4096 x 8192 at 1 row 6.3 -> 5.4 us).
+    const bool narrow = (N + 63) / 64 * 2 <= device_cus();
     if (M > 4) {
         const size_t lds = stream_lds(M, K, 4, 8, 16);
         const long long per_round = (long long)device_cus() * (long long)(kLdsMax / lds);
+        if (narrow && stream_fits(M, K, N, G, 2, 8, 16, 1))
+            return launch_stream_prog<2, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
         if ((N + 63) / 64 <= per_round && stream_fits(M, K, N, G, 4, 8, 16, 1))
             return launch_stream_prog<4, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
         if (stream_fits(M, K, N, G, 8, 8, 16, 1))
             return launch_stream_prog<8, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     }
+    if (narrow && stream_fits(M, K, N, G, 2, 8, 16, 2))
+        return launch_stream_m<2, 8, 16, 2>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 2))
         return launch_stream_m<4, 8, 16, 2>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 1))
