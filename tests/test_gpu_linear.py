@@ -152,6 +152,17 @@ def test_deterministic_and_power_of_two(entry, name):
     assert torch.equal((y1.float() * 2).half()[normal].view(torch.int16), y3[normal].view(torch.int16))
 
 
+@pytest.mark.parametrize("M,K,N,G", [(1, 4096, 4096, 128), (16, 4096, 4096, 128),
+                                     (1, 14336, 4096, 128), (8, 4096, 8192, 128)])
+def test_gemv_narrow_layers(M, K, N, G):
+    """Layers whose 64-column strips would leave half the CUs idle (attention
+    output and down projections of the 8B model) run on 32-column strips."""
+    X, codes, zeros, scales = random_case(5100 + M + K + N, M, K, N, G, False)
+    _, Y16 = oracle_case(X, codes, zeros, scales, G)
+    y = to_host_bits(binding.gemv(to_dev(X), device_case(codes, zeros, scales, G)))
+    assert_y_close(y, Y16, f"gemv M={M} K={K} N={N}")
+
+
 SCALE_CASES = [(1, 4096, 264, 128, False), (16, 1024, 136, 128, True), (5, 2048, 200, 2048, False)]
 
 
