@@ -470,8 +470,14 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     // chunk stays in its row): an A-operand read takes one chunk of 16
     // different rows per 16 lanes, which then fall in 16 different bank groups
     // instead of one.
-    uint4 *xs = lds + wave * (M * rows_w);
-    float2 *tabs = reinterpret_cast<float2 *>(lds + M * KR);
+    // Progressive staging keeps one segment's slot per wave: a wave stages a
+    // segment right before multiplying it, after its reads of the previous one
+    // (a wave's LDS operations execute in order), so one slot suffices and the
+    // kernel takes any K.  Otherwise the wave's whole slice is staged.
+    constexpr bool SLOT = XS > 0;
+    const int XR = SLOT ? SEGR : rows_w;         // staged chunks per row of a wave's region
+    uint4 *xs = lds + wave * (M * XR);
+    float2 *tabs = reinterpret_cast<float2 *>(lds + NW * M * XR);
     float2 *tab = tabs + wave * (M * per);
     float *red = reinterpret_cast<float *>(lds);
 
@@ -514,7 +520,7 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         t = lane_group_sum<SEGR>(t);
         u = lane_group_sum<SEGR>(u);
         if (live) {
-            xs[m * rows_w + (rr ^ (m & 15))] = a;
+            xs[m * XR + ((SLOT ? rr % SEGR : rr) ^ (m & 15))] = a;
             if (rr % SEGR == 0) tab[m * per + rr / SEGR] = make_float2(1024.f * t, u);
         }
     };
@@ -599,7 +605,7 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         const int rl0 = (seg - s_begin) * SEGR;   // local packed row of the segment
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            const half8_t a = as_half8(xs[xrow * rows_w + ((rl0 + 4 * st + kb) ^ (xrow & 15))]);
+            const half8_t a = as_half8(xs[xrow * XR + (((SLOT ? 0 : rl0) + 4 * st + kb) ^ (xrow & 15))]);
 #pragma unroll
             for (int i = 0; i < WPL; ++i) {
                 uint32_t p[4];
@@ -694,6 +700,14 @@ inline size_t stream_lds(int M, int K, int WPL, int NW, int SEGR) {
     return staged > red ? staged : red;
 }
 
+// The same with X staged segment by segment (one segment's slot per wave).
+inline size_t stream_lds_prog(int M, int K, int WPL, int NW, int SEGR) {
+    const int per = K / 8 / SEGR / NW;
+    const size_t staged = (size_t)NW * M * SEGR * 16 + (size_t)NW * M * per * 8;
+    const size_t red = (size_t)NW * M * 16 * WPL * 4;
+    return staged > red ? staged : red;
+}
+
 template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false,
           int XS = 0>
 hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
@@ -702,7 +716,7 @@ hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *s
     constexpr int TO = GU ? 8 * WPL : 16 * WPL;   // output columns per workgroup
     const int NO = GU ? N / 2 : N;
     auto kernel = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS>;
-    const size_t lds = stream_lds(M, K, WPL, NW, SEGR);
+    const size_t lds = XS > 0 ? stream_lds_prog(M, K, WPL, NW, SEGR) : stream_lds(M, K, WPL, NW, SEGR);
     if (lds > 64 * 1024) {
         // Beyond 64 KB the kernel must be allowed the larger allocation (once).
         static const hipError_t raised = hipFuncSetAttribute(
@@ -726,6 +740,16 @@ inline bool stream_fits(int M, int K, int N, int G, int WPL, int NW, int SEGR, i
     const int per = nseg / NW;
     if (M * per * SEGR > 64 * kStageChunks) return false;
     return stream_lds(M, K, WPL, NW, SEGR) <= kLdsMax;
+}
+
+// Whether the progressive kernel (16-row segments, X staged segment by
+// segment) can take this shape: any K whose segments split evenly over the
+// waves in pipelines of D, and the slots, tables and reduction within LDS.
+inline bool stream_fits_prog(int M, int K, int N, int G, int WPL, int NW, int D) {
+    if (M > 16 || G % 128 != 0) return false;
+    const int nseg = K / 128;
+    if (nseg % NW != 0 || (nseg / NW) % D != 0) return false;
+    return stream_lds_prog(M, K, WPL, NW, 16) <= kLdsMax;
 }
 
 template <int WPL, int NW, int SEGR, int D, int VR, int XCH>
@@ -987,26 +1011,27 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
                        hipStream_t s) {
     using namespace gemv;
-    // Per-wave staged X (up to 160 KB of LDS), D-deep load pipeline.  Beyond
-    // four rows X is staged segment by segment, one segment in flight per wave,
-    // and the strip width depends on the layer: 64-column strips whenever all
-    // of them run in one round (the CUs times the workgroups one CU's LDS
-    // holds), since every CU then streams; else 128-column strips, fewer
-    // workgroups each staging X once.  (Measured: 4096 x 14336 at 16 rows,
-    // 10.5 against 15.5 us; 4096 x 28672 at 16 rows, one workgroup per CU,
-    // 17.3 against 18.6 us the other way round.)
-    // On narrow layers, where 64-column strips would leave half the CUs or
-    // more idle, 32-column strips (measured: 4096 x 4096 at 1 row 5.9 ->
-    // 4.7 us, at 16 rows 9.6 -> 8.5 us; 4096 x 8192 at 1 row 6.3 -> 5.4 us).
-    const bool narrow = (N + 63) / 64 * 2 <= device_cus();
+    // Per-wave staged X, D-deep load pipeline.  The strip width depends on the
+    // layer.  On narrow layers, where 64-column strips would leave half the
+    // CUs or more idle, 32-column strips (4096 x 4096 at 1 row: 5.9 -> 4.7 us;
+    // 14336 x 4096 at 1 row: 16.1 -> 11.0 us).
+    const int cus = device_cus();
+    const long long n64 = (N + 63) / 64, n128 = (N + 127) / 128;
+    const bool narrow = n64 * 2 <= cus;
     if (M > 4) {
-        const size_t lds = stream_lds(M, K, 4, 8, 16);
-        const long long per_round = (long long)device_cus() * (long long)(kLdsMax / lds);
-        if (narrow && stream_fits(M, K, N, G, 2, 8, 16, 1))
+        // Beyond four rows X is staged segment by segment, one segment in
+        // flight per wave, which takes any K.  Every workgroup reads all of X
+        // (M K 2 bytes) beside its strip, so 128-column strips, half as many
+        // workgroups, pay where they still keep three quarters of the CUs
+        // busy and X is large (4096 x 28672 at 16 rows: 17.1 against 18.9
+        // us); else 64-column strips (4096 x 14336 at 16 rows: 9.9 against
+        // 15.5 us).
+        const bool wide = n128 * 4 >= 3LL * cus && (M > 8 || n64 > 2LL * cus);
+        if (narrow && stream_fits_prog(M, K, N, G, 2, 8, 1))
             return launch_stream_prog<2, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
-        if ((N + 63) / 64 <= per_round && stream_fits(M, K, N, G, 4, 8, 16, 1))
+        if (!wide && stream_fits_prog(M, K, N, G, 4, 8, 1))
             return launch_stream_prog<4, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
-        if (stream_fits(M, K, N, G, 8, 8, 16, 1))
+        if (stream_fits_prog(M, K, N, G, 8, 8, 1))
             return launch_stream_prog<8, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     }
     if (narrow && stream_fits(M, K, N, G, 2, 8, 16, 2))
