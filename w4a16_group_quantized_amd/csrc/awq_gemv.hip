@@ -27,15 +27,17 @@
 //      FMAs per output.
 //
 // Kernels:
-//   stream_kernel (M <= 16, G a multiple of 128, X in LDS): each wave stages
-//     the slice of X its K range needs into its own LDS region, odd k divided
-//     by 16 so that the 64-biased upper nibbles need no shift, together with
-//     the per-segment sums U and S; no workgroup barrier before the loop.  Up
-//     to four rows the slice is staged before the first multiply; beyond four
-//     (128 KB per workgroup at 16 rows), each segment's part is loaded with
-//     that segment's weights and staged just before it is multiplied;
-//   fold_kernel (G a multiple of 32, or X beyond LDS): the same fold, with X
-//     from LDS or L2 and S from an MFMA against an all-ones B;
+//   stream_kernel (M <= 16, G a multiple of 128): each wave stages the slice
+//     of X its K range needs into its own LDS region, odd k divided by 16 so
+//     that the 64-biased upper nibbles need no shift, together with the
+//     per-segment sums U and S; no workgroup barrier before the loop.  Up to
+//     four rows the slice is staged before the first multiply (X must fit
+//     LDS); beyond four, each segment's part is loaded with that segment's
+//     weights and staged into a one-segment slot just before it is
+//     multiplied, so any K fits;
+//   fold_kernel (G a multiple of 32, or up to four rows with X beyond LDS):
+//     the same fold, with X from LDS or L2 and S from an MFMA against an
+//     all-ones B;
 //   exact_kernel (any other G): every word dequantized exactly first.
 //
 // Tiling: one workgroup owns TN = 16 * WPL columns and all of K.  Each lane
