@@ -58,6 +58,8 @@ RAGGED = [
     # chunks per lane: 7, 12 and 13 rows, with groups of one segment, of two, and
     # one group per column
     (12, 2048, 264, 128, False), (7, 4096, 200, 256, True), (13, 1024, 72, 1024, False),
+    # up to four rows with X beyond LDS (172 and 164 KB): staged segment by segment too
+    (3, 28672, 264, 128, False), (4, 20480, 1032, 256, True),
 ]
 
 

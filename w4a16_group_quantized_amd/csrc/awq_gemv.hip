@@ -34,10 +34,9 @@
 //     four rows the slice is staged before the first multiply (X must fit
 //     LDS); beyond four, each segment's part is loaded with that segment's
 //     weights and staged into a one-segment slot just before it is
-//     multiplied, so any K fits;
-//   fold_kernel (G a multiple of 32, or up to four rows with X beyond LDS):
-//     the same fold, with X from LDS or L2 and S from an MFMA against an
-//     all-ones B;
+//     multiplied, so any K fits (also up to four rows when X exceeds LDS);
+//   fold_kernel (G a multiple of 32 but not of 128): the same fold, with X
+//     from LDS or L2 and S from an MFMA against an all-ones B;
 //   exact_kernel (any other G): every word dequantized exactly first.
 //
 // Tiling: one workgroup owns TN = 16 * WPL columns and all of K.  Each lane
@@ -808,6 +807,7 @@ template <int WPL, int NW, int D, bool GU>
 hipError_t launch_stream_prog(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                               const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                               hipStream_t s) {
+    if (M <= 4) return launch_stream_prog_xs<WPL, NW, D, GU, 1>(x, qw, sc, qz, y, M, K, N, G, s);
     if (M <= 8) return launch_stream_prog_xs<WPL, NW, D, GU, 2>(x, qw, sc, qz, y, M, K, N, G, s);
     if (M <= 12) return launch_stream_prog_xs<WPL, NW, D, GU, 3>(x, qw, sc, qz, y, M, K, N, G, s);
     return launch_stream_prog_xs<WPL, NW, D, GU, 4>(x, qw, sc, qz, y, M, K, N, G, s);
@@ -1042,6 +1042,11 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
         return launch_stream_m<4, 8, 16, 2>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 1))
         return launch_stream_m<4, 8, 16, 1>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    // Up to four rows with X beyond LDS: staged segment by segment as well.
+    if (narrow && stream_fits_prog(M, K, N, G, 2, 8, 1))
+        return launch_stream_prog<2, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    if (stream_fits_prog(M, K, N, G, 4, 8, 1))
+        return launch_stream_prog<4, 8, 1, false>(x, qweight, scales, qzeros, y, M, K, N, G, s);
     // A segment (SEGR packed rows) must sit inside one group and be whole 32-k steps.
     // Narrow layers on 32-column strips here too (14336 x 4096 at 16 rows:
     // 27.4 -> 22.1 us).
