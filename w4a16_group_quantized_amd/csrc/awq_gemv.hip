@@ -35,8 +35,9 @@
 //     LDS); beyond four, each segment's part is loaded with that segment's
 //     weights and staged into a one-segment slot just before it is
 //     multiplied, so any K fits (also up to four rows when X exceeds LDS);
-//   fold_kernel (G a multiple of 32 but not of 128): the same fold, with X
-//     from LDS or L2 and S from an MFMA against an all-ones B;
+//   fold_kernel (G a multiple of 32, for shapes the stream kernel does not
+//     take: G not a multiple of 128, or K not a multiple of 1024): the same
+//     fold, with X from LDS or L2 and S from an MFMA against an all-ones B;
 //   exact_kernel (any other G): every word dequantized exactly first.
 //
 // Tiling: one workgroup owns TN = 16 * WPL columns and all of K.  Each lane
