@@ -26,7 +26,8 @@ def _oracle_h(X, W):
 
 
 @pytest.mark.parametrize("name,M", [("gate_up_m16", 16), ("gate_up_m16", 1), ("gate_up_m16", 4),
-                                    ("sym70b_m1", 1), ("sym70b_m1", 8)])
+                                    ("sym70b_m1", 1), ("sym70b_m1", 8),
+                                    ("sym70b_m1", 16)])   # X of 256 KB: staged segment by segment
 def test_workload_gate_up(name, M):
     X, _, _, _ = workload_host(name)
     if X.shape[0] < M:                                  # more rows of the same distribution

@@ -990,15 +990,23 @@ hipError_t launch_gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *
 
 bool gemv_gate_up_supported(int M, int K, int N, int G) {
     using namespace gemv;
-    return M >= 1 && M <= 16 && N % 16 == 0 &&
-           (stream_fits(M, K, N, G, 8, 8, 16, 2) || stream_fits(M, K, N, G, 8, 8, 16, 1) ||
-            stream_fits(M, K, N, G, 8, 2, 16, 1) || stream_fits(M, K, N, G, 8, 1, 16, 1));
+    if (M < 1 || M > 16 || N % 16 != 0) return false;
+    if (M > 4 && (stream_fits_prog(M, K, N, G, 8, 8, 2) || stream_fits_prog(M, K, N, G, 8, 8, 1)))
+        return true;   // X staged segment by segment: any K
+    return stream_fits(M, K, N, G, 8, 8, 16, 2) || stream_fits(M, K, N, G, 8, 8, 16, 1) ||
+           stream_fits(M, K, N, G, 8, 2, 16, 1) || stream_fits(M, K, N, G, 8, 1, 16, 1);
 }
 
 hipError_t launch_gemv_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                                const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
                                hipStream_t s) {
     using namespace gemv;
+    if (M > 4) {   // launch_gate_up stages X segment by segment beyond four rows
+        if (stream_fits_prog(M, K, N, G, 8, 8, 2))
+            return launch_gate_up<8, 2>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+        if (stream_fits_prog(M, K, N, G, 8, 8, 1))
+            return launch_gate_up<8, 1>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    }
     if (stream_fits(M, K, N, G, 8, 8, 16, 2))
         return launch_gate_up<8, 2>(x, qweight, scales, qzeros, h, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 8, 8, 16, 1))
