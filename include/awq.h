@@ -161,9 +161,9 @@ awq_status awq_quantize(const uint16_t *w, int32_t K, int32_t N, int32_t group_s
  * Rules beyond the layer's: 1 <= M <= 16 (M == 0 is a no-op); N % 16 == 0
  * (I a multiple of 8).  Shapes the fused kernel does not cover return
  * AWQ_ERROR_UNSUPPORTED with nothing launched: G must be a multiple of 128;
- * beyond four rows K a multiple of 1024 (X is staged segment by segment, any
- * K otherwise); up to four rows M * K * 2 bytes of X must also fit next to the
- * kernel's tables in the 160 KB of LDS of one workgroup.
+ * beyond four rows X is staged segment by segment (any K); up to four rows
+ * M * K * 2 bytes of X must also fit next to the kernel's tables in the
+ * 160 KB of LDS of one workgroup.
  */
 awq_status awq_gemv_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t *h, int32_t M,
                             void *stream);

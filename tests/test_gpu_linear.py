@@ -166,6 +166,22 @@ def test_gemv_narrow_layers(M, K, N, G):
     assert_y_close(y, Y16, f"gemv M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N,G,sym", [
+    (1, 11008, 4096, 128, False), (4, 11008, 4096, 128, True), (16, 11008, 4096, 128, False),
+    (1, 13824, 5120, 128, True), (1, 11264, 4096, 128, False), (3, 1152, 200, 128, False),
+    (7, 2176, 264, 128, True), (16, 1280, 136, 256, False), (2, 1536, 72, 384, True),
+])
+def test_gemv_uneven_k(M, K, N, G, sym):
+    """K whose 128-k segments do not split evenly over the eight waves of a
+    workgroup (K = 11008: 86 segments; 11264: 88, eleven a wave, odd against a
+    two-deep pipeline): the first waves take one segment more.  Groups of 256
+    and 384 put wave boundaries inside a group."""
+    X, codes, zeros, scales = random_case(5300 + M + K + N, M, K, N, G, sym)
+    _, Y16 = oracle_case(X, codes, zeros, scales, G)
+    y = to_host_bits(binding.gemv(to_dev(X), device_case(codes, zeros, scales, G)))
+    assert_y_close(y, Y16, f"gemv M={M} K={K} N={N} G={G} sym={sym}")
+
+
 SCALE_CASES = [(1, 4096, 264, 128, False), (16, 1024, 136, 128, True), (5, 2048, 200, 2048, False)]
 
 

@@ -36,15 +36,17 @@
 //     weights and staged into a one-segment slot just before it is
 //     multiplied, so any K fits (also up to four rows when X exceeds LDS);
 //   fold_kernel (G a multiple of 32, for shapes the stream kernel does not
-//     take: G not a multiple of 128, or K not a multiple of 1024): the same
-//     fold, with X from LDS or L2 and S from an MFMA against an all-ones B;
+//     take: G not a multiple of 128, or K below 1024): the same fold, with X
+//     from LDS or L2 and S from an MFMA against an all-ones B;
 //   exact_kernel (any other G): every word dequantized exactly first.
 //
 // Tiling: one workgroup owns TN = 16 * WPL columns and all of K.  Each lane
 // loads WPL consecutive words (columns) of one packed row; lanes 16j..16j+15
 // take packed row 4t + j of step t, so a step covers 32 k.  The NW waves split
-// K into contiguous ranges; their fp32 partial sums are added in LDS in a fixed
-// order (deterministic) and written as fp16.
+// K into contiguous ranges of whole 128-k segments (when the segment count is
+// not a multiple of the waves, the first waves take one more); their fp32
+// partial sums are added in LDS in a fixed order (deterministic) and written
+// as fp16.
 #include "awq_device.h"
 #include "awq_internal.h"
 
@@ -440,8 +442,13 @@ constexpr size_t kLdsMax = 160 * 1024;
 // just before the segment is multiplied, instead of the whole slice up front.
 // With 16 rows the whole slice is 128 KB per workgroup, and every workgroup
 // asking for it at once delays the first multiply by microseconds.
+// UNEV: the K range's segments do not split into whole pipelines of D per
+// wave (K not a multiple of 8 NW SEGR, or an odd count per wave): the first
+// nseg % NW waves take one segment more, and the loads ahead are guarded by
+// the wave's own count (a uniform branch).  The even case keeps the
+// unconditional pipeline.
 template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false,
-          int XS = 0>
+          int XS = 0, bool UNEV = false>
 __global__ void __launch_bounds__(NW * 64)
 stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
@@ -461,9 +468,13 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const int ncol = n0 + WO * c16;
     const int ncl = ncol < NO ? ncol : NO - WO;  // clamped: in bounds, result dropped
     const int KR = K / 8;
-    const int per = KR / SEGR / NW;              // segments per wave (multiple of D)
-    const int rows_w = per * SEGR;               // packed rows per wave
-    const int r_begin = wave * rows_w;
+    const int nseg = KR / SEGR;
+    const int per_base = nseg / NW, extra = UNEV ? nseg % NW : 0;
+    const int per = per_base + (wave < extra ? 1 : 0);   // this wave's segments
+    const int tper = per_base + (extra > 0 ? 1 : 0);     // stride of the per-wave regions
+    const int rows_w = per * SEGR;               // packed rows of this wave
+    const int s_begin = wave * per_base + (wave < extra ? wave : extra);
+    const int r_begin = s_begin * SEGR;
     const int spg = G / (8 * SEGR);              // segments per group
 
     // LDS: staged X slices (all waves), then (U, S) tables; once every wave is
@@ -477,10 +488,10 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     // (a wave's LDS operations execute in order), so one slot suffices and the
     // kernel takes any K.  Otherwise the wave's whole slice is staged.
     constexpr bool SLOT = XS > 0;
-    const int XR = SLOT ? SEGR : rows_w;         // staged chunks per row of a wave's region
+    const int XR = SLOT ? SEGR : tper * SEGR;    // staged chunks per row of a wave's region
     uint4 *xs = lds + wave * (M * XR);
     float2 *tabs = reinterpret_cast<float2 *>(lds + NW * M * XR);
-    float2 *tab = tabs + wave * (M * per);
+    float2 *tab = tabs + wave * (M * tper);
     float *red = reinterpret_cast<float *>(lds);
 
     const int xrow = c16 < M ? c16 : M - 1;      // A row of this lane (clamped)
@@ -523,7 +534,7 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         u = lane_group_sum<SEGR>(u);
         if (live) {
             xs[m * XR + ((SLOT ? rr % SEGR : rr) ^ (m & 15))] = a;
-            if (rr % SEGR == 0) tab[m * per + rr / SEGR] = make_float2(1024.f * t, u);
+            if (rr % SEGR == 0) tab[m * tper + rr / SEGR] = make_float2(1024.f * t, u);
         }
     };
     // Only this wave reads its slice; LDS operations of one wave execute in order.
@@ -534,7 +545,6 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     };
     const uint4 *X4 = reinterpret_cast<const uint4 *>(X);
     WSeg<WPL, STEPS, SYM> b[D];
-    const int s_begin = wave * per;
     // Progressive staging: chunk c = lane + 64 j of segment sl is row c / SEGR,
     // packed row sl * SEGR + c % SEGR of the wave's slice (clamped loads).
     // A segment's swizzled chunks (rr ^ (m % 16)) stay in its own 16 packed rows.
@@ -619,7 +629,7 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #pragma unroll
         for (int v = 0; v < VR; ++v) {
             const int m = min(4 * kb + v, M - 1);
-            const float2 us = tab[m * per + (seg - s_begin)];
+            const float2 us = tab[m * tper + (seg - s_begin)];
             Ug[v] += us.x;
             Sg[v] += us.y;
         }
@@ -643,19 +653,42 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         }
     };
 
-    for (int i = 0; i < per - D; i += D) {
+    if constexpr (!UNEV) {
+        for (int i = 0; i < per - D; i += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if constexpr (XS > 0) stage_x_seg(i + d, xq[d]);
+                compute_seg(s_begin + i + d, b[d]);
+                if constexpr (XS > 0) load_x_seg(i + d + D, xq[d]);
+                load_seg(s_begin + i + d + D, b[d]);
+            }
+        }
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if constexpr (XS > 0) stage_x_seg(i + d, xq[d]);
-            compute_seg(s_begin + i + d, b[d]);
-            if constexpr (XS > 0) load_x_seg(i + d + D, xq[d]);
-            load_seg(s_begin + i + d + D, b[d]);
+            if constexpr (XS > 0) stage_x_seg(per - D + d, xq[d]);
+            compute_seg(s_begin + per - D + d, b[d]);
         }
-    }
+    } else {
+        // Segment i sits in buffer i % D; per >= D (the launcher's condition).
+        int i = 0;
+        for (; i + D < per; i += D) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        if constexpr (XS > 0) stage_x_seg(per - D + d, xq[d]);
-        compute_seg(s_begin + per - D + d, b[d]);
+            for (int d = 0; d < D; ++d) {
+                if constexpr (XS > 0) stage_x_seg(i + d, xq[d]);
+                compute_seg(s_begin + i + d, b[d]);
+                if (i + d + D < per) {   // uniform
+                    if constexpr (XS > 0) load_x_seg(i + d + D, xq[d]);
+                    load_seg(s_begin + i + d + D, b[d]);
+                }
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (i + d < per) {           // uniform
+                if constexpr (XS > 0) stage_x_seg(i + d, xq[d]);
+                compute_seg(s_begin + i + d, b[d]);
+            }
+        }
     }
 
     // C layout of the 16x16 MFMA: lane (kb, c16) holds rows 4 kb + v of column c16.
@@ -696,15 +729,15 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 // Dynamic LDS of stream_kernel: staged X and tables, or the reduction buffer
 // that replaces them at the end, whichever is larger.
 inline size_t stream_lds(int M, int K, int WPL, int NW, int SEGR) {
-    const int per = K / 8 / SEGR / NW;
-    const size_t staged = (size_t)M * K * 2 + (size_t)NW * M * per * 8;
+    const int per = (K / 8 / SEGR + NW - 1) / NW;   // the largest count per wave
+    const size_t staged = (size_t)NW * M * per * SEGR * 16 + (size_t)NW * M * per * 8;
     const size_t red = (size_t)NW * M * 16 * WPL * 4;
     return staged > red ? staged : red;
 }
 
 // The same with X staged segment by segment (one segment's slot per wave).
 inline size_t stream_lds_prog(int M, int K, int WPL, int NW, int SEGR) {
-    const int per = K / 8 / SEGR / NW;
+    const int per = (K / 8 / SEGR + NW - 1) / NW;
     const size_t staged = (size_t)NW * M * SEGR * 16 + (size_t)NW * M * per * 8;
     const size_t red = (size_t)NW * M * 16 * WPL * 4;
     return staged > red ? staged : red;
@@ -717,14 +750,21 @@ hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *s
                          hipStream_t s) {
     constexpr int TO = GU ? 8 * WPL : 16 * WPL;   // output columns per workgroup
     const int NO = GU ? N / 2 : N;
-    auto kernel = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS>;
+    auto even = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS, false>;
+    auto uneven = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS, true>;
+    const int nseg = K / 8 / SEGR;
+    auto kernel = (nseg % NW != 0 || (nseg / NW) % D != 0) ? uneven : even;
     const size_t lds = XS > 0 ? stream_lds_prog(M, K, WPL, NW, SEGR) : stream_lds(M, K, WPL, NW, SEGR);
     if (lds > 64 * 1024) {
-        // Beyond 64 KB the kernel must be allowed the larger allocation (once).
-        static const hipError_t raised = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+        // Beyond 64 KB a kernel must be allowed the larger allocation (once each).
+        static const hipError_t raised_even = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(even), hipFuncAttributeMaxDynamicSharedMemorySize,
             (int)kLdsMax);
-        if (raised != hipSuccess) return raised;
+        static const hipError_t raised_uneven = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(uneven), hipFuncAttributeMaxDynamicSharedMemorySize,
+            (int)kLdsMax);
+        if (raised_even != hipSuccess) return raised_even;
+        if (raised_uneven != hipSuccess) return raised_uneven;
     }
     hipLaunchKernelGGL(kernel, dim3((NO + TO - 1) / TO), dim3(NW * 64), lds, s, x,
                        reinterpret_cast<const uint32_t *>(qw), sc,
@@ -732,25 +772,25 @@ hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *s
     return hipGetLastError();
 }
 
-// Whether stream_kernel<.., NW, SEGR, D, ..> can take this shape: the segments
-// split evenly over the waves in whole pipelines of D, each wave's X slice fits
+// Whether stream_kernel<.., NW, SEGR, D, ..> can take this shape: every wave
+// gets at least D segments (one pipeline), the largest wave's X slice fits
 // kStageChunks chunks per lane, and LDS stays within the workgroup maximum.
 inline bool stream_fits(int M, int K, int N, int G, int WPL, int NW, int SEGR, int D) {
     if (M > 16 || G % (8 * SEGR) != 0) return false;
     const int nseg = K / 8 / SEGR;
-    if (nseg % NW != 0 || (nseg / NW) % D != 0) return false;
-    const int per = nseg / NW;
+    if (nseg / NW < D) return false;             // every wave fills its pipeline
+    const int per = (nseg + NW - 1) / NW;        // the largest count per wave
     if (M * per * SEGR > 64 * kStageChunks) return false;
     return stream_lds(M, K, WPL, NW, SEGR) <= kLdsMax;
 }
 
 // Whether the progressive kernel (16-row segments, X staged segment by
-// segment) can take this shape: any K whose segments split evenly over the
-// waves in pipelines of D, and the slots, tables and reduction within LDS.
+// segment) can take this shape: any K with at least D segments per wave, and
+// the slots, tables and reduction within LDS.
 inline bool stream_fits_prog(int M, int K, int N, int G, int WPL, int NW, int D) {
     if (M > 16 || G % 128 != 0) return false;
     const int nseg = K / 128;
-    if (nseg % NW != 0 || (nseg / NW) % D != 0) return false;
+    if (nseg / NW < D) return false;             // every wave fills its pipeline
     return stream_lds_prog(M, K, WPL, NW, 16) <= kLdsMax;
 }
 
@@ -770,7 +810,7 @@ template <int WPL, int NW, int SEGR, int D, int VR>
 hipError_t launch_stream_x(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                            const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                            hipStream_t s) {
-    const int chunks_w = M * (K / 8 / NW);
+    const int chunks_w = M * ((K / 8 / SEGR + NW - 1) / NW) * SEGR;   // the largest wave's
     if (chunks_w <= 64) return launch_stream_sg<WPL, NW, SEGR, D, VR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
     if (chunks_w <= 128) return launch_stream_sg<WPL, NW, SEGR, D, VR, 2>(x, qw, sc, qz, y, M, K, N, G, s);
     if (chunks_w <= 256) return launch_stream_sg<WPL, NW, SEGR, D, VR, 4>(x, qw, sc, qz, y, M, K, N, G, s);
