@@ -156,7 +156,7 @@ def test_deterministic_and_power_of_two(entry, name):
 
 @pytest.mark.parametrize("M,K,N,G", [(1, 4096, 4096, 128), (16, 4096, 4096, 128),
                                      (1, 14336, 4096, 128), (8, 4096, 8192, 128),
-                                     (16, 14336, 4096, 128)])   # X beyond LDS: the fold kernel
+                                     (16, 14336, 4096, 128)])   # X beyond LDS: staged per segment
 def test_gemv_narrow_layers(M, K, N, G):
     """Layers whose 64-column strips would leave half the CUs idle (attention
     output and down projections of the 8B model) run on 32-column strips."""

@@ -8,9 +8,9 @@ scales and the zero points are seeded host draws (uniform words, scales in
 [0.001, 0.01]); the oracle takes the same host arrays, restricted to seeded
 blocks of 8 columns across the whole width (always the first and the last),
 and computes those columns.  Rows of X come from the synthetic generator.
-Each kernel variant the shapes select is covered: the decode kernel (1 row),
-the fold kernel (16 rows: X does not fit LDS at K = 8192), the GEMM, split K
-and the exact dequantization.  Two more cases take the largest batch (M K just
+Each kernel variant the shapes select is covered: the decode kernel at 1 row
+and in its slot-staged form at 16 rows (X staged segment by segment), the GEMM,
+split K and the exact dequantization.  Two more cases take the largest batch (M K just
 below 2^31, a 4.3 GB X through the GEMM) and the largest fp16 W through the
 quantizer.
 """
