@@ -44,7 +44,7 @@ def test_workload_gate_up(name, M):
     (1, 128, 8, 128, False), (3, 256, 136, 128, False), (16, 1024, 40, 256, True),
     (5, 2048, 264, 128, False), (2, 384, 72, 384, True), (16, 4096, 520, 128, False),
     (11, 2048, 136, 256, True), (16, 1152, 136, 128, False), (1, 11008, 264, 128, True),
-    (6, 1280, 40, 256, False),
+    (6, 1280, 40, 256, False), (3, 2688, 72, 128, False), (4, 1664, 40, 128, True),
 ])
 def test_ragged_gate_up(M, K, I, G, sym):
     X, codes, zeros, scales = random_case(900 + M + K, M, K, 2 * I, G, sym)

@@ -433,7 +433,8 @@ constexpr int kStageChunks = 16;
 // LDS of one workgroup, at most (gfx950: 160 KB per workgroup).
 constexpr size_t kLdsMax = 160 * 1024;
 
-// XCH: 16-byte chunks of X each lane stages (M * K / 8 / NW <= 64 * XCH).
+// XCH: 16-byte chunks of X each lane stages (the largest wave's slice,
+// M * ceil(segments / NW) * SEGR chunks, is at most 64 * XCH).
 // GU (fused gate/up): the layer's N columns are [gate | up]; a lane's WPL words
 // are WPL / 2 gate columns and the same WPL / 2 columns of the up half, and the
 // output is h = fp16(SiLU(gate) * up), N / 2 columns wide.
@@ -523,6 +524,10 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     // aligned groups of SEGR lanes that hold that row's chunks of one segment.
     auto stage = [&](const uint4 &raw, bool live, int m, int rr) {
         const uint4 a = stage_chunk(raw);
+        if constexpr (SLOT) {   // the segment sums come from the matrix cores
+            if (live) xs[m * XR + ((rr % SEGR) ^ (m & 15))] = a;
+            return;
+        }
         const half2_t one2 = {(half_t)1.0f, (half_t)1.0f};
         const float lo = __builtin_amdgcn_fdot2(as_half2(a.x), one2,
                          __builtin_amdgcn_fdot2(as_half2(a.z), one2, 0.f, false), false);
@@ -612,12 +617,23 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     float Ug[VR], Sg[VR];
 #pragma unroll
     for (int v = 0; v < VR; ++v) Ug[v] = Sg[v] = 0.f;
+    // Slot mode: the sums of the staged values (T) and of x (S) of each row,
+    // over the group so far, from two more MFMAs per step against constant B
+    // operands: all ones, and 1 for the even-k halves, 16 for the odd-k ones
+    // (staged as x / 16).  Lane (kb, c16) receives them for its C rows 4 kb + v.
+    float4_t CT = float4_t{0.f, 0.f, 0.f, 0.f}, CS = CT;
+    const half8_t ones8 = as_half8(make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
+    const half8_t xsum8 = as_half8(make_uint4(0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u));
 
     auto compute_seg = [&](int seg, const WSeg<WPL, STEPS, SYM> &bb) {
         const int rl0 = (seg - s_begin) * SEGR;   // local packed row of the segment
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             const half8_t a = as_half8(xs[xrow * XR + (((SLOT ? 0 : rl0) + 4 * st + kb) ^ (xrow & 15))]);
+            if constexpr (SLOT) {
+                CT = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones8, CT, 0, 0, 0);
+                CS = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, xsum8, CS, 0, 0, 0);
+            }
 #pragma unroll
             for (int i = 0; i < WPL; ++i) {
                 uint32_t p[4];
@@ -626,15 +642,26 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             }
         }
         // (U, S) of this segment for the lane's live C rows 4 kb + v (clamped).
+        if constexpr (!SLOT) {
 #pragma unroll
-        for (int v = 0; v < VR; ++v) {
-            const int m = min(4 * kb + v, M - 1);
-            const float2 us = tab[m * tper + (seg - s_begin)];
-            Ug[v] += us.x;
-            Sg[v] += us.y;
+            for (int v = 0; v < VR; ++v) {
+                const int m = min(4 * kb + v, M - 1);
+                const float2 us = tab[m * tper + (seg - s_begin)];
+                Ug[v] += us.x;
+                Sg[v] += us.y;
+            }
         }
         const bool fold = GRP1 || (seg + 1) % spg == 0 || seg == s_begin + per - 1;   // uniform
         if (fold) {
+            if constexpr (SLOT) {
+#pragma unroll
+                for (int v = 0; v < VR; ++v) {
+                    Ug[v] = 1024.f * CT[v];
+                    Sg[v] = CS[v];
+                }
+                CT = float4_t{0.f, 0.f, 0.f, 0.f};
+                CS = CT;
+            }
             const uint32_t zw = SYM ? 0u : bb.zw >> (4 * (ncl % 8));
             const uint32_t zw2 = SYM || !GU ? 0u : bb.zw2 >> (4 * (ncl % 8));   // NO % 8 == 0
 #pragma unroll
@@ -726,6 +753,12 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     }
 }
 
+// Whether K's segments split over the NW waves in whole pipelines of D each.
+inline bool stream_even(int K, int NW, int SEGR, int D) {
+    const int nseg = K / 8 / SEGR;
+    return nseg % NW == 0 && (nseg / NW) % D == 0;
+}
+
 // Dynamic LDS of stream_kernel: staged X and tables, or the reduction buffer
 // that replaces them at the end, whichever is larger.
 inline size_t stream_lds(int M, int K, int WPL, int NW, int SEGR) {
@@ -737,8 +770,8 @@ inline size_t stream_lds(int M, int K, int WPL, int NW, int SEGR) {
 
 // The same with X staged segment by segment (one segment's slot per wave).
 inline size_t stream_lds_prog(int M, int K, int WPL, int NW, int SEGR) {
-    const int per = (K / 8 / SEGR + NW - 1) / NW;
-    const size_t staged = (size_t)NW * M * SEGR * 16 + (size_t)NW * M * per * 8;
+    (void)K;   // one segment's slot per wave, whatever K; no tables
+    const size_t staged = (size_t)NW * M * SEGR * 16;
     const size_t red = (size_t)NW * M * 16 * WPL * 4;
     return staged > red ? staged : red;
 }
@@ -750,10 +783,15 @@ hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *s
                          hipStream_t s) {
     constexpr int TO = GU ? 8 * WPL : 16 * WPL;   // output columns per workgroup
     const int NO = GU ? N / 2 : N;
+    // The guarded pipeline of the fused gate/up kernel at depth 2 with two or
+    // more X chunks per lane runs out of registers; such shapes take depth 1
+    // (the dispatch checks stream_even first) and that variant is not built.
+    constexpr bool kUneven = !(GU && D > 1 && XS > 1);
     auto even = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS, false>;
-    auto uneven = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS, true>;
-    const int nseg = K / 8 / SEGR;
-    auto kernel = (nseg % NW != 0 || (nseg / NW) % D != 0) ? uneven : even;
+    auto uneven = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS, kUneven>;
+    const bool split_uneven = !stream_even(K, NW, SEGR, D);
+    if (!kUneven && split_uneven) return hipErrorNotSupported;
+    auto kernel = split_uneven ? uneven : even;
     const size_t lds = XS > 0 ? stream_lds_prog(M, K, WPL, NW, SEGR) : stream_lds(M, K, WPL, NW, SEGR);
     if (lds > 64 * 1024) {
         // Beyond 64 KB a kernel must be allowed the larger allocation (once each).
@@ -786,7 +824,7 @@ inline bool stream_fits(int M, int K, int N, int G, int WPL, int NW, int SEGR, i
 
 // Whether the progressive kernel (16-row segments, X staged segment by
 // segment) can take this shape: any K with at least D segments per wave, and
-// the slots, tables and reduction within LDS.
+// the slots and the reduction within LDS.
 inline bool stream_fits_prog(int M, int K, int N, int G, int WPL, int NW, int D) {
     if (M > 16 || G % 128 != 0) return false;
     const int nseg = K / 128;
@@ -1014,7 +1052,7 @@ hipError_t launch_gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *
                           hipStream_t s) {
     if (M > 4) return launch_stream_prog<8, NW, D, true>(x, qw, sc, qz, y, M, K, N, G, s);
     const bool sym = qz == nullptr, grp1 = G == 8 * 16;
-    const bool big = M * (K / 8 / NW) > 128;
+    const bool big = M * ((K / 128 + NW - 1) / NW) * 16 > 128;   // the largest wave's chunks
 #define AWQ_GU(SYMV, GRPV, XCHV) \
     launch_stream<8, NW, 16, D, 4, SYMV, GRPV, XCHV, true>(x, qw, sc, qz, y, M, K, N, G, s)
     if (big) {
@@ -1031,7 +1069,8 @@ hipError_t launch_gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *
 bool gemv_gate_up_supported(int M, int K, int N, int G) {
     using namespace gemv;
     if (M < 1 || M > 16 || N % 16 != 0) return false;
-    if (M > 4 && (stream_fits_prog(M, K, N, G, 8, 8, 2) || stream_fits_prog(M, K, N, G, 8, 8, 1)))
+    if (M > 4 && ((stream_even(K, 8, 16, 2) && stream_fits_prog(M, K, N, G, 8, 8, 2)) ||
+                  stream_fits_prog(M, K, N, G, 8, 8, 1)))
         return true;   // X staged segment by segment: any K
     return stream_fits(M, K, N, G, 8, 8, 16, 2) || stream_fits(M, K, N, G, 8, 8, 16, 1) ||
            stream_fits(M, K, N, G, 8, 2, 16, 1) || stream_fits(M, K, N, G, 8, 1, 16, 1);
@@ -1042,7 +1081,7 @@ hipError_t launch_gemv_gate_up(const uint16_t *x, const int32_t *qweight, const 
                                hipStream_t s) {
     using namespace gemv;
     if (M > 4) {   // launch_gate_up stages X segment by segment beyond four rows
-        if (stream_fits_prog(M, K, N, G, 8, 8, 2))
+        if (stream_even(K, 8, 16, 2) && stream_fits_prog(M, K, N, G, 8, 8, 2))
             return launch_gate_up<8, 2>(x, qweight, scales, qzeros, h, M, K, N, G, s);
         if (stream_fits_prog(M, K, N, G, 8, 8, 1))
             return launch_gate_up<8, 1>(x, qweight, scales, qzeros, h, M, K, N, G, s);
