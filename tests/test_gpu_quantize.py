@@ -44,6 +44,8 @@ def _check(W, G, sym, what):
     (128, 64, 128, False), (256, 40, 64, False), (512, 136, 128, True), (64, 8, 8, False),
     (1024, 200, 1024, True), (384, 24, 32, False), (4096, 512, 128, False), (96, 72, 96, True),
     (2048, 136, 2048, False), (8192, 72, 8192, True), (3072, 64, 1536, False),
+    # long groups over several 64-column tiles: 16 waves a group (4096), 8 (1024)
+    (4096, 1032, 4096, False), (2048, 520, 1024, True), (16384, 64, 16384, False),
 ])
 def test_quantize_bit_exact(K, N, G, sym):
     _check(_weights(K * 7 + N, K, N), G, sym, f"K={K} N={N} G={G} sym={sym}")

@@ -52,6 +52,8 @@ def test_channel_stats(M, K, N, G):
 @pytest.mark.parametrize("M,K,N,G,sym", [
     (64, 256, 128, 64, False), (48, 512, 72, 128, True), (32, 384, 64, 384, False),
     (128, 4096, 512, 128, False),
+    # long groups: the migrating quantizer with 8 waves a group
+    (64, 2048, 136, 1024, False), (32, 4096, 72, 4096, True),
 ])
 def test_scale_search(M, K, N, G, sym):
     X, W = _calibration(7 * M + K, M, K, N, G)

@@ -20,8 +20,8 @@
 // second pass takes packed rows p = r + 8 v, + 8 WPG, ...: it re-reads the
 // group's rows 8 p .. 8 p + 7 (from cache), computes the codes and writes the
 // eight packed words of the chunk as two 16-byte stores.  Bound: HBM, 2 K N
-// bytes read, K N / 2 written.  WPG = 4 for layers with few (group, column)
-// tiles and long groups, so that those are read by enough lanes at once.
+// bytes read, K N / 2 written.  WPG = 4, 8 or 16 for layers with few (group,
+// column) tiles and long groups, so that those are read by enough lanes at once.
 // Groups of 64 to 256 rows are instead read once: the first pass takes the
 // second pass's packed rows and keeps them in registers.
 //
@@ -251,10 +251,20 @@ hipError_t launch_quantize_any(const uint16_t *w, const float *c, int32_t *qweig
     if (G == 64) return launch_q<1, 1, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
     if (G == 128) return launch_q<1, 2, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
     if (G == 256) return launch_q<1, 4, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
-    // One wave per (group, 64 columns); four for long groups (1024 rows or more)
-    // when there are too few tiles to fill the GPU several times over.
+    // One wave per (group, 64 columns) where there are tiles enough.  Long
+    // groups (1024 rows or more) with too few tiles to fill the GPU several
+    // times over are read by 4, 8 or 16 waves: about 32 rows per lane, and
+    // twice the waves where the tiles alone give fewer than 4096 (a 70B layer
+    // with one group per column, 8192 x 28672: 257 us with 4 waves, 230 us
+    // with 16; 4096 x 14336 in groups of 1024: 58 us with 4, 53 us with 8).
     if (blocks >= 4096 || G < 1024)
         return launch_q<1, 0, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
+    // (The migrating form stops at 8 waves: at 16 its registers overflow.)
+    int wpg = G >= 4096 ? 16 : G >= 2048 ? 8 : 4;
+    if (wpg < 16 && blocks * wpg < 4096) wpg *= 2;
+    if constexpr (!MIG)
+        if (wpg == 16) return launch_q<16, 0, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
+    if (wpg >= 8) return launch_q<8, 0, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
     return launch_q<4, 0, MIG>(w, c, q, scales, z, K, N, G, tiles_n, blocks, symmetric, s);
 }
 
