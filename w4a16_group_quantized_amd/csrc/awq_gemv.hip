@@ -29,12 +29,13 @@
 // Kernels:
 //   stream_kernel (M <= 16, G a multiple of 128): each wave stages the slice
 //     of X its K range needs into its own LDS region, odd k divided by 16 so
-//     that the 64-biased upper nibbles need no shift, together with the
-//     per-segment sums U and S; no workgroup barrier before the loop.  Up to
-//     four rows the slice is staged before the first multiply (X must fit
-//     LDS); beyond four, each segment's part is loaded with that segment's
-//     weights and staged into a one-segment slot just before it is
-//     multiplied, so any K fits (also up to four rows when X exceeds LDS);
+//     that the 64-biased upper nibbles need no shift; no workgroup barrier
+//     before the loop.  Up to four rows the slice is staged before the first
+//     multiply (X must fit LDS), together with the per-segment sums U and S;
+//     beyond four, each segment's part is loaded with that segment's weights
+//     and staged into a one-segment slot just before it is multiplied, so any
+//     K fits (also up to four rows when X exceeds LDS), and U and S come from
+//     two more MFMAs per step against constant B operands;
 //   fold_kernel (G a multiple of 32, for shapes the stream kernel does not
 //     take: G not a multiple of 128, or K below 1024): the same fold, with X
 //     from LDS or L2 and S from an MFMA against an all-ones B;
