@@ -72,3 +72,26 @@ def test_summary_traffic_arithmetic(tmp_path, monkeypatch):
     with open(out, "w") as f:
         f.write(stale)
     assert bench.committed_traffic() is None
+
+
+def test_splitk_splits_rule():
+    """The split-K slice count: up to 64 rows the measured rule (at least 512 k
+    per slice, at most 448 workgroups of 64 x 256 up to 32 rows and 256 beyond),
+    beyond 64 rows the cost model; only slice counts the layer allows."""
+    from types import SimpleNamespace
+    from w4a16_group_quantized_amd import binding
+
+    def lay(K, N, G=128):
+        return SimpleNamespace(K=K, N=N, group_size=G)
+    assert binding.splitk_splits(16, lay(4096, 4096)) == 8        # 16 tiles, 512 k a slice
+    assert binding.splitk_splits(16, lay(14336, 4096)) == 16      # 896 k a slice
+    assert binding.splitk_splits(16, lay(4096, 28672)) == 4       # 448 workgroups
+    assert binding.splitk_splits(64, lay(4096, 28672)) == 2       # 256 beyond 32 rows
+    assert binding.splitk_splits(64, lay(4096, 14336)) == 4
+    assert binding.splitk_splits(16, lay(1024, 4096)) == 2        # 512 k a slice at most 2
+    assert binding.splitk_splits(16, lay(4096, 4096, 4096)) == 8  # one group per column
+    assert binding.splitk_splits(16, lay(4096, 4096, 2048)) == 2  # slices of whole groups
+    assert binding.splitk_splits(16, lay(3072, 4096, 1024)) == 1  # 1536 k: not whole groups
+    for M in (96, 512, 2048):                                     # the cost model's range
+        assert binding.splitk_splits(M, lay(4096, 4096)) in (1, 2, 4, 8, 16)
+    assert binding.splitk_splits(2048, lay(4096, 4096)) == 1

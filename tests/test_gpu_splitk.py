@@ -4,7 +4,8 @@ Each slice dequantizes exactly like awq_gemm and sums in fp32; the slices are
 added in a fixed order and rounded once, so the output is held to the layer's
 parity bar and repeated calls are bit-identical.  Cases cover 64-k and 32-k
 steps, group indexing by shift and by division, one group per column, both
-variants, ragged M and N, and the automatic choice of slices.
+variants, ragged M and N, 64-row tiles (up to 64 rows) and 128-row ones, and
+the automatic choice of slices.
 """
 import numpy as np
 import pytest
@@ -26,6 +27,7 @@ pytestmark = pytest.mark.gpu
     (300, 2048, 264, 64, True, 4),       # several row tiles
     (130, 1536, 72, 96, False, 4),       # 32-k steps, group index by division
     (16, 8192, 64, 8192, False, 16),     # one group, 16 slices of 512 k
+    (48, 1536, 72, 96, True, 4),         # 64-row tiles with 32-k steps, group by division
 ])
 def test_splitk_parity(M, K, N, G, sym, splits):
     X, codes, zeros, scales = random_case(7000 + M + K + splits, M, K, N, G, sym)

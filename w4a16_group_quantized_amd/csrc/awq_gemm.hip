@@ -821,12 +821,17 @@ hipError_t launch_gemm_splitk(const uint16_t *x, const int32_t *qweight, const u
     const bool sym = qzeros == nullptr;
     auto *part = static_cast<float *>(workspace);
     hipError_t e;
+    // Up to 64 rows, 64-row tiles: a 128-row tile would spend half its MFMAs
+    // or more on padding rows.
+    const bool rows64 = M <= 64;
+#define AWQ_SPLIT(KBV, MTV)                                                                          \
+    (sym ? m32::launch_split<KBV, MTV, true>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s) \
+         : m32::launch_split<KBV, MTV, false>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s))
     if (splitk_bk(K, G, splits) == 64)
-        e = sym ? m32::launch_split<4, 4, true>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s)
-                : m32::launch_split<4, 4, false>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s);
+        e = rows64 ? AWQ_SPLIT(4, 2) : AWQ_SPLIT(4, 4);
     else
-        e = sym ? m32::launch_split<2, 4, true>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s)
-                : m32::launch_split<2, 4, false>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s);
+        e = rows64 ? AWQ_SPLIT(2, 2) : AWQ_SPLIT(2, 4);
+#undef AWQ_SPLIT
     if (e != hipSuccess) return e;
     const long long count = (long long)M * N;
     long long blocks = (count / 4 + 255) / 256;
