@@ -77,7 +77,9 @@ def test_ragged_parity(entry, M, K, N, G, sym):
 @pytest.mark.parametrize("M,K,N,G", [(37, 200, 136, 8), (130, 1032, 264, 8), (257, 1024, 8, 128),
                                      (300, 4096, 520, 128),
                                      # 32-k steps: G a multiple of 32, K of 128 but not 256
-                                     (130, 640, 264, 32), (300, 384, 520, 128), (65, 896, 136, 64)])
+                                     (130, 640, 264, 32), (300, 384, 520, 128), (65, 896, 136, 64),
+                                     # 64-row tiles (up to 64 rows), 32-k and 64-k steps
+                                     (64, 640, 264, 32), (50, 2048, 200, 128)])
 def test_gemm_large_ragged(M, K, N, G):
     X, codes, zeros, scales = random_case(77 + M, M, K, N, G, False)
     _, Y16 = oracle_case(X, codes, zeros, scales, G)

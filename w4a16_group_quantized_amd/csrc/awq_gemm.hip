@@ -785,8 +785,8 @@ hipError_t launch_general(const uint16_t *x, const int32_t *qw, const uint16_t *
 
 // Kernel choice: 256-row tiles with 32-k steps for large batches (half the
 // dequantization per MFMA), as long as they fill the GPU twice over; 128-row
-// tiles with 64-k steps otherwise; 32-k steps when G or K only allow those;
-// the general kernel for the rest.
+// tiles with 64-k steps otherwise, 64-row ones up to 64 rows; 32-k steps when
+// G or K only allow those; the general kernel for the rest.
 hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                   uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
     const bool sym = qz == nullptr;
@@ -796,9 +796,17 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
     if (k32 && wide_tiles >= 512)
         return sym ? m32::launch<2, 8, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
                    : m32::launch<2, 8, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+    // Up to 64 rows, 64-row tiles: a 128-row tile would spend half its MFMAs
+    // or more on padding rows.
+    if (k64 && M <= 64)
+        return sym ? m32::launch<4, 2, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
+                   : m32::launch<4, 2, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
     if (k64)
         return sym ? m32::launch<4, 4, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
                    : m32::launch<4, 4, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (k32 && M <= 64)
+        return sym ? m32::launch<2, 2, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
+                   : m32::launch<2, 2, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
     if (k32)
         return sym ? m32::launch<2, 4, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
                    : m32::launch<2, 4, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
