@@ -124,7 +124,7 @@ def test_gemm_gate_up_workload(name, M):
 
 @pytest.mark.parametrize("M,K,I,G,sym", [
     (37, 512, 200, 64, False), (130, 256, 8, 128, True), (1, 1024, 264, 256, False),
-    (257, 768, 136, 768, True),
+    (257, 768, 136, 768, True), (64, 1024, 136, 128, True), (65, 512, 72, 64, False),
 ])
 def test_gemm_gate_up_ragged(M, K, I, G, sym):
     X, codes, zeros, scales = random_case(1300 + M + I, M, K, 2 * I, G, sym)

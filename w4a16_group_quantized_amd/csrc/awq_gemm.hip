@@ -856,6 +856,11 @@ bool gemm_gate_up_supported(int K, int N, int G) {
 hipError_t launch_gemm_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                                const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
                                hipStream_t s) {
+    // Up to 64 rows, 64-row tiles, as in awq_gemm.
+    if (M <= 64)
+        return qzeros == nullptr
+                   ? gemm::m32::launch<4, 2, true, true>(x, qweight, scales, qzeros, h, M, K, N, G, s)
+                   : gemm::m32::launch<4, 2, false, true>(x, qweight, scales, qzeros, h, M, K, N, G, s);
     return qzeros == nullptr
                ? gemm::m32::launch<4, 4, true, true>(x, qweight, scales, qzeros, h, M, K, N, G, s)
                : gemm::m32::launch<4, 4, false, true>(x, qweight, scales, qzeros, h, M, K, N, G, s);
