@@ -35,6 +35,17 @@ namespace gemm {
 constexpr int kBN = 256;      // tile columns (4 waves x 64)
 constexpr int kBK = 64;       // k per step
 constexpr int kXcds = 8;      // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr int kCus = kXcds * 32;
+
+// 64-row tiles (MT 2) instead of 128-row ones: up to 64 rows, where a 128-row
+// tile spends half its MFMAs or more on padding, and wherever 64-row tiles
+// still fit one per CU, where they double the workgroups at work (4096 x 4096
+// at 512 rows: 44.4 -> 38.5 us; 4096 x 28672 at 128 rows: 48.5 -> 42.0 us;
+// beyond one tile per CU the 128-row tiles are faster).  Each output's sum
+// runs over k in the same order either way: the results are bit-identical.
+inline bool rows64(int M, int N) {
+    return M <= 64 || (long long)((M + 63) / 64) * ((N + kBN - 1) / kBN) <= kCus;
+}
 constexpr int kGroupM = 4;    // tile rows per band of the tile order
 
 // Workgroup id -> output tile (tm, tn).  Ids are dealt to XCDs round-robin, so
@@ -785,8 +796,8 @@ hipError_t launch_general(const uint16_t *x, const int32_t *qw, const uint16_t *
 
 // Kernel choice: 256-row tiles with 32-k steps for large batches (half the
 // dequantization per MFMA), as long as they fill the GPU twice over; 128-row
-// tiles with 64-k steps otherwise, 64-row ones up to 64 rows; 32-k steps when
-// G or K only allow those; the general kernel for the rest.
+// tiles with 64-k steps otherwise, 64-row ones where rows64 says; 32-k steps
+// when G or K only allow those; the general kernel for the rest.
 hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                   uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
     const bool sym = qz == nullptr;
@@ -796,15 +807,14 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
     if (k32 && wide_tiles >= 512)
         return sym ? m32::launch<2, 8, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
                    : m32::launch<2, 8, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
-    // Up to 64 rows, 64-row tiles: a 128-row tile would spend half its MFMAs
-    // or more on padding rows.
-    if (k64 && M <= 64)
+    const bool small = rows64(M, N);
+    if (k64 && small)
         return sym ? m32::launch<4, 2, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
                    : m32::launch<4, 2, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
     if (k64)
         return sym ? m32::launch<4, 4, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
                    : m32::launch<4, 4, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (k32 && M <= 64)
+    if (k32 && small)
         return sym ? m32::launch<2, 2, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
                    : m32::launch<2, 2, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
     if (k32)
@@ -856,8 +866,9 @@ bool gemm_gate_up_supported(int K, int N, int G) {
 hipError_t launch_gemm_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                                const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
                                hipStream_t s) {
-    // Up to 64 rows, 64-row tiles, as in awq_gemm.
-    if (M <= 64)
+    // 64-row tiles where they pay, as in awq_gemm (the tile count is the same:
+    // 128 output columns are 256 layer columns).
+    if (gemm::rows64(M, N))
         return qzeros == nullptr
                    ? gemm::m32::launch<4, 2, true, true>(x, qweight, scales, qzeros, h, M, K, N, G, s)
                    : gemm::m32::launch<4, 2, false, true>(x, qweight, scales, qzeros, h, M, K, N, G, s);
