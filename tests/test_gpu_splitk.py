@@ -28,6 +28,7 @@ pytestmark = pytest.mark.gpu
     (130, 1536, 72, 96, False, 4),       # 32-k steps, group index by division
     (16, 8192, 64, 8192, False, 16),     # one group, 16 slices of 512 k
     (48, 1536, 72, 96, True, 4),         # 64-row tiles with 32-k steps, group by division
+    (200, 2048, 264, 128, False, 4),     # 64-row tiles beyond 64 rows (4 x 2 tiles x 4 slices)
 ])
 def test_splitk_parity(M, K, N, G, sym, splits):
     X, codes, zeros, scales = random_case(7000 + M + K + splits, M, K, N, G, sym)
