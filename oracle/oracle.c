@@ -50,13 +50,15 @@
  *       (pyshine.com AutoAWQ tour, "The Quantization Flow Up Close": the
  *       pseudo-quantization pass; "From Install to Your First Model":
  *       zero_point, q_group_size, w_bit).  The pages give no formula; this is
- *       textbook min-max, with every decision that yields an integer taken in
- *       fp32 (IEEE, round to nearest even), the precision the GPU kernel uses:
+ *       textbook min-max:
  *         asymmetric: r = hi - lo (r = |hi| if hi == lo), s = fp16(r / 15),
  *                     z = clamp(rint(-lo / s), 0, 15)
  *         symmetric:  r = max |w|, s = fp16(r / 7), z = 8
  *         both:       s = 1 if it rounds to 0; q = clamp(rint(w / s) + z, 0, 15)
- *       with lo, hi the group's minimum and maximum.
+ *       with lo, hi the group's minimum and maximum.  The scale is the exact
+ *       real r / 15 (or r / 7) rounded once to fp16.  The two decisions that
+ *       yield integers (z and q) are taken in fp32 (IEEE, round to nearest
+ *       even), the precision the GPU kernel decides them in.
  *   R12 fused gate/up: the layer's N = 2I columns are [gate | up]; the output
  *       is h[m][n] = fp16(SiLU(y(m, n)) * y(m, I + n)), n < I, with y the
  *       layer's exact (unrounded) sums and SiLU(t) = t / (1 + e^-t), rounded
@@ -300,8 +302,20 @@ void oracle_gate_up(const double *Y64, int M, int I, uint16_t *H16)
 }
 
 /* ------------------------------------------------------------------------- */
-/* Quantizer (R13).  float arithmetic is IEEE single precision here (SSE, no */
-/* contraction), the same precision the GPU kernel decides in.               */
+/* Quantizer (R13).                                                          */
+/*                                                                           */
+/* Scale: the group's extremes are fp16 values, so hi - lo is exact in       */
+/* double (two halves span at most 2^-24 .. 2^16, 40 bits < 53).  The double */
+/* quotient range / 15 then rounds to fp16 exactly as the real quotient      */
+/* would: the real quotient either equals an fp16 rounding midpoint m (then */
+/* m, with 12 significant bits, is a double and the correctly rounded double */
+/* quotient is m itself) or lies at least 2^-42 |q| away from every midpoint (range - 15 m */
+/* is a nonzero multiple of the smaller of their lowest bits), far beyond    */
+/* the double's 2^-53 relative error.  The same holds for max|w| / 7.  So    */
+/* oracle_d2h of the double quotient is the exact scale rounded once.        */
+/*                                                                           */
+/* Codes and zero points: float arithmetic is IEEE single precision here     */
+/* (SSE, no contraction), the precision the GPU kernel decides them in.      */
 /* ------------------------------------------------------------------------- */
 
 static float clamp_code(float v)
@@ -321,16 +335,17 @@ void oracle_quantize(const uint16_t *W, int K, int N, int G, int symmetric,
                 if (w > hi) hi = w;
                 if (fabsf(w) > amax) amax = fabsf(w);
             }
-            float r, z;
+            double r;
+            float z;
             if (symmetric) {
-                r = amax / 7.0f;
+                r = (double)amax / 7.0;
                 z = 8.0f;
             } else {
-                float range = hi - lo;
-                if (range == 0.0f) range = fabsf(hi);
-                r = range / 15.0f;
+                double range = (double)hi - (double)lo;
+                if (range == 0.0) range = fabs((double)hi);
+                r = range / 15.0;
             }
-            uint16_t sh = oracle_d2h((double)r);
+            uint16_t sh = oracle_d2h(r);
             if ((sh & 0x7FFF) == 0) sh = 0x3C00;            /* 1.0 */
             float sv = (float)oracle_h2d(sh);
             if (!symmetric) z = clamp_code(rintf(-lo / sv));

@@ -60,6 +60,32 @@ def _same_halves(a, b):
     return bool(np.all((a == b) | (nan_a & nan_b)))
 
 
+def _frac_to_half(q):
+    """IEEE binary16 bits of the rational q rounded once, to nearest, ties to
+    even (exact rational arithmetic; overflow to infinity at 65520)."""
+    q = Fraction(q)
+    sign = 0x8000 if q < 0 else 0
+    a = -q if q < 0 else q
+    if a == 0:
+        return sign
+    if a >= 65520:
+        return sign | 0x7C00
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                               # now 2^e <= a < 2^(e+1)
+    e = max(e, -14)                          # subnormals share the exponent -14
+    m = a / Fraction(2) ** (e - 10)          # significand in units of the last place
+    n = m.numerator // m.denominator
+    rest = m - n
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    if n == 2048:                            # rounded up into the next binade
+        n, e = 1024, e + 1
+    if n < 1024:                             # subnormal
+        return sign | n
+    return sign | ((e + 15) << 10) | (n - 1024)
+
+
 def _pack_by_hand(codes_col):
     """One word from eight codes, code j in bits 4j.. (for building inputs only)."""
     w = 0
@@ -502,8 +528,10 @@ def pin_quantize_nearest_code(o):
         w = _np_h2d(W)
         for g in range(K // G):
             blk = w[g * G:(g + 1) * G]
-            r = (blk.max(0) - blk.min(0)) / 15.0 if not sym else np.abs(blk).max(0) / 7.0
-            assert np.array_equal(S[g], _np_d2h(r.astype(np.float32).astype(np.float64))), sym
+            for n in range(N):
+                col = [Fraction(float(v)) for v in blk[:, n]]
+                r = (max(col) - min(col)) / 15 if not sym else max(abs(v) for v in col) / 7
+                assert int(S[g][n]) == _frac_to_half(r), (sym, g, n)
             s = _np_h2d(S[g])
             z = np.full(N, 8) if sym else Z[g].astype(np.int64)
             levels = (np.arange(16)[:, None] - z[None, :]) * s[None, :]      # [16][N]
@@ -512,6 +540,69 @@ def pin_quantize_nearest_code(o):
                 best = err.min(0)
                 got = err[codes[k], np.arange(N)]
                 assert np.all(got <= best * (1 + 1e-6) + 1e-12), (sym, k)
+
+
+def _scale_groups(o, pairs, symmetric):
+    """Quantize one 8-row group per column whose extremes are the given fp16
+    (hi, lo) pairs (the other rows lie between them); return the scales."""
+    pairs = list(pairs)
+    N = -(-len(pairs) // 8) * 8
+    hi = np.full(N, 0x3C00, dtype=np.uint16)
+    lo = np.full(N, 0xBC00, dtype=np.uint16)
+    for i, (h, l) in enumerate(pairs):
+        hi[i], lo[i] = h, l
+    W = np.empty((8, N), dtype=np.uint16)
+    W[0], W[1:] = hi, lo
+    _, S, _ = o.quantize(W, 8, symmetric)
+    return S[0][:len(pairs)]
+
+
+def pin_quantize_scale_exact(o):
+    """The scale is the exact (hi - lo) / 15 (or max|w| / 7) rounded once to
+    fp16, checked with rational arithmetic.  The fp16 extremes hi = 693.5,
+    lo = -0.015594482421875 give (hi - lo) / 15 = 46.2343729..., which rounds
+    to 46.21875 (0x51C7); forming hi - lo in fp32 first lands on a tie and
+    gives 46.25 (0x51C8).  More such groups come from a seeded search over
+    random fp16 extremes for pairs where an fp32 range or quotient would
+    round differently; their expected scales are computed exactly here.
+    Symmetric: every positive finite fp16 max|w|, exhaustively."""
+    h = lambda v: int(np.float16(v).view(np.uint16))
+    want = _frac_to_half((Fraction(693.5) + Fraction(0.015594482421875)) / 15)
+    assert want == 0x51C7
+    S = _scale_groups(o, [(h(693.5), h(-0.015594482421875))], False)
+    assert int(S[0]) == 0x51C7, hex(int(S[0]))
+
+    rng = np.random.default_rng(34)
+    a = rng.integers(0, 0x7C00, 1 << 21).astype(np.uint16)
+    b = rng.integers(0, 0x7C00, 1 << 21).astype(np.uint16) | np.uint16(0x8000)
+    fa = a.view(np.float16).astype(np.float32)
+    fb = b.view(np.float16).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        f32 = ((fa - fb) / np.float32(15)).astype(np.float16).view(np.uint16)
+        f64 = ((fa.astype(np.float64) - fb) / 15.0).astype(np.float16).view(np.uint16)
+    # candidates only: the expected value of each is the exact one below
+    cand = np.nonzero((f32 != f64) & np.isfinite(fa - fb))[0][:48]
+    pairs = []
+    for i in cand:
+        exact = _frac_to_half((Fraction(float(fa[i])) - Fraction(float(fb[i]))) / 15)
+        if exact != int(f32[i]):
+            pairs.append((int(a[i]), int(b[i]), exact))
+    assert len(pairs) >= 8, len(pairs)
+    # and a plain sample of ordinary pairs
+    for i in range(200):
+        exact = _frac_to_half((Fraction(float(fa[i])) - Fraction(float(fb[i]))) / 15)
+        pairs.append((int(a[i]), int(b[i]), exact))
+    S = _scale_groups(o, [(p[0], p[1]) for p in pairs], False)
+    for (hh, ll, exact), got in zip(pairs, S):
+        want = exact if exact & 0x7FFF else 0x3C00
+        assert int(got) == want, (hex(hh), hex(ll), hex(int(got)), hex(want))
+
+    amax = np.arange(1, 0x7C00, dtype=np.uint16)
+    S = _scale_groups(o, [(int(v), 0) for v in amax], True)
+    for v, got in zip(amax, S):
+        exact = _frac_to_half(Fraction(float(np.uint16(v).view(np.float16))) / 7)
+        want = exact if exact & 0x7FFF else 0x3C00
+        assert int(got) == want, (hex(int(v)), hex(int(got)), hex(want))
 
 
 def pin_quantize_round_trip_bound(o):

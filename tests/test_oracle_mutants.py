@@ -42,8 +42,11 @@ MUTANTS = [
     ("matmul_w_transposed", "acc[n] += x * wrow[n];", "acc[n] += x * Wd[((size_t)n * K + k) % ((size_t)K * N)];", 0),
     ("matmul_fp32_accumulate", "acc[n] += x * wrow[n];", "acc[n] = (float)(acc[n] + x * wrow[n]);", 0),
     ("matmul_y_row_offset", "Y16[(size_t)m * N + n] = oracle_d2h(acc[n]);", "Y16[(size_t)m * N + n] = oracle_d2h(acc[(n + 1) % N]);", 0),
-    ("quant_range_16", "r = range / 15.0f;", "r = range / 16.0f;", 0),
-    ("quant_sym_8", "r = amax / 7.0f;", "r = amax / 8.0f;", 0),
+    ("quant_range_16", "r = range / 15.0;", "r = range / 16.0;", 0),
+    ("quant_sym_8", "r = (double)amax / 7.0;", "r = (double)amax / 8.0;", 0),
+    # the scale's range or quotient formed in fp32 before the fp16 rounding
+    ("quant_range_fp32", "double range = (double)hi - (double)lo;", "double range = (double)(hi - lo);", 0),
+    ("quant_quotient_fp32", "r = range / 15.0;", "r = (double)((float)range / 15.0f);", 0),
     ("quant_zero_sign", "z = clamp_code(rintf(-lo / sv));", "z = clamp_code(rintf(lo / sv));", 0),
     ("quant_truncate", "clamp_code(rintf(w / sv) + z)", "clamp_code(truncf(w / sv) + z)", 0),
     ("quant_no_clamp_low", "return v < 0.0f ? 0.0f : (v > 15.0f ? 15.0f : v);", "return v > 15.0f ? 15.0f : v;", 0),
