@@ -1,7 +1,8 @@
 """GPU parity of the group quantizer (awq_quantize) against the oracle.
 
-Codes, scales and zero points are integers or fp16 bit patterns decided in
-fp32 on both sides, so they are compared bit for bit.  Shapes cover several
+Codes and zero points are integers decided in fp32 on both sides, and each
+scale is the exact (hi - lo) / 15 or max|w| / 7 rounded once to fp16, so all
+three are compared bit for bit.  Shapes cover several
 group sizes (including one group per column), ragged column counts, both
 variants, weights spanning many magnitudes, constant and all-zero groups, and
 a Llama-shaped layer; the quantized layer then runs through the fused GEMV
@@ -96,3 +97,37 @@ def test_quantize_exact_ties():
     assert np.array_equal(W16.astype(np.float64), W)          # all exact in fp16
     codes, _, _, _ = _check(W16.view(np.uint16), G, False, "exact ties")
     assert codes.max() <= 15
+
+
+def test_quantize_scale_rounded_once():
+    """Groups whose exact range / 15 rounds differently from the same range or
+    quotient formed in fp32: hi = 693.5, lo = -0.015594482421875 (exact scale
+    46.21875, 0x51C7; 46.25 through fp32), and the first such pairs of a seeded
+    draw of fp16 extremes.  Symmetric: every positive finite fp16 max|w|."""
+    rng = np.random.default_rng(34)
+    a = rng.integers(0, 0x7C00, 1 << 21).astype(np.uint16)
+    b = rng.integers(0, 0x7C00, 1 << 21).astype(np.uint16) | np.uint16(0x8000)
+    fa = a.view(np.float16).astype(np.float32)
+    fb = b.view(np.float16).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        f32 = ((fa - fb) / np.float32(15)).astype(np.float16).view(np.uint16)
+        f64 = ((fa.astype(np.float64) - fb) / 15.0).astype(np.float16).view(np.uint16)
+    pick = np.nonzero((f32 != f64) & np.isfinite(fa - fb))[0][:248]
+    hi = np.concatenate([[np.float16(693.5).view(np.uint16)], a[pick], a[:255 - len(pick)]])
+    lo = np.concatenate([[np.float16(-0.015594482421875).view(np.uint16)], b[pick],
+                         b[:255 - len(pick)]])
+    N = len(hi)
+    assert N % 8 == 0
+    W = np.empty((16, N), dtype=np.uint16)
+    W[0], W[1:8] = hi, lo                 # group 0: extremes hi, lo
+    W[8:] = hi                            # group 1: constant hi
+    W[9] = lo                             #          ... with one lo row
+    codes, S, Z, _ = _check(W, 8, False, "scale rounded once")
+    assert int(S[0][0]) == 0x51C7
+
+    amax = np.arange(1, 0x7C00, dtype=np.uint16)
+    amax = np.concatenate([amax, np.zeros((-len(amax)) % 8, dtype=np.uint16)])
+    W = np.zeros((8, len(amax)), dtype=np.uint16)
+    W[0] = amax
+    W[1] = amax | 0x8000                  # -max|w| in the same group
+    _check(W, 8, True, "symmetric scale, every max|w|")

@@ -4,12 +4,19 @@
 // and zero point (pyshine.com AutoAWQ tour, "The Quantization Flow Up Close":
 // the pseudo-quantization pass; "From Install to Your First Model":
 // zero_point, q_group_size, w_bit).  The pages give no formula; this is
-// textbook min-max, every decision that yields an integer taken in fp32 with
-// round-to-nearest-even (correctly rounded division, rint):
+// textbook min-max:
 //   asymmetric: r = hi - lo (|hi| for a constant group), s = fp16(r / 15),
 //               z = clamp(rint(-lo / s), 0, 15)
 //   symmetric:  s = fp16(max|w| / 7), z = 8
 //   both:       s = 1 if it rounds to 0; q = clamp(rint(w / s) + z, 0, 15)
+// The scale is the exact real r / 15 (or r / 7) rounded once to fp16: the
+// range of two fp16 values is exact in fp64 (at most 40 significant bits), and
+// the fp64 quotient is never closer to an fp16 rounding midpoint than the real
+// one unless both equal it (they differ by 2^-53 relative; a real quotient
+// that is not a midpoint lies at least 2^-42 relative away from all of them),
+// so rounding it to fp16 once gives the exact scale.  The integer decisions (z
+// and the codes) are taken in fp32 with round-to-nearest-even (correctly
+// rounded division, rint).
 //
 // A workgroup of WPG waves owns one group of 64 columns: lane (c, r) =
 // (lane / 8, lane % 8) of wave v takes the 8 columns 8 c .. 8 c + 7 and the
@@ -48,6 +55,20 @@ __device__ __forceinline__ float rint_quotient(float w, float s, float inv) {
     const float t = __builtin_rintf(q);
     if (fabsf(q - t) >= 0.5f - fabsf(q) * 0x1p-21f) return __builtin_rintf(w / s);
     return t;
+}
+
+// fp16 bits of a finite x >= 0, rounded once to nearest, ties to even.
+__device__ __forceinline__ uint16_t f64_to_f16_rne(double x) {
+    if (x >= 65520.0) return 0x7C00u;                // rounds to infinity
+    if (x == 0.0) return 0u;
+    int e = ilogb(x);
+    if (e < -14) e = -14;                            // subnormals share exponent -14
+    int n = (int)__builtin_rint(ldexp(x, 10 - e));   // exact scaling, then RNE
+    if (n == 2048) {                                 // carried into the next binade
+        n = 1024;
+        ++e;
+    }
+    return n < 1024 ? (uint16_t)n : (uint16_t)(((e + 15) << 10) | (n - 1024));
 }
 
 // Columns of one column chunk, one chunk per eight lanes.
@@ -174,15 +195,15 @@ quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Q, uint16
     uint32_t sh[4] = {0u, 0u, 0u, 0u}, zword = 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float rg;
+        double rg;
         if (SYM) {
-            rg = amax[i] / 7.0f;
+            rg = (double)amax[i] / 7.0;
         } else {
-            float range = hi[i] - lo[i];
-            if (range == 0.0f) range = fabsf(hi[i]);
-            rg = range / 15.0f;
+            double range = (double)hi[i] - (double)lo[i];
+            if (range == 0.0) range = fabs((double)hi[i]);
+            rg = range / 15.0;
         }
-        uint16_t s16 = as_u16((half_t)rg);
+        uint16_t s16 = f64_to_f16_rne(rg);
         if ((s16 & 0x7FFFu) == 0u) s16 = 0x3C00u;   // 1.0
         sv[i] = (float)as_half(s16);
         inv[i] = 1.0f / sv[i];
