@@ -59,8 +59,8 @@ typedef enum awq_status {
     AWQ_ERROR_SHAPE = 2,         /* a shape rule above is broken               */
     AWQ_ERROR_ALIGNMENT = 3,     /* a tensor pointer is not 16-byte aligned    */
     AWQ_ERROR_UNSUPPORTED = 4,   /* valid layer, but outside this entry point (gemv: M > 16) */
-    AWQ_ERROR_HIP = 5,           /* the HIP runtime refused the launch          */
-    AWQ_ERROR_WORKSPACE = 6      /* workspace NULL, unaligned or too small      */
+    AWQ_ERROR_WORKSPACE = 5,     /* workspace NULL, unaligned or too small      */
+    AWQ_ERROR_HIP = 6            /* the HIP runtime refused the launch          */
 } awq_status;
 
 /* Non-owning view of one quantized linear layer (logical weight W[K][N]). */
@@ -87,27 +87,48 @@ awq_status awq_pack(const uint8_t *codes, int32_t *qweight, int32_t K, int32_t N
 
 /*
  * awq_pack_zeros: zeros uint8 [groups][N] -> qzeros int32 [groups][N/8],
- * eight consecutive columns per word (the stored zero points of the pages'
- * asymmetric, zero_point=True configuration).  groups = K / G.
+ * eight consecutive columns per word, zero of column 8c + j in bits 4j..4j+3
+ * of word c (bits above the low nibble of each byte are ignored).  groups =
+ * K / G.  The layer stores one zero point per group beside its scale, and
+ * asymmetric quantization (zero_point=True) uses them (mbrenndoerfer.com,
+ * "AWQ > Implementation", "Understanding the Quantization Structure": the
+ * qzeros tensor; pyshine.com AutoAWQ tour, "From Install to Your First
+ * Model": zero_point).  Done once per layer, when it is loaded.
  */
 awq_status awq_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int32_t groups,
                           int32_t N, void *stream);
 
 /*
  * awq_dequant: materializes W[K][N] fp16 from the layer, bit-exactly
- * w = fp16_rne(scale * (code - zero)).  Not on the decode path (the fused
- * kernels never write W); it exposes the exact dequantization the fused
- * kernels perform.  w_out: device fp16 [K][N].
+ * w = fp16_rne(scale * (code - zero)): the weight of a code is its scale times
+ * its distance from the zero point, 8 in the symmetric form (fak explainer,
+ * "Format Specification > Dequantization Formula"; with the stored per-group
+ * zero points of mbrenndoerfer.com, "AWQ > Implementation", "Understanding
+ * the Quantization Structure").  Not on the decode path (the fused kernels
+ * never write W); it exposes the exact dequantization the fused kernels
+ * perform.  w_out: device fp16 [K][N], 16-byte aligned (AWQ_ERROR_ALIGNMENT);
+ * NULL is AWQ_ERROR_INVALID_VALUE.
  */
 awq_status awq_dequant(const awq_layer *layer, uint16_t *w_out, void *stream);
 
 /*
  * awq_gemv: fused dequantize-and-multiply for small batches, 1 <= M <= 16 (the
- * pages' matrix-vector module for single-token decoding).  Streams the packed
+ * pages' matrix-vector module for single-token decoding: pyshine.com AutoAWQ
+ * tour, the overview bullet on WQLinear_GEMM / WQLinear_GEMV; fak explainer, "Integration with Forward
+ * Pass": one matrix-vector call over a quantized tensor).  Streams the packed
  * weight once.  M > 16 returns AWQ_ERROR_UNSUPPORTED; use awq_gemm.
+ *   x: device fp16 [M][K];  y: device fp16 [M][N], 16-byte aligned.
+ *   workspace: device scratch of at least awq_gemv_workspace_bytes(M, K, N)
+ *     bytes, owned by the caller.  The query returns 0 for every shape (the
+ *     K-split partial sums are reduced inside each workgroup, through LDS), so
+ *     workspace may be NULL with workspace_bytes 0; a non-NULL workspace must
+ *     be 16-byte aligned (AWQ_ERROR_WORKSPACE otherwise).  It is never read or
+ *     written.
  */
+size_t awq_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N);
+
 awq_status awq_gemv(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
-                    void *stream);
+                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * awq_gemm: fused dequantize-and-multiply for any M >= 0 (the pages' GEMM
@@ -128,13 +149,15 @@ awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int3
  * integer levels against a scale and zero point: pyshine.com AutoAWQ tour,
  * "The Quantization Flow Up Close"; zero_point / q_group_size / w_bit in
  * "From Install to Your First Model").  Per group of G rows and column n,
- * textbook min-max with every integer decision in fp32 (round to nearest
- * even, correctly rounded division):
+ * textbook min-max:
  *   asymmetric (symmetric == 0): r = hi - lo (|hi| for a constant group),
  *       s = fp16(r / 15), z = clamp(rint(-lo / s), 0, 15)
  *   symmetric (symmetric != 0): s = fp16(max|w| / 7), zero point 8
  *   both: s = 1 if it rounds to 0; code = clamp(rint(w / s) + z, 0, 15)
- * lo, hi: the group's minimum and maximum.  Weights must be finite.
+ * lo, hi: the group's minimum and maximum.  The scale is the exact real
+ * r / 15 (or r / 7) rounded once to fp16 (round to nearest even); z and the
+ * codes are decided in fp32 (correctly rounded division, round to nearest
+ * even).  Weights must be finite.
  *   w: device fp16 [K][N].  Outputs as in awq_layer: qweight int32 [K/8][N],
  *   scales fp16 [K/G][N], qzeros int32 [K/G][N/8] (not written, and may be
  *   NULL, when symmetric).  Shape and alignment rules are the layer's.

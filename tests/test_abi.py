@@ -19,6 +19,7 @@ HEADER = os.path.join(ROOT, "include", "awq.h")
 
 FAKE = 0x10000000          # 16-byte aligned, never dereferenced
 MISALIGNED = FAKE + 2
+WS = binding.AWQ_ERROR_WORKSPACE
 
 
 def header_functions():
@@ -55,6 +56,13 @@ def layer(K=128, N=64, G=128, qw=FAKE, sc=FAKE, qz=FAKE):
     return binding.CLayer(qw, sc, qz, K, N, G)
 
 
+def _call(lib, fn, x, c, y, M):
+    """One layer call; awq_gemv also takes its (empty) workspace."""
+    if fn == "awq_gemv":
+        return lib.awq_gemv(x, c, y, M, None, 0, None)
+    return getattr(lib, fn)(x, c, y, M, None)
+
+
 @pytest.mark.parametrize("fn", ["awq_gemv", "awq_gemm", "awq_gemv_gate_up", "awq_gemm_gate_up"])
 @pytest.mark.parametrize("case,want", [
     (dict(K=0), 1), (dict(N=-8), 1), (dict(G=0), 1),
@@ -65,28 +73,53 @@ def layer(K=128, N=64, G=128, qw=FAKE, sc=FAKE, qz=FAKE):
 ])
 def test_layer_validation(lib, fn, case, want):
     c = layer(**case)
-    got = getattr(lib, fn)(FAKE, ctypes.byref(c), FAKE, 1, None)
+    got = _call(lib, fn, FAKE, ctypes.byref(c), FAKE, 1)
     assert got == want
 
 
 @pytest.mark.parametrize("fn", ["awq_gemv", "awq_gemm", "awq_gemv_gate_up", "awq_gemm_gate_up"])
 def test_io_validation(lib, fn):
     c = layer()
-    f = getattr(lib, fn)
-    assert f(FAKE, None, FAKE, 1, None) == 1               # null layer
-    assert f(None, ctypes.byref(c), FAKE, 1, None) == 1    # null x
-    assert f(FAKE, ctypes.byref(c), None, 1, None) == 1    # null y
-    assert f(FAKE, ctypes.byref(c), FAKE, -1, None) == 1   # negative M
-    assert f(MISALIGNED, ctypes.byref(c), FAKE, 1, None) == 3
-    assert f(FAKE, ctypes.byref(c), MISALIGNED, 1, None) == 3
-    assert f(FAKE, ctypes.byref(c), FAKE, 1 << 30, None) == 2   # M*K beyond 2^31
+    f = lambda x, cc, y, M: _call(lib, fn, x, cc, y, M)
+    assert f(FAKE, None, FAKE, 1) == 1               # null layer
+    assert f(None, ctypes.byref(c), FAKE, 1) == 1    # null x
+    assert f(FAKE, ctypes.byref(c), None, 1) == 1    # null y
+    assert f(FAKE, ctypes.byref(c), FAKE, -1) == 1   # negative M
+    assert f(MISALIGNED, ctypes.byref(c), FAKE, 1) == 3
+    assert f(FAKE, ctypes.byref(c), MISALIGNED, 1) == 3
+    assert f(FAKE, ctypes.byref(c), FAKE, 1 << 30) == 2   # M*K beyond 2^31
     # M == 0 is an empty batch: success, nothing launched
-    assert f(FAKE, ctypes.byref(c), FAKE, 0, None) == 0
+    assert f(FAKE, ctypes.byref(c), FAKE, 0) == 0
 
 
 def test_gemv_rejects_large_batches(lib):
     c = layer()
-    assert lib.awq_gemv(FAKE, ctypes.byref(c), FAKE, 17, None) == 4
+    assert lib.awq_gemv(FAKE, ctypes.byref(c), FAKE, 17, None, 0, None) == 4
+
+
+def test_gemv_workspace(lib):
+    """The GEMV reduces its K split inside each workgroup: the query is 0 for
+    every shape, a NULL workspace is accepted, a misaligned one is not."""
+    for M, K, N in ((1, 4096, 14336), (16, 4096, 28672), (1, 8192, 28672), (0, 8, 8)):
+        assert lib.awq_gemv_workspace_bytes(M, K, N) == 0
+    c = layer()
+    assert lib.awq_gemv(FAKE, ctypes.byref(c), FAKE, 1, MISALIGNED, 64, None) == WS
+    assert lib.awq_gemv(FAKE, ctypes.byref(c), FAKE, 0, None, 0, None) == 0
+
+
+def test_status_enum_matches_header():
+    """awq_status numbering as the header declares it: invalid value 1, shape 2,
+    alignment 3, unsupported 4, workspace 5, HIP 6."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef enum awq_status \{(.*?)\} awq_status;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    declared = {k: int(v) for k, v in re.findall(r"(AWQ_\w+)\s*=\s*(\d+)", body)}
+    assert declared == {"AWQ_SUCCESS": 0, "AWQ_ERROR_INVALID_VALUE": 1, "AWQ_ERROR_SHAPE": 2,
+                        "AWQ_ERROR_ALIGNMENT": 3, "AWQ_ERROR_UNSUPPORTED": 4,
+                        "AWQ_ERROR_WORKSPACE": 5, "AWQ_ERROR_HIP": 6}
+    for name, value in declared.items():
+        assert getattr(binding, name) == value
+        assert binding.STATUS_NAMES[value] == name
 
 
 def test_gemm_gate_up_validation(lib):
@@ -166,7 +199,7 @@ def test_channel_stats_validation(lib):
     assert call(x=None) == 1 and call(M=0) == 1 and call(xb=None) == 1 and call(G=0) == 1
     assert call(K=260) == 2 and call(N=100) == 2 and call(G=48) == 2
     assert call(x=MISALIGNED) == 3 and call(w=MISALIGNED) == 3
-    assert call(wsp=None) == 6 and call(wsp=MISALIGNED) == 6 and call(nb=ws - 1) == 6
+    assert call(wsp=None) == WS and call(wsp=MISALIGNED) == WS and call(nb=ws - 1) == WS
 
 
 def test_scale_search_validation(lib):
@@ -184,7 +217,7 @@ def test_scale_search_validation(lib):
     assert call(K=260) == 2 and call(G=48) == 2
     assert call(M=1 << 20, K=4096) == 2          # M * K beyond 2^31
     assert call(x=MISALIGNED) == 3
-    assert call(wsp=None) == 6 and call(nb=ws - 1) == 6
+    assert call(wsp=None) == WS and call(nb=ws - 1) == WS
 
 
 def test_gemm_splitk_validation(lib):
@@ -200,7 +233,7 @@ def test_gemm_splitk_validation(lib):
     assert call(M=0) == 0                       # empty batch: nothing launched
     assert call(splits=3) == 4                  # 1024 / 3 is not whole
     assert call(splits=16) == 4                 # 64-k slices: less than a 128-k ring turn
-    assert call(wsp=None) == 6 and call(wsp=MISALIGNED) == 6 and call(nb=ws - 1) == 6
+    assert call(wsp=None) == WS and call(wsp=MISALIGNED) == WS and call(nb=ws - 1) == WS
     lay = layer(K=1024, N=256, G=256)
     assert lib.awq_gemm_splitk(FAKE, ctypes.byref(lay), FAKE, 64, 8, FAKE, 8 * 64 * 256 * 4,
                                None) == 4       # 128-k slices cut the 256-row groups

@@ -20,16 +20,25 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libawq.so")
 
 # Entry points declared in include/awq.h, in declaration order.
-ENTRY_POINTS = ("awq_status_string", "awq_pack", "awq_pack_zeros", "awq_dequant", "awq_gemv",
+ENTRY_POINTS = ("awq_status_string", "awq_pack", "awq_pack_zeros", "awq_dequant",
+                "awq_gemv_workspace_bytes", "awq_gemv",
                 "awq_gemm", "awq_gemv_gate_up", "awq_quantize", "awq_gemm_gate_up",
                 "awq_gemm_splitk_workspace_bytes", "awq_gemm_splitk",
                 "awq_channel_stats_workspace_bytes", "awq_channel_stats",
                 "awq_scale_search_workspace_bytes", "awq_scale_search")
 
+# awq_status values of include/awq.h
 AWQ_SUCCESS = 0
-STATUS_NAMES = {0: "AWQ_SUCCESS", 1: "AWQ_ERROR_INVALID_VALUE", 2: "AWQ_ERROR_SHAPE",
-                3: "AWQ_ERROR_ALIGNMENT", 4: "AWQ_ERROR_UNSUPPORTED", 5: "AWQ_ERROR_HIP",
-                6: "AWQ_ERROR_WORKSPACE"}
+AWQ_ERROR_INVALID_VALUE = 1
+AWQ_ERROR_SHAPE = 2
+AWQ_ERROR_ALIGNMENT = 3
+AWQ_ERROR_UNSUPPORTED = 4
+AWQ_ERROR_WORKSPACE = 5
+AWQ_ERROR_HIP = 6
+STATUS_NAMES = {AWQ_SUCCESS: "AWQ_SUCCESS", AWQ_ERROR_INVALID_VALUE: "AWQ_ERROR_INVALID_VALUE",
+                AWQ_ERROR_SHAPE: "AWQ_ERROR_SHAPE", AWQ_ERROR_ALIGNMENT: "AWQ_ERROR_ALIGNMENT",
+                AWQ_ERROR_UNSUPPORTED: "AWQ_ERROR_UNSUPPORTED",
+                AWQ_ERROR_WORKSPACE: "AWQ_ERROR_WORKSPACE", AWQ_ERROR_HIP: "AWQ_ERROR_HIP"}
 SCALE_SEARCH_MAX_ALPHAS = 64
 
 
@@ -70,10 +79,14 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.awq_dequant.argtypes = [ctypes.POINTER(CLayer), vp, vp]
     lib.awq_quantize.restype = ctypes.c_int
     lib.awq_quantize.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
-    for name in ("awq_gemv", "awq_gemm", "awq_gemv_gate_up", "awq_gemm_gate_up"):
+    for name in ("awq_gemm", "awq_gemv_gate_up", "awq_gemm_gate_up"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.POINTER(CLayer), vp, i32, vp]
+    lib.awq_gemv_workspace_bytes.restype = ctypes.c_size_t
+    lib.awq_gemv_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.awq_gemv.restype = ctypes.c_int
+    lib.awq_gemv.argtypes = [vp, ctypes.POINTER(CLayer), vp, i32, vp, ctypes.c_size_t, vp]
     lib.awq_gemm_splitk_workspace_bytes.restype = ctypes.c_size_t
     lib.awq_gemm_splitk_workspace_bytes.argtypes = [i32, i32, i32]
     lib.awq_gemm_splitk.restype = ctypes.c_int
@@ -106,6 +119,17 @@ def _stream(stream=None) -> int:
     return s.cuda_stream
 
 
+def _new(shape, dtype: torch.dtype, device, stream=None) -> torch.Tensor:
+    """torch.empty for an output or workspace of a call enqueued on ``stream``.
+    The caching allocator ties a block to the stream current at allocation; when
+    the kernels run on another stream, the block is recorded on that stream too,
+    so it is not handed out again before they are done."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+    return t
+
+
 def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
@@ -128,16 +152,33 @@ class Layer:
     group_size: int
 
     def c_struct(self) -> CLayer:
-        return CLayer(_dev(self.qweight, torch.int32, "qweight"),
-                      _dev(self.scales, torch.float16, "scales"),
-                      None if self.qzeros is None else _dev(self.qzeros, torch.int32, "qzeros"),
-                      self.K, self.N, self.group_size)
+        """The C view, after checking that the tensors have the shapes K, N and
+        group_size imply and sit on one device (the library trusts both)."""
+        K, N, G = self.K, self.N, self.group_size
+        if G > 0 and K > 0 and K % G == 0 and K % 8 == 0 and N % 8 == 0:
+            want = {"qweight": (K // 8, N), "scales": (K // G, N), "qzeros": (K // G, N // 8)}
+            for name, t in (("qweight", self.qweight), ("scales", self.scales),
+                            ("qzeros", self.qzeros)):
+                if t is not None and tuple(t.shape) != want[name]:
+                    raise ValueError(f"{name} must be {list(want[name])} for K={K} N={N} "
+                                     f"G={G}, got {list(t.shape)}")
+        for name, t in (("scales", self.scales), ("qzeros", self.qzeros)):
+            if t is not None and t.device != self.qweight.device:
+                raise ValueError(f"{name} is on {t.device}, qweight on {self.qweight.device}")
+        qw = _dev(self.qweight, torch.int32, "qweight")
+        sc = _dev(self.scales, torch.float16, "scales")
+        qz = None if self.qzeros is None else _dev(self.qzeros, torch.int32, "qzeros")
+        return CLayer(qw, sc, qz, K, N, G)
+
+    @property
+    def device(self) -> torch.device:
+        return self.qweight.device
 
 
 def pack(codes: torch.Tensor, stream=None) -> torch.Tensor:
     """uint8 codes [K][N] -> int32 qweight [K/8][N]."""
     K, N = codes.shape
-    out = torch.empty((K // 8, N), dtype=torch.int32, device=codes.device)
+    out = _new((K // 8, N), torch.int32, codes.device, stream)
     _check(load().awq_pack(_dev(codes, torch.uint8, "codes"), out.data_ptr(), K, N,
                            _stream(stream)))
     return out
@@ -146,7 +187,7 @@ def pack(codes: torch.Tensor, stream=None) -> torch.Tensor:
 def pack_zeros(zeros: torch.Tensor, stream=None) -> torch.Tensor:
     """uint8 zeros [K/G][N] -> int32 qzeros [K/G][N/8]."""
     groups, N = zeros.shape
-    out = torch.empty((groups, N // 8), dtype=torch.int32, device=zeros.device)
+    out = _new((groups, N // 8), torch.int32, zeros.device, stream)
     _check(load().awq_pack_zeros(_dev(zeros, torch.uint8, "zeros"), out.data_ptr(), groups, N,
                                  _stream(stream)))
     return out
@@ -171,10 +212,9 @@ def quantize(w: torch.Tensor, group_size: int, symmetric: bool = False, stream=N
     per-group min-max."""
     K, N = w.shape
     dev = w.device
-    qweight = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
-    scales = torch.empty((K // group_size, N), dtype=torch.float16, device=dev)
-    qzeros = None if symmetric else torch.empty((K // group_size, N // 8), dtype=torch.int32,
-                                                 device=dev)
+    qweight = _new((K // 8, N), torch.int32, dev, stream)
+    scales = _new((K // group_size, N), torch.float16, dev, stream)
+    qzeros = None if symmetric else _new((K // group_size, N // 8), torch.int32, dev, stream)
     _check(load().awq_quantize(_dev(w, torch.float16, "w"), K, N, group_size, int(symmetric),
                                qweight.data_ptr(), scales.data_ptr(),
                                None if qzeros is None else qzeros.data_ptr(), _stream(stream)))
@@ -183,32 +223,51 @@ def quantize(w: torch.Tensor, group_size: int, symmetric: bool = False, stream=N
 
 def dequant(layer: Layer, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Exact fp16 W[K][N]."""
-    if out is None:
-        out = torch.empty((layer.K, layer.N), dtype=torch.float16, device=layer.qweight.device)
     c = layer.c_struct()
+    if out is None:
+        out = _new((layer.K, layer.N), torch.float16, layer.device, stream)
     _check(load().awq_dequant(ctypes.byref(c), _dev(out, torch.float16, "out"), _stream(stream)))
     return out
 
 
-def _linear(fn_name: str, x: torch.Tensor, layer: Layer, out: torch.Tensor | None, stream,
-            width: int | None = None):
-    M = x.shape[0]
-    width = layer.N if width is None else width
+def _io(x: torch.Tensor, layer: Layer, out: torch.Tensor | None, stream, width: int):
+    """Checks x [M][K] (and out [M][width]) against the layer; allocates out."""
     if x.dim() != 2 or x.shape[1] != layer.K:
         raise ValueError(f"x must be [M][{layer.K}], got {tuple(x.shape)}")
-    if out is None:
-        out = torch.empty((M, width), dtype=torch.float16, device=x.device)
-    elif tuple(out.shape) != (M, width):
-        raise ValueError(f"out must be [{M}][{width}], got {tuple(out.shape)}")
     c = layer.c_struct()
+    if x.device != layer.device:
+        raise ValueError(f"x is on {x.device}, the layer on {layer.device}")
+    M = x.shape[0]
+    if out is None:
+        out = _new((M, width), torch.float16, x.device, stream)
+    elif tuple(out.shape) != (M, width) or out.device != x.device:
+        raise ValueError(f"out must be [{M}][{width}] on {x.device}, got {tuple(out.shape)} "
+                         f"on {out.device}")
+    return M, c, out
+
+
+def _linear(fn_name: str, x: torch.Tensor, layer: Layer, out: torch.Tensor | None, stream,
+            width: int | None = None):
+    M, c, out = _io(x, layer, out, stream, layer.N if width is None else width)
     _check(getattr(load(), fn_name)(_dev(x, torch.float16, "x"), ctypes.byref(c),
                                     _dev(out, torch.float16, "out"), M, _stream(stream)))
     return out
 
 
-def gemv(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=None):
-    """y = x @ dequant(layer) for 1 <= M <= 16 (decode)."""
-    return _linear("awq_gemv", x, layer, out, stream)
+def gemv(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=None,
+         workspace: torch.Tensor | None = None):
+    """y = x @ dequant(layer) for 1 <= M <= 16 (decode).  The library asks for no
+    workspace here (awq_gemv_workspace_bytes is 0); one may still be passed."""
+    M, c, out = _io(x, layer, out, stream, layer.N)
+    lib = load()
+    need = lib.awq_gemv_workspace_bytes(M, layer.K, layer.N)
+    if workspace is None and need > 0:
+        workspace = _new(need, torch.uint8, x.device, stream)
+    ws = None if workspace is None else _dev(workspace, torch.uint8, "workspace")
+    nbytes = 0 if workspace is None else workspace.numel()
+    _check(lib.awq_gemv(_dev(x, torch.float16, "x"), ctypes.byref(c),
+                        _dev(out, torch.float16, "out"), M, ws, nbytes, _stream(stream)))
+    return out
 
 
 def gemm(x: torch.Tensor, layer: Layer, out: torch.Tensor | None = None, stream=None):
@@ -270,17 +329,12 @@ def gemm_splitk(x: torch.Tensor, layer: Layer, splits: int | None = None,
     """awq_gemm's output with K split across workgroups (``splits`` slices, chosen by
     splitk_splits when None); the fp32 partials go to ``workspace`` (allocated here
     unless given)."""
-    M = x.shape[0]
-    if x.dim() != 2 or x.shape[1] != layer.K:
-        raise ValueError(f"x must be [M][{layer.K}], got {tuple(x.shape)}")
+    M, c, out = _io(x, layer, out, stream, layer.N)
     splits = splitk_splits(M, layer) if splits is None else splits
-    if out is None:
-        out = torch.empty((M, layer.N), dtype=torch.float16, device=x.device)
     lib = load()
     if workspace is None:
         nbytes = lib.awq_gemm_splitk_workspace_bytes(max(M, 1), layer.N, splits)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
-    c = layer.c_struct()
+        workspace = _new(max(nbytes, 16), torch.uint8, x.device, stream)
     _check(lib.awq_gemm_splitk(_dev(x, torch.float16, "x"), ctypes.byref(c),
                                _dev(out, torch.float16, "out"), M, splits,
                                _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
@@ -305,10 +359,10 @@ def channel_stats(x: torch.Tensor, w: torch.Tensor, group_size: int, stream=None
     and the mean over output columns of |w| over its group's largest |w|."""
     M, K, N = _calibration(x, w)
     lib = load()
-    xbar = torch.empty(K, dtype=torch.float32, device=x.device)
-    wbar = torch.empty(K, dtype=torch.float32, device=x.device)
+    xbar = _new(K, torch.float32, x.device, stream)
+    wbar = _new(K, torch.float32, x.device, stream)
     nbytes = lib.awq_channel_stats_workspace_bytes(M, K, N, group_size)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    ws = _new(max(nbytes, 16), torch.uint8, x.device, stream)
     _check(lib.awq_channel_stats(_dev(x, torch.float16, "x"), M, _dev(w, torch.float16, "w"), K, N,
                                  group_size, xbar.data_ptr(), wbar.data_ptr(), ws.data_ptr(),
                                  ws.numel(), _stream(stream)))
@@ -324,12 +378,12 @@ def scale_search(x: torch.Tensor, w: torch.Tensor, group_size: int, alphas, symm
     M, K, N = _calibration(x, w)
     lib = load()
     a = (ctypes.c_float * len(alphas))(*[float(v) for v in alphas])
-    losses = torch.empty(len(alphas), dtype=torch.float64, device=x.device)
-    best = torch.empty(1, dtype=torch.int32, device=x.device)
-    scales = torch.empty(K, dtype=torch.float32, device=x.device)
+    losses = _new(len(alphas), torch.float64, x.device, stream)
+    best = _new(1, torch.int32, x.device, stream)
+    scales = _new(K, torch.float32, x.device, stream)
     if workspace is None:
         nbytes = lib.awq_scale_search_workspace_bytes(M, K, N, group_size)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+        workspace = _new(max(nbytes, 16), torch.uint8, x.device, stream)
     _check(lib.awq_scale_search(_dev(x, torch.float16, "x"), M, _dev(w, torch.float16, "w"), K, N,
                                 group_size, int(symmetric), a, len(alphas), losses.data_ptr(),
                                 best.data_ptr(), scales.data_ptr(),

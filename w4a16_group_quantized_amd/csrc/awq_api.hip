@@ -65,8 +65,8 @@ const char *awq_status_string(awq_status status) {
     case AWQ_ERROR_SHAPE: return "AWQ_ERROR_SHAPE: K%8, N%8, G%8, K%G must be 0 and arrays below 2^31 elements";
     case AWQ_ERROR_ALIGNMENT: return "AWQ_ERROR_ALIGNMENT: tensor pointers must be 16-byte aligned";
     case AWQ_ERROR_UNSUPPORTED: return "AWQ_ERROR_UNSUPPORTED: outside this entry point (awq_gemv takes M <= 16; awq_gemv_gate_up also needs G % 128 == 0 and X in LDS; awq_gemm_gate_up needs G % 64 == 0 and K % 256 == 0; awq_gemm_splitk needs slices of whole groups (or one group) and whole 128- or 256-k ring turns)";
-    case AWQ_ERROR_HIP: return "AWQ_ERROR_HIP: the HIP runtime refused the launch";
     case AWQ_ERROR_WORKSPACE: return "AWQ_ERROR_WORKSPACE: null, unaligned or smaller than the *_workspace_bytes query";
+    case AWQ_ERROR_HIP: return "AWQ_ERROR_HIP: the HIP runtime refused the launch";
     }
     return "AWQ_ERROR_UNKNOWN";
 }
@@ -96,13 +96,22 @@ awq_status awq_dequant(const awq_layer *layer, uint16_t *w_out, void *stream) {
                                         layer->K, layer->N, layer->group_size, as_stream(stream)));
 }
 
+size_t awq_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) {
+    (void)M;
+    (void)K;
+    (void)N;
+    return 0;   // the K split is reduced inside each workgroup (LDS)
+}
+
 awq_status awq_gemv(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
-                    void *stream) {
+                    void *workspace, size_t workspace_bytes, void *stream) {
     awq_status st = check_layer(layer);
     if (st != AWQ_SUCCESS) return st;
     st = check_io(x, y, layer, M);
     if (st != AWQ_SUCCESS || M == 0) return st;
     if (M > 16) return AWQ_ERROR_UNSUPPORTED;
+    if (workspace != nullptr && !aligned16(workspace)) return AWQ_ERROR_WORKSPACE;
+    if (workspace_bytes < awq_gemv_workspace_bytes(M, layer->K, layer->N)) return AWQ_ERROR_WORKSPACE;
     return from_hip(awq::launch_gemv(x, layer->qweight, layer->scales, layer->qzeros, y, M,
                                      layer->K, layer->N, layer->group_size, as_stream(stream)));
 }
