@@ -43,7 +43,7 @@ GEMV kernel, and only while the hash of its sources still matches.
 
 "ceilings" in the JSON line (context, not the metric) are what this part
 sustains on the two bound resources, measured live by the probes in
-w4a16_group_quantized_amd/probes: a plain streaming read of the decode layer's
+probes/ (beside this file): a plain streaming read of the decode layer's
 byte count from the same number of cold copies (the floor for any kernel that
 must read those bytes once), and fp16 MFMA chains on operands that change every
 instruction (the matrix cores' rate once the clock has dropped to the power
@@ -79,7 +79,7 @@ CSRC = os.path.join(ROOT, "w4a16_group_quantized_amd", "csrc")
 # Sources that define each profiled kernel (the launcher declarations in
 # awq_internal.h generate no code): a counter summary is valid only for them.
 KERNEL_SOURCES = {
-    "gemv": ["awq_gemv.hip", "awq_device.h"],
+    "gemv": ["awq_gemv_kernels.h", "awq_device.h"],
     "gemm": ["awq_gemm.hip", "awq_device.h"],
 }
 KERNEL_NAMES = {"gemv": ("stream_kernel", "fold_kernel", "exact_kernel"), "gemm": ("gemm_kernel", "mfma32_kernel")}
@@ -364,10 +364,10 @@ def torch_matmul_context(name, steps):
 
 def _probes():
     import ctypes
-    from w4a16_group_quantized_amd import build as hip_build
-    if not os.path.exists(hip_build.PROBE_LIBRARY):
-        raise RuntimeError(f"{hip_build.PROBE_LIBRARY} is not built (run the package build first)")
-    lib = ctypes.CDLL(hip_build.PROBE_LIBRARY)
+    import probes
+    if not os.path.exists(probes.LIBRARY):
+        raise RuntimeError(f"{probes.LIBRARY} is not built (run `python -m probes` first)")
+    lib = ctypes.CDLL(probes.LIBRARY)
     lib.awq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
                                           ctypes.c_void_p, ctypes.c_void_p]
     lib.awq_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,

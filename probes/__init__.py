@@ -1,0 +1,24 @@
+"""Measurement probes for bench.py: a plain streaming read and an MFMA rate
+probe (``ceilings.hip``), built into ``libawq_probes.so`` here.
+
+They measure what this GPU sustains on the two bound resources (HBM reads and
+fp16 matrix-core chains), as context for the bench line.  They are not part of
+the library and nothing in it loads them.
+
+    python -m probes
+"""
+from __future__ import annotations
+
+import glob
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libawq_probes.so")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the probes with the library's hipcc flags (always recompiles)."""
+    from w4a16_group_quantized_amd import build as hip_build
+    return hip_build.build(LIBRARY, verbose=verbose,
+                           srcs=sorted(glob.glob(os.path.join(HERE, "*.hip"))))
+

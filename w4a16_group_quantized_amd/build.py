@@ -2,11 +2,11 @@
 
     python -m w4a16_group_quantized_amd.build
 
-Every HIP source under ``csrc/`` goes into one shared library next to this
-file.  The measurement probes under ``probes/`` (a plain streaming read and an
-MFMA rate probe, used only by bench.py) go into ``probes/libawq_probes.so``.  Flags: -O3 for gfx950 only; no fast-math and no denormal flushing (the
-dequantized weights must round exactly as IEEE fp16); packed-fp32 VALU
-instructions disabled.
+Every HIP source under ``csrc/`` is compiled to an object in its own hipcc
+process (in parallel) and the objects are linked into one shared library next
+to this file.  Flags: -O3 for gfx950 only; no fast-math and no denormal
+flushing (the dequantized weights must round exactly as IEEE fp16); packed-fp32
+VALU instructions disabled.
 """
 from __future__ import annotations
 
@@ -14,12 +14,11 @@ import glob
 import os
 import shutil
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libawq.so")
-PROBES = os.path.join(HERE, "probes")
-PROBE_LIBRARY = os.path.join(PROBES, "libawq_probes.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -47,25 +46,32 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(out: str = LIBRARY, extra_flags: list[str] | None = None, verbose: bool = False,
-          srcs: list[str] | None = None) -> str:
-    """Compile every HIP source into ``out`` (always recompiles)."""
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), *(srcs or sources()), "-o", out + ".tmp"]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
-        print(" ".join(cmd))
+        print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+
+
+def build(out: str = LIBRARY, extra_flags: list[str] | None = None, verbose: bool = False,
+          srcs: list[str] | None = None, jobs: int | None = None) -> str:
+    """Compile every HIP source into ``out`` (always recompiles): each source to
+    an object in its own hipcc process, in parallel, then one link."""
+    srcs = srcs or sources()
+    objdir = os.path.join(os.path.dirname(out), "_build", os.path.splitext(os.path.basename(out))[0])
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra_flags or [])
+    objs = [os.path.join(objdir, os.path.splitext(os.path.basename(src))[0] + ".o") for src in srcs]
+    jobs = jobs or min(len(srcs), max(1, min(os.cpu_count() or 1, 16)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for f in [ex.submit(_run, [hipcc(), *compile_flags, "-c", src, "-o", obj], verbose)
+                  for src, obj in zip(srcs, objs)]:
+            f.result()
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out + ".tmp"], verbose)
     os.replace(out + ".tmp", out)
     return out
 
 
-def build_probes(verbose: bool = False) -> str:
-    """Compile the measurement probes into ``probes/libawq_probes.so``."""
-    return build(PROBE_LIBRARY, verbose=verbose,
-                 srcs=sorted(glob.glob(os.path.join(PROBES, "*.hip"))))
-
-
 if __name__ == "__main__":
     print(build(verbose=True))
-    print(build_probes(verbose=True))
