@@ -226,6 +226,24 @@ awq_status awq_gemm_splitk(const uint16_t *x, const awq_layer *layer, uint16_t *
                            int32_t splits, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * awq_gemm_splitk_static: awq_gemm_splitk without a caller workspace and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The fp32 partial outputs go into a static scratch array of
+ * AWQ_GEMM_SPLITK_STATIC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on, from the first call there until the process ends; the call itself
+ * allocates nothing.  Same arguments, rules and output as awq_gemm_splitk
+ * (bit-identical: the same kernels), except that splits * M * N * 4 bytes
+ * above the scratch size return AWQ_ERROR_WORKSPACE before any launch.
+ * All calls on one GPU share its scratch: calls that overlap in time on one
+ * GPU (two streams, two host threads) race and give undefined outputs.
+ */
+#define AWQ_GEMM_SPLITK_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+awq_status awq_gemm_splitk_static(const uint16_t *x, const awq_layer *layer, uint16_t *y,
+                                  int32_t M, int32_t splits, void *stream);
+
+/*
  * The scale search of AWQ's calibration (pyshine.com AutoAWQ tour, "The
  * Quantization Flow Up Close": per-channel means of normalized weights and of
  * activations, the FP16 module run once as the reference, the candidate

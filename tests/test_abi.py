@@ -237,3 +237,20 @@ def test_gemm_splitk_validation(lib):
     lay = layer(K=1024, N=256, G=256)
     assert lib.awq_gemm_splitk(FAKE, ctypes.byref(lay), FAKE, 64, 8, FAKE, 8 * 64 * 256 * 4,
                                None) == 4       # 128-k slices cut the 256-row groups
+
+
+def test_gemm_splitk_static_validation(lib):
+    """The no-allocation split-K rejects, before any launch, what awq_gemm_splitk
+    rejects, and partial sums beyond its static scratch."""
+    f = lib.awq_gemm_splitk_static
+    lay = layer(K=1024, N=256, G=128)
+    assert f(FAKE, ctypes.byref(lay), FAKE, 64, 0, None) == 1
+    assert f(FAKE, ctypes.byref(lay), FAKE, 64, 17, None) == 1
+    assert f(FAKE, ctypes.byref(lay), FAKE, -1, 4, None) == 1
+    assert f(FAKE, ctypes.byref(lay), FAKE, 0, 4, None) == 0          # empty batch
+    assert f(FAKE, ctypes.byref(lay), FAKE, 64, 3, None) == 4         # 1024 / 3 not whole
+    assert f(MISALIGNED, ctypes.byref(lay), FAKE, 64, 4, None) == 3
+    big = layer(K=4096, N=28672, G=128)
+    scratch = binding.GEMM_SPLITK_STATIC_SCRATCH_BYTES
+    assert 2 * 4096 * 28672 * 4 > scratch
+    assert f(FAKE, ctypes.byref(big), FAKE, 4096, 2, None) == WS

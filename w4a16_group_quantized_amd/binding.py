@@ -23,7 +23,7 @@ LIBRARY = os.path.join(HERE, "libawq.so")
 ENTRY_POINTS = ("awq_status_string", "awq_pack", "awq_pack_zeros", "awq_dequant",
                 "awq_gemv_workspace_bytes", "awq_gemv",
                 "awq_gemm", "awq_gemv_gate_up", "awq_quantize", "awq_gemm_gate_up",
-                "awq_gemm_splitk_workspace_bytes", "awq_gemm_splitk",
+                "awq_gemm_splitk_workspace_bytes", "awq_gemm_splitk", "awq_gemm_splitk_static",
                 "awq_channel_stats_workspace_bytes", "awq_channel_stats",
                 "awq_scale_search_workspace_bytes", "awq_scale_search")
 
@@ -91,6 +91,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.awq_gemm_splitk_workspace_bytes.argtypes = [i32, i32, i32]
     lib.awq_gemm_splitk.restype = ctypes.c_int
     lib.awq_gemm_splitk.argtypes = [vp, ctypes.POINTER(CLayer), vp, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.awq_gemm_splitk_static.restype = ctypes.c_int
+    lib.awq_gemm_splitk_static.argtypes = [vp, ctypes.POINTER(CLayer), vp, i32, i32, vp]
     for name in ("awq_channel_stats_workspace_bytes", "awq_scale_search_workspace_bytes"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_size_t
@@ -339,6 +341,24 @@ def gemm_splitk(x: torch.Tensor, layer: Layer, splits: int | None = None,
                                _dev(out, torch.float16, "out"), M, splits,
                                _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
                                _stream(stream)))
+    return out
+
+
+# Size of the library's static split-K scratch (AWQ_GEMM_SPLITK_STATIC_SCRATCH_BYTES).
+GEMM_SPLITK_STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def gemm_splitk_static(x: torch.Tensor, layer: Layer, splits: int, out: torch.Tensor,
+                       stream=None):
+    """awq_gemm_splitk's output on the library's static per-device scratch: the
+    call allocates nothing (``out`` is required).  Calls overlapping in time on
+    one GPU share that scratch and race."""
+    if out is None:
+        raise ValueError("gemm_splitk_static allocates nothing: pass out [M][N]")
+    M, c, out = _io(x, layer, out, stream, layer.N)
+    _check(load().awq_gemm_splitk_static(_dev(x, torch.float16, "x"), ctypes.byref(c),
+                                         _dev(out, torch.float16, "out"), M, splits,
+                                         _stream(stream)))
     return out
 
 

@@ -194,6 +194,26 @@ awq_status awq_gemm_splitk(const uint16_t *x, const awq_layer *layer, uint16_t *
                                             as_stream(stream)));
 }
 
+awq_status awq_gemm_splitk_static(const uint16_t *x, const awq_layer *layer, uint16_t *y,
+                                  int32_t M, int32_t splits, void *stream) {
+    static_assert(awq::kStaticScratchBytes == AWQ_GEMM_SPLITK_STATIC_SCRATCH_BYTES,
+                  "the header states the scratch size");
+    awq_status st = check_layer(layer);
+    if (st != AWQ_SUCCESS) return st;
+    if (splits < 1 || splits > kMaxSplits) return AWQ_ERROR_INVALID_VALUE;
+    st = check_io(x, y, layer, M);
+    if (st != AWQ_SUCCESS || M == 0) return st;
+    if (splits == 1)
+        return from_hip(awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
+                                         layer->K, layer->N, layer->group_size, as_stream(stream)));
+    if (!awq::gemm_splitk_supported(layer->K, layer->group_size, splits)) return AWQ_ERROR_UNSUPPORTED;
+    if (awq::gemm_splitk_workspace(M, layer->N, splits) > awq::kStaticScratchBytes)
+        return AWQ_ERROR_WORKSPACE;
+    return from_hip(awq::launch_gemm_splitk_static(x, layer->qweight, layer->scales, layer->qzeros,
+                                                   y, M, layer->K, layer->N, layer->group_size,
+                                                   splits, as_stream(stream)));
+}
+
 size_t awq_channel_stats_workspace_bytes(int32_t M, int32_t K, int32_t N, int32_t group_size) {
     if (M <= 0 || K <= 0 || N <= 0 || group_size <= 0 || K % group_size) return 0;
     return awq::channel_stats_workspace(M, K, N, group_size);

@@ -41,6 +41,12 @@ size_t gemm_splitk_workspace(int M, int N, int splits);
 hipError_t launch_gemm_splitk(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                               const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
                               int splits, void *workspace, hipStream_t s);
+// The same on the library's static per-device scratch (splits * M * N * 4
+// bytes must be at most kStaticScratchBytes; hipErrorInvalidValue otherwise).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t launch_gemm_splitk_static(const uint16_t *x, const int32_t *qweight,
+                                     const uint16_t *scales, const int32_t *qzeros, uint16_t *y,
+                                     int M, int K, int N, int G, int splits, hipStream_t s);
 // Scale search (per-channel statistics, candidates, migrated layer, loss).
 constexpr int kScaleSearchMaxAlphas = 64;
 size_t channel_stats_workspace(int M, int K, int N, int G);
