@@ -15,6 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -204,6 +205,55 @@ class Oracle:
             raise MemoryError("oracle_linear could not allocate the dequantized weight")
         return Y64, Y16
 
+
+    def linear_columns(self, X: np.ndarray, Q: np.ndarray, S: np.ndarray,
+                       QZ: np.ndarray | None, G: int, threads: int):
+        """``linear`` computed over column slices by ``threads`` host threads.
+
+        Each output column is summed by one call over its own slice of the layer,
+        in the same increasing-k order, so the result is bit-identical to
+        ``linear``; only the columns are spread over threads (the C calls run
+        without the GIL)."""
+        Q = np.ascontiguousarray(Q, dtype=np.int32)
+        S = np.ascontiguousarray(S, dtype=np.uint16)
+        M, N = X.shape[0], Q.shape[1]
+        if threads <= 1 or N < 16:
+            return self.linear(X, Q, S, QZ, G)
+        blocks = N // 8
+        cuts = [8 * (blocks * i // threads) for i in range(threads + 1)]
+        Y64 = np.empty((M, N), dtype=np.float64)
+        Y16 = np.empty((M, N), dtype=np.uint16)
+
+        def part(i):
+            a, b = cuts[i], cuts[i + 1]
+            if a == b:
+                return
+            qz = None if QZ is None else QZ[:, a // 8:b // 8]
+            y64, y16 = self.linear(X, Q[:, a:b], S[:, a:b], qz, G)
+            Y64[:, a:b], Y16[:, a:b] = y64, y16
+
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(part, range(threads)))
+        return Y64, Y16
+
+    def matmul_w_columns(self, X: np.ndarray, W: np.ndarray, threads: int):
+        """``matmul_w`` over column slices of W on ``threads`` host threads
+        (bit-identical: every column keeps its increasing-k sum)."""
+        M, N = X.shape[0], W.shape[1]
+        if threads <= 1 or N < 16:
+            return self.matmul_w(X, W)
+        cuts = [N * i // threads for i in range(threads + 1)]
+        Y64 = np.empty((M, N), dtype=np.float64)
+        Y16 = np.empty((M, N), dtype=np.uint16)
+
+        def part(i):
+            a, b = cuts[i], cuts[i + 1]
+            if a < b:
+                Y64[:, a:b], Y16[:, a:b] = self.matmul_w(X, W[:, a:b])
+
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(part, range(threads)))
+        return Y64, Y16
 
     # -- quantizer ------------------------------------------------------------
     def quantize(self, W: np.ndarray, G: int, symmetric: bool):

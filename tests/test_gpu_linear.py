@@ -7,6 +7,8 @@ run in the launch configuration the benchmark times; for the two large-batch
 GEMMs the oracle computes a seeded sample of rows (all columns), since every
 output row depends on its own row of X only.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +23,7 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 ENTRY = {"gemv": binding.gemv, "gemm": binding.gemm}
+HOST_THREADS = min(16, len(os.sched_getaffinity(0)))
 
 
 def _sample_rows(M, count, seed):
@@ -29,6 +32,13 @@ def _sample_rows(M, count, seed):
     rng = np.random.default_rng(seed)
     rest = rng.choice(np.arange(1, M - 1), size=count - 2, replace=False)
     return np.sort(np.concatenate([[0, M - 1], rest]))
+
+
+def _leading_and_seeded_rows(M, lead, count, seed):
+    """The first ``lead`` rows, the last one, and ``count`` seeded others."""
+    rng = np.random.default_rng(seed)
+    rest = rng.choice(np.arange(lead, M - 1), size=count, replace=False)
+    return np.unique(np.concatenate([np.arange(lead), [M - 1], rest]))
 
 
 @pytest.mark.parametrize("entry,name", [
@@ -43,8 +53,11 @@ def test_workload_parity(entry, name):
     layer = device_layer(name)
     y = to_host_bits(ENTRY[entry](to_dev(X), layer))
     torch.cuda.synchronize()
-    rows = _sample_rows(w.M, 64 if w.K * w.N <= 1 << 25 else 16, w.wid)
-    _, Y16 = oracle.load().matmul_w(np.ascontiguousarray(X[rows]), W)
+    if w.K * w.N <= 1 << 25:
+        rows = _sample_rows(w.M, 64, w.wid)
+    else:   # the 70B-shape batch: 64 leading rows and 64 seeded ones (rows are independent)
+        rows = _leading_and_seeded_rows(w.M, 64, 64, w.wid)
+    _, Y16 = oracle.load().matmul_w_columns(np.ascontiguousarray(X[rows]), W, HOST_THREADS)
     assert_y_close(y[rows], Y16, f"{entry} {name} rows={len(rows)}")
 
 

@@ -131,3 +131,24 @@ def test_quantize_scale_rounded_once():
     W[0] = amax
     W[1] = amax | 0x8000                  # -max|w| in the same group
     _check(W, 8, True, "symmetric scale, every max|w|")
+
+
+@pytest.mark.parametrize("sym", [False, True])
+def test_quantize_subnormal_scales_and_run(sym):
+    """Groups whose range is below 15 * 2^-14 get subnormal fp16 scales
+    (about 7e-6 here): codes, scales and zeros bit-exact, then the layer
+    through awq_gemv (1 and 16 rows) and awq_gemm (64 rows) against the
+    oracle's layer built from the same codes."""
+    K, N, G = 2048, 1024, 128
+    rng = np.random.default_rng(57)
+    W = (rng.standard_normal((K, N)) * 2e-5).astype(np.float16).view(np.uint16)
+    codes, S, Z, lay = _check(W, G, sym, f"subnormal scales sym={sym}")
+    assert np.mean((S & 0x7C00) == 0) > 0.99                   # subnormal (or zero) scales
+    o = oracle.load()
+    Wq = o.dequant(o.pack(codes), S, None if sym else o.pack_zeros(Z), G)
+    for fn, M in ((binding.gemv, 1), (binding.gemv, 16), (binding.gemm, 64)):
+        X = synth.make_x(M, K, 58 + M)
+        _, Y16 = o.matmul_w(X, Wq)
+        y = to_host_bits(fn(to_dev(X), lay))
+        torch.cuda.synchronize()
+        assert_y_close(y, Y16, f"{fn.__name__} M={M} on subnormal scales sym={sym}")
