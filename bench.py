@@ -18,9 +18,21 @@ timed too, as context; the default run times only cold calls, so that a
 kernel-trace profile of it averages the same calls the value comes from.
 
 Prints one JSON line: value = algorithmic bytes per step / time per step, in
-GB/s.  Also reported: the roofline of the dominant kernel (awq_gemv), the
-batched GEMM (awq_gemm, prefill shape M=2048) in TFLOP/s, and the CPU oracle
-timed on a bounded sample of the same workload.
+GB/s.  Also reported:
+* roofline: the dominant kernel (awq_gemv's decode kernel) against 8 TB/s;
+* gemm: the batched GEMM (awq_gemm, prefill shape M=2048) in TFLOP/s against
+  the fp16 MFMA peak;
+* configs: every workload configuration, each timed the same way on its entry
+  points -- the tiny layer (launch-bound), the decode layer, the fused gate/up
+  layer at 16 rows through awq_gemv, awq_gemv_gate_up and awq_gemm (the
+  GEMV/GEMM crossover), the prefill GEMM, and the 70B-shape layer at 1 row
+  (awq_gemv) and 4096 rows (awq_gemm) -- with the fraction of the roofline
+  that bounds each;
+* context: torch.matmul (hipBLASLt) on a plain fp16 weight of the prefill
+  shape, not the metric;
+* cpu_baseline: the oracle at every configuration on one host thread and on
+  all of them (bit-identical outputs), the 70B-shape batch from its first 64
+  rows scaled by M / 64; value is the decode layer on all host threads.
 
 Profiling helpers (the figures under profiles/ come from these):
 
@@ -173,15 +185,18 @@ def time_calls(fn_name, x, layers, y, steps, warmup, reps=1, settle_s=0.0):
     return times[0], statistics.median(times), min(times), max(times)
 
 
-def bench_gemv(name, steps, warmup, reps=1, hot=False):
+def bench_gemv(name, steps, warmup, reps=1, hot=False, max_copies=None):
     """awq_gemv on the workload, cycling through enough weight copies that every
     call reads HBM; ``reps`` replays give the median (and min, max); ``hot``
-    adds the same calls on one copy (cache-resident), as context."""
+    adds the same calls on one copy (cache-resident), as context.
+    ``max_copies`` caps the copies (the tiny layer: launch-bound, cache-resident)."""
     import torch
     from w4a16_group_quantized_amd import synth
     w = synth.WORKLOADS[name]
     per_copy = alg_bytes(w, 0)
     copies = max(2, math.ceil(ROTATE_BYTES / per_copy))
+    if max_copies is not None:
+        copies = min(copies, max_copies)
     layers = build_layers(w, copies)
     X = to_dev(synth.make_x(w.M, w.K, w.wid, w.n_outliers, w.outlier_gain))
     y = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
@@ -453,11 +468,14 @@ def ceiling_mfma(blocks=1024, iters=4000, reps=5):
             "frac_of_peak": round(flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
 
 
-def bench_gemm(name, steps, warmup):
+def bench_gemm(name, steps, warmup, rotate=False):
+    """awq_gemm on the workload; ``rotate`` cycles through weight copies (1 GiB)
+    as the GEMV bench does, for batches small enough to be HBM-bound."""
     import torch
     from w4a16_group_quantized_amd import synth
     w = synth.WORKLOADS[name]
-    layers = build_layers(w, 1)
+    copies = max(2, math.ceil(ROTATE_BYTES / alg_bytes(w, 0))) if rotate else 1
+    layers = build_layers(w, copies)
     X = to_dev(synth.make_x(w.M, w.K, w.wid, w.n_outliers, w.outlier_gain))
     y = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
     t = time_calls("gemm", X, layers, y, steps, warmup, settle_s=GEMM_SETTLE_S)
@@ -466,30 +484,79 @@ def bench_gemm(name, steps, warmup):
     torch.cuda.empty_cache()
     return {"workload": name, "M": w.M, "K": w.K, "N": w.N, "group_size": w.G,
             "symmetric": w.symmetric, "entry": "awq_gemm", "us_per_call": t * 1e6,
+            "weight_copies": copies,
             "tflops": flops / t / 1e12, "mfma_frac": flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS}
 
 
-def cpu_baseline(name, budget_s=10.0):
-    """The oracle as it stands, single threaded, from packed inputs to Y, repeated
-    over the whole decode layer until ``budget_s`` seconds have passed."""
+# The oracle's timed samples, one per configuration: (configuration, workload,
+# rows timed or None for all of them).  The 70B-shape batch is timed on its
+# first 64 rows and scaled by M / 64: rows are independent.
+CPU_SAMPLES = (("cfg1", "tiny", None), ("cfg2", "decode_8b_gate", None),
+               ("cfg3", "gate_up_m16", None), ("cfg4", "prefill_out_proj", None),
+               ("cfg5a", "sym70b_m1", None), ("cfg5b", "sym70b_m4096", 64))
+
+
+def host_threads():
+    """Host threads this process may run on (the machine's CPU share)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(min_s=1.0):
+    """The oracle as it stands, from packed inputs to Y (unpack, exact dequant,
+    fp64 matmul), on one thread and on all host threads, at every configuration.
+
+    All threads run the same oracle over column slices of the layer: each
+    column keeps its increasing-k sum, so the outputs are bit-identical to the
+    single-threaded run (checked here).  Each setting repeats whole passes for
+    at least ``min_s`` seconds (one pass for the large configurations).  The
+    headline value is the decode layer on all host threads."""
     import oracle
     from w4a16_group_quantized_amd import synth
-    w = synth.WORKLOADS[name]
-    X, codes, zeros, scales = synth.workload_inputs(w)
     o = oracle.load()
-    Q, QZ = o.pack(codes), (None if zeros is None else o.pack_zeros(zeros))
-    runs, t0 = 0, time.perf_counter()
-    while True:
-        o.linear(X, Q, scales, QZ, w.G)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per = el / runs
-    return {"value": alg_bytes(w, w.M) / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{runs} full passes of the {name} layer (M={w.M} K={w.K} N={w.N}), "
-                      f"unpack + exact dequant + fp64 matmul, {per:.2f} s each",
-            "host": {"cpu": host_cpu_model(), "nproc": os.cpu_count()}}
+    threads = host_threads()
+    results = []
+    for cfg, name, rows in CPU_SAMPLES:
+        w = synth.WORKLOADS[name]
+        X, codes, zeros, scales = synth.workload_inputs(w, M=rows)
+        Q, QZ = o.pack(codes), (None if zeros is None else o.pack_zeros(zeros))
+        scale = w.M / X.shape[0]
+        entry = {"config": cfg, "workload": name, "M": w.M, "K": w.K, "N": w.N,
+                 "rows_timed": X.shape[0]}
+        if scale != 1:
+            entry["extrapolated"] = f"{X.shape[0]} of {w.M} rows timed, x{scale:g}; rows independent"
+        outs = []
+        for th in (1, threads):
+            passes, t0 = 0, time.perf_counter()
+            while True:
+                y64, y16 = o.linear_columns(X, Q, scales, QZ, w.G, th)
+                passes += 1
+                el = time.perf_counter() - t0
+                if el >= min_s:
+                    break
+            outs.append(y16)
+            per = el / passes * scale
+            key = "one_thread" if th == 1 else "all_threads"
+            rec = {"threads": th, "passes": passes, "s_per_call": round(per, 4)}
+            if w.M <= 16:
+                rec["gbs"] = round(alg_bytes(w, w.M) / per / 1e9, 4)
+            else:
+                rec["tflops"] = round(2.0 * w.M * w.N * w.K / per / 1e12, 6)
+            entry[key] = rec
+        entry["bits_identical"] = bool(np.array_equal(outs[0], outs[1]))
+        results.append(entry)
+    head = next(e for e in results if e["workload"] == "decode_8b_gate")
+    return {"value": head["all_threads"]["gbs"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"full passes of the decode_8b_gate layer (M=1 K=4096 N=14336) on {threads} "
+                      f"host threads over column slices, unpack + exact dequant + fp64 matmul, "
+                      f"{head['all_threads']['s_per_call']:.3f} s each "
+                      f"({head['one_thread']['s_per_call']:.3f} s on one thread); "
+                      f"every configuration below at 1 and {threads} threads",
+            "single_thread": {"value": head["one_thread"]["gbs"], "unit": "GB/s", "cores": 1},
+            "configs": results,
+            "host": {"cpu": host_cpu_model(), "nproc": os.cpu_count(), "threads": threads}}
 
 
 def host_cpu_model():
@@ -625,6 +692,31 @@ def committed_traffic():
     return traffic
 
 
+def config_line(cfg, r):
+    """One configuration's figures: time per call and its fraction of the roofline
+    that bounds it (HBM bytes for the GEMV entries, MFMA flops for the GEMMs)."""
+    line = {"config": cfg, "workload": r["workload"], "entry": r["entry"], "M": r["M"], "K": r["K"],
+            "N": r["N"], "group_size": r["group_size"], "symmetric": r["symmetric"],
+            "us_per_call": round(r["us_per_call"], 3)}
+    if "gbs" in r:
+        line.update(bound="hbm", gbs=round(r["gbs"], 1), frac=round(r["hbm_frac"], 4),
+                    weight_copies=r["weight_copies"])
+    else:
+        flops = 2.0 * r["M"] * r["N"] * r["K"]
+        b = alg_bytes(synth_workload(r["workload"]), r["M"])
+        line.update(bound="mfma", tflops=round(r["tflops"], 1), frac=round(r["mfma_frac"], 4),
+                    weight_copies=r["weight_copies"],
+                    hbm_gbs=round(b / (r["us_per_call"] * 1e-6) / 1e9, 1),
+                    hbm_frac=round(b / (r["us_per_call"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    arith_intensity=round(flops / b, 1))
+    return line
+
+
+def synth_workload(name):
+    from w4a16_group_quantized_amd import synth
+    return synth.WORKLOADS[name]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -668,20 +760,25 @@ def main():
 
     head = bench_gemv("decode_8b_gate", args.steps, args.warmup, reps=5, hot=args.all)
     gemm = bench_gemm("prefill_out_proj", args.steps, args.warmup)
+    # Every configuration of the workload list, each on its own entry point(s).
+    configs = [
+        ("cfg1", bench_gemv("tiny", args.steps, args.warmup, max_copies=2)),
+        ("cfg2", head),
+        ("cfg3", bench_gemv("gate_up_m16", args.steps, args.warmup)),
+        ("cfg3", bench_gate_up("gate_up_m16", 16, args.steps, args.warmup)),
+        ("cfg3", bench_gemm("gate_up_m16", args.steps, args.warmup, rotate=True)),
+        ("cfg4", gemm),
+        ("cfg5a", bench_gemv("sym70b_m1", args.steps, args.warmup)),
+        ("cfg5b", bench_gemm("sym70b_m4096", max(5, args.steps // 40), 2)),
+    ]
     extra = []
     if args.all:
-        extra.append(bench_gemv("gate_up_m16", args.steps, args.warmup))
-        extra.append(bench_gemv("sym70b_m1", args.steps, args.warmup))
-        extra.append(bench_gemm("gate_up_m16", args.steps, args.warmup))
-        extra.append(bench_gemm("sym70b_m4096", max(5, args.steps // 40), 2))
-        extra.append(bench_gate_up("gate_up_m16", 16, args.steps, args.warmup))
         extra.append(bench_gate_up("gate_up_m16", 1, args.steps, args.warmup))
         extra.append(bench_gemm_gate_up("gate_up_m16", 2048, 20, 3))
         for m in (64, 256, 512):
             extra.append(bench_gemm_splitk("prefill_out_proj", m, 100, 10))
         extra.append(bench_quantize("decode_8b_gate", 20, 3))
         extra.append(bench_scale_search("decode_8b_gate", 4096, 20, 3))
-        extra.append(torch_matmul_context("prefill_out_proj", 50))
         extra.append(torch_matmul_context("sym70b_m4096", 5))
 
     traffic = committed_traffic()
@@ -716,10 +813,12 @@ def main():
     read, mfma = ceiling_read("decode_8b_gate"), ceiling_mfma()
     out["ceilings"] = {"hbm_read": read, "gemv_frac_of_read": round(head["gbs"] / read["gbs"], 4),
                        "mfma_f16": mfma, "gemm_frac_of_mfma": round(gemm["tflops"] / mfma["tflops"], 4)}
+    out["configs"] = [config_line(cfg, r) for cfg, r in configs]
+    out["context"] = {"torch_matmul": torch_matmul_context("prefill_out_proj", 50)}
     if extra:
         out["extra"] = extra
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline("decode_8b_gate")
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
 
 
