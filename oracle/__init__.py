@@ -78,6 +78,8 @@ class Oracle:
         lib.oracle_pack_zeros.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, _i32p]
         lib.oracle_unpack.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, _u8p]
         lib.oracle_unpack_zeros.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, _u8p]
+        lib.oracle_interleave.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, _i32p]
+        lib.oracle_deinterleave.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, _i32p]
         lib.oracle_dequant_one.restype = ctypes.c_uint16
         lib.oracle_dequant_one.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint16]
         lib.oracle_dequant.argtypes = [_i32p, _u16p, _i32p, ctypes.c_int, ctypes.c_int,
@@ -154,6 +156,22 @@ class Oracle:
         zeros = np.empty((groups, 8 * C), dtype=np.uint8)
         self.lib.oracle_unpack_zeros(_ptr(QZ, _i32p), groups, 8 * C, _ptr(zeros, _u8p))
         return zeros
+
+    # -- kernel-private layout (R17) ------------------------------------------
+    def interleave(self, Q: np.ndarray) -> np.ndarray:
+        """Canonical packed words -> the interleaved layout (even k in the low
+        half-word, odd k in the high half-word)."""
+        Q = np.ascontiguousarray(Q, dtype=np.int32)
+        out = np.empty_like(Q)
+        self.lib.oracle_interleave(_ptr(Q, _i32p), 8 * Q.shape[0], Q.shape[1], _ptr(out, _i32p))
+        return out
+
+    def deinterleave(self, Q: np.ndarray) -> np.ndarray:
+        """The inverse of ``interleave``."""
+        Q = np.ascontiguousarray(Q, dtype=np.int32)
+        out = np.empty_like(Q)
+        self.lib.oracle_deinterleave(_ptr(Q, _i32p), 8 * Q.shape[0], Q.shape[1], _ptr(out, _i32p))
+        return out
 
     # -- dequantization -------------------------------------------------------
     def dequant_one(self, q: int, z: int, s: int) -> int:

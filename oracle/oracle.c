@@ -59,6 +59,12 @@
  *       real r / 15 (or r / 7) rounded once to fp16.  The two decisions that
  *       yield integers (z and q) are taken in fp32 (IEEE, round to nearest
  *       even), the precision the GPU kernel decides them in.
+ *   R17 kernel-private layout (the step after packing, for faster kernels):
+ *       the code of k = 8r + j moves to nibble 4 (j % 2) + j / 2 of the same
+ *       word: even k in the low half-word, odd k in the high half-word.  The
+ *       pages name private packing formats (GEMVFast, Marlin) without giving
+ *       one; oracle_interleave / oracle_deinterleave are that permutation and
+ *       its inverse.
  *   R12 fused gate/up: the layer's N = 2I columns are [gate | up]; the output
  *       is h[m][n] = fp16(SiLU(y(m, n)) * y(m, I + n)), n < I, with y the
  *       layer's exact (unrounded) sums and SiLU(t) = t / (1 + e^-t), rounded
@@ -212,6 +218,38 @@ void oracle_unpack_zeros(const int32_t *QZ, int groups, int N, uint8_t *zeros)
     for (int g = 0; g < groups; ++g)
         for (int n = 0; n < N; ++n)
             zeros[(size_t)g * N + n] = (uint8_t)oracle_zero(QZ, N, g, n);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Kernel-private layout (R17): the same words, nibbles reordered inside each  */
+/* word.  The pages name packing formats private to faster kernels (GEMVFast,  */
+/* Marlin; unpack_reorder_pack repacks bits for another runtime: pyshine.com   */
+/* AutoAWQ tour, "The Quantization Flow Up Close") without giving one; the     */
+/* reading here: the code of k = 8r + j sits at nibble 4 (j % 2) + j / 2 of    */
+/* word [r][n], i.e. the four even k in the low half-word (k 0, 2, 4, 6 at     */
+/* nibbles 0..3) and the four odd k in the high half-word (nibbles 4..7).      */
+/* ------------------------------------------------------------------------- */
+
+static int interleaved_nibble(int j) { return 4 * (j % 2) + j / 2; }
+
+void oracle_interleave(const int32_t *Q, int K, int N, int32_t *out)
+{
+    for (size_t i = 0; i < (size_t)(K / 8) * N; ++i) {
+        uint32_t w = (uint32_t)Q[i], o = 0;
+        for (int j = 0; j < 8; ++j)
+            o |= ((w >> (4 * j)) & 0xFu) << (4 * interleaved_nibble(j));
+        out[i] = (int32_t)o;
+    }
+}
+
+void oracle_deinterleave(const int32_t *Q, int K, int N, int32_t *out)
+{
+    for (size_t i = 0; i < (size_t)(K / 8) * N; ++i) {
+        uint32_t w = (uint32_t)Q[i], o = 0;
+        for (int j = 0; j < 8; ++j)
+            o |= ((w >> (4 * interleaved_nibble(j))) & 0xFu) << (4 * j);
+        out[i] = (int32_t)o;
+    }
 }
 
 /* ------------------------------------------------------------------------- */

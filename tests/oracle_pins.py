@@ -211,6 +211,37 @@ def pin_packed_size(o):
         assert Q.nbytes == K * N // 2 and 2 * K * N == 4 * Q.nbytes
 
 
+def pin_interleave_golden(o):
+    """Hand-worked interleaved words (tests/golden/interleave_words.txt), from
+    the unpacked codes of one column; and back."""
+    for codes, canon, inter in _rows("interleave_words.txt"):
+        col = np.array([int(c) for c in codes.split(",")], dtype=np.uint8)
+        Q = o.pack(col[:, None])
+        assert int(np.uint32(Q[0, 0])) == int(canon, 16), codes
+        I = o.interleave(Q)
+        assert int(np.uint32(I[0, 0])) == int(inter, 16), (codes, hex(int(np.uint32(I[0, 0]))))
+        assert np.array_equal(o.deinterleave(I), Q)
+
+
+def pin_interleave_positions_and_round_trip(o):
+    """On random codes, code k of the interleaved word [k/8][n] is the nibble at
+    bit 4 (4 (k % 2) + (k % 8) / 2), read with Python integers from the
+    unpacked codes; deinterleave undoes interleave and interleave undoes
+    deinterleave on arbitrary 32-bit words (a permutation of nibbles)."""
+    rng = np.random.default_rng(35)
+    K, N = 64, 24
+    codes = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    I = o.interleave(o.pack(codes)).view(np.uint32)
+    for k in range(K):
+        for n in range(0, N, 5):
+            pos = 4 * (k % 2) + (k % 8) // 2
+            assert (int(I[k // 8, n]) >> (4 * pos)) & 0xF == codes[k, n], (k, n)
+    W = rng.integers(-(1 << 31), 1 << 31, (16, 40), dtype=np.int64).astype(np.int32)
+    assert np.array_equal(o.deinterleave(o.interleave(W)), W)
+    assert np.array_equal(o.interleave(o.deinterleave(W)), W)
+    assert not np.array_equal(o.interleave(W), W)
+
+
 # ----------------------------------------------------------------------------
 # dequantization w = fp16(s * (q - z))
 # ----------------------------------------------------------------------------

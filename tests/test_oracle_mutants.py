@@ -51,6 +51,10 @@ MUTANTS = [
     ("quant_truncate", "clamp_code(rintf(w / sv) + z)", "clamp_code(truncf(w / sv) + z)", 0),
     ("quant_no_clamp_low", "return v < 0.0f ? 0.0f : (v > 15.0f ? 15.0f : v);", "return v > 15.0f ? 15.0f : v;", 0),
     ("quant_group_rows", "for (int k = g * G; k < (g + 1) * G; ++k) {\n                float w = (float)oracle_h2d(W[(size_t)k * N + n]);\n                if (w < lo)", "for (int k = g * G; k < (g + 1) * G - 1; ++k) {\n                float w = (float)oracle_h2d(W[(size_t)k * N + n]);\n                if (w < lo)", 0),
+    ("interleave_order", "static int interleaved_nibble(int j) { return 4 * (j % 2) + j / 2; }",
+     "static int interleaved_nibble(int j) { return 2 * (j % 4) + j / 4; }", 0),
+    ("deinterleave_as_interleave", "o |= ((w >> (4 * interleaved_nibble(j))) & 0xFu) << (4 * j);",
+     "o |= ((w >> (4 * j)) & 0xFu) << (4 * interleaved_nibble(j));", 0),
     ("silu_is_sigmoid", "return t / (1.0 + exp(-t));", "return 1.0 / (1.0 + exp(-t));", 0),
     ("silu_exp_sign", "return t / (1.0 + exp(-t));", "return t / (1.0 + exp(t));", 0),
     ("gate_up_swapped", "oracle_silu(row[n]) * row[I + n]", "oracle_silu(row[I + n]) * row[n]", 0),
