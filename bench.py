@@ -121,18 +121,27 @@ def to_dev(a):
     return t.to("cuda")
 
 
+# qweight layout of every benchmarked layer (--layout): canonical, or the
+# kernel-private interleaved one (repacked once after packing, as at load time).
+LAYOUT = {"canonical": 0, "interleaved": 1}
+BENCH_LAYOUT = "canonical"
+
+
 def build_layers(w, copies):
-    """The workload's layer packed on the GPU, then replicated ``copies`` times."""
+    """The workload's layer packed on the GPU (repacked to BENCH_LAYOUT), then
+    replicated ``copies`` times."""
     from w4a16_group_quantized_amd import binding, synth
     import torch
     _, codes, zeros, scales = synth.workload_inputs(w, M=1)
     base = binding.make_layer(to_dev(codes), None if zeros is None else to_dev(zeros),
                               to_dev(scales), w.G)
+    if LAYOUT[BENCH_LAYOUT] != base.layout:
+        base = binding.repack(base, LAYOUT[BENCH_LAYOUT])
     layers = [base]
     for _ in range(copies - 1):
         layers.append(binding.Layer(base.qweight.clone(), base.scales.clone(),
                                     None if base.qzeros is None else base.qzeros.clone(),
-                                    base.K, base.N, base.group_size))
+                                    base.K, base.N, base.group_size, base.layout))
     torch.cuda.synchronize()
     return layers
 
@@ -723,6 +732,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
+    ap.add_argument("--layout", choices=sorted(LAYOUT), default="canonical",
+                    help="qweight layout of the benchmarked layers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--ceilings", action="store_true", help="only measure the two ceilings")
     ap.add_argument("--profile", choices=["gemv", "gemm"], help="dispatch sequence for counter passes")
@@ -734,6 +745,8 @@ def main():
     ap.add_argument("--command", action="append", default=[],
                     help="command line(s) that produced the profiled data, recorded in the summary")
     args = ap.parse_args()
+    global BENCH_LAYOUT
+    BENCH_LAYOUT = args.layout
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1:], args.kind, args.command)
         return
@@ -797,7 +810,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_8b_gate", "M": 1, "K": 4096, "N": 14336, "group_size": 128,
                    "symmetric": False, "entry": "awq_gemv", "weight_copies": head["weight_copies"],
-                   "launch": "hip_graph"},
+                   "launch": "hip_graph", "layout": BENCH_LAYOUT},
         "roofline": {"bound": "hbm", "achieved": round(head["gbs"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(head["hbm_frac"], 4), "traffic": traffic},
         "timing": {"replays": head["reps"]["n"], "calls_each": head["reps"]["calls_each"],

@@ -30,6 +30,8 @@
  *
  * Shape rules (AWQ_ERROR_SHAPE otherwise): K, N, G > 0; K % 8 == 0;
  * N % 8 == 0; G % 8 == 0; K % G == 0; every array below 2^31 elements.
+ * Every call that takes an awq_layer takes it in either qweight layout (see
+ * AWQ_LAYOUT_*) with the same results, bit for bit where the call is exact.
  * M == 0 is an empty batch: success, nothing launched.  M < 0 is invalid.
  *
  * Pointers: every tensor pointer is a DEVICE pointer, 16-byte aligned
@@ -63,14 +65,28 @@ typedef enum awq_status {
     AWQ_ERROR_HIP = 6            /* the HIP runtime refused the launch          */
 } awq_status;
 
-/* Non-owning view of one quantized linear layer (logical weight W[K][N]). */
+/*
+ * Layouts of qweight.  AWQ_LAYOUT_CANONICAL is the layout above.
+ * AWQ_LAYOUT_INTERLEAVED is a kernel-private repacking of the same words
+ * (faster to unpack in the batched kernel; the pages name such formats,
+ * GEMVFast and Marlin, in pyshine.com's AutoAWQ tour, "The Quantization Flow
+ * Up Close", without giving one): the code of k = 8r + j sits in nibble
+ * 4 (j % 2) + j / 2 of word [r][n] -- the even k in the low half-word, the odd
+ * k in the high half-word.  awq_repack converts between the two.
+ */
+#define AWQ_LAYOUT_CANONICAL 0
+#define AWQ_LAYOUT_INTERLEAVED 1
+
+/* Non-owning view of one quantized linear layer (logical weight W[K][N]).
+ * A zero-initialized layout field is the canonical layout. */
 typedef struct awq_layer {
-    const int32_t *qweight;      /* [K/8][N]                                   */
+    const int32_t *qweight;      /* [K/8][N] in `layout`                       */
     const uint16_t *scales;      /* [K/G][N] fp16                              */
     const int32_t *qzeros;       /* [K/G][N/8], or NULL for symmetric (zero 8) */
     int32_t K;
     int32_t N;
     int32_t group_size;          /* G; G == K gives one scale per column        */
+    int32_t layout;              /* AWQ_LAYOUT_*; any other value is AWQ_ERROR_INVALID_VALUE */
 } awq_layer;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -97,6 +113,20 @@ awq_status awq_pack(const uint8_t *codes, int32_t *qweight, int32_t K, int32_t N
  */
 awq_status awq_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int32_t groups,
                           int32_t N, void *stream);
+
+/*
+ * awq_repack: packed words qweight [K/8][N] from layout `from` to layout `to`
+ * (AWQ_LAYOUT_*; from == to copies).  A fixed permutation of the nibbles of
+ * each word, done once per layer when it is loaded: the kernel-private layouts
+ * of the pages' faster kernels are such repackings of the packed weight
+ * (pyshine.com AutoAWQ tour, "The Quantization Flow Up Close": GEMVFast,
+ * Marlin, unpack_reorder_pack).  src and dst: device int32 [K/8][N], 16-byte
+ * aligned; dst may equal src (in place).  K % 8 == 0, N % 8 == 0, K * N below
+ * 2^31 (AWQ_ERROR_SHAPE otherwise); an unknown layout is
+ * AWQ_ERROR_INVALID_VALUE.
+ */
+awq_status awq_repack(const int32_t *src, int32_t *dst, int32_t K, int32_t N, int32_t from,
+                      int32_t to, void *stream);
 
 /*
  * awq_dequant: materializes W[K][N] fp16 from the layer, bit-exactly

@@ -52,8 +52,8 @@ def test_status_strings(lib):
     assert lib.awq_status_string(99).decode() == "AWQ_ERROR_UNKNOWN"
 
 
-def layer(K=128, N=64, G=128, qw=FAKE, sc=FAKE, qz=FAKE):
-    return binding.CLayer(qw, sc, qz, K, N, G)
+def layer(K=128, N=64, G=128, qw=FAKE, sc=FAKE, qz=FAKE, layout=0):
+    return binding.CLayer(qw, sc, qz, K, N, G, layout)
 
 
 def _call(lib, fn, x, c, y, M):
@@ -70,6 +70,7 @@ def _call(lib, fn, x, c, y, M):
     (dict(K=1 << 16, N=1 << 16, G=128), 2),
     (dict(qw=None), 1), (dict(sc=None), 1),
     (dict(qw=MISALIGNED), 3), (dict(sc=MISALIGNED), 3), (dict(qz=MISALIGNED), 3),
+    (dict(layout=2), 1), (dict(layout=-1), 1),
 ])
 def test_layer_validation(lib, fn, case, want):
     c = layer(**case)
@@ -254,3 +255,28 @@ def test_gemm_splitk_static_validation(lib):
     scratch = binding.GEMM_SPLITK_STATIC_SCRATCH_BYTES
     assert 2 * 4096 * 28672 * 4 > scratch
     assert f(FAKE, ctypes.byref(big), FAKE, 4096, 2, None) == WS
+
+
+def test_layout_struct_and_constants():
+    """awq_layer ends with the layout field (a zeroed one is canonical); the
+    header's layout values are the binding's."""
+    assert ctypes.sizeof(binding.CLayer) == 40
+    assert binding.CLayer.layout.offset == 36
+    text = open(HEADER).read()
+    assert re.search(r"#define AWQ_LAYOUT_CANONICAL 0\b", text)
+    assert re.search(r"#define AWQ_LAYOUT_INTERLEAVED 1\b", text)
+    assert binding.LAYOUT_CANONICAL == 0 and binding.LAYOUT_INTERLEAVED == 1
+
+
+def test_repack_validation(lib):
+    f = lib.awq_repack
+    assert f(None, FAKE, 64, 64, 0, 1, None) == 1
+    assert f(FAKE, None, 64, 64, 0, 1, None) == 1
+    assert f(FAKE, FAKE, 0, 64, 0, 1, None) == 1
+    assert f(FAKE, FAKE, 64, 64, 0, 2, None) == 1
+    assert f(FAKE, FAKE, 64, 64, 3, 0, None) == 1
+    assert f(FAKE, FAKE, 60, 64, 0, 1, None) == 2
+    assert f(FAKE, FAKE, 64, 60, 0, 1, None) == 2
+    assert f(FAKE, FAKE, 1 << 16, 1 << 16, 0, 1, None) == 2
+    assert f(MISALIGNED, FAKE, 64, 64, 0, 1, None) == 3
+    assert f(FAKE, FAKE, 64, 64, 1, 1, None) == 0          # same layout, in place: nothing to do

@@ -53,10 +53,11 @@ def test_workload_parity(entry, name):
     layer = device_layer(name)
     y = to_host_bits(ENTRY[entry](to_dev(X), layer))
     torch.cuda.synchronize()
-    if w.K * w.N <= 1 << 25:
-        rows = _sample_rows(w.M, 64, w.wid)
-    else:   # the 70B-shape batch: 64 leading rows and 64 seeded ones (rows are independent)
+    if w.M > 128 and w.K * w.N > 1 << 25:
+        # the 70B-shape batch: 64 leading rows, the last and 64 seeded ones (rows are independent)
         rows = _leading_and_seeded_rows(w.M, 64, 64, w.wid)
+    else:
+        rows = _sample_rows(w.M, 64, w.wid)
     _, Y16 = oracle.load().matmul_w_columns(np.ascontiguousarray(X[rows]), W, HOST_THREADS)
     assert_y_close(y[rows], Y16, f"{entry} {name} rows={len(rows)}")
 

@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libawq.so")
 
 # Entry points declared in include/awq.h, in declaration order.
-ENTRY_POINTS = ("awq_status_string", "awq_pack", "awq_pack_zeros", "awq_dequant",
+ENTRY_POINTS = ("awq_status_string", "awq_pack", "awq_pack_zeros", "awq_repack", "awq_dequant",
                 "awq_gemv_workspace_bytes", "awq_gemv",
                 "awq_gemm", "awq_gemv_gate_up", "awq_quantize", "awq_gemm_gate_up",
                 "awq_gemm_splitk_workspace_bytes", "awq_gemm_splitk", "awq_gemm_splitk_static",
@@ -40,6 +40,9 @@ STATUS_NAMES = {AWQ_SUCCESS: "AWQ_SUCCESS", AWQ_ERROR_INVALID_VALUE: "AWQ_ERROR_
                 AWQ_ERROR_UNSUPPORTED: "AWQ_ERROR_UNSUPPORTED",
                 AWQ_ERROR_WORKSPACE: "AWQ_ERROR_WORKSPACE", AWQ_ERROR_HIP: "AWQ_ERROR_HIP"}
 SCALE_SEARCH_MAX_ALPHAS = 64
+# qweight layouts (AWQ_LAYOUT_* of include/awq.h)
+LAYOUT_CANONICAL = 0
+LAYOUT_INTERLEAVED = 1
 
 
 class AwqError(RuntimeError):
@@ -53,7 +56,7 @@ class CLayer(ctypes.Structure):
 
     _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("qzeros", ctypes.c_void_p), ("K", ctypes.c_int32), ("N", ctypes.c_int32),
-                ("group_size", ctypes.c_int32)]
+                ("group_size", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 _LIB = None
@@ -75,6 +78,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.awq_pack.argtypes = [vp, vp, i32, i32, vp]
     lib.awq_pack_zeros.restype = ctypes.c_int
     lib.awq_pack_zeros.argtypes = [vp, vp, i32, i32, vp]
+    lib.awq_repack.restype = ctypes.c_int
+    lib.awq_repack.argtypes = [vp, vp, i32, i32, i32, i32, vp]
     lib.awq_dequant.restype = ctypes.c_int
     lib.awq_dequant.argtypes = [ctypes.POINTER(CLayer), vp, vp]
     lib.awq_quantize.restype = ctypes.c_int
@@ -152,6 +157,7 @@ class Layer:
     K: int
     N: int
     group_size: int
+    layout: int = LAYOUT_CANONICAL   # of qweight (LAYOUT_*)
 
     def c_struct(self) -> CLayer:
         """The C view, after checking that the tensors have the shapes K, N and
@@ -170,7 +176,7 @@ class Layer:
         qw = _dev(self.qweight, torch.int32, "qweight")
         sc = _dev(self.scales, torch.float16, "scales")
         qz = None if self.qzeros is None else _dev(self.qzeros, torch.int32, "qzeros")
-        return CLayer(qw, sc, qz, K, N, G)
+        return CLayer(qw, sc, qz, K, N, G, self.layout)
 
     @property
     def device(self) -> torch.device:
@@ -193,6 +199,26 @@ def pack_zeros(zeros: torch.Tensor, stream=None) -> torch.Tensor:
     _check(load().awq_pack_zeros(_dev(zeros, torch.uint8, "zeros"), out.data_ptr(), groups, N,
                                  _stream(stream)))
     return out
+
+
+def repack_words(qweight: torch.Tensor, to: int, frm: int = LAYOUT_CANONICAL,
+                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Packed words int32 [K/8][N] from layout ``frm`` to layout ``to`` (LAYOUT_*);
+    ``out`` may be ``qweight`` itself (in place)."""
+    R, N = qweight.shape
+    if out is None:
+        out = _new((R, N), torch.int32, qweight.device, stream)
+    elif tuple(out.shape) != (R, N):
+        raise ValueError(f"out must be [{R}][{N}], got {tuple(out.shape)}")
+    _check(load().awq_repack(_dev(qweight, torch.int32, "qweight"), _dev(out, torch.int32, "out"),
+                             8 * R, N, frm, to, _stream(stream)))
+    return out
+
+
+def repack(layer: Layer, to: int = LAYOUT_INTERLEAVED, stream=None) -> Layer:
+    """The same layer with its packed words in layout ``to`` (a new qweight)."""
+    q = repack_words(layer.qweight, to, layer.layout, stream=stream)
+    return Layer(q, layer.scales, layer.qzeros, layer.K, layer.N, layer.group_size, to)
 
 
 def make_layer(codes: torch.Tensor, zeros: torch.Tensor | None, scales: torch.Tensor,

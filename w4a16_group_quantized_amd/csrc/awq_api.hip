@@ -21,6 +21,8 @@ awq_status check_layer(const awq_layer *w) {
         return AWQ_ERROR_INVALID_VALUE;
     const long long K = w->K, N = w->N, G = w->group_size;
     if (K <= 0 || N <= 0 || G <= 0) return AWQ_ERROR_INVALID_VALUE;
+    if (w->layout != AWQ_LAYOUT_CANONICAL && w->layout != AWQ_LAYOUT_INTERLEAVED)
+        return AWQ_ERROR_INVALID_VALUE;
     if (K % 8 || N % 8 || G % 8 || K % G) return AWQ_ERROR_SHAPE;
     if (K * N > kMaxElems) return AWQ_ERROR_SHAPE;  // the dequantized weight's element count
     if (!aligned16(w->qweight) || !aligned16(w->scales) ||
@@ -41,6 +43,8 @@ awq_status check_io(const uint16_t *x, const uint16_t *y, const awq_layer *w, in
 awq_status from_hip(hipError_t e) { return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP; }
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool interleaved(const awq_layer *w) { return w->layout == AWQ_LAYOUT_INTERLEAVED; }
 
 // Calibration X [M][K] and fp16 weight W [K][N] of the scale search.
 awq_status check_calibration(const uint16_t *x, int32_t M, const uint16_t *w, int32_t K, int32_t N,
@@ -87,13 +91,29 @@ awq_status awq_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int32_t groups,
     return from_hip(awq::launch_pack_zeros(zeros, qzeros, groups, N, as_stream(stream)));
 }
 
+awq_status awq_repack(const int32_t *src, int32_t *dst, int32_t K, int32_t N, int32_t from,
+                      int32_t to, void *stream) {
+    if (src == nullptr || dst == nullptr || K <= 0 || N <= 0) return AWQ_ERROR_INVALID_VALUE;
+    const auto known = [](int32_t l) { return l == AWQ_LAYOUT_CANONICAL || l == AWQ_LAYOUT_INTERLEAVED; };
+    if (!known(from) || !known(to)) return AWQ_ERROR_INVALID_VALUE;
+    if (K % 8 || N % 8 || (long long)K * N > kMaxElems) return AWQ_ERROR_SHAPE;
+    if (!aligned16(src) || !aligned16(dst)) return AWQ_ERROR_ALIGNMENT;
+    const long long words = (long long)(K / 8) * N;
+    if (from == to) {
+        if (src == dst) return AWQ_SUCCESS;
+        return from_hip(hipMemcpyAsync(dst, src, (size_t)words * 4, hipMemcpyDeviceToDevice,
+                                       as_stream(stream)));
+    }
+    return from_hip(awq::launch_repack(src, dst, words, to == AWQ_LAYOUT_INTERLEAVED, as_stream(stream)));
+}
+
 awq_status awq_dequant(const awq_layer *layer, uint16_t *w_out, void *stream) {
     awq_status st = check_layer(layer);
     if (st != AWQ_SUCCESS) return st;
     if (w_out == nullptr) return AWQ_ERROR_INVALID_VALUE;
     if (!aligned16(w_out)) return AWQ_ERROR_ALIGNMENT;
     return from_hip(awq::launch_dequant(layer->qweight, layer->scales, layer->qzeros, w_out,
-                                        layer->K, layer->N, layer->group_size, as_stream(stream)));
+                                        layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
 }
 
 size_t awq_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) {
@@ -113,7 +133,7 @@ awq_status awq_gemv(const uint16_t *x, const awq_layer *layer, uint16_t *y, int3
     if (workspace != nullptr && !aligned16(workspace)) return AWQ_ERROR_WORKSPACE;
     if (workspace_bytes < awq_gemv_workspace_bytes(M, layer->K, layer->N)) return AWQ_ERROR_WORKSPACE;
     return from_hip(awq::launch_gemv(x, layer->qweight, layer->scales, layer->qzeros, y, M,
-                                     layer->K, layer->N, layer->group_size, as_stream(stream)));
+                                     layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
 }
 
 awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
@@ -123,7 +143,7 @@ awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int3
     st = check_io(x, y, layer, M);
     if (st != AWQ_SUCCESS || M == 0) return st;
     return from_hip(awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
-                                     layer->K, layer->N, layer->group_size, as_stream(stream)));
+                                     layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
 }
 
 awq_status awq_quantize(const uint16_t *w, int32_t K, int32_t N, int32_t group_size,
@@ -152,7 +172,7 @@ awq_status awq_gemv_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
         return AWQ_ERROR_UNSUPPORTED;
     return from_hip(awq::launch_gemv_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
                                              layer->K, layer->N, layer->group_size,
-                                             as_stream(stream)));
+                                             interleaved(layer), as_stream(stream)));
 }
 
 awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t *h, int32_t M,
@@ -166,7 +186,7 @@ awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
         return AWQ_ERROR_UNSUPPORTED;
     return from_hip(awq::launch_gemm_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
                                              layer->K, layer->N, layer->group_size,
-                                             as_stream(stream)));
+                                             interleaved(layer), as_stream(stream)));
 }
 
 size_t awq_gemm_splitk_workspace_bytes(int32_t M, int32_t N, int32_t splits) {
@@ -183,7 +203,7 @@ awq_status awq_gemm_splitk(const uint16_t *x, const awq_layer *layer, uint16_t *
     if (st != AWQ_SUCCESS || M == 0) return st;
     if (splits == 1)
         return from_hip(awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
-                                         layer->K, layer->N, layer->group_size, as_stream(stream)));
+                                         layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
     if (!awq::gemm_splitk_supported(layer->K, layer->group_size, splits)) return AWQ_ERROR_UNSUPPORTED;
     if ((long long)splits * M * layer->N > kMaxElems) return AWQ_ERROR_SHAPE;
     if (workspace == nullptr || !aligned16(workspace) ||
@@ -191,7 +211,7 @@ awq_status awq_gemm_splitk(const uint16_t *x, const awq_layer *layer, uint16_t *
         return AWQ_ERROR_WORKSPACE;
     return from_hip(awq::launch_gemm_splitk(x, layer->qweight, layer->scales, layer->qzeros, y, M,
                                             layer->K, layer->N, layer->group_size, splits, workspace,
-                                            as_stream(stream)));
+                                            interleaved(layer), as_stream(stream)));
 }
 
 awq_status awq_gemm_splitk_static(const uint16_t *x, const awq_layer *layer, uint16_t *y,
@@ -205,13 +225,13 @@ awq_status awq_gemm_splitk_static(const uint16_t *x, const awq_layer *layer, uin
     if (st != AWQ_SUCCESS || M == 0) return st;
     if (splits == 1)
         return from_hip(awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
-                                         layer->K, layer->N, layer->group_size, as_stream(stream)));
+                                         layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
     if (!awq::gemm_splitk_supported(layer->K, layer->group_size, splits)) return AWQ_ERROR_UNSUPPORTED;
     if (awq::gemm_splitk_workspace(M, layer->N, splits) > awq::kStaticScratchBytes)
         return AWQ_ERROR_WORKSPACE;
     return from_hip(awq::launch_gemm_splitk_static(x, layer->qweight, layer->scales, layer->qzeros,
                                                    y, M, layer->K, layer->N, layer->group_size,
-                                                   splits, as_stream(stream)));
+                                                   splits, interleaved(layer), as_stream(stream)));
 }
 
 size_t awq_channel_stats_workspace_bytes(int32_t M, int32_t K, int32_t N, int32_t group_size) {

@@ -132,6 +132,57 @@ __device__ __forceinline__ uint4 dequant_word_natural(uint32_t w, uint32_t mask,
     return pairs_to_natural(d);
 }
 
+// ---------------------------------------------------------------------------
+// Kernel-private interleaved words (the layout awq_repack makes): the code of
+// k = 8r + j sits at nibble 4 (j % 2) + j / 2, i.e. the even k of the word in
+// the low half-word (k 2i at nibble i) and the odd k in the high half-word
+// (k 2i + 1 at nibble 4 + i).  Each natural-order pair (k 2e, k 2e + 1) is then
+// at the same bit of the two half-words.
+constexpr uint32_t kHighNibblePairMask = 0x00F000F0u;
+// fp16 0x5400 | (c << 4) is exactly 64 + c: exponent 2^6, ulp 1/16, so a nibble
+// at bits 4..7 of a half counts units.
+constexpr uint32_t kBias64x2 = 0x54005400u;
+
+// The high-nibble pair mask in a vector register (see nibble_mask_vgpr).
+__device__ __forceinline__ uint32_t high_mask_vgpr() {
+    uint32_t v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(kHighNibblePairMask));
+    return v;
+}
+
+// Interleaved word -> the four natural-order pairs
+//   p[e] = (b_e + q_2e, b_e + q_2e+1),  b_e = 1024 for even e, 64 for odd e,
+// with one shift and four AND-ORs.  lo_mask / hi_mask: kNibblePairMask and
+// kHighNibblePairMask, in vector registers.
+__device__ __forceinline__ void unpack_interleaved(uint32_t w, uint32_t lo_mask, uint32_t hi_mask,
+                                                   uint32_t p[4]) {
+    const uint32_t w8 = w >> 8;
+    p[0] = (w & lo_mask) | kBias1024x2;
+    p[1] = (w & hi_mask) | kBias64x2;
+    p[2] = (w8 & lo_mask) | kBias1024x2;
+    p[3] = (w8 & hi_mask) | kBias64x2;
+}
+
+// Bytes (0, 2, 1, 3) of w: swaps the middle two bytes.
+__device__ __forceinline__ uint32_t swap_middle_bytes(uint32_t w) {
+    return __builtin_amdgcn_perm(w, w, 0x03010200u);
+}
+// Swaps nibbles 1 and 2 of each half-word.
+__device__ __forceinline__ uint32_t swap_middle_nibbles(uint32_t w) {
+    const uint32_t d = ((w >> 4) ^ w) & 0x00F000F0u;
+    return w ^ d ^ (d << 4);
+}
+// Interleaved word -> canonical word (code j at nibble j), and back.  The
+// half-words of an interleaved word hold (k0 k2 k4 k6 | k1 k3 k5 k7); after the
+// byte swap they hold (k0 k2 k1 k3 | k4 k6 k5 k7), and the nibble swap gives
+// (k0 k1 k2 k3 | k4 k5 k6 k7).
+__device__ __forceinline__ uint32_t deinterleave_word(uint32_t w) {
+    return swap_middle_nibbles(swap_middle_bytes(w));
+}
+__device__ __forceinline__ uint32_t interleave_word(uint32_t w) {
+    return swap_middle_bytes(swap_middle_nibbles(w));
+}
+
 // 1024 + z as fp16, from the 4-bit zero point z.
 __device__ __forceinline__ half_t biased_zero(uint32_t z) {
     return __builtin_bit_cast(half_t, (uint16_t)(0x6400u | (z & 0xFu)));

@@ -118,11 +118,12 @@ __device__ __forceinline__ void global_to_lds16(const void *src, uint4 *dst) {
 // General path, for the shapes the 32x32 kernels below do not take (G not a
 // multiple of 32 or K not a multiple of 128): 16x16x32 MFMAs, packed words in
 // registers, clamped addresses, and the weights of k past K zeroed.
+// il: interleaved packed words, turned back to canonical order as they are read.
 template <int BM, bool SYM>
 __global__ void __launch_bounds__(256)
 gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
-            uint16_t *__restrict__ Y, int M, int K, int N, int G) {
+            uint16_t *__restrict__ Y, int M, int K, int N, int G, int il) {
     constexpr int MT = BM / 16;                    // 16-row MFMA tiles per wave
     constexpr int ACH = BM * kBK / 8 / 256;        // X chunks per thread per step
     constexpr int P = kRing - 1;                   // steps loaded ahead
@@ -219,7 +220,10 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             decode(cur.sc[s], cur.zw[s]);
-            const uint32_t q4[4] = {cur.q[s].x, cur.q[s].y, cur.q[s].z, cur.q[s].w};
+            uint32_t q4[4] = {cur.q[s].x, cur.q[s].y, cur.q[s].z, cur.q[s].w};
+            if (il)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q4[i] = deinterleave_word(q4[i]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t p[4], d[4];
@@ -362,7 +366,11 @@ __device__ __forceinline__ void unpack_natural(uint32_t w, uint32_t exps, uint32
 // MFMA columns are then 32 gate columns and the same 32 columns of the up half
 // (column tile 0: gate, tile 1: up, for the same output column), and the
 // output is h[M][I] = fp16(SiLU(gate) * up), 32 columns per wave.
-template <int KB, int MT, bool SYM, int GMODE, bool GU, bool SPLIT = false>
+// IL: the packed words are in the kernel-private interleaved layout; each
+// natural-order pair is then one AND-OR (unpack_interleaved), against the two
+// v_perm + AND of the canonical word, and the bias of a pair is 1024 + z for
+// the even pairs and 64 + z for the odd ones.
+template <int KB, int MT, bool SYM, int GMODE, bool GU, bool SPLIT = false, bool IL = false>
 __global__ void __launch_bounds__(256)
 mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
@@ -494,10 +502,13 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         return r;
     };
     const uint32_t exps = 0x54006400u;
+    const uint32_t lo_mask = IL ? nibble_mask_vgpr() : 0u, hi_mask = IL ? high_mask_vgpr() : 0u;
     half8_t bA[KB][2], bB[KB][2];
-    // Biased zero pairs (1024 + z, 64 + z) and scale pairs of the two columns.
+    // Biased zero pairs and scale pairs of the two columns: (1024 + z, 64 + z)
+    // for every canonical pair; for interleaved words (1024 + z, 1024 + z) for
+    // the even pairs (bz2) and (64 + z, 64 + z) for the odd ones (bzo).
     struct Dq {
-        half2_t bz2[2], s2[2];
+        half2_t bz2[2], bzo[2], s2[2];
     };
     auto decode = [&](const Raw &r) {
         Dq dq;
@@ -505,7 +516,13 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             const uint32_t z = (z2 >> (4 * ct)) & 0xFu;
-            dq.bz2[ct] = as_half2(0x54006400u | (z << 20) | z);
+            if constexpr (IL) {
+                dq.bz2[ct] = as_half2(kBias1024x2 | (z << 16) | z);
+                dq.bzo[ct] = as_half2(kBias64x2 | (z << 20) | (z << 4));
+            } else {
+                dq.bz2[ct] = as_half2(0x54006400u | (z << 20) | z);
+                dq.bzo[ct] = dq.bz2[ct];
+            }
             const half_t sv = as_half((uint16_t)(r.sc >> (16 * ct)));
             dq.s2[ct] = half2_t{sv, sv};
         }
@@ -536,13 +553,15 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             uint32_t p[4], d[4];
-            unpack_natural(ct ? r.q[kb].y : r.q[kb].x, exps, p);
+            if constexpr (IL) unpack_interleaved(ct ? r.q[kb].y : r.q[kb].x, lo_mask, hi_mask, p);
+            else unpack_natural(ct ? r.q[kb].y : r.q[kb].x, exps, p);
             // One group: B is q - z (exact small integers); the column's scale
             // multiplies the fp32 sums once, in the epilogue.
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                d[e] = ONEG ? as_u32(as_half2(p[e]) - dq.bz2[ct])
-                            : dequant_pair(p[e], dq.bz2[ct], dq.s2[ct]);
+            for (int e = 0; e < 4; ++e) {
+                const half2_t bz = e % 2 ? dq.bzo[ct] : dq.bz2[ct];
+                d[e] = ONEG ? as_u32(as_half2(p[e]) - bz) : dequant_pair(p[e], bz, dq.s2[ct]);
+            }
             b[ct] = as_half8(make_uint4(d[0], d[1], d[2], d[3]));
         }
     };
@@ -558,7 +577,7 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     // A(kt + 1, kb 0) and the packed weights of kt + 2, and the loads of step
     // kt + 4 go into the ring slots of kt.  Neither LDS latency nor the
     // barrier reaches the matrix cores by more than a block's lead.
-    constexpr int VG = KB == 2 ? 2 : 4;   // dequantization VALU per MFMA (about)
+    constexpr int VG = KB == 2 ? 2 : (IL ? 3 : 4);   // dequantization VALU per MFMA (about)
     half8_t a0[kMT], a1[kMT];
     Raw r;
     // One group: the lane's scale pair (columns n0 + 2 j, +1) and zero word,
@@ -696,7 +715,7 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         }
 }
 
-template <int KB, int MT, bool SYM, bool GU>
+template <int KB, int MT, bool SYM, bool GU, bool IL>
 hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                   uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
     using Gm = Geom<KB, MT>;
@@ -710,16 +729,16 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
     const auto *z = reinterpret_cast<const uint32_t *>(qz);
     if constexpr (!GU) {
         if (G == K) {
-            hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 2, false>), dim3((unsigned)tiles), dim3(256),
+            hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 2, false, false, IL>), dim3((unsigned)tiles), dim3(256),
                                0, s, x, q, sc, z, y, M, K, N, G, 0, K);
             return hipGetLastError();
         }
     }
     if (gshift >= 0)
-        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 1, GU>), dim3((unsigned)tiles), dim3(256), 0,
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 1, GU, false, IL>), dim3((unsigned)tiles), dim3(256), 0,
                            s, x, q, sc, z, y, M, K, N, G, gshift, K);
     else
-        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 0, GU>), dim3((unsigned)tiles), dim3(256), 0,
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 0, GU, false, IL>), dim3((unsigned)tiles), dim3(256), 0,
                            s, x, q, sc, z, y, M, K, N, G, 0, K);
     return hipGetLastError();
 }
@@ -727,7 +746,7 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
 // Split K: `splits` slices of K / splits k, each a whole number of steps and
 // of groups (or inside the single group), as a second grid dimension; fp32
 // partial tiles into part[splits][M][N].
-template <int KB, int MT, bool SYM>
+template <int KB, int MT, bool SYM, bool IL>
 hipError_t launch_split(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                         float *part, int M, int K, int N, int G, int splits, hipStream_t s) {
     using Gm = Geom<KB, MT>;
@@ -739,13 +758,13 @@ hipError_t launch_split(const uint16_t *x, const int32_t *qw, const uint16_t *sc
     auto *y = reinterpret_cast<uint16_t *>(part);
     const int gsteps = G / Gm::BK;
     if (G == K)
-        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 2, false, true>), grid, dim3(256), 0, s, x, q, sc,
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 2, false, true, IL>), grid, dim3(256), 0, s, x, q, sc,
                            z, y, M, K, N, G, 0, kslice);
     else if ((gsteps & (gsteps - 1)) == 0)
-        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 1, false, true>), grid, dim3(256), 0, s, x, q, sc,
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 1, false, true, IL>), grid, dim3(256), 0, s, x, q, sc,
                            z, y, M, K, N, G, __builtin_ctz((unsigned)gsteps), kslice);
     else
-        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 0, false, true>), grid, dim3(256), 0, s, x, q, sc,
+        hipLaunchKernelGGL((mfma32_kernel<KB, MT, SYM, 0, false, true, IL>), grid, dim3(256), 0, s, x, q, sc,
                            z, y, M, K, N, G, 0, kslice);
     return hipGetLastError();
 }
@@ -786,11 +805,12 @@ inline int splitk_bk(int K, int G, int splits) {
 
 template <int BM, bool SYM>
 hipError_t launch_general(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
+                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
+                          hipStream_t s) {
     const long long tiles = (long long)((M + BM - 1) / BM) * ((N + kBN - 1) / kBN);
     hipLaunchKernelGGL((gemm_kernel<BM, SYM>), dim3((unsigned)tiles), dim3(256), 0, s, x,
                        reinterpret_cast<const uint32_t *>(qw), sc,
-                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
+                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G, il ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -798,30 +818,37 @@ hipError_t launch_general(const uint16_t *x, const int32_t *qw, const uint16_t *
 // dequantization per MFMA), as long as they fill the GPU twice over; 128-row
 // tiles with 64-k steps otherwise, 64-row ones where rows64 says; 32-k steps
 // when G or K only allow those; the general kernel for the rest.
-hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
-                  uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
+template <bool IL>
+hipError_t launch_layout(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
+                         uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
     const bool sym = qz == nullptr;
     const bool k32 = G % 32 == 0 && K % (kRing * 32) == 0;
     const bool k64 = G % 64 == 0 && K % (kRing * 64) == 0;
     const long long wide_tiles = (long long)((M + 255) / 256) * ((N + kBN - 1) / kBN);
     if (k32 && wide_tiles >= 512)
-        return sym ? m32::launch<2, 8, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
-                   : m32::launch<2, 8, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+        return sym ? m32::launch<2, 8, true, false, IL>(x, qw, sc, qz, y, M, K, N, G, s)
+                   : m32::launch<2, 8, false, false, IL>(x, qw, sc, qz, y, M, K, N, G, s);
     const bool small = rows64(M, N);
     if (k64 && small)
-        return sym ? m32::launch<4, 2, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
-                   : m32::launch<4, 2, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+        return sym ? m32::launch<4, 2, true, false, IL>(x, qw, sc, qz, y, M, K, N, G, s)
+                   : m32::launch<4, 2, false, false, IL>(x, qw, sc, qz, y, M, K, N, G, s);
     if (k64)
-        return sym ? m32::launch<4, 4, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
-                   : m32::launch<4, 4, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+        return sym ? m32::launch<4, 4, true, false, IL>(x, qw, sc, qz, y, M, K, N, G, s)
+                   : m32::launch<4, 4, false, false, IL>(x, qw, sc, qz, y, M, K, N, G, s);
     if (k32 && small)
-        return sym ? m32::launch<2, 2, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
-                   : m32::launch<2, 2, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+        return sym ? m32::launch<2, 2, true, false, IL>(x, qw, sc, qz, y, M, K, N, G, s)
+                   : m32::launch<2, 2, false, false, IL>(x, qw, sc, qz, y, M, K, N, G, s);
     if (k32)
-        return sym ? m32::launch<2, 4, true, false>(x, qw, sc, qz, y, M, K, N, G, s)
-                   : m32::launch<2, 4, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
-    return sym ? launch_general<128, true>(x, qw, sc, qz, y, M, K, N, G, s)
-               : launch_general<128, false>(x, qw, sc, qz, y, M, K, N, G, s);
+        return sym ? m32::launch<2, 4, true, false, IL>(x, qw, sc, qz, y, M, K, N, G, s)
+                   : m32::launch<2, 4, false, false, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    return sym ? launch_general<128, true>(x, qw, sc, qz, y, M, K, N, G, IL, s)
+               : launch_general<128, false>(x, qw, sc, qz, y, M, K, N, G, IL, s);
+}
+
+hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
+                  uint16_t *y, int M, int K, int N, int G, bool il, hipStream_t s) {
+    return il ? launch_layout<true>(x, qw, sc, qz, y, M, K, N, G, s)
+              : launch_layout<false>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
 }  // namespace gemm
@@ -834,7 +861,7 @@ size_t gemm_splitk_workspace(int M, int N, int splits) {
 
 hipError_t launch_gemm_splitk(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                               const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
-                              int splits, void *workspace, hipStream_t s) {
+                              int splits, void *workspace, bool il, hipStream_t s) {
     using namespace gemm;
     const bool sym = qzeros == nullptr;
     auto *part = static_cast<float *>(workspace);
@@ -845,14 +872,16 @@ hipError_t launch_gemm_splitk(const uint16_t *x, const int32_t *qweight, const u
     // 22.4 -> 21.0 us; at 256 rows in 4: 23.8 -> 22.1 us).
     const bool rows64 = M <= 64 ||
                         (long long)((M + 63) / 64) * ((N + kBN - 1) / kBN) * splits <= kCus;
-#define AWQ_SPLIT(KBV, MTV)                                                                          \
-    (sym ? m32::launch_split<KBV, MTV, true>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s) \
-         : m32::launch_split<KBV, MTV, false>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s))
+#define AWQ_SPLIT_L(KBV, MTV, ILV)                                                                  \
+    (sym ? m32::launch_split<KBV, MTV, true, ILV>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s) \
+         : m32::launch_split<KBV, MTV, false, ILV>(x, qweight, scales, qzeros, part, M, K, N, G, splits, s))
+#define AWQ_SPLIT(KBV, MTV) (il ? AWQ_SPLIT_L(KBV, MTV, true) : AWQ_SPLIT_L(KBV, MTV, false))
     if (splitk_bk(K, G, splits) == 64)
         e = rows64 ? AWQ_SPLIT(4, 2) : AWQ_SPLIT(4, 4);
     else
         e = rows64 ? AWQ_SPLIT(2, 2) : AWQ_SPLIT(2, 4);
 #undef AWQ_SPLIT
+#undef AWQ_SPLIT_L
     if (e != hipSuccess) return e;
     const long long count = (long long)M * N;
     long long blocks = (count / 4 + 255) / 256;
@@ -868,22 +897,25 @@ bool gemm_gate_up_supported(int K, int N, int G) {
 
 hipError_t launch_gemm_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                                const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
-                               hipStream_t s) {
+                               bool il, hipStream_t s) {
     // 64-row tiles where they pay, as in awq_gemm (the tile count is the same:
     // 128 output columns are 256 layer columns).
-    if (gemm::rows64(M, N))
-        return qzeros == nullptr
-                   ? gemm::m32::launch<4, 2, true, true>(x, qweight, scales, qzeros, h, M, K, N, G, s)
-                   : gemm::m32::launch<4, 2, false, true>(x, qweight, scales, qzeros, h, M, K, N, G, s);
-    return qzeros == nullptr
-               ? gemm::m32::launch<4, 4, true, true>(x, qweight, scales, qzeros, h, M, K, N, G, s)
-               : gemm::m32::launch<4, 4, false, true>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    using gemm::m32::launch;
+    const bool r64 = gemm::rows64(M, N), sym = qzeros == nullptr;
+#define AWQ_GU(MTV, SYMV, ILV) launch<4, MTV, SYMV, true, ILV>(x, qweight, scales, qzeros, h, M, K, N, G, s)
+    if (il) {
+        if (r64) return sym ? AWQ_GU(2, true, true) : AWQ_GU(2, false, true);
+        return sym ? AWQ_GU(4, true, true) : AWQ_GU(4, false, true);
+    }
+    if (r64) return sym ? AWQ_GU(2, true, false) : AWQ_GU(2, false, false);
+    return sym ? AWQ_GU(4, true, false) : AWQ_GU(4, false, false);
+#undef AWQ_GU
 }
 
 hipError_t launch_gemm(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
-                       const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
+                       const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G, bool il,
                        hipStream_t s) {
-    return gemm::launch(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    return gemm::launch(x, qweight, scales, qzeros, y, M, K, N, G, il, s);
 }
 
 }  // namespace awq

@@ -228,7 +228,7 @@ template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool XLDS>
 __global__ void __launch_bounds__(NW * 64)
 fold_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
-            uint16_t *__restrict__ Y, int M, int K, int N, int G) {
+            uint16_t *__restrict__ Y, int M, int K, int N, int G, int il) {
     constexpr int TN = 16 * WPL;
     constexpr int STEPS = SEGR / 4;
     constexpr int XMAX = (int)(kXLdsBytes / 16) / (NW * 64);   // X chunks per thread
@@ -289,7 +289,7 @@ fold_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #pragma unroll
             for (int i = 0; i < WPL; ++i) {
                 uint32_t p[4];
-                unpack_biased(b.q[st].w[i], nmask, p);
+                unpack_biased(il ? deinterleave_word(b.q[st].w[i]) : b.q[st].w[i], nmask, p);
                 C[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_b(p), C[i], 0, 0, 0);
             }
             Cs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, Cs, 0, 0, 0);
@@ -379,13 +379,7 @@ fold_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 // ---------------------------------------------------------------------------
 
 constexpr uint32_t kSixteenthX2 = 0x2C002C00u;   // (1/16, 1/16) in fp16
-constexpr uint32_t kHighNibblePairMask = 0x00F000F0u;
 
-__device__ __forceinline__ uint32_t high_mask_vgpr() {
-    uint32_t v;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(kHighNibblePairMask));
-    return v;
-}
 
 __device__ __forceinline__ void unpack_biased16(uint32_t w, uint32_t lo_mask, uint32_t hi_mask,
                                                 uint32_t p[4]) {
@@ -451,13 +445,18 @@ constexpr size_t kLdsMax = 160 * 1024;
 // just before the segment is multiplied, instead of the whole slice up front.
 // With 16 rows the whole slice is 128 KB per workgroup, and every workgroup
 // asking for it at once delays the first multiply by microseconds.
+// IL: the packed words are in the kernel-private interleaved layout
+// (awq_repack).  A word then unpacks into the natural-order pairs (k 2e,
+// k 2e + 1) as (1024 + q, 1024 + q') for even e and (64 + q, 64 + q') for odd
+// e, so X is staged in natural order with no x / 16, and the bias sum U weighs
+// the odd pairs' x by 64 instead of 1024.
 // UNEV: the K range's segments do not split into whole pipelines of D per
 // wave (K not a multiple of 8 NW SEGR, or an odd count per wave): the first
 // nseg % NW waves take one segment more, and the loads ahead are guarded by
 // the wave's own count (a uniform branch).  The even case keeps the
 // unconditional pipeline.
 template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false,
-          int XS = 0, bool UNEV = false>
+          int XS = 0, bool UNEV = false, bool IL = false>
 __global__ void __launch_bounds__(NW * 64)
 stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
@@ -531,7 +530,7 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     // the padding lanes.  The segment sums (U, S) of a row are reduced over the
     // aligned groups of SEGR lanes that hold that row's chunks of one segment.
     auto stage = [&](const uint4 &raw, bool live, int m, int rr) {
-        const uint4 a = stage_chunk(raw);
+        const uint4 a = IL ? raw : stage_chunk(raw);
         if constexpr (SLOT) {   // the segment sums come from the matrix cores
             if (live) xs[m * XR + ((rr % SEGR) ^ (m & 15))] = a;
             return;
@@ -541,8 +540,10 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
                          __builtin_amdgcn_fdot2(as_half2(a.z), one2, 0.f, false), false);
         const float hi = __builtin_amdgcn_fdot2(as_half2(a.y), one2,
                          __builtin_amdgcn_fdot2(as_half2(a.w), one2, 0.f, false), false);
-        float t = live ? lo + hi : 0.f;          // sum of the staged values
-        float u = live ? lo + 16.f * hi : 0.f;   // sum of x
+        // t: U / 1024 (the staged values weighed by their pairs' bias / 1024);
+        // u: the sum of x.
+        float t = live ? (IL ? lo + 0.0625f * hi : lo + hi) : 0.f;
+        float u = live ? (IL ? lo + hi : lo + 16.f * hi) : 0.f;
         t = lane_group_sum<SEGR>(t);
         u = lane_group_sum<SEGR>(u);
         if (live) {
@@ -632,6 +633,8 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     float4_t CT = float4_t{0.f, 0.f, 0.f, 0.f}, CS = CT;
     const half8_t ones8 = as_half8(make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
     const half8_t xsum8 = as_half8(make_uint4(0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u));
+    // Interleaved words: U / 1024 weighs the odd pairs by 1/16; S is the plain sum.
+    const half8_t tsum8 = as_half8(make_uint4(0x3C003C00u, 0x2C002C00u, 0x3C003C00u, 0x2C002C00u));
 
     auto compute_seg = [&](int seg, const WSeg<WPL, STEPS, SYM> &bb) {
         const int rl0 = (seg - s_begin) * SEGR;   // local packed row of the segment
@@ -639,13 +642,14 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         for (int st = 0; st < STEPS; ++st) {
             const half8_t a = as_half8(xs[xrow * XR + (((SLOT ? 0 : rl0) + 4 * st + kb) ^ (xrow & 15))]);
             if constexpr (SLOT) {
-                CT = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones8, CT, 0, 0, 0);
-                CS = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, xsum8, CS, 0, 0, 0);
+                CT = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, IL ? tsum8 : ones8, CT, 0, 0, 0);
+                CS = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, IL ? ones8 : xsum8, CS, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < WPL; ++i) {
                 uint32_t p[4];
-                unpack_biased16(bb.q[st].w[i], lo_mask, hi_mask, p);
+                if constexpr (IL) unpack_interleaved(bb.q[st].w[i], lo_mask, hi_mask, p);
+                else unpack_biased16(bb.q[st].w[i], lo_mask, hi_mask, p);
                 C[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_b(p), C[i], 0, 0, 0);
             }
         }
@@ -785,7 +789,7 @@ inline size_t stream_lds_prog(int M, int K, int WPL, int NW, int SEGR) {
 }
 
 template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false,
-          int XS = 0>
+          int XS = 0, bool IL = false>
 hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                          hipStream_t s) {
@@ -795,8 +799,8 @@ hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *s
     // more X chunks per lane runs out of registers; such shapes take depth 1
     // (the dispatch checks stream_even first) and that variant is not built.
     constexpr bool kUneven = !(GU && D > 1 && XS > 1);
-    auto even = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS, false>;
-    auto uneven = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS, kUneven>;
+    auto even = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS, false, IL>;
+    auto uneven = stream_kernel<WPL, NW, SEGR, D, VR, SYM, GRP1, XCH, GU, XS, kUneven, IL>;
     const bool split_uneven = !stream_even(K, NW, SEGR, D);
     if (!kUneven && split_uneven) return hipErrorNotSupported;
     auto kernel = split_uneven ? uneven : even;
@@ -840,28 +844,28 @@ inline bool stream_fits_prog(int M, int K, int N, int G, int WPL, int NW, int D)
     return stream_lds_prog(M, K, WPL, NW, 16) <= kLdsMax;
 }
 
-template <int WPL, int NW, int SEGR, int D, int VR, int XCH>
+template <int WPL, int NW, int SEGR, int D, int VR, int XCH, bool IL>
 hipError_t launch_stream_sg(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                             const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                             hipStream_t s) {
     const bool grp1 = G == 8 * SEGR;
     if (qz == nullptr)
-        return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, true, true, XCH>(x, qw, sc, qz, y, M, K, N, G, s)
-                    : launch_stream<WPL, NW, SEGR, D, VR, true, false, XCH>(x, qw, sc, qz, y, M, K, N, G, s);
-    return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, false, true, XCH>(x, qw, sc, qz, y, M, K, N, G, s)
-                : launch_stream<WPL, NW, SEGR, D, VR, false, false, XCH>(x, qw, sc, qz, y, M, K, N, G, s);
+        return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, true, true, XCH, false, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s)
+                    : launch_stream<WPL, NW, SEGR, D, VR, true, false, XCH, false, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, false, true, XCH, false, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s)
+                : launch_stream<WPL, NW, SEGR, D, VR, false, false, XCH, false, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
-template <int WPL, int NW, int SEGR, int D, int VR>
+template <int WPL, int NW, int SEGR, int D, int VR, bool IL>
 hipError_t launch_stream_x(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                            const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                            hipStream_t s) {
     const int chunks_w = M * ((K / 8 / SEGR + NW - 1) / NW) * SEGR;   // the largest wave's
-    if (chunks_w <= 64) return launch_stream_sg<WPL, NW, SEGR, D, VR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (chunks_w <= 128) return launch_stream_sg<WPL, NW, SEGR, D, VR, 2>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (chunks_w <= 256) return launch_stream_sg<WPL, NW, SEGR, D, VR, 4>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (chunks_w <= 512) return launch_stream_sg<WPL, NW, SEGR, D, VR, 8>(x, qw, sc, qz, y, M, K, N, G, s);
-    return launch_stream_sg<WPL, NW, SEGR, D, VR, kStageChunks>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (chunks_w <= 64) return launch_stream_sg<WPL, NW, SEGR, D, VR, 1, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (chunks_w <= 128) return launch_stream_sg<WPL, NW, SEGR, D, VR, 2, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (chunks_w <= 256) return launch_stream_sg<WPL, NW, SEGR, D, VR, 4, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (chunks_w <= 512) return launch_stream_sg<WPL, NW, SEGR, D, VR, 8, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    return launch_stream_sg<WPL, NW, SEGR, D, VR, kStageChunks, IL>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
 // Compute units of the current device (queried once per process).
@@ -878,36 +882,36 @@ inline int device_cus() {
 
 // Beyond four rows (all four C rows of a lane live), X staged progressively:
 // XS = ceil(M * 16 / 64) chunks per lane per 16-row segment.
-template <int WPL, int NW, int D, bool GU, int XS>
+template <int WPL, int NW, int D, bool GU, int XS, bool IL>
 hipError_t launch_stream_prog_xs(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                                  const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                                  hipStream_t s) {
     const bool grp1 = G == 8 * 16;
 #define AWQ_PROG(SYMV, GRPV) \
-    launch_stream<WPL, NW, 16, D, 4, SYMV, GRPV, 1, GU, XS>(x, qw, sc, qz, y, M, K, N, G, s)
+    launch_stream<WPL, NW, 16, D, 4, SYMV, GRPV, 1, GU, XS, IL>(x, qw, sc, qz, y, M, K, N, G, s)
     if (qz == nullptr) return grp1 ? AWQ_PROG(true, true) : AWQ_PROG(true, false);
     return grp1 ? AWQ_PROG(false, true) : AWQ_PROG(false, false);
 #undef AWQ_PROG
 }
 
-template <int WPL, int NW, int D, bool GU>
+template <int WPL, int NW, int D, bool GU, bool IL>
 hipError_t launch_stream_prog(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                               const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                               hipStream_t s) {
-    if (M <= 4) return launch_stream_prog_xs<WPL, NW, D, GU, 1>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (M <= 8) return launch_stream_prog_xs<WPL, NW, D, GU, 2>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (M <= 12) return launch_stream_prog_xs<WPL, NW, D, GU, 3>(x, qw, sc, qz, y, M, K, N, G, s);
-    return launch_stream_prog_xs<WPL, NW, D, GU, 4>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (M <= 4) return launch_stream_prog_xs<WPL, NW, D, GU, 1, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (M <= 8) return launch_stream_prog_xs<WPL, NW, D, GU, 2, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (M <= 12) return launch_stream_prog_xs<WPL, NW, D, GU, 3, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    return launch_stream_prog_xs<WPL, NW, D, GU, 4, IL>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
-template <int WPL, int NW, int SEGR, int D>
+template <int WPL, int NW, int SEGR, int D, bool IL>
 hipError_t launch_stream_m(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                            const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                            hipStream_t s) {
     switch (live_rows(M)) {
-    case 1: return launch_stream_x<WPL, NW, SEGR, D, 1>(x, qw, sc, qz, y, M, K, N, G, s);
-    case 2: return launch_stream_x<WPL, NW, SEGR, D, 2>(x, qw, sc, qz, y, M, K, N, G, s);
-    default: return launch_stream_x<WPL, NW, SEGR, D, 4>(x, qw, sc, qz, y, M, K, N, G, s);
+    case 1: return launch_stream_x<WPL, NW, SEGR, D, 1, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    case 2: return launch_stream_x<WPL, NW, SEGR, D, 2, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    default: return launch_stream_x<WPL, NW, SEGR, D, 4, IL>(x, qw, sc, qz, y, M, K, N, G, s);
     }
 }
 
@@ -917,7 +921,7 @@ template <int WPL, int NW>
 __global__ void __launch_bounds__(NW * 64)
 exact_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
              const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
-             uint16_t *__restrict__ Y, int M, int K, int N, int G) {
+             uint16_t *__restrict__ Y, int M, int K, int N, int G, int il) {
     constexpr int TN = 16 * WPL;
     extern __shared__ __attribute__((aligned(16))) uint4 lds[];
     float *red = reinterpret_cast<float *>(lds);
@@ -954,7 +958,7 @@ exact_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
                 const half_t sv = as_half(sp[i]);
                 const half2_t bz2 = {bz, bz}, s2 = {sv, sv};
                 uint32_t p[4];
-                unpack_biased(q.w[i], nmask, p);
+                unpack_biased(il ? deinterleave_word(q.w[i]) : q.w[i], nmask, p);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) d[i][j] = dequant_pair(p[j], bz2, s2);
             }
@@ -990,35 +994,35 @@ exact_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 
 template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool XLDS>
 hipError_t launch_fold(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
-                       uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
+                       uint16_t *y, int M, int K, int N, int G, bool il, hipStream_t s) {
     constexpr int TN = 16 * WPL;
     const size_t lds = (XLDS ? (size_t)M * K * 2 : 0) + (size_t)NW * M * TN * sizeof(float);
     hipLaunchKernelGGL((fold_kernel<WPL, NW, SEGR, D, VR, SYM, XLDS>), dim3((N + TN - 1) / TN),
                        dim3(NW * 64), lds, s, x, reinterpret_cast<const uint32_t *>(qw), sc,
-                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
+                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G, il ? 1 : 0);
     return hipGetLastError();
 }
 
 template <int WPL, int NW, int SEGR, int D, int VR>
 hipError_t launch_fold_vr(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
                           hipStream_t s) {
     const bool xlds = (size_t)M * K * 2 <= kXLdsBytes;
     if (qz == nullptr)
-        return xlds ? launch_fold<WPL, NW, SEGR, D, VR, true, true>(x, qw, sc, qz, y, M, K, N, G, s)
-                    : launch_fold<WPL, NW, SEGR, D, VR, true, false>(x, qw, sc, qz, y, M, K, N, G, s);
-    return xlds ? launch_fold<WPL, NW, SEGR, D, VR, false, true>(x, qw, sc, qz, y, M, K, N, G, s)
-                : launch_fold<WPL, NW, SEGR, D, VR, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
+        return xlds ? launch_fold<WPL, NW, SEGR, D, VR, true, true>(x, qw, sc, qz, y, M, K, N, G, il, s)
+                    : launch_fold<WPL, NW, SEGR, D, VR, true, false>(x, qw, sc, qz, y, M, K, N, G, il, s);
+    return xlds ? launch_fold<WPL, NW, SEGR, D, VR, false, true>(x, qw, sc, qz, y, M, K, N, G, il, s)
+                : launch_fold<WPL, NW, SEGR, D, VR, false, false>(x, qw, sc, qz, y, M, K, N, G, il, s);
 }
 
 template <int WPL, int NW, int SEGR, int D>
 hipError_t launch_fold_m(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                         const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                         const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
                          hipStream_t s) {
     switch (live_rows(M)) {
-    case 1: return launch_fold_vr<WPL, NW, SEGR, D, 1>(x, qw, sc, qz, y, M, K, N, G, s);
-    case 2: return launch_fold_vr<WPL, NW, SEGR, D, 2>(x, qw, sc, qz, y, M, K, N, G, s);
-    default: return launch_fold_vr<WPL, NW, SEGR, D, 4>(x, qw, sc, qz, y, M, K, N, G, s);
+    case 1: return launch_fold_vr<WPL, NW, SEGR, D, 1>(x, qw, sc, qz, y, M, K, N, G, il, s);
+    case 2: return launch_fold_vr<WPL, NW, SEGR, D, 2>(x, qw, sc, qz, y, M, K, N, G, il, s);
+    default: return launch_fold_vr<WPL, NW, SEGR, D, 4>(x, qw, sc, qz, y, M, K, N, G, il, s);
     }
 }
 
@@ -1026,43 +1030,43 @@ hipError_t launch_fold_m(const uint16_t *x, const int32_t *qw, const uint16_t *s
 // pipeline depth (the largest of 4, 2, 1 dividing the segments per wave).
 template <int WPL, int SEGR>
 hipError_t launch_fold_any(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
                            hipStream_t s) {
     const int nseg = K / 8 / SEGR;
     if (nseg % 8 == 0) {
         const int per = nseg / 8;
-        if (per % 4 == 0) return launch_fold_m<WPL, 8, SEGR, 4>(x, qw, sc, qz, y, M, K, N, G, s);
-        if (per % 2 == 0) return launch_fold_m<WPL, 8, SEGR, 2>(x, qw, sc, qz, y, M, K, N, G, s);
-        return launch_fold_m<WPL, 8, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
+        if (per % 4 == 0) return launch_fold_m<WPL, 8, SEGR, 4>(x, qw, sc, qz, y, M, K, N, G, il, s);
+        if (per % 2 == 0) return launch_fold_m<WPL, 8, SEGR, 2>(x, qw, sc, qz, y, M, K, N, G, il, s);
+        return launch_fold_m<WPL, 8, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, il, s);
     }
-    if (nseg % 4 == 0) return launch_fold_m<WPL, 4, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (nseg % 2 == 0) return launch_fold_m<WPL, 2, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
-    return launch_fold_m<WPL, 1, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (nseg % 4 == 0) return launch_fold_m<WPL, 4, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, il, s);
+    if (nseg % 2 == 0) return launch_fold_m<WPL, 2, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, il, s);
+    return launch_fold_m<WPL, 1, SEGR, 1>(x, qw, sc, qz, y, M, K, N, G, il, s);
 }
 
 template <int WPL, int NW>
 hipError_t launch_exact(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                        const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                        const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
                         hipStream_t s) {
     constexpr int TN = 16 * WPL;
     hipLaunchKernelGGL((exact_kernel<WPL, NW>), dim3((N + TN - 1) / TN), dim3(NW * 64),
                        (size_t)NW * M * TN * sizeof(float), s, x,
                        reinterpret_cast<const uint32_t *>(qw), sc,
-                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G);
+                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G, il ? 1 : 0);
     return hipGetLastError();
 }
 
 // Fused gate/up: 8 words per lane (4 gate + 4 up columns), all live rows, X
 // staged in LDS; the shape must fit stream_kernel.
-template <int NW, int D>
+template <int NW, int D, bool IL>
 hipError_t launch_gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                           hipStream_t s) {
-    if (M > 4) return launch_stream_prog<8, NW, D, true>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (M > 4) return launch_stream_prog<8, NW, D, true, IL>(x, qw, sc, qz, y, M, K, N, G, s);
     const bool sym = qz == nullptr, grp1 = G == 8 * 16;
     const bool big = M * ((K / 128 + NW - 1) / NW) * 16 > 128;   // the largest wave's chunks
 #define AWQ_GU(SYMV, GRPV, XCHV) \
-    launch_stream<8, NW, 16, D, 4, SYMV, GRPV, XCHV, true>(x, qw, sc, qz, y, M, K, N, G, s)
+    launch_stream<8, NW, 16, D, 4, SYMV, GRPV, XCHV, true, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s)
     if (big) {
         if (sym) return grp1 ? AWQ_GU(true, true, kStageChunks) : AWQ_GU(true, false, kStageChunks);
         return grp1 ? AWQ_GU(false, true, kStageChunks) : AWQ_GU(false, false, kStageChunks);
@@ -1073,21 +1077,26 @@ hipError_t launch_gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *
 }
 
 // One instantiated family of launchers per translation unit (arguments as
-// launch_stream's).
+// launch_stream's): the staged kernel on canonical words (name) and on
+// interleaved ones (name_il); the folded and exact kernels take the layout as
+// an argument.
 using Launcher = hipError_t(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                             const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                             hipStream_t s);
-Launcher stream_m_w2_d2;
-Launcher stream_m_w4_d2;
-Launcher stream_m_w4_d1;
-Launcher prog_w2;
-Launcher prog_w4;
-Launcher prog_w8;
-Launcher fold_w2_s16;
-Launcher fold_w4_s16;
-Launcher fold_w4_s8;
-Launcher fold_w4_s4;
-Launcher exact_w4;
+using LayoutLauncher = hipError_t(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                                  const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                                  bool il, hipStream_t s);
+Launcher stream_m_w2_d2, stream_m_w2_d2_il;
+Launcher stream_m_w4_d2, stream_m_w4_d2_il;
+Launcher stream_m_w4_d1, stream_m_w4_d1_il;
+Launcher prog_w2, prog_w2_il;
+Launcher prog_w4, prog_w4_il;
+Launcher prog_w8, prog_w8_il;
+LayoutLauncher fold_w2_s16;
+LayoutLauncher fold_w4_s16;
+LayoutLauncher fold_w4_s8;
+LayoutLauncher fold_w4_s4;
+LayoutLauncher exact_w4;
 
 }  // namespace gemv
 }  // namespace awq

@@ -1,4 +1,4 @@
-// Small-batch GEMV, X staged segment by segment: 128-column strips.
+// Small-batch GEMV, X staged segment by segment: 128-column strips; canonical words.
 #include "awq_gemv_kernels.h"
 
 namespace awq {
@@ -7,7 +7,7 @@ namespace gemv {
 hipError_t prog_w8(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                    const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                    hipStream_t s) {
-    return launch_stream_prog<8, 8, 1, false>(x, qw, sc, qz, y, M, K, N, G, s);
+    return launch_stream_prog<8, 8, 1, false, false>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
 }  // namespace gemv

@@ -1,4 +1,5 @@
-// Decode GEMV, X staged before the loop: 64-column strips, one segment in flight per wave.
+// Decode GEMV, X staged before the loop: 64-column strips, one segment in flight per wave;
+// canonical words.
 #include "awq_gemv_kernels.h"
 
 namespace awq {
@@ -7,7 +8,7 @@ namespace gemv {
 hipError_t stream_m_w4_d1(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                           hipStream_t s) {
-    return launch_stream_m<4, 8, 16, 1>(x, qw, sc, qz, y, M, K, N, G, s);
+    return launch_stream_m<4, 8, 16, 1, false>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
 }  // namespace gemv

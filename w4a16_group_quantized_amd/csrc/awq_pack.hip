@@ -57,7 +57,7 @@ pack_zeros_kernel(const uint8_t *__restrict__ zeros, int32_t *__restrict__ qzero
 __global__ void __launch_bounds__(256)
 dequant_kernel(const uint32_t *__restrict__ qweight, const uint16_t *__restrict__ scales,
                const uint32_t *__restrict__ qzeros, uint16_t *__restrict__ w, int K, int N,
-               int G) {
+               int G, int il) {
     const int n4 = N / 4;
     const long long total = (long long)(K / 8) * n4;
     const uint32_t nmask = nibble_mask_vgpr();
@@ -70,7 +70,10 @@ dequant_kernel(const uint32_t *__restrict__ qweight, const uint16_t *__restrict_
         const uint2 s = *reinterpret_cast<const uint2 *>(scales + (size_t)g * N + n);
         const uint32_t zw = qzeros ? qzeros[(size_t)g * (N / 8) + n / 8] >> (4 * (n % 8))
                                    : 0x8888u;
-        const uint32_t qs[4] = {q.x, q.y, q.z, q.w};
+        uint32_t qs[4] = {q.x, q.y, q.z, q.w};
+        if (il)   // interleaved words: back to the canonical nibble order first
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qs[i] = deinterleave_word(qs[i]);
         const uint16_t ss[4] = {(uint16_t)s.x, (uint16_t)(s.x >> 16), (uint16_t)s.y,
                                 (uint16_t)(s.y >> 16)};
         uint4 col[4];
@@ -112,10 +115,40 @@ hipError_t launch_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int groups, 
 }
 
 hipError_t launch_dequant(const int32_t *qweight, const uint16_t *scales, const int32_t *qzeros,
-                          uint16_t *w, int K, int N, int G, hipStream_t s) {
+                          uint16_t *w, int K, int N, int G, bool il, hipStream_t s) {
     hipLaunchKernelGGL(dequant_kernel, dim3(grid_for((long long)(K / 8) * (N / 4))), dim3(256), 0,
                        s, reinterpret_cast<const uint32_t *>(qweight), scales,
-                       reinterpret_cast<const uint32_t *>(qzeros), w, K, N, G);
+                       reinterpret_cast<const uint32_t *>(qzeros), w, K, N, G, il ? 1 : 0);
+    return hipGetLastError();
+}
+
+// Canonical <-> interleaved packed words: the nibble permutation of each word
+// (a byte swap and a nibble swap, see interleave_word), 16 bytes per thread.
+__global__ void __launch_bounds__(256)
+repack_kernel(const uint4 *src, uint4 *dst, long long quads, int to_il) {   // src may equal dst
+    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < quads; i += (long long)gridDim.x * 256) {
+        uint4 v = src[i];
+        if (to_il) {
+            v.x = interleave_word(v.x);
+            v.y = interleave_word(v.y);
+            v.z = interleave_word(v.z);
+            v.w = interleave_word(v.w);
+        } else {
+            v.x = deinterleave_word(v.x);
+            v.y = deinterleave_word(v.y);
+            v.z = deinterleave_word(v.z);
+            v.w = deinterleave_word(v.w);
+        }
+        dst[i] = v;
+    }
+}
+
+hipError_t launch_repack(const int32_t *src, int32_t *dst, long long words, bool to_interleaved,
+                         hipStream_t s) {
+    const long long quads = words / 4;   // words is a multiple of 8 (K / 8 * N, N % 8 == 0)
+    hipLaunchKernelGGL(repack_kernel, dim3(grid_for(quads)), dim3(256), 0, s,
+                       reinterpret_cast<const uint4 *>(src), reinterpret_cast<uint4 *>(dst), quads,
+                       to_interleaved ? 1 : 0);
     return hipGetLastError();
 }
 
