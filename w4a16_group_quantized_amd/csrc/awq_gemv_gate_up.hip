@@ -13,33 +13,10 @@ bool gemv_gate_up_supported(int M, int K, int N, int G) {
            stream_fits(M, K, N, G, 8, 2, 16, 1) || stream_fits(M, K, N, G, 8, 1, 16, 1);
 }
 
-template <bool IL>
-static hipError_t gate_up_layout(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
-                                 const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
-                                 hipStream_t s) {
-    using namespace gemv;
-    if (M > 4) {   // launch_gate_up stages X segment by segment beyond four rows
-        if (stream_even(K, 8, 16, 2) && stream_fits_prog(M, K, N, G, 8, 8, 2))
-            return launch_gate_up<8, 2, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
-        if (stream_fits_prog(M, K, N, G, 8, 8, 1))
-            return launch_gate_up<8, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
-    }
-    if (stream_fits(M, K, N, G, 8, 8, 16, 2))
-        return launch_gate_up<8, 2, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
-    if (stream_fits(M, K, N, G, 8, 8, 16, 1))
-        return launch_gate_up<8, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
-    if (stream_fits(M, K, N, G, 8, 2, 16, 1))
-        return launch_gate_up<2, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
-    if (stream_fits(M, K, N, G, 8, 1, 16, 1))
-        return launch_gate_up<1, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
-    return hipErrorNotSupported;
-}
-
 hipError_t launch_gemv_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                                const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
                                bool il, hipStream_t s) {
-    return il ? gate_up_layout<true>(x, qweight, scales, qzeros, h, M, K, N, G, s)
-              : gate_up_layout<false>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    return (il ? gemv::gate_up_il : gemv::gate_up)(x, qweight, scales, qzeros, h, M, K, N, G, s);
 }
 
 }  // namespace awq

@@ -1,0 +1,14 @@
+// Fused gate/up GEMV (h = SiLU(gate) * up) on canonical words.
+#include "awq_gemv_kernels.h"
+
+namespace awq {
+namespace gemv {
+
+hipError_t gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+                   const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
+                   hipStream_t s) {
+    return gate_up_layout<false>(x, qw, sc, qz, y, M, K, N, G, s);
+}
+
+}  // namespace gemv
+}  // namespace awq

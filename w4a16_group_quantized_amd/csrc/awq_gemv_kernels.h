@@ -1076,6 +1076,28 @@ hipError_t launch_gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *
 #undef AWQ_GU
 }
 
+// Fused gate/up launcher for one layout (awq_gemv_gate_up*.hip instantiate it).
+template <bool IL>
+hipError_t gate_up_layout(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                                 const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
+                                 hipStream_t s) {
+        if (M > 4) {   // launch_gate_up stages X segment by segment beyond four rows
+        if (stream_even(K, 8, 16, 2) && stream_fits_prog(M, K, N, G, 8, 8, 2))
+            return launch_gate_up<8, 2, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+        if (stream_fits_prog(M, K, N, G, 8, 8, 1))
+            return launch_gate_up<8, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    }
+    if (stream_fits(M, K, N, G, 8, 8, 16, 2))
+        return launch_gate_up<8, 2, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    if (stream_fits(M, K, N, G, 8, 8, 16, 1))
+        return launch_gate_up<8, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    if (stream_fits(M, K, N, G, 8, 2, 16, 1))
+        return launch_gate_up<2, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    if (stream_fits(M, K, N, G, 8, 1, 16, 1))
+        return launch_gate_up<1, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    return hipErrorNotSupported;
+}
+
 // One instantiated family of launchers per translation unit (arguments as
 // launch_stream's): the staged kernel on canonical words (name) and on
 // interleaved ones (name_il); the folded and exact kernels take the layout as
@@ -1086,6 +1108,7 @@ using Launcher = hipError_t(const uint16_t *x, const int32_t *qw, const uint16_t
 using LayoutLauncher = hipError_t(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                                   const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                                   bool il, hipStream_t s);
+Launcher gate_up, gate_up_il;
 Launcher stream_m_w2_d2, stream_m_w2_d2_il;
 Launcher stream_m_w4_d2, stream_m_w4_d2_il;
 Launcher stream_m_w4_d1, stream_m_w4_d1_il;
