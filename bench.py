@@ -4,8 +4,10 @@
 
 A step is one call of the fused layer (awq_gemv at M = 1) on the decode
 workload: the Llama-3-8B MLP gate shape, M=1, K=4096, N=14336, group 128,
-asymmetric zero points.  The layer is packed once (as when a checkpoint is
-loaded); each step streams the packed weight, unpacks, dequantizes, multiplies,
+asymmetric zero points.  The layer is packed once and its words repacked
+into the library's interleaved layout (as when a checkpoint is loaded;
+--layout canonical keeps awq_pack's word order); each step streams the packed
+weight, unpacks, dequantizes, multiplies,
 reduces and writes Y.  The weight is replicated into enough copies (>= 1 GiB)
 that successive steps read different copies, so every step streams from HBM
 rather than from the 256 MB last-level cache.  Inputs are resident in HBM before
@@ -92,7 +94,7 @@ CSRC = os.path.join(ROOT, "w4a16_group_quantized_amd", "csrc")
 # awq_internal.h generate no code): a counter summary is valid only for them.
 KERNEL_SOURCES = {
     "gemv": ["awq_gemv_kernels.h", "awq_device.h"],
-    "gemm": ["awq_gemm.hip", "awq_device.h"],
+    "gemm": ["awq_gemm_kernels.h", "awq_device.h"],
 }
 KERNEL_NAMES = {"gemv": ("stream_kernel", "fold_kernel", "exact_kernel"), "gemm": ("gemm_kernel", "mfma32_kernel")}
 PROFILE_WORKLOAD = {"gemv": "decode_8b_gate", "gemm": "prefill_out_proj"}
@@ -124,7 +126,7 @@ def to_dev(a):
 # qweight layout of every benchmarked layer (--layout): canonical, or the
 # kernel-private interleaved one (repacked once after packing, as at load time).
 LAYOUT = {"canonical": 0, "interleaved": 1}
-BENCH_LAYOUT = "canonical"
+BENCH_LAYOUT = "interleaved"
 
 
 def build_layers(w, copies):
@@ -609,14 +611,24 @@ def _per_dispatch(dirs):
     out = {}
     for d in dirs:
         for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
-            acc = {}
+            acc, dur = {}, {}
             with open(f) as fh:
                 for row in csv.DictReader(fh):
                     k = row["Kernel_Name"]
-                    key = (k, row["Counter_Name"], row["Dispatch_Id"])
-                    acc[key] = acc.get(key, 0.0) + float(row["Counter_Value"])
+                    if row.get("Start_Timestamp") and row.get("End_Timestamp"):
+                        dur[(k, row["Dispatch_Id"])] = (float(row["End_Timestamp"]) -
+                                                        float(row["Start_Timestamp"]))
+                    c = row["Counter_Name"]
+                    key = (k, c, row["Dispatch_Id"])
+                    v = float(row["Counter_Value"])
+                    # GRBM counters are per XCD and count the same clock on
+                    # each: take the largest; every other counter is summed
+                    # over its instances
+                    acc[key] = max(acc.get(key, 0.0), v) if c.startswith("GRBM_") else acc.get(key, 0.0) + v
             for (k, c, did), v in acc.items():
                 out.setdefault(k, {}).setdefault(c, []).append((int(did), v))
+            for (k, did), ns in dur.items():
+                out.setdefault(k, {}).setdefault("duration_ns", []).append((int(did), ns))
     for per in out.values():
         for c in per:
             per[c].sort()
@@ -659,6 +671,18 @@ def summarize_pmc(out_path, dirs, kind, commands):
                              f"{med[(ck, c)]:.1f} KiB -> factor {f:.4f}")
             traffic = sum(med[(kern[0], c)] * 1024.0 * f for c, f in facs.items())
             lines.append(f"traffic_bytes_per_launch: {traffic:.0f}")
+    if kern and all((kern[0], c) in med for c in ("SQ_BUSY_CYCLES", "duration_ns")):
+        # SQ_BUSY_CYCLES counts, per shader engine (32: 8 XCDs x 4), the clock
+        # cycles in which it holds a wave of the dispatch: the kernel's length
+        # in shader clocks
+        se_cycles = med[(kern[0], "SQ_BUSY_CYCLES")] / 32.0
+        lines.append(f"shader_clock_ghz: {se_cycles / med[(kern[0], 'duration_ns')]:.3f} "
+                     f"(SQ_BUSY_CYCLES / 32 shader engines / dispatch duration)")
+        if (kern[0], "SQ_VALU_MFMA_BUSY_CYCLES") in med:
+            # matrix-core busy cycles per SIMD (1024: 256 CUs x 4) over those cycles
+            simd_busy = med[(kern[0], "SQ_VALU_MFMA_BUSY_CYCLES")] / 1024.0
+            lines.append(f"mfma_busy_frac: {simd_busy / se_cycles:.4f} "
+                         f"(SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (SQ_BUSY_CYCLES / 32))")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -732,7 +756,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
-    ap.add_argument("--layout", choices=sorted(LAYOUT), default="canonical",
+    ap.add_argument("--layout", choices=sorted(LAYOUT), default="interleaved",
                     help="qweight layout of the benchmarked layers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--ceilings", action="store_true", help="only measure the two ceilings")

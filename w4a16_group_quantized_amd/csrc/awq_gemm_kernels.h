@@ -335,11 +335,17 @@ struct Geom {
 };
 
 // LDS chunk of (row, 16-byte k chunk kc) in an X tile of XCH chunks per row,
-// XOR-swizzled so that the 16 rows one A-operand read touches in a 16-lane
-// phase fall in different bank groups.
+// XOR-swizzled so that the A-operand read of one k chunk by 16 consecutive
+// rows (16 lanes of a 16-byte LDS read) falls in 16 different 16-byte bank
+// groups of a 256-byte span, and the read by any 8 consecutive rows in 8
+// different ones of a 128-byte span.  128-byte X rows (XCH 8): rows r and
+// r + 8 share r & 7 and a 256-byte span's bank groups, so the XOR of r + 8
+// differs in its low bit; 64-byte rows (XCH 4): the XOR (r / 2) ^ (r / 8)
+// differs between the rows that share r % 2 in 8 and those that share r % 4
+// in 16.
 template <int XCH>
 __device__ __forceinline__ int xswz(int row, int kc) {
-    return row * XCH + (kc ^ (XCH == 8 ? (row & 7) : ((row >> 2) & 3)));
+    return row * XCH + (kc ^ (XCH == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : (((row >> 1) ^ (row >> 3)) & 3)));
 }
 
 typedef float float16x_t __attribute__((ext_vector_type(16)));
@@ -582,7 +588,12 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     // A(kt + 1, kb 0) and the packed weights of kt + 2, and the loads of step
     // kt + 4 go into the ring slots of kt.  Neither LDS latency nor the
     // barrier reaches the matrix cores by more than a block's lead.
-    constexpr int VG = KB == 2 ? 2 : (IL ? 3 : 4);   // dequantization VALU per MFMA (about)
+    // VALU slots between two MFMAs in the schedule.  With 64-k steps, 4 for
+    // either layout: on interleaved words (about 3.3 dequantization VALU per
+    // MFMA) 3 leaves a tail of VALU after the last MFMA before the barrier,
+    // and 4 measured 1.6 to 3.4% faster (4096 x 4096, M 2048, K 4096 and
+    // 16384); 5 and 6 are slower again.
+    constexpr int VG = KB == 2 ? 2 : 4;
     half8_t a0[kMT], a1[kMT];
     Raw r;
     // One group: the lane's scale pair (columns n0 + 2 j, +1) and zero word,
