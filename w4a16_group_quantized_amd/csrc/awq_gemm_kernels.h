@@ -685,14 +685,18 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
                 const int row = m0 + 32 * t + 8 * (v / 4) + 4 * h + (v % 4);
                 if (row < M) {
                     const float g = acc[t][0][v];
-                    Y[(size_t)row * I + col] = as_u16((half_t)(g / (1.0f + __expf(-g)) * acc[t][1][v]));
+                    __builtin_nontemporal_store(as_u16((half_t)(g / (1.0f + __expf(-g)) * acc[t][1][v])),
+                                                Y + (size_t)row * I + col);
                 }
             }
         return;
     }
     // column tiles 0 and 1 are the adjacent columns n0 + 2 j and n0 + 2 j + 1,
     // stored as one 4-byte word (split K: one 8-byte fp32 pair of the slice's
-    // partial tile).
+    // partial tile).  The fp16 outputs (here and in the gate/up epilogue) are
+    // nontemporal stores: every CU writes its whole tile at once at the end,
+    // and lines that bypass the L2 need no write-back when the kernel ends
+    // (prefill shape 61.3 -> 60.1 us; the waves' own time is unchanged).
     const int col = n0 + 2 * j;
     if (col >= N) return;
     if constexpr (ONEG) {
@@ -726,7 +730,7 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             if (row < M) {
                 const uint32_t w = (uint32_t)as_u16((half_t)acc[t][0][v]) |
                                    ((uint32_t)as_u16((half_t)acc[t][1][v]) << 16);
-                *reinterpret_cast<uint32_t *>(Y + (size_t)row * N + col) = w;
+                __builtin_nontemporal_store(w, reinterpret_cast<uint32_t *>(Y + (size_t)row * N + col));
             }
         }
 }
