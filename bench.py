@@ -38,10 +38,12 @@ GB/s.  Also reported:
 
 Profiling helpers (the figures under profiles/ come from these):
 
-    python bench.py --profile gemv|gemm
+    python bench.py --profile gemv|gemv16|gemm
         a short fixed sequence for rocprofv3 counter passes: 20 calls of the
-        kernel on its workload, each its own dispatch, then 5 device copies of
-        64 MiB -- the plain copy kernel that calibrates FETCH_SIZE/WRITE_SIZE
+        kernel on its workload (gemv: awq_gemv on the decode layer; gemv16:
+        awq_gemv on the fused gate/up layer's 16 rows; gemm: awq_gemm on the
+        prefill layer), each its own dispatch, then 5 device copies of 64 MiB
+        -- the plain copy kernel that calibrates FETCH_SIZE/WRITE_SIZE
     python bench.py --summarize-pmc OUT DIR...
         folds the counter CSVs of rocprofv3 --pmc runs into a text summary with
         per-dispatch medians, the copy calibration, the HBM traffic per launch
@@ -96,9 +98,15 @@ KERNEL_SOURCES = {
     "gemv": ["awq_gemv_kernels.h", "awq_device.h"],
     "gemm": ["awq_gemm_kernels.h", "awq_device.h"],
 }
+KERNEL_SOURCES["gemv16"] = KERNEL_SOURCES["gemv"]
 KERNEL_NAMES = {"gemv": ("stream_kernel", "fold_kernel", "exact_kernel"), "gemm": ("gemm_kernel", "mfma32_kernel")}
-PROFILE_WORKLOAD = {"gemv": "decode_8b_gate", "gemm": "prefill_out_proj"}
+KERNEL_NAMES["gemv16"] = KERNEL_NAMES["gemv"]
+# --profile kinds: the workload and the binding entry of each (gemv16: the fused
+# gate/up layer's 16 rows through awq_gemv)
+PROFILE_WORKLOAD = {"gemv": "decode_8b_gate", "gemm": "prefill_out_proj", "gemv16": "gate_up_m16"}
+PROFILE_ENTRY = {"gemv": "gemv", "gemm": "gemm", "gemv16": "gemv"}
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "awq_gemv_decode_8b_gate_counters.txt")
+GEMM_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "awq_gemm_prefill_out_proj_counters.txt")
 
 
 def source_hash(kind):
@@ -589,11 +597,11 @@ def profile_run(kind):
     binding.load()
     name = PROFILE_WORKLOAD[kind]
     w = synth.WORKLOADS[name]
-    copies = max(2, math.ceil(ROTATE_BYTES / alg_bytes(w, 0))) if kind == "gemv" else 1
+    copies = max(2, math.ceil(ROTATE_BYTES / alg_bytes(w, 0))) if kind != "gemm" else 1
     layers = build_layers(w, copies)
     X = to_dev(synth.make_x(w.M, w.K, w.wid, w.n_outliers, w.outlier_gain))
     y = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
-    fn = getattr(binding, kind)
+    fn = getattr(binding, PROFILE_ENTRY[kind])
     for i in range(PROFILE_CALLS):
         fn(X, layers[i % copies], out=y)
     torch.cuda.synchronize()
@@ -602,7 +610,7 @@ def profile_run(kind):
     for _ in range(5):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(f"profiled {PROFILE_CALLS} x awq_{kind} on {name}, then 5 copies of "
+    print(f"profiled {PROFILE_CALLS} x awq_{PROFILE_ENTRY[kind]} on {name}, then 5 copies of "
           f"{CALIBRATION_COPY_BYTES} bytes", flush=True)
 
 
@@ -644,7 +652,7 @@ def summarize_pmc(out_path, dirs, kind, commands):
     data = _per_dispatch(dirs)
     kern = [k for k in data if any(n in k for n in KERNEL_NAMES[kind])]
     copyk = [k for k in data if "copyBuffer" in k]
-    lines = [f"# rocprofv3 --pmc counters: awq_{kind} on {PROFILE_WORKLOAD[kind]}",
+    lines = [f"# rocprofv3 --pmc counters: awq_{PROFILE_ENTRY[kind]} on {PROFILE_WORKLOAD[kind]}",
              "# commands (each a run of its own):"]
     lines += [f"#   {c}" for c in commands]
     lines.append(f"# source_sha256: {source_hash(kind)}")
@@ -706,11 +714,12 @@ def summarize_stats(out_path, d, command):
     print("\n".join(lines))
 
 
-def committed_traffic():
-    """HBM bytes per launch of awq_gemv from the committed counter summary, or
-    None if there is none or the kernel's sources have changed since."""
+def committed_traffic(kind="gemv"):
+    """HBM bytes per launch of awq_gemv (or awq_gemm, kind "gemm") from the
+    committed counter summary, or None if there is none or the kernel's sources
+    have changed since."""
     try:
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(TRAFFIC_SUMMARY if kind == "gemv" else GEMM_TRAFFIC_SUMMARY) as f:
             text = f.read()
     except OSError:
         return None
@@ -720,7 +729,7 @@ def committed_traffic():
             sha = line.split(":", 1)[1].strip()
         elif line.startswith("traffic_bytes_per_launch:"):
             traffic = float(line.split(":", 1)[1])
-    if sha != source_hash("gemv"):
+    if sha != source_hash(kind):
         return None
     return traffic
 
@@ -760,12 +769,12 @@ def main():
                     help="qweight layout of the benchmarked layers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--ceilings", action="store_true", help="only measure the two ceilings")
-    ap.add_argument("--profile", choices=["gemv", "gemm"], help="dispatch sequence for counter passes")
+    ap.add_argument("--profile", choices=sorted(PROFILE_WORKLOAD), help="dispatch sequence for counter passes")
     ap.add_argument("--summarize-pmc", nargs="+", metavar=("OUT", "DIR"),
                     help="fold rocprofv3 --pmc CSV directories into a summary file")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("OUT", "DIR"),
                     help="fold a rocprofv3 --kernel-trace --stats directory into a summary file")
-    ap.add_argument("--kind", choices=["gemv", "gemm"], default="gemv", help="kernel of --summarize-pmc")
+    ap.add_argument("--kind", choices=sorted(PROFILE_WORKLOAD), default="gemv", help="kernel of --summarize-pmc")
     ap.add_argument("--command", action="append", default=[],
                     help="command line(s) that produced the profiled data, recorded in the summary")
     args = ap.parse_args()
@@ -844,6 +853,12 @@ def main():
         "gemm": {"workload": gemm["workload"], "M": gemm["M"], "K": gemm["K"], "N": gemm["N"],
                  "tflops": round(gemm["tflops"], 1), "peak": MFMA_F16_PEAK_TFLOPS,
                  "frac": round(gemm["mfma_frac"], 4), "us_per_call": round(gemm["us_per_call"], 2)},
+        # the metric's GEMM half: awq_gemm's kernel on the prefill shape against
+        # the fp16 MFMA peak, in the same form as the decode kernel's roofline
+        "roofline_gemm": {"bound": "mfma", "achieved": round(gemm["tflops"], 1),
+                          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(gemm["mfma_frac"], 4),
+                          "traffic": committed_traffic("gemm")},
     }
     if "hot_cache_us" in head:
         out["timing"]["hot_cache_us"] = round(head["hot_cache_us"], 3)

@@ -44,6 +44,11 @@
  * code with nothing launched if they are wrong, and otherwise enqueues its
  * kernels and returns without waiting.  A fault inside a kernel surfaces at the
  * caller's next synchronization, as HIP reports it.  Calls are thread safe.
+ *
+ * Debugging: with AWQ_SYNC set in the environment to anything but "" or "0"
+ * (read once, at the first call), every call that launched work waits for its
+ * stream before returning and reports a failure of its own kernels as
+ * AWQ_ERROR_HIP.  A stream being captured into a graph is not waited for.
  */
 #ifndef AWQ_MI355X_H
 #define AWQ_MI355X_H

@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -280,3 +281,31 @@ def test_repack_validation(lib):
     assert f(FAKE, FAKE, 1 << 16, 1 << 16, 0, 1, None) == 2
     assert f(MISALIGNED, FAKE, 64, 64, 0, 1, None) == 3
     assert f(FAKE, FAKE, 64, 64, 1, 1, None) == 0          # same layout, in place: nothing to do
+
+
+SYNC_CHILD = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+from w4a16_group_quantized_amd import binding
+lib = binding.load()
+FAKE, MIS = 0x10000000, 0x10000002
+c = binding.CLayer(FAKE, FAKE, FAKE, 128, 64, 128, 0)
+bad = binding.CLayer(FAKE, FAKE, FAKE, 12, 64, 128, 0)
+codes = [lib.awq_gemv(FAKE, ctypes.byref(c), FAKE, 17, None, 0, None),
+         lib.awq_gemv(FAKE, ctypes.byref(bad), FAKE, 1, None, 0, None),
+         lib.awq_gemm(MIS, ctypes.byref(c), FAKE, 1, None),
+         lib.awq_gemm(FAKE, ctypes.byref(c), FAKE, 0, None),
+         lib.awq_pack(None, FAKE, 8, 8, None)]
+print(" ".join(str(v) for v in codes))
+"""
+
+
+@pytest.mark.parametrize("value", ["1", "yes"])
+def test_sync_mode_keeps_validation(value):
+    """AWQ_SYNC changes only what happens after a launch: rejected calls and
+    empty batches return their codes with no HIP call (this host has no GPU)."""
+    env = dict(os.environ, AWQ_SYNC=value)
+    r = subprocess.run([sys.executable, "-c", SYNC_CHILD, ROOT], env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.split() == ["4", "2", "3", "0", "1"]

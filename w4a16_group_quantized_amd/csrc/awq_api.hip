@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <stdlib.h>
 
 #include "awq_internal.h"
 
@@ -40,9 +41,32 @@ awq_status check_io(const uint16_t *x, const uint16_t *y, const awq_layer *w, in
     return AWQ_SUCCESS;
 }
 
-awq_status from_hip(hipError_t e) { return e == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP; }
-
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// AWQ_SYNC set to anything but "" or "0" in the environment (read once, at the
+// first call): every call that launched work waits for its stream and reports
+// a fault of its own kernels as AWQ_ERROR_HIP, instead of leaving it to the
+// caller's next synchronization.  A stream that is being captured into a graph
+// is not waited for (a capture cannot synchronize).  For debugging only: the
+// wait serializes the caller with the GPU.
+bool sync_mode() {
+    static const bool on = [] {
+        const char *v = getenv("AWQ_SYNC");
+        return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
+    }();
+    return on;
+}
+
+// The status of a call whose launches returned e on `stream`.
+awq_status done(void *stream, hipError_t e) {
+    if (e != hipSuccess) return AWQ_ERROR_HIP;
+    if (!sync_mode()) return AWQ_SUCCESS;
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(as_stream(stream), &capture) != hipSuccess) return AWQ_ERROR_HIP;
+    if (capture != hipStreamCaptureStatusNone) return AWQ_SUCCESS;
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return AWQ_ERROR_HIP;
+    return hipGetLastError() == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
+}
 
 bool interleaved(const awq_layer *w) { return w->layout == AWQ_LAYOUT_INTERLEAVED; }
 
@@ -79,7 +103,7 @@ awq_status awq_pack(const uint8_t *codes, int32_t *qweight, int32_t K, int32_t N
     if (codes == nullptr || qweight == nullptr || K <= 0 || N <= 0) return AWQ_ERROR_INVALID_VALUE;
     if (K % 8 || N % 8 || (long long)K * N > kMaxElems) return AWQ_ERROR_SHAPE;
     if (!aligned16(codes) || !aligned16(qweight)) return AWQ_ERROR_ALIGNMENT;
-    return from_hip(awq::launch_pack(codes, qweight, K, N, as_stream(stream)));
+    return done(stream, awq::launch_pack(codes, qweight, K, N, as_stream(stream)));
 }
 
 awq_status awq_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int32_t groups, int32_t N,
@@ -88,7 +112,7 @@ awq_status awq_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int32_t groups,
         return AWQ_ERROR_INVALID_VALUE;
     if (N % 8 || (long long)groups * N > kMaxElems) return AWQ_ERROR_SHAPE;
     if (!aligned16(zeros) || !aligned16(qzeros)) return AWQ_ERROR_ALIGNMENT;
-    return from_hip(awq::launch_pack_zeros(zeros, qzeros, groups, N, as_stream(stream)));
+    return done(stream, awq::launch_pack_zeros(zeros, qzeros, groups, N, as_stream(stream)));
 }
 
 awq_status awq_repack(const int32_t *src, int32_t *dst, int32_t K, int32_t N, int32_t from,
@@ -101,10 +125,10 @@ awq_status awq_repack(const int32_t *src, int32_t *dst, int32_t K, int32_t N, in
     const long long words = (long long)(K / 8) * N;
     if (from == to) {
         if (src == dst) return AWQ_SUCCESS;
-        return from_hip(hipMemcpyAsync(dst, src, (size_t)words * 4, hipMemcpyDeviceToDevice,
+        return done(stream, hipMemcpyAsync(dst, src, (size_t)words * 4, hipMemcpyDeviceToDevice,
                                        as_stream(stream)));
     }
-    return from_hip(awq::launch_repack(src, dst, words, to == AWQ_LAYOUT_INTERLEAVED, as_stream(stream)));
+    return done(stream, awq::launch_repack(src, dst, words, to == AWQ_LAYOUT_INTERLEAVED, as_stream(stream)));
 }
 
 awq_status awq_dequant(const awq_layer *layer, uint16_t *w_out, void *stream) {
@@ -112,7 +136,7 @@ awq_status awq_dequant(const awq_layer *layer, uint16_t *w_out, void *stream) {
     if (st != AWQ_SUCCESS) return st;
     if (w_out == nullptr) return AWQ_ERROR_INVALID_VALUE;
     if (!aligned16(w_out)) return AWQ_ERROR_ALIGNMENT;
-    return from_hip(awq::launch_dequant(layer->qweight, layer->scales, layer->qzeros, w_out,
+    return done(stream, awq::launch_dequant(layer->qweight, layer->scales, layer->qzeros, w_out,
                                         layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
 }
 
@@ -132,7 +156,7 @@ awq_status awq_gemv(const uint16_t *x, const awq_layer *layer, uint16_t *y, int3
     if (M > 16) return AWQ_ERROR_UNSUPPORTED;
     if (workspace != nullptr && !aligned16(workspace)) return AWQ_ERROR_WORKSPACE;
     if (workspace_bytes < awq_gemv_workspace_bytes(M, layer->K, layer->N)) return AWQ_ERROR_WORKSPACE;
-    return from_hip(awq::launch_gemv(x, layer->qweight, layer->scales, layer->qzeros, y, M,
+    return done(stream, awq::launch_gemv(x, layer->qweight, layer->scales, layer->qzeros, y, M,
                                      layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
 }
 
@@ -142,7 +166,7 @@ awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int3
     if (st != AWQ_SUCCESS) return st;
     st = check_io(x, y, layer, M);
     if (st != AWQ_SUCCESS || M == 0) return st;
-    return from_hip(awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
+    return done(stream, awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
                                      layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
 }
 
@@ -157,7 +181,7 @@ awq_status awq_quantize(const uint16_t *w, int32_t K, int32_t N, int32_t group_s
     if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) ||
         (!symmetric && !aligned16(qzeros)))
         return AWQ_ERROR_ALIGNMENT;
-    return from_hip(awq::launch_quantize(w, qweight, scales, qzeros, K, N, group_size,
+    return done(stream, awq::launch_quantize(w, qweight, scales, qzeros, K, N, group_size,
                                          symmetric != 0, as_stream(stream)));
 }
 
@@ -170,7 +194,7 @@ awq_status awq_gemv_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
     if (st != AWQ_SUCCESS || M == 0) return st;
     if (!awq::gemv_gate_up_supported(M, layer->K, layer->N, layer->group_size))
         return AWQ_ERROR_UNSUPPORTED;
-    return from_hip(awq::launch_gemv_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
+    return done(stream, awq::launch_gemv_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
                                              layer->K, layer->N, layer->group_size,
                                              interleaved(layer), as_stream(stream)));
 }
@@ -184,7 +208,7 @@ awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
     if (st != AWQ_SUCCESS || M == 0) return st;
     if (!awq::gemm_gate_up_supported(layer->K, layer->N, layer->group_size))
         return AWQ_ERROR_UNSUPPORTED;
-    return from_hip(awq::launch_gemm_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
+    return done(stream, awq::launch_gemm_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
                                              layer->K, layer->N, layer->group_size,
                                              interleaved(layer), as_stream(stream)));
 }
@@ -202,14 +226,14 @@ awq_status awq_gemm_splitk(const uint16_t *x, const awq_layer *layer, uint16_t *
     st = check_io(x, y, layer, M);
     if (st != AWQ_SUCCESS || M == 0) return st;
     if (splits == 1)
-        return from_hip(awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
+        return done(stream, awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
                                          layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
     if (!awq::gemm_splitk_supported(layer->K, layer->group_size, splits)) return AWQ_ERROR_UNSUPPORTED;
     if ((long long)splits * M * layer->N > kMaxElems) return AWQ_ERROR_SHAPE;
     if (workspace == nullptr || !aligned16(workspace) ||
         workspace_bytes < awq::gemm_splitk_workspace(M, layer->N, splits))
         return AWQ_ERROR_WORKSPACE;
-    return from_hip(awq::launch_gemm_splitk(x, layer->qweight, layer->scales, layer->qzeros, y, M,
+    return done(stream, awq::launch_gemm_splitk(x, layer->qweight, layer->scales, layer->qzeros, y, M,
                                             layer->K, layer->N, layer->group_size, splits, workspace,
                                             interleaved(layer), as_stream(stream)));
 }
@@ -224,12 +248,12 @@ awq_status awq_gemm_splitk_static(const uint16_t *x, const awq_layer *layer, uin
     st = check_io(x, y, layer, M);
     if (st != AWQ_SUCCESS || M == 0) return st;
     if (splits == 1)
-        return from_hip(awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
+        return done(stream, awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
                                          layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
     if (!awq::gemm_splitk_supported(layer->K, layer->group_size, splits)) return AWQ_ERROR_UNSUPPORTED;
     if (awq::gemm_splitk_workspace(M, layer->N, splits) > awq::kStaticScratchBytes)
         return AWQ_ERROR_WORKSPACE;
-    return from_hip(awq::launch_gemm_splitk_static(x, layer->qweight, layer->scales, layer->qzeros,
+    return done(stream, awq::launch_gemm_splitk_static(x, layer->qweight, layer->scales, layer->qzeros,
                                                    y, M, layer->K, layer->N, layer->group_size,
                                                    splits, interleaved(layer), as_stream(stream)));
 }
@@ -253,7 +277,7 @@ awq_status awq_channel_stats(const uint16_t *x, int32_t M, const uint16_t *w, in
     if (workspace == nullptr || !aligned16(workspace) ||
         workspace_bytes < awq::channel_stats_workspace(M, K, N, group_size))
         return AWQ_ERROR_WORKSPACE;
-    return from_hip(awq::launch_channel_stats(x, M, w, K, N, group_size, xbar, wbar, workspace,
+    return done(stream, awq::launch_channel_stats(x, M, w, K, N, group_size, xbar, wbar, workspace,
                                               as_stream(stream)));
 }
 
@@ -271,7 +295,7 @@ awq_status awq_scale_search(const uint16_t *x, int32_t M, const uint16_t *w, int
     if (workspace == nullptr || !aligned16(workspace) ||
         workspace_bytes < awq::scale_search_workspace(M, K, N, group_size))
         return AWQ_ERROR_WORKSPACE;
-    return from_hip(awq::launch_scale_search(x, M, w, K, N, group_size, symmetric != 0, alphas,
+    return done(stream, awq::launch_scale_search(x, M, w, K, N, group_size, symmetric != 0, alphas,
                                              n_alpha, losses, best, best_scales, workspace,
                                              as_stream(stream)));
 }
