@@ -863,7 +863,11 @@ def main():
     if "hot_cache_us" in head:
         out["timing"]["hot_cache_us"] = round(head["hot_cache_us"], 3)
     read, mfma = ceiling_read("decode_8b_gate"), ceiling_mfma()
+    read70 = ceiling_read("sym70b_m1", steps=50)
+    gemv70 = next(r for c, r in configs if c == "cfg5a")
     out["ceilings"] = {"hbm_read": read, "gemv_frac_of_read": round(head["gbs"] / read["gbs"], 4),
+                       "hbm_read_sym70b_m1": read70,
+                       "gemv_sym70b_m1_frac_of_read": round(gemv70["gbs"] / read70["gbs"], 4),
                        "mfma_f16": mfma, "gemm_frac_of_mfma": round(gemm["tflops"] / mfma["tflops"], 4)}
     out["configs"] = [config_line(cfg, r) for cfg, r in configs]
     out["context"] = {"torch_matmul": torch_matmul_context("prefill_out_proj", 50)}
