@@ -1,11 +1,14 @@
-"""Measurement probes for bench.py: a plain streaming read and an MFMA rate
-probe (``ceilings.hip``), built into ``libawq_probes.so`` here.
+"""Measurement probes: a plain streaming read and an MFMA rate probe
+(``ceilings.hip``, used by bench.py), and the timeline probe (``timeline.hip``:
+the library's decode GEMV and prefill GEMM kernels compiled with per-wave
+timestamps), built into ``libawq_probes.so`` here.
 
 They measure what this GPU sustains on the two bound resources (HBM reads and
-fp16 matrix-core chains), as context for the bench line.  They are not part of
+fp16 matrix-core chains), and where a call's time goes.  They are not part of
 the library and nothing in it loads them.
 
-    python -m probes
+    python -m probes                    # build
+    python -m probes timeline [--out FILE]
 """
 from __future__ import annotations
 

@@ -95,3 +95,18 @@ def test_splitk_splits_rule():
     for M in (96, 512, 2048):                                     # the cost model's range
         assert binding.splitk_splits(M, lay(4096, 4096)) in (1, 2, 4, 8, 16)
     assert binding.splitk_splits(2048, lay(4096, 4096)) == 1
+
+
+def test_probe_library_exports():
+    """The measurement probes (built by build()) export the read and MFMA
+    ceilings and the timeline probe's calls."""
+    import shutil
+    import subprocess
+    import probes
+    if not os.path.exists(probes.LIBRARY) or shutil.which("nm") is None:
+        pytest.skip("probes not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", probes.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    for name in ("awq_probe_stream_read", "awq_probe_mfma", "awq_timeline_gemv", "awq_timeline_gemm",
+                 "awq_timeline_read", "awq_timeline_slots"):
+        assert f" T {name}" in out, name

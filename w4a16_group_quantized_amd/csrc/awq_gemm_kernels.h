@@ -32,6 +32,7 @@
 // awq_gemm.hip holds the entry points and the split-K reduction.
 #pragma once
 #include "awq_device.h"
+#include "awq_timeline.h"
 #include "awq_internal.h"
 
 namespace awq {
@@ -386,6 +387,7 @@ __global__ void __launch_bounds__(256)
 mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
               uint16_t *__restrict__ Y, int M, int K, int N, int G, int gshift, int kslice) {
+    AWQ_TL_STAMP(tl_start);
     constexpr bool ONEG = GMODE == 2;
     static_assert(!(ONEG && GU), "one-group mode is for the plain layer");
     static_assert(!(SPLIT && GU), "split K is for the plain layer");
@@ -664,6 +666,8 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     }
     r = read_raw(bring1);
     read_a(ring0, 0, a0);
+    AWQ_TL_STAMP(tl_loop0);
+    AWQ_TL_CLOCK(tc_loop0);
     for (int kt = 0; kt < KT; kt += kRing) {
         step(kt + 0, ring0, bA, bB, ring1, bring2, ring0, bring0);
         step(kt + 1, ring1, bB, bA, ring2, bring3, ring1, bring1);
@@ -671,6 +675,8 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         step(kt + 3, ring3, bB, bA, ring0, bring1, ring3, bring3);
     }
     wait_vmcnt<0>();   // no load into LDS may outlive the workgroup
+    AWQ_TL_STAMP(tl_loop1);
+    AWQ_TL_CLOCK(tc_loop1);
 
     // C layout of the 32x32 MFMA: lane (h, j) holds, in register v, row
     // 8 (v / 4) + 4 h + v % 4 of column slot j.
@@ -733,6 +739,13 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
                 __builtin_nontemporal_store(w, reinterpret_cast<uint32_t *>(Y + (size_t)row * N + col));
             }
         }
+#ifdef AWQ_TIMELINE
+    __builtin_amdgcn_s_waitcnt(0);   // the stores have completed
+    AWQ_TL_STAMP(tl_end);
+    if (threadIdx.x == 0)
+        awq_tl_record((int)(blockIdx.x + gridDim.x * blockIdx.y), tl_start, tl_loop0, tl_loop1, tl_end,
+                      tc_loop0, tc_loop1);
+#endif
 }
 
 template <int KB, int MT, bool SYM, bool GU, bool IL>

@@ -56,6 +56,7 @@
 #pragma once
 
 #include "awq_device.h"
+#include "awq_timeline.h"
 #include "awq_internal.h"
 
 namespace awq {
@@ -461,6 +462,8 @@ __global__ void __launch_bounds__(NW * 64)
 stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
               uint16_t *__restrict__ Y, int M, int K, int N, int G) {
+    AWQ_TL_STAMP(tl_start);
+    AWQ_TL_CLOCK(tc_start);
     constexpr int TN = 16 * WPL;              // weight columns (MFMA column slots) per workgroup
     constexpr int WO = GU ? WPL / 2 : WPL;    // output columns per lane
     constexpr int TO = 16 * WO;               // output columns per workgroup
@@ -730,8 +733,11 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         }
     }
 
+    AWQ_TL_STAMP(tl_loop);
+    AWQ_TL_CLOCK(tc_loop);
     // C layout of the 16x16 MFMA: lane (kb, c16) holds rows 4 kb + v of column c16.
     __syncthreads();   // every wave is done with the staged X and the tables
+    AWQ_TL_STAMP(tl_red);
 #pragma unroll
     for (int v = 0; v < VR; ++v) {
         const int m = 4 * kb + v;
@@ -763,6 +769,12 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             if (n0 + c < N) Y[(size_t)m * N + n0 + c] = as_u16((half_t)sum);
         }
     }
+#ifdef AWQ_TIMELINE
+    __builtin_amdgcn_s_waitcnt(0);   // the stores have completed
+    AWQ_TL_STAMP(tl_end);
+    if (lane == 0)
+        awq_tl_record((int)blockIdx.x * NW + wave, tl_start, tl_loop, tl_red, tl_end, tc_start, tc_loop);
+#endif
 }
 
 // Whether K's segments split over the NW waves in whole pipelines of D each.
