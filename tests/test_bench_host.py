@@ -92,6 +92,9 @@ def test_splitk_splits_rule():
     assert binding.splitk_splits(16, lay(4096, 4096, 4096)) == 8  # one group per column
     assert binding.splitk_splits(16, lay(4096, 4096, 2048)) == 2  # slices of whole groups
     assert binding.splitk_splits(16, lay(3072, 4096, 1024)) == 1  # 1536 k: not whole groups
+    assert binding.splitk_splits(16, lay(4096, 4096, 32)) == 8    # 32-k steps (G % 64 != 0)
+    assert binding.splitk_splits(16, lay(4096, 4096, 16)) == 1    # the library splits no G = 16
+    assert binding.splitk_splits(16, lay(4096, 4096, 8)) == 1
     for M in (96, 512, 2048):                                     # the cost model's range
         assert binding.splitk_splits(M, lay(4096, 4096)) in (1, 2, 4, 8, 16)
     assert binding.splitk_splits(2048, lay(4096, 4096)) == 1

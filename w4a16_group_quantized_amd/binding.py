@@ -320,11 +320,16 @@ def splitk_splits(M: int, layer: Layer, cus: int = 256) -> int:
     the partial sums, splits * M * N * 4 bytes written and read again at about
     7.9 TB/s.  More slices are taken only where the model saves at least 5%."""
     def allowed(s):
+        # the library's rule (AWQ_ERROR_UNSUPPORTED otherwise): slices of
+        # whole groups (or inside the single group), in whole ring turns of
+        # 64-k steps (G a multiple of 64) or of 32-k steps (G of 32)
         if layer.K % s:
             return False
-        ks = layer.K // s
-        whole = layer.group_size == layer.K or ks % layer.group_size == 0
-        return whole and (ks % 256 == 0 or (ks % 128 == 0 and layer.group_size % 32 == 0))
+        ks, G = layer.K // s, layer.group_size
+        one = G == layer.K
+        whole = one or ks % G == 0
+        return whole and (((one or G % 64 == 0) and ks % 256 == 0) or
+                          ((one or G % 32 == 0) and ks % 128 == 0))
 
     if M <= 64:
         tiles = -(-layer.N // 256)
