@@ -93,10 +93,11 @@ CALIBRATION_COPY_BYTES = 64 << 20
 PROFILE_CALLS = 20
 CSRC = os.path.join(ROOT, "w4a16_group_quantized_amd", "csrc")
 # Sources that define each profiled kernel (the launcher declarations in
-# awq_internal.h generate no code): a counter summary is valid only for them.
+# awq_internal.h generate no code), and the build script that sets its compile
+# flags: a counter summary is valid only for them.
 KERNEL_SOURCES = {
-    "gemv": ["awq_gemv_kernels.h", "awq_device.h"],
-    "gemm": ["awq_gemm_kernels.h", "awq_device.h"],
+    "gemv": ["awq_gemv_kernels.h", "awq_device.h", "../build.py"],
+    "gemm": ["awq_gemm_kernels.h", "awq_device.h", "../build.py"],
 }
 KERNEL_SOURCES["gemv16"] = KERNEL_SOURCES["gemv"]
 KERNEL_NAMES = {"gemv": ("stream_kernel", "fold_kernel", "exact_kernel"), "gemm": ("gemm_kernel", "mfma32_kernel")}

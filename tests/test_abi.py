@@ -309,3 +309,15 @@ def test_sync_mode_keeps_validation(value):
                        text=True, timeout=120)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.split() == ["4", "2", "3", "0", "1"]
+
+
+def test_decode_sources_take_preloaded_arguments():
+    """The decode kernels' sources, and only they, are built with kernarg
+    preloading; the prefix still names existing sources."""
+    from w4a16_group_quantized_amd import build as hip_build
+    names = [os.path.basename(s) for s in hip_build.sources()]
+    decode = [n for n in names if n.startswith("awq_gemv_stream_")]
+    assert len(decode) >= 6
+    for n in names:
+        want = hip_build.KERNARG_PRELOAD if n in decode else []
+        assert hip_build.source_flags(n, hip_build.SOURCE_FLAGS) == want, n
