@@ -132,9 +132,10 @@ def to_dev(a):
     return t.to("cuda")
 
 
-# qweight layout of every benchmarked layer (--layout): canonical, or the
-# kernel-private interleaved one (repacked once after packing, as at load time).
-LAYOUT = {"canonical": 0, "interleaved": 1}
+# qweight layout of every benchmarked layer (--layout): canonical, or one of the
+# kernel-private ones, interleaved or blocked (repacked once after packing, as
+# at load time).
+LAYOUT = {"canonical": 0, "interleaved": 1, "blocked": 2}
 BENCH_LAYOUT = "interleaved"
 
 

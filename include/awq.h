@@ -30,7 +30,7 @@
  *
  * Shape rules (AWQ_ERROR_SHAPE otherwise): K, N, G > 0; K % 8 == 0;
  * N % 8 == 0; G % 8 == 0; K % G == 0; every array below 2^31 elements.
- * Every call that takes an awq_layer takes it in either qweight layout (see
+ * Every call that takes an awq_layer takes it in any qweight layout (see
  * AWQ_LAYOUT_*) with the same results, bit for bit where the call is exact.
  * M == 0 is an empty batch: success, nothing launched.  M < 0 is invalid.
  *
@@ -77,10 +77,17 @@ typedef enum awq_status {
  * GEMVFast and Marlin, in pyshine.com's AutoAWQ tour, "The Quantization Flow
  * Up Close", without giving one): the code of k = 8r + j sits in nibble
  * 4 (j % 2) + j / 2 of word [r][n] -- the even k in the low half-word, the odd
- * k in the high half-word.  awq_repack converts between the two.
+ * k in the high half-word.  AWQ_LAYOUT_BLOCKED holds the interleaved words,
+ * moved so that each block of 128 columns is one contiguous run: word [r][n]
+ * sits at index (n / 128) * (K / 8) * 128 + r * 128 + n % 128 of the int32
+ * array, which keeps its size K/8 * N.  A kernel that streams one strip of
+ * columns over all of K then reads one run per block instead of a short piece
+ * of every row.  It needs N % 128 == 0 (AWQ_ERROR_SHAPE otherwise).
+ * awq_repack converts between any two layouts.
  */
 #define AWQ_LAYOUT_CANONICAL 0
 #define AWQ_LAYOUT_INTERLEAVED 1
+#define AWQ_LAYOUT_BLOCKED 2
 
 /* Non-owning view of one quantized linear layer (logical weight W[K][N]).
  * A zero-initialized layout field is the canonical layout. */
@@ -122,13 +129,16 @@ awq_status awq_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int32_t groups,
 /*
  * awq_repack: packed words qweight [K/8][N] from layout `from` to layout `to`
  * (AWQ_LAYOUT_*; from == to copies).  A fixed permutation of the nibbles of
- * each word, done once per layer when it is loaded: the kernel-private layouts
- * of the pages' faster kernels are such repackings of the packed weight
- * (pyshine.com AutoAWQ tour, "The Quantization Flow Up Close": GEMVFast,
- * Marlin, unpack_reorder_pack).  src and dst: device int32 [K/8][N], 16-byte
- * aligned; dst may equal src (in place).  K % 8 == 0, N % 8 == 0, K * N below
- * 2^31 (AWQ_ERROR_SHAPE otherwise); an unknown layout is
- * AWQ_ERROR_INVALID_VALUE.
+ * each word, and of the words' places for the blocked layout, done once per
+ * layer when it is loaded: the kernel-private layouts of the pages' faster
+ * kernels are such repackings of the packed weight (pyshine.com AutoAWQ tour,
+ * "The Quantization Flow Up Close": GEMVFast, Marlin, unpack_reorder_pack).
+ * src and dst: device int32 arrays of K/8 * N words, 16-byte aligned, not
+ * overlapping, except that dst may equal src (in place) when neither or both
+ * layouts are blocked; in place across the blocked layout is
+ * AWQ_ERROR_INVALID_VALUE.  K % 8 == 0, N % 8 == 0 (N % 128 == 0 if either
+ * layout is blocked), K * N below 2^31 (AWQ_ERROR_SHAPE otherwise); an unknown
+ * layout is AWQ_ERROR_INVALID_VALUE.
  */
 awq_status awq_repack(const int32_t *src, int32_t *dst, int32_t K, int32_t N, int32_t from,
                       int32_t to, void *stream);

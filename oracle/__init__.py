@@ -80,6 +80,8 @@ class Oracle:
         lib.oracle_unpack_zeros.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, _u8p]
         lib.oracle_interleave.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, _i32p]
         lib.oracle_deinterleave.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, _i32p]
+        lib.oracle_block.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, _i32p]
+        lib.oracle_unblock.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, _i32p]
         lib.oracle_dequant_one.restype = ctypes.c_uint16
         lib.oracle_dequant_one.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint16]
         lib.oracle_dequant.argtypes = [_i32p, _u16p, _i32p, ctypes.c_int, ctypes.c_int,
@@ -171,6 +173,25 @@ class Oracle:
         Q = np.ascontiguousarray(Q, dtype=np.int32)
         out = np.empty_like(Q)
         self.lib.oracle_deinterleave(_ptr(Q, _i32p), 8 * Q.shape[0], Q.shape[1], _ptr(out, _i32p))
+        return out
+
+    def block(self, Q: np.ndarray) -> np.ndarray:
+        """Packed words [K/8][N] -> their places in 128-column blocks (R18), as a
+        flat int32 array of K/8 * N words; nibbles untouched."""
+        Q = np.ascontiguousarray(Q, dtype=np.int32)
+        if Q.shape[1] % 128:
+            raise ValueError("the blocked layout needs N % 128 == 0")
+        out = np.empty(Q.size, dtype=np.int32)
+        self.lib.oracle_block(_ptr(Q, _i32p), 8 * Q.shape[0], Q.shape[1], _ptr(out, _i32p))
+        return out
+
+    def unblock(self, B: np.ndarray, K: int, N: int) -> np.ndarray:
+        """The inverse of ``block``: [K/8][N] words from a flat blocked array."""
+        B = np.ascontiguousarray(B, dtype=np.int32).reshape(-1)
+        if N % 128 or B.size != (K // 8) * N:
+            raise ValueError("the blocked layout needs N % 128 == 0 and K/8 * N words")
+        out = np.empty((K // 8, N), dtype=np.int32)
+        self.lib.oracle_unblock(_ptr(B, _i32p), K, N, _ptr(out, _i32p))
         return out
 
     # -- dequantization -------------------------------------------------------

@@ -65,6 +65,13 @@
  *       pages name private packing formats (GEMVFast, Marlin) without giving
  *       one; oracle_interleave / oracle_deinterleave are that permutation and
  *       its inverse.
+ *   R18 kernel-private blocked layout: the interleaved words, moved so that
+ *       each run of 128 columns holds all K/8 packed rows together: word
+ *       [r][n] goes to index (n / 128) * (K/8) * 128 + r * 128 + n % 128
+ *       (N % 128 == 0).  Same reading as R17: the pages name private formats
+ *       without giving one.  oracle_block / oracle_unblock move the words
+ *       (nibbles untouched); the blocked layout is oracle_block of the
+ *       interleaved words.
  *   R12 fused gate/up: the layer's N = 2I columns are [gate | up]; the output
  *       is h[m][n] = fp16(SiLU(y(m, n)) * y(m, I + n)), n < I, with y the
  *       layer's exact (unrounded) sums and SiLU(t) = t / (1 + e^-t), rounded
@@ -250,6 +257,23 @@ void oracle_deinterleave(const int32_t *Q, int K, int N, int32_t *out)
             o |= ((w >> (4 * interleaved_nibble(j))) & 0xFu) << (4 * j);
         out[i] = (int32_t)o;
     }
+}
+
+/* R18: word (r, n) of a [K/8][N] array to its place in 128-column blocks.    */
+void oracle_block(const int32_t *Q, int K, int N, int32_t *out)
+{
+    const int R = K / 8;
+    for (int r = 0; r < R; ++r)
+        for (int n = 0; n < N; ++n)
+            out[(size_t)(n / 128) * R * 128 + (size_t)r * 128 + n % 128] = Q[(size_t)r * N + n];
+}
+
+void oracle_unblock(const int32_t *B, int K, int N, int32_t *out)
+{
+    const int R = K / 8;
+    for (int r = 0; r < R; ++r)
+        for (int n = 0; n < N; ++n)
+            out[(size_t)r * N + n] = B[(size_t)(n / 128) * R * 128 + (size_t)r * 128 + n % 128];
 }
 
 /* ------------------------------------------------------------------------- */

@@ -41,6 +41,8 @@ void oracle_unpack_zeros(const int32_t *QZ, int groups, int N, uint8_t *zeros);
 /* Kernel-private layout: nibble of k % 8 = j moved to 4 (j % 2) + j / 2. */
 void oracle_interleave(const int32_t *Q, int K, int N, int32_t *out);
 void oracle_deinterleave(const int32_t *Q, int K, int N, int32_t *out);
+void oracle_block(const int32_t *Q, int K, int N, int32_t *out);
+void oracle_unblock(const int32_t *B, int K, int N, int32_t *out);
 
 uint16_t oracle_dequant_one(int q, int z, uint16_t s);
 void oracle_dequant(const int32_t *Q, const uint16_t *S, const int32_t *QZ,

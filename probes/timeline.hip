@@ -22,7 +22,7 @@ namespace awq {
 namespace gemm {
 // The general path is not timed here.
 hipError_t launch_general(const uint16_t *, const int32_t *, const uint16_t *, const int32_t *,
-                          uint16_t *, int, int, int, int, bool, hipStream_t) {
+                          uint16_t *, int, int, int, int, int, hipStream_t) {
     return hipErrorNotSupported;
 }
 }  // namespace gemm

@@ -242,6 +242,41 @@ def pin_interleave_positions_and_round_trip(o):
     assert not np.array_equal(o.interleave(W), W)
 
 
+def pin_block_hand_worked(o):
+    """The blocked layout's places, worked by hand from its definition for
+    K = 16 (two packed rows) and N = 256 (two blocks), word (r, n) = 1000 r + n:
+    block 0 holds row 0 then row 1 of columns 0..127, block 1 the same for
+    columns 128..255."""
+    Q = (1000 * np.arange(2)[:, None] + np.arange(256)[None, :]).astype(np.int32)
+    B = o.block(Q)
+    want = {0: 0, 1: 1, 127: 127, 128: 1000, 129: 1001, 255: 1127,
+            256: 128, 383: 255, 384: 1128, 511: 1255}
+    for i, v in want.items():
+        assert int(B[i]) == v, (i, int(B[i]), v)
+    assert np.array_equal(o.unblock(B, 16, 256), Q)
+
+
+def pin_block_strips_and_round_trip(o):
+    """Each 128-column strip of the words is one contiguous run, its rows in
+    order (numpy slicing of the logical array); unblock undoes block; with one
+    block or one packed row the words do not move; the words are only moved
+    (same multiset)."""
+    rng = np.random.default_rng(36)
+    for K, N in ((64, 384), (8, 512), (1024, 128), (24, 1280)):
+        Q = rng.integers(-(1 << 31), 1 << 31, (K // 8, N), dtype=np.int64).astype(np.int32)
+        B = o.block(Q)
+        R = K // 8
+        for b in range(N // 128):
+            run = B[b * R * 128:(b + 1) * R * 128].reshape(R, 128)
+            assert np.array_equal(run, Q[:, 128 * b:128 * (b + 1)]), (K, N, b)
+        assert np.array_equal(o.unblock(B, K, N), Q)
+        assert np.array_equal(np.sort(B), np.sort(Q.reshape(-1)))
+        if N == 128 or R == 1:
+            assert np.array_equal(B, Q.reshape(-1))
+        else:
+            assert not np.array_equal(B, Q.reshape(-1))
+
+
 # ----------------------------------------------------------------------------
 # dequantization w = fp16(s * (q - z))
 # ----------------------------------------------------------------------------

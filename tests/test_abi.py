@@ -71,7 +71,8 @@ def _call(lib, fn, x, c, y, M):
     (dict(K=1 << 16, N=1 << 16, G=128), 2),
     (dict(qw=None), 1), (dict(sc=None), 1),
     (dict(qw=MISALIGNED), 3), (dict(sc=MISALIGNED), 3), (dict(qz=MISALIGNED), 3),
-    (dict(layout=2), 1), (dict(layout=-1), 1),
+    (dict(layout=3), 1), (dict(layout=-1), 1),
+    (dict(layout=2), 2),                       # blocked words need N % 128 == 0
 ])
 def test_layer_validation(lib, fn, case, want):
     c = layer(**case)
@@ -266,7 +267,9 @@ def test_layout_struct_and_constants():
     text = open(HEADER).read()
     assert re.search(r"#define AWQ_LAYOUT_CANONICAL 0\b", text)
     assert re.search(r"#define AWQ_LAYOUT_INTERLEAVED 1\b", text)
+    assert re.search(r"#define AWQ_LAYOUT_BLOCKED 2\b", text)
     assert binding.LAYOUT_CANONICAL == 0 and binding.LAYOUT_INTERLEAVED == 1
+    assert binding.LAYOUT_BLOCKED == 2
 
 
 def test_repack_validation(lib):
@@ -274,8 +277,14 @@ def test_repack_validation(lib):
     assert f(None, FAKE, 64, 64, 0, 1, None) == 1
     assert f(FAKE, None, 64, 64, 0, 1, None) == 1
     assert f(FAKE, FAKE, 0, 64, 0, 1, None) == 1
-    assert f(FAKE, FAKE, 64, 64, 0, 2, None) == 1
+    assert f(FAKE, FAKE, 64, 64, 0, 3, None) == 1
     assert f(FAKE, FAKE, 64, 64, 3, 0, None) == 1
+    other = FAKE + 0x1000000
+    assert f(FAKE, other, 64, 64, 0, 2, None) == 2       # blocked words need N % 128 == 0
+    assert f(FAKE, other, 64, 136, 2, 1, None) == 2
+    assert f(FAKE, FAKE, 64, 128, 0, 2, None) == 1       # in place across the blocked layout
+    assert f(FAKE, FAKE, 64, 128, 2, 1, None) == 1
+    assert f(FAKE, FAKE, 64, 128, 2, 2, None) == 0       # same layout, in place: nothing to do
     assert f(FAKE, FAKE, 60, 64, 0, 1, None) == 2
     assert f(FAKE, FAKE, 64, 60, 0, 1, None) == 2
     assert f(FAKE, FAKE, 1 << 16, 1 << 16, 0, 1, None) == 2

@@ -101,13 +101,16 @@ def test_splitk_splits_rule():
 
 
 def test_probe_library_exports():
-    """The measurement probes (built by build()) export the read and MFMA
-    ceilings and the timeline probe's calls."""
+    """The measurement probes (built by build()) load, every symbol resolved
+    (bench.py loads them), and export the read and MFMA ceilings and the
+    timeline probe's calls."""
+    import ctypes
     import shutil
     import subprocess
     import probes
     if not os.path.exists(probes.LIBRARY) or shutil.which("nm") is None:
         pytest.skip("probes not built")
+    ctypes.CDLL(probes.LIBRARY, mode=os.RTLD_NOW)
     out = subprocess.run(["nm", "-D", "--defined-only", probes.LIBRARY], capture_output=True,
                          text=True, check=True).stdout
     for name in ("awq_probe_stream_read", "awq_probe_mfma", "awq_timeline_gemv", "awq_timeline_gemm",

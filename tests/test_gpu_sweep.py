@@ -2,8 +2,8 @@
 layouts, against the oracle.
 
 Each case draws a group size (8 to 256, or one group), K (a multiple of it),
-N (a multiple of 8), the symmetric or asymmetric form, the word layout and a
-batch, so that the launchers' choices -- strip widths, staging modes, uneven
+N (a multiple of 8, of 128 for blocked words), the symmetric or asymmetric
+form, the word layout (canonical, interleaved or blocked) and a batch, so that the launchers' choices -- strip widths, staging modes, uneven
 segment splits, tile heights and step sizes, the general paths -- are crossed
 with one another rather than exercised one shape at a time.  Shapes the
 documented rules exclude are expected to be rejected with their status, not
@@ -35,6 +35,8 @@ def draw_case(seed):
     N = 8 * int(rng.integers(1, 257))            # 8 .. 2048
     sym = bool(rng.integers(0, 2))
     layout = int(rng.integers(0, 2))
+    if layout and seed % 3 == 0:                 # blocked words: N a multiple of 128
+        N, layout = 128 * max(1, N // 128), 2
     m_gemv = int(rng.integers(1, 17))
     m_gemm = int(rng.choice([1, 3, 16, 33, 64, 130, 257, 600]))
     return K, N, G, sym, layout, m_gemv, m_gemm
@@ -44,7 +46,7 @@ def _layer(seed, M, K, N, G, sym, layout):
     X, codes, zeros, scales = random_case(20_000 + seed, M, K, N, G, sym)
     lay = device_case(codes, zeros, scales, G)
     if layout:
-        lay = binding.repack(lay, binding.LAYOUT_INTERLEAVED)
+        lay = binding.repack(lay, layout)
     return X, codes, zeros, scales, lay
 
 
@@ -89,6 +91,6 @@ def test_sweep_covers_the_launchers():
     cases = [draw_case(s) for s in range(N_CASES)]
     assert {c[2] for c in cases if c[2] != c[0]} >= {8, 32, 64, 128}
     assert any(c[2] == c[0] for c in cases)
-    assert {c[3] for c in cases} == {False, True} and {c[4] for c in cases} == {0, 1}
+    assert {c[3] for c in cases} == {False, True} and {c[4] for c in cases} == {0, 1, 2}
     assert any(c[6] <= 16 for c in cases) and any(c[6] > 64 for c in cases)
     assert max(c[0] for c in cases) >= 2048 and max(c[1] for c in cases) >= 1024

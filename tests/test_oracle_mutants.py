@@ -55,6 +55,12 @@ MUTANTS = [
      "static int interleaved_nibble(int j) { return 2 * (j % 4) + j / 4; }", 0),
     ("deinterleave_as_interleave", "o |= ((w >> (4 * interleaved_nibble(j))) & 0xFu) << (4 * j);",
      "o |= ((w >> (4 * j)) & 0xFu) << (4 * interleaved_nibble(j));", 0),
+    ("block_rows_columns_swapped",
+     "out[(size_t)(n / 128) * R * 128 + (size_t)r * 128 + n % 128] = Q[(size_t)r * N + n];",
+     "out[(size_t)(n / 128) * R * 128 + (size_t)(n % 128) * R + r] = Q[(size_t)r * N + n];", 0),
+    ("block_stride_N",
+     "out[(size_t)(n / 128) * R * 128 + (size_t)r * 128 + n % 128] = Q[(size_t)r * N + n];",
+     "out[(size_t)(n / 128) * 128 + (size_t)r * N + n % 128] = Q[(size_t)r * N + n];", 0),
     ("silu_is_sigmoid", "return t / (1.0 + exp(-t));", "return 1.0 / (1.0 + exp(-t));", 0),
     ("silu_exp_sign", "return t / (1.0 + exp(-t));", "return t / (1.0 + exp(t));", 0),
     ("gate_up_swapped", "oracle_silu(row[n]) * row[I + n]", "oracle_silu(row[I + n]) * row[n]", 0),

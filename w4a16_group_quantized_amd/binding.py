@@ -43,6 +43,7 @@ SCALE_SEARCH_MAX_ALPHAS = 64
 # qweight layouts (AWQ_LAYOUT_* of include/awq.h)
 LAYOUT_CANONICAL = 0
 LAYOUT_INTERLEAVED = 1
+LAYOUT_BLOCKED = 2        # interleaved words, 128-column blocks contiguous (N % 128 == 0)
 
 
 class AwqError(RuntimeError):
@@ -204,7 +205,8 @@ def pack_zeros(zeros: torch.Tensor, stream=None) -> torch.Tensor:
 def repack_words(qweight: torch.Tensor, to: int, frm: int = LAYOUT_CANONICAL,
                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Packed words int32 [K/8][N] from layout ``frm`` to layout ``to`` (LAYOUT_*);
-    ``out`` may be ``qweight`` itself (in place)."""
+    ``out`` may be ``qweight`` itself (in place) unless exactly one of the two
+    layouts is LAYOUT_BLOCKED, which moves words."""
     R, N = qweight.shape
     if out is None:
         out = _new((R, N), torch.int32, qweight.device, stream)

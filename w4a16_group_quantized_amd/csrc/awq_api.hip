@@ -22,9 +22,11 @@ awq_status check_layer(const awq_layer *w) {
         return AWQ_ERROR_INVALID_VALUE;
     const long long K = w->K, N = w->N, G = w->group_size;
     if (K <= 0 || N <= 0 || G <= 0) return AWQ_ERROR_INVALID_VALUE;
-    if (w->layout != AWQ_LAYOUT_CANONICAL && w->layout != AWQ_LAYOUT_INTERLEAVED)
+    if (w->layout != AWQ_LAYOUT_CANONICAL && w->layout != AWQ_LAYOUT_INTERLEAVED &&
+        w->layout != AWQ_LAYOUT_BLOCKED)
         return AWQ_ERROR_INVALID_VALUE;
     if (K % 8 || N % 8 || G % 8 || K % G) return AWQ_ERROR_SHAPE;
+    if (w->layout == AWQ_LAYOUT_BLOCKED && N % 128) return AWQ_ERROR_SHAPE;
     if (K * N > kMaxElems) return AWQ_ERROR_SHAPE;  // the dequantized weight's element count
     if (!aligned16(w->qweight) || !aligned16(w->scales) ||
         (w->qzeros != nullptr && !aligned16(w->qzeros)))
@@ -68,7 +70,8 @@ awq_status done(void *stream, hipError_t e) {
     return hipGetLastError() == hipSuccess ? AWQ_SUCCESS : AWQ_ERROR_HIP;
 }
 
-bool interleaved(const awq_layer *w) { return w->layout == AWQ_LAYOUT_INTERLEAVED; }
+// The launchers take the layout as AWQ_LAYOUT_* (checked by check_layer).
+int layout_of(const awq_layer *w) { return w->layout; }
 
 // Calibration X [M][K] and fp16 weight W [K][N] of the scale search.
 awq_status check_calibration(const uint16_t *x, int32_t M, const uint16_t *w, int32_t K, int32_t N,
@@ -90,7 +93,7 @@ const char *awq_status_string(awq_status status) {
     switch (status) {
     case AWQ_SUCCESS: return "AWQ_SUCCESS";
     case AWQ_ERROR_INVALID_VALUE: return "AWQ_ERROR_INVALID_VALUE: null pointer or non-positive size";
-    case AWQ_ERROR_SHAPE: return "AWQ_ERROR_SHAPE: K%8, N%8, G%8, K%G must be 0 and arrays below 2^31 elements";
+    case AWQ_ERROR_SHAPE: return "AWQ_ERROR_SHAPE: K%8, N%8, G%8, K%G must be 0 (and N%128 in the blocked layout) and arrays below 2^31 elements";
     case AWQ_ERROR_ALIGNMENT: return "AWQ_ERROR_ALIGNMENT: tensor pointers must be 16-byte aligned";
     case AWQ_ERROR_UNSUPPORTED: return "AWQ_ERROR_UNSUPPORTED: outside this entry point (awq_gemv takes M <= 16; awq_gemv_gate_up also needs G % 128 == 0 and X in LDS; awq_gemm_gate_up needs G % 64 == 0 and K % 256 == 0; awq_gemm_splitk needs slices of whole groups (or one group) and whole 128- or 256-k ring turns)";
     case AWQ_ERROR_WORKSPACE: return "AWQ_ERROR_WORKSPACE: null, unaligned or smaller than the *_workspace_bytes query";
@@ -118,9 +121,15 @@ awq_status awq_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int32_t groups,
 awq_status awq_repack(const int32_t *src, int32_t *dst, int32_t K, int32_t N, int32_t from,
                       int32_t to, void *stream) {
     if (src == nullptr || dst == nullptr || K <= 0 || N <= 0) return AWQ_ERROR_INVALID_VALUE;
-    const auto known = [](int32_t l) { return l == AWQ_LAYOUT_CANONICAL || l == AWQ_LAYOUT_INTERLEAVED; };
+    const auto known = [](int32_t l) {
+        return l == AWQ_LAYOUT_CANONICAL || l == AWQ_LAYOUT_INTERLEAVED || l == AWQ_LAYOUT_BLOCKED;
+    };
     if (!known(from) || !known(to)) return AWQ_ERROR_INVALID_VALUE;
+    // In place only where no word moves: the blocked layout moves words.
+    if (src == dst && (from == AWQ_LAYOUT_BLOCKED) != (to == AWQ_LAYOUT_BLOCKED))
+        return AWQ_ERROR_INVALID_VALUE;
     if (K % 8 || N % 8 || (long long)K * N > kMaxElems) return AWQ_ERROR_SHAPE;
+    if ((from == AWQ_LAYOUT_BLOCKED || to == AWQ_LAYOUT_BLOCKED) && N % 128) return AWQ_ERROR_SHAPE;
     if (!aligned16(src) || !aligned16(dst)) return AWQ_ERROR_ALIGNMENT;
     const long long words = (long long)(K / 8) * N;
     if (from == to) {
@@ -128,7 +137,7 @@ awq_status awq_repack(const int32_t *src, int32_t *dst, int32_t K, int32_t N, in
         return done(stream, hipMemcpyAsync(dst, src, (size_t)words * 4, hipMemcpyDeviceToDevice,
                                        as_stream(stream)));
     }
-    return done(stream, awq::launch_repack(src, dst, words, to == AWQ_LAYOUT_INTERLEAVED, as_stream(stream)));
+    return done(stream, awq::launch_repack(src, dst, K, N, from, to, as_stream(stream)));
 }
 
 awq_status awq_dequant(const awq_layer *layer, uint16_t *w_out, void *stream) {
@@ -137,7 +146,7 @@ awq_status awq_dequant(const awq_layer *layer, uint16_t *w_out, void *stream) {
     if (w_out == nullptr) return AWQ_ERROR_INVALID_VALUE;
     if (!aligned16(w_out)) return AWQ_ERROR_ALIGNMENT;
     return done(stream, awq::launch_dequant(layer->qweight, layer->scales, layer->qzeros, w_out,
-                                        layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
+                                        layer->K, layer->N, layer->group_size, layout_of(layer), as_stream(stream)));
 }
 
 size_t awq_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) {
@@ -157,7 +166,7 @@ awq_status awq_gemv(const uint16_t *x, const awq_layer *layer, uint16_t *y, int3
     if (workspace != nullptr && !aligned16(workspace)) return AWQ_ERROR_WORKSPACE;
     if (workspace_bytes < awq_gemv_workspace_bytes(M, layer->K, layer->N)) return AWQ_ERROR_WORKSPACE;
     return done(stream, awq::launch_gemv(x, layer->qweight, layer->scales, layer->qzeros, y, M,
-                                     layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
+                                     layer->K, layer->N, layer->group_size, layout_of(layer), as_stream(stream)));
 }
 
 awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int32_t M,
@@ -167,7 +176,7 @@ awq_status awq_gemm(const uint16_t *x, const awq_layer *layer, uint16_t *y, int3
     st = check_io(x, y, layer, M);
     if (st != AWQ_SUCCESS || M == 0) return st;
     return done(stream, awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
-                                     layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
+                                     layer->K, layer->N, layer->group_size, layout_of(layer), as_stream(stream)));
 }
 
 awq_status awq_quantize(const uint16_t *w, int32_t K, int32_t N, int32_t group_size,
@@ -196,7 +205,7 @@ awq_status awq_gemv_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
         return AWQ_ERROR_UNSUPPORTED;
     return done(stream, awq::launch_gemv_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
                                              layer->K, layer->N, layer->group_size,
-                                             interleaved(layer), as_stream(stream)));
+                                             layout_of(layer), as_stream(stream)));
 }
 
 awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t *h, int32_t M,
@@ -210,7 +219,7 @@ awq_status awq_gemm_gate_up(const uint16_t *x, const awq_layer *layer, uint16_t 
         return AWQ_ERROR_UNSUPPORTED;
     return done(stream, awq::launch_gemm_gate_up(x, layer->qweight, layer->scales, layer->qzeros, h, M,
                                              layer->K, layer->N, layer->group_size,
-                                             interleaved(layer), as_stream(stream)));
+                                             layout_of(layer), as_stream(stream)));
 }
 
 size_t awq_gemm_splitk_workspace_bytes(int32_t M, int32_t N, int32_t splits) {
@@ -227,7 +236,7 @@ awq_status awq_gemm_splitk(const uint16_t *x, const awq_layer *layer, uint16_t *
     if (st != AWQ_SUCCESS || M == 0) return st;
     if (splits == 1)
         return done(stream, awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
-                                         layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
+                                         layer->K, layer->N, layer->group_size, layout_of(layer), as_stream(stream)));
     if (!awq::gemm_splitk_supported(layer->K, layer->group_size, splits)) return AWQ_ERROR_UNSUPPORTED;
     if ((long long)splits * M * layer->N > kMaxElems) return AWQ_ERROR_SHAPE;
     if (workspace == nullptr || !aligned16(workspace) ||
@@ -235,7 +244,7 @@ awq_status awq_gemm_splitk(const uint16_t *x, const awq_layer *layer, uint16_t *
         return AWQ_ERROR_WORKSPACE;
     return done(stream, awq::launch_gemm_splitk(x, layer->qweight, layer->scales, layer->qzeros, y, M,
                                             layer->K, layer->N, layer->group_size, splits, workspace,
-                                            interleaved(layer), as_stream(stream)));
+                                            layout_of(layer), as_stream(stream)));
 }
 
 awq_status awq_gemm_splitk_static(const uint16_t *x, const awq_layer *layer, uint16_t *y,
@@ -249,13 +258,13 @@ awq_status awq_gemm_splitk_static(const uint16_t *x, const awq_layer *layer, uin
     if (st != AWQ_SUCCESS || M == 0) return st;
     if (splits == 1)
         return done(stream, awq::launch_gemm(x, layer->qweight, layer->scales, layer->qzeros, y, M,
-                                         layer->K, layer->N, layer->group_size, interleaved(layer), as_stream(stream)));
+                                         layer->K, layer->N, layer->group_size, layout_of(layer), as_stream(stream)));
     if (!awq::gemm_splitk_supported(layer->K, layer->group_size, splits)) return AWQ_ERROR_UNSUPPORTED;
     if (awq::gemm_splitk_workspace(M, layer->N, splits) > awq::kStaticScratchBytes)
         return AWQ_ERROR_WORKSPACE;
     return done(stream, awq::launch_gemm_splitk_static(x, layer->qweight, layer->scales, layer->qzeros,
                                                    y, M, layer->K, layer->N, layer->group_size,
-                                                   splits, interleaved(layer), as_stream(stream)));
+                                                   splits, layout_of(layer), as_stream(stream)));
 }
 
 size_t awq_channel_stats_workspace_bytes(int32_t M, int32_t K, int32_t N, int32_t group_size) {

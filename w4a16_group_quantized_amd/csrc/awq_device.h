@@ -183,6 +183,25 @@ __device__ __forceinline__ uint32_t interleave_word(uint32_t w) {
     return swap_middle_bytes(swap_middle_nibbles(w));
 }
 
+// Where the packed words sit.  The kernels take the qweight layout as a
+// template parameter IL: 0 canonical, 1 interleaved, 2 blocked (see
+// include/awq.h); a nonzero IL means interleaved nibble order.  In the blocked
+// layout the columns are cut into blocks of kQBlock, and block b stores packed
+// row 0 of its columns, then row 1, and so on: word (r, n) sits at
+//   (n / kQBlock) * KR * kQBlock + r * kQBlock + n % kQBlock   (KR = K / 8).
+// A run of columns inside one block is contiguous in both layouts, so every
+// kernel load (at most 8 words, aligned to its width) stays one load.
+constexpr int kQBlock = 128;
+constexpr bool blocked_layout(int il) { return il == 2; }
+// Words between packed rows r and r + 1 of one column.
+__host__ __device__ __forceinline__ int q_pitch(bool blk, int N) { return blk ? kQBlock : N; }
+// Offset of word (0, n), in words.
+__host__ __device__ __forceinline__ uint32_t q_col(bool blk, int n, int KR) {
+    return blk ? (uint32_t)(n / kQBlock) * (uint32_t)KR * (uint32_t)kQBlock +
+                     (uint32_t)(n % kQBlock)
+               : (uint32_t)n;
+}
+
 // 1024 + z as fp16, from the 4-bit zero point z.
 __device__ __forceinline__ half_t biased_zero(uint32_t z) {
     return __builtin_bit_cast(half_t, (uint16_t)(0x6400u | (z & 0xFu)));

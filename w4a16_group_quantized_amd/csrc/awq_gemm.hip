@@ -10,17 +10,17 @@ namespace gemm {
 
 template <int BM, bool SYM>
 hipError_t launch_general_bm(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
+                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, int il,
                           hipStream_t s) {
     const long long tiles = (long long)((M + BM - 1) / BM) * ((N + kBN - 1) / kBN);
     hipLaunchKernelGGL((gemm_kernel<BM, SYM>), dim3((unsigned)tiles), dim3(256), 0, s, x,
                        reinterpret_cast<const uint32_t *>(qw), sc,
-                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G, il ? 1 : 0);
+                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G, il);
     return hipGetLastError();
 }
 
 hipError_t launch_general(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
+                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, int il,
                           hipStream_t s) {
     return qz == nullptr ? launch_general_bm<128, true>(x, qw, sc, qz, y, M, K, N, G, il, s)
                          : launch_general_bm<128, false>(x, qw, sc, qz, y, M, K, N, G, il, s);
@@ -56,9 +56,9 @@ size_t gemm_splitk_workspace(int M, int N, int splits) {
 
 hipError_t launch_gemm_splitk(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                               const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
-                              int splits, void *workspace, bool il, hipStream_t s) {
+                              int splits, void *workspace, int il, hipStream_t s) {
     auto *part = static_cast<float *>(workspace);
-    const hipError_t e = (il ? gemm::split_il : gemm::split_canon)(x, qweight, scales, qzeros, part,
+    const hipError_t e = (il == 2 ? gemm::split_blk : il ? gemm::split_il : gemm::split_canon)(x, qweight, scales, qzeros, part,
                                                                    M, K, N, G, splits, s);
     if (e != hipSuccess) return e;
     const long long count = (long long)M * N;
@@ -75,15 +75,15 @@ bool gemm_gate_up_supported(int K, int N, int G) {
 
 hipError_t launch_gemm_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                                const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
-                               bool il, hipStream_t s) {
-    return (il ? gemm::gate_up_il : gemm::gate_up_canon)(x, qweight, scales, qzeros, h, M, K, N, G,
+                               int il, hipStream_t s) {
+    return (il == 2 ? gemm::gate_up_blk : il ? gemm::gate_up_il : gemm::gate_up_canon)(x, qweight, scales, qzeros, h, M, K, N, G,
                                                          s);
 }
 
 hipError_t launch_gemm(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
-                       const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G, bool il,
+                       const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G, int il,
                        hipStream_t s) {
-    return (il ? gemm::plain_il : gemm::plain_canon)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    return (il == 2 ? gemm::plain_blk : il ? gemm::plain_il : gemm::plain_canon)(x, qweight, scales, qzeros, y, M, K, N, G, s);
 }
 
 }  // namespace awq

@@ -157,6 +157,9 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const int KT = (K + kBK - 1) / kBK;
     const int KTP = (KT + kRing - 1) / kRing * kRing;   // steps, padded to whole rings
     const uint32_t nmask = nibble_mask_vgpr();
+    const bool blk = il == 2;   // il: the qweight layout (nonzero: interleaved nibbles)
+    const int qp = q_pitch(blk, N);
+    const uint32_t qc = q_col(blk, ncl, KR);
 
     // X: chunk p of a tile (16 bytes) is written by lane p % 64 of one wave's
     // direct-to-LDS load; the swizzle is undone on the global side, so chunk p
@@ -186,7 +189,7 @@ gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             const int r0 = kt * (kBK / 8) + 4 * s + kb;
             const int r = r0 < KR ? r0 : KR - 1;
             const int g = (8 * r) / G;
-            b.q[s] = *reinterpret_cast<const uint4 *>(Q + (size_t)r * N + ncl);
+            b.q[s] = *reinterpret_cast<const uint4 *>(Q + (size_t)r * qp + qc);
             b.sc[s] = *reinterpret_cast<const uint2 *>(S + (size_t)g * N + ncl);
             if constexpr (SYM) b.zw[s] = 0x88888888u;
             else b.zw[s] = QZ[(size_t)g * (N / 8) + ncl / 8];
@@ -378,11 +381,13 @@ __device__ __forceinline__ void unpack_natural(uint32_t w, uint32_t exps, uint32
 // MFMA columns are then 32 gate columns and the same 32 columns of the up half
 // (column tile 0: gate, tile 1: up, for the same output column), and the
 // output is h[M][I] = fp16(SiLU(gate) * up), 32 columns per wave.
-// IL: the packed words are in the kernel-private interleaved layout; each
-// natural-order pair is then one AND-OR (unpack_interleaved), against the two
-// v_perm + AND of the canonical word, and the bias of a pair is 1024 + z for
-// the even pairs and 64 + z for the odd ones.
-template <int KB, int MT, bool SYM, int GMODE, bool GU, bool SPLIT = false, bool IL = false>
+// IL: the qweight layout (0 canonical, 1 interleaved, 2 blocked).  Nonzero:
+// interleaved nibbles; each natural-order pair is then one AND-OR
+// (unpack_interleaved), against the two v_perm + AND of the canonical word, and
+// the bias of a pair is 1024 + z for the even pairs and 64 + z for the odd
+// ones.  2: a wave's 64 columns lie in one 128-column block, whose packed rows
+// are 512 bytes apart (q_col, q_pitch).
+template <int KB, int MT, bool SYM, int GMODE, bool GU, bool SPLIT = false, int IL = 0>
 __global__ void __launch_bounds__(256)
 mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
@@ -423,10 +428,12 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     // The k this workgroup sums: all of K, or its slice under split K.
     const int k0 = SPLIT ? (int)blockIdx.y * kslice : 0;
     const int KL = SPLIT ? kslice : K;
+    constexpr bool BLK = blocked_layout(IL);
+    const int qp = q_pitch(BLK, N);
     const int groups = ONEG ? 1 : (K - k0) / G;   // scale rows from the slice's first group on
     if constexpr (SPLIT) {
         X += k0;
-        Q += (size_t)(k0 / 8) * N;
+        Q += (size_t)(k0 / 8) * qp;
         if constexpr (!ONEG) {
             S += (size_t)(k0 / G) * N;
             if constexpr (!SYM) QZ += (size_t)(k0 / G) * (N / 8);
@@ -440,7 +447,11 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     // keep their stride K; the buffer ends after the slice's part of row M - 1.
     const __amdgpu_buffer_rsrc_t xrs =
         make_rsrc(X, ((uint32_t)(M - 1) * (uint32_t)K + (uint32_t)KL) * 2u);
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, (uint32_t)KR * (uint32_t)N * 4u);
+    // Blocked words: the buffer runs to the end of qweight (every block's rows
+    // of the slice lie in it; columns past N fall past its end and read zeros).
+    const uint32_t qwords = BLK ? (uint32_t)(K / 8) * (uint32_t)N - (uint32_t)(k0 / 8) * kQBlock
+                                : (uint32_t)KR * (uint32_t)N;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, qwords * 4u);
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(S, (uint32_t)groups * (uint32_t)N * 2u);
     const __amdgpu_buffer_rsrc_t zrs = make_rsrc(QZ, SYM ? 0u : (uint32_t)groups * (uint32_t)N / 2u);
     uint32_t xvoff[kACH];
@@ -453,12 +464,13 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         xvoff[i] = ((uint32_t)xr * (uint32_t)K + (uint32_t)xkc * 8u) * 2u;
     }
     // packed rows: load d (0, 1) of a step, lane i -> row 4 d + i / 16, columns n0 + 4 (i % 16) ..
-    const uint32_t qvoff = ((uint32_t)(lane >> 4) * (uint32_t)N + (uint32_t)src_col(4 * (lane & 15))) * 4u;
+    const uint32_t qvoff =
+        ((uint32_t)(lane >> 4) * (uint32_t)qp + q_col(BLK, src_col(4 * (lane & 15)), K / 8)) * 4u;
     const uint32_t svoff = (uint32_t)src_col(2 * (lane & 31)) * 2u;
     const uint32_t zvoff = (uint32_t)(src_col(8 * (lane & 7)) / 8) * 4u;
 
     // Byte strides: a step of packed rows, half of it, a scale row, a zero row.
-    const int qstep = Gm::QROWS * 4 * N, qhalf = 16 * N, srow = 2 * N, zrow = N / 2;
+    const int qstep = Gm::QROWS * 4 * qp, qhalf = 16 * qp, srow = 2 * N, zrow = N / 2;
     const int gsteps = G / kBKs;
     auto load_step = [&](int kt, uint4 *xbuf, uint4 *bbuf) {
         uint4 *dst = bbuf + wave * kWave;
@@ -748,7 +760,7 @@ mfma32_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 #endif
 }
 
-template <int KB, int MT, bool SYM, bool GU, bool IL>
+template <int KB, int MT, bool SYM, bool GU, int IL>
 hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                   uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
     using Gm = Geom<KB, MT>;
@@ -779,7 +791,7 @@ hipError_t launch(const uint16_t *x, const int32_t *qw, const uint16_t *sc, cons
 // Split K: `splits` slices of K / splits k, each a whole number of steps and
 // of groups (or inside the single group), as a second grid dimension; fp32
 // partial tiles into part[splits][M][N].
-template <int KB, int MT, bool SYM, bool IL>
+template <int KB, int MT, bool SYM, int IL>
 hipError_t launch_split(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                         float *part, int M, int K, int N, int G, int splits, hipStream_t s) {
     using Gm = Geom<KB, MT>;
@@ -819,7 +831,7 @@ inline int splitk_bk(int K, int G, int splits) {
 // The general kernel (16x16x32 MFMAs, any G and K), both layouts: it reads the
 // layout as a kernel argument.
 hipError_t launch_general(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
+                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, int il,
                           hipStream_t s);
 
 // One layout's launchers, defined in awq_gemm_canon.hip (canonical words) and
@@ -830,14 +842,14 @@ using PlainLauncher = hipError_t(const uint16_t *x, const int32_t *qw, const uin
 using SplitLauncher = hipError_t(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                                  const int32_t *qz, float *part, int M, int K, int N, int G,
                                  int splits, hipStream_t s);
-PlainLauncher plain_canon, plain_il, gate_up_canon, gate_up_il;
-SplitLauncher split_canon, split_il;
+PlainLauncher plain_canon, plain_il, plain_blk, gate_up_canon, gate_up_il, gate_up_blk;
+SplitLauncher split_canon, split_il, split_blk;
 
 // Kernel choice: 256-row tiles with 32-k steps for large batches (half the
 // dequantization per MFMA), as long as they fill the GPU twice over; 128-row
 // tiles with 64-k steps otherwise, 64-row ones where rows64 says; 32-k steps
 // when G or K only allow those; the general kernel for the rest.
-template <bool IL>
+template <int IL>
 hipError_t launch_layout(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                          uint16_t *y, int M, int K, int N, int G, hipStream_t s) {
     const bool sym = qz == nullptr;
@@ -868,7 +880,7 @@ hipError_t launch_layout(const uint16_t *x, const int32_t *qw, const uint16_t *s
 // more on padding rows), and wherever the 64-row tiles times the slices still
 // fit one workgroup per CU (4096 x 4096 at 128 rows in 8 slices: 22.4 -> 21.0
 // us; at 256 rows in 4: 23.8 -> 22.1 us).
-template <bool IL>
+template <int IL>
 hipError_t split_layout(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
                         float *part, int M, int K, int N, int G, int splits, hipStream_t s) {
     const bool sym = qz == nullptr;
@@ -883,7 +895,7 @@ hipError_t split_layout(const uint16_t *x, const int32_t *qw, const uint16_t *sc
 
 // Fused gate/up: 64-row tiles where they pay, as in the plain GEMM (the tile
 // count is the same: 128 output columns are 256 layer columns).
-template <bool IL>
+template <int IL>
 hipError_t gate_up_layout(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                           const int32_t *qz, uint16_t *h, int M, int K, int N, int G,
                           hipStream_t s) {

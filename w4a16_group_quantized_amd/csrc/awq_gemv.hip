@@ -8,7 +8,7 @@
 namespace awq {
 
 hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
-                       const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G, bool il,
+                       const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G, int il,
                        hipStream_t s) {
     using namespace gemv;
     // Per-wave staged X, D-deep load pipeline.  The strip width depends on the
@@ -28,23 +28,23 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
         // 15.5 us).
         const bool wide = n128 * 4 >= 3LL * cus && (M > 8 || n64 > 2LL * cus);
         if (narrow && stream_fits_prog(M, K, N, G, 2, 8, 1))
-            return (il ? prog_w2_il : prog_w2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+            return (il == 2 ? prog_w2_blk : il ? prog_w2_il : prog_w2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
         if (!wide && stream_fits_prog(M, K, N, G, 4, 8, 1))
-            return (il ? prog_w4_il : prog_w4)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+            return (il == 2 ? prog_w4_blk : il ? prog_w4_il : prog_w4)(x, qweight, scales, qzeros, y, M, K, N, G, s);
         if (stream_fits_prog(M, K, N, G, 8, 8, 1))
-            return (il ? prog_w8_il : prog_w8)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+            return (il == 2 ? prog_w8_blk : il ? prog_w8_il : prog_w8)(x, qweight, scales, qzeros, y, M, K, N, G, s);
     }
     if (narrow && stream_fits(M, K, N, G, 2, 8, 16, 2))
-        return (il ? stream_m_w2_d2_il : stream_m_w2_d2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        return (il == 2 ? stream_m_w2_d2_blk : il ? stream_m_w2_d2_il : stream_m_w2_d2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 2))
-        return (il ? stream_m_w4_d2_il : stream_m_w4_d2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        return (il == 2 ? stream_m_w4_d2_blk : il ? stream_m_w4_d2_il : stream_m_w4_d2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 4, 8, 16, 1))
-        return (il ? stream_m_w4_d1_il : stream_m_w4_d1)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        return (il == 2 ? stream_m_w4_d1_blk : il ? stream_m_w4_d1_il : stream_m_w4_d1)(x, qweight, scales, qzeros, y, M, K, N, G, s);
     // Up to four rows with X beyond LDS: staged segment by segment as well.
     if (narrow && stream_fits_prog(M, K, N, G, 2, 8, 1))
-        return (il ? prog_w2_il : prog_w2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        return (il == 2 ? prog_w2_blk : il ? prog_w2_il : prog_w2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
     if (stream_fits_prog(M, K, N, G, 4, 8, 1))
-        return (il ? prog_w4_il : prog_w4)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        return (il == 2 ? prog_w4_blk : il ? prog_w4_il : prog_w4)(x, qweight, scales, qzeros, y, M, K, N, G, s);
     // A segment (SEGR packed rows) must sit inside one group and be whole 32-k steps.
     // Narrow layers on 32-column strips here too (14336 x 4096 at 16 rows:
     // 27.4 -> 22.1 us).

@@ -252,7 +252,10 @@ fold_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, (uint32_t)KR * (uint32_t)N * 4u);
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(S, (uint32_t)(K / G) * (uint32_t)N * 2u);
     const __amdgpu_buffer_rsrc_t zrs = make_rsrc(QZ, SYM ? 0u : (uint32_t)(K / G) * (uint32_t)N / 2u);
-    const int qvoff = (ncl + kb * N) * 4;
+    // il: the qweight layout (nonzero: interleaved nibble order; 2: blocked).
+    const bool blk = il == 2;
+    const int qp = q_pitch(blk, N);
+    const int qvoff = (int)(q_col(blk, ncl, KR) + (uint32_t)(kb * qp)) * 4;
     const int svoff = ncl * 2;
     const int zvoff = (ncl / 8) * 4;
     const int zshift = 4 * (ncl % 8);
@@ -264,7 +267,7 @@ fold_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         const int r0 = seg * SEGR;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st)
-            b.q[st] = buffer_words<WPL>(qrs, qvoff, (r0 + 4 * st) * N * 4);
+            b.q[st] = buffer_words<WPL>(qrs, qvoff, (r0 + 4 * st) * qp * 4);
         const int g = (8 * r0) / G;
         b.sc = buffer_scales<WPL>(srs, svoff, g * N * 2);
         if constexpr (!SYM) b.zw = __builtin_amdgcn_raw_buffer_load_b32(zrs, zvoff, g * (N / 8) * 4, 0);
@@ -446,18 +449,19 @@ constexpr size_t kLdsMax = 160 * 1024;
 // just before the segment is multiplied, instead of the whole slice up front.
 // With 16 rows the whole slice is 128 KB per workgroup, and every workgroup
 // asking for it at once delays the first multiply by microseconds.
-// IL: the packed words are in the kernel-private interleaved layout
-// (awq_repack).  A word then unpacks into the natural-order pairs (k 2e,
+// IL: the qweight layout (0 canonical, 1 interleaved, 2 blocked; awq_repack).
+// Nonzero: interleaved nibble order.  A word then unpacks into the natural-order pairs (k 2e,
 // k 2e + 1) as (1024 + q, 1024 + q') for even e and (64 + q, 64 + q') for odd
 // e, so X is staged in natural order with no x / 16, and the bias sum U weighs
-// the odd pairs' x by 64 instead of 1024.
+// the odd pairs' x by 64 instead of 1024.  2: the words of a workgroup's strip
+// are one contiguous run per 128-column block (q_col, q_pitch).
 // UNEV: the K range's segments do not split into whole pipelines of D per
 // wave (K not a multiple of 8 NW SEGR, or an odd count per wave): the first
 // nseg % NW waves take one segment more, and the loads ahead are guarded by
 // the wave's own count (a uniform branch).  The even case keeps the
 // unconditional pipeline.
 template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false,
-          int XS = 0, bool UNEV = false, bool IL = false>
+          int XS = 0, bool UNEV = false, int IL = 0>
 __global__ void __launch_bounds__(NW * 64)
 stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
               const uint16_t *__restrict__ S, const uint32_t *__restrict__ QZ,
@@ -506,16 +510,19 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     float *red = reinterpret_cast<float *>(lds);
 
     const int xrow = c16 < M ? c16 : M - 1;      // A row of this lane (clamped)
-    const uint32_t lane_q = (uint32_t)(ncl + kb * N);
+    constexpr bool BLK = blocked_layout(IL);
+    const int qp = q_pitch(BLK, N);
+    const uint32_t lane_q = q_col(BLK, ncl, KR) + (uint32_t)(kb * qp);
+    const uint32_t lane_q2 = GU ? q_col(BLK, ncl + NO, KR) + (uint32_t)(kb * qp) : 0u;   // up half
 
     // Scale and zero of one segment; loads of one segment.
     auto load_seg = [&](int seg, WSeg<WPL, STEPS, SYM> &b) {
         const int r0 = seg * SEGR;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            const uint32_t *qrow = Q + (size_t)(r0 + 4 * st) * N;   // wave-uniform
+            const uint32_t *qrow = Q + (size_t)(r0 + 4 * st) * qp;   // wave-uniform
             if constexpr (GU)
-                b.q[st] = join<WPL>(load_words<WO>(qrow + lane_q), load_words<WO>(qrow + lane_q + NO));
+                b.q[st] = join<WPL>(load_words<WO>(qrow + lane_q), load_words<WO>(qrow + lane_q2));
             else
                 b.q[st] = load_words<WPL>(qrow + lane_q);
         }
@@ -801,7 +808,7 @@ inline size_t stream_lds_prog(int M, int K, int WPL, int NW, int SEGR) {
 }
 
 template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false,
-          int XS = 0, bool IL = false>
+          int XS = 0, int IL = 0>
 hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                          hipStream_t s) {
@@ -856,7 +863,7 @@ inline bool stream_fits_prog(int M, int K, int N, int G, int WPL, int NW, int D)
     return stream_lds_prog(M, K, WPL, NW, 16) <= kLdsMax;
 }
 
-template <int WPL, int NW, int SEGR, int D, int VR, int XCH, bool IL>
+template <int WPL, int NW, int SEGR, int D, int VR, int XCH, int IL>
 hipError_t launch_stream_sg(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                             const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                             hipStream_t s) {
@@ -868,7 +875,7 @@ hipError_t launch_stream_sg(const uint16_t *x, const int32_t *qw, const uint16_t
                 : launch_stream<WPL, NW, SEGR, D, VR, false, false, XCH, false, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
-template <int WPL, int NW, int SEGR, int D, int VR, bool IL>
+template <int WPL, int NW, int SEGR, int D, int VR, int IL>
 hipError_t launch_stream_x(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                            const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                            hipStream_t s) {
@@ -894,7 +901,7 @@ inline int device_cus() {
 
 // Beyond four rows (all four C rows of a lane live), X staged progressively:
 // XS = ceil(M * 16 / 64) chunks per lane per 16-row segment.
-template <int WPL, int NW, int D, bool GU, int XS, bool IL>
+template <int WPL, int NW, int D, bool GU, int XS, int IL>
 hipError_t launch_stream_prog_xs(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                                  const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                                  hipStream_t s) {
@@ -906,7 +913,7 @@ hipError_t launch_stream_prog_xs(const uint16_t *x, const int32_t *qw, const uin
 #undef AWQ_PROG
 }
 
-template <int WPL, int NW, int D, bool GU, bool IL>
+template <int WPL, int NW, int D, bool GU, int IL>
 hipError_t launch_stream_prog(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                               const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                               hipStream_t s) {
@@ -916,7 +923,7 @@ hipError_t launch_stream_prog(const uint16_t *x, const int32_t *qw, const uint16
     return launch_stream_prog_xs<WPL, NW, D, GU, 4, IL>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
-template <int WPL, int NW, int SEGR, int D, bool IL>
+template <int WPL, int NW, int SEGR, int D, int IL>
 hipError_t launch_stream_m(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                            const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                            hipStream_t s) {
@@ -948,6 +955,9 @@ exact_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     const int xrow = c16 < M ? c16 : M - 1;
     const int KR = K / 8;
     const uint32_t nmask = nibble_mask_vgpr();
+    const bool blk = il == 2;   // il: the qweight layout (nonzero: interleaved nibbles)
+    const int qp = q_pitch(blk, N);
+    const uint32_t qc = q_col(blk, ncl, KR);
 
     float4_t C[WPL];
 #pragma unroll
@@ -959,7 +969,7 @@ exact_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
         uint4 xa = make_uint4(0u, 0u, 0u, 0u);
         if (r < KR) {
             xa = reinterpret_cast<const uint4 *>(X + (size_t)xrow * K)[r];
-            const Words<WPL> q = load_words<WPL>(Q + (size_t)r * N + ncl);
+            const Words<WPL> q = load_words<WPL>(Q + (size_t)r * qp + qc);
             const int g = (8 * r) / G;
             const uint32_t zw = QZ ? QZ[(size_t)g * (N / 8) + ncl / 8] >> (4 * (ncl % 8))
                                    : 0x88888888u;
@@ -1006,18 +1016,18 @@ exact_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
 
 template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool XLDS>
 hipError_t launch_fold(const uint16_t *x, const int32_t *qw, const uint16_t *sc, const int32_t *qz,
-                       uint16_t *y, int M, int K, int N, int G, bool il, hipStream_t s) {
+                       uint16_t *y, int M, int K, int N, int G, int il, hipStream_t s) {
     constexpr int TN = 16 * WPL;
     const size_t lds = (XLDS ? (size_t)M * K * 2 : 0) + (size_t)NW * M * TN * sizeof(float);
     hipLaunchKernelGGL((fold_kernel<WPL, NW, SEGR, D, VR, SYM, XLDS>), dim3((N + TN - 1) / TN),
                        dim3(NW * 64), lds, s, x, reinterpret_cast<const uint32_t *>(qw), sc,
-                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G, il ? 1 : 0);
+                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G, il);
     return hipGetLastError();
 }
 
 template <int WPL, int NW, int SEGR, int D, int VR>
 hipError_t launch_fold_vr(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
+                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G, int il,
                           hipStream_t s) {
     const bool xlds = (size_t)M * K * 2 <= kXLdsBytes;
     if (qz == nullptr)
@@ -1029,7 +1039,7 @@ hipError_t launch_fold_vr(const uint16_t *x, const int32_t *qw, const uint16_t *
 
 template <int WPL, int NW, int SEGR, int D>
 hipError_t launch_fold_m(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                         const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
+                         const int32_t *qz, uint16_t *y, int M, int K, int N, int G, int il,
                          hipStream_t s) {
     switch (live_rows(M)) {
     case 1: return launch_fold_vr<WPL, NW, SEGR, D, 1>(x, qw, sc, qz, y, M, K, N, G, il, s);
@@ -1042,7 +1052,7 @@ hipError_t launch_fold_m(const uint16_t *x, const int32_t *qw, const uint16_t *s
 // pipeline depth (the largest of 4, 2, 1 dividing the segments per wave).
 template <int WPL, int SEGR>
 hipError_t launch_fold_any(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
+                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G, int il,
                            hipStream_t s) {
     const int nseg = K / 8 / SEGR;
     if (nseg % 8 == 0) {
@@ -1058,19 +1068,19 @@ hipError_t launch_fold_any(const uint16_t *x, const int32_t *qw, const uint16_t 
 
 template <int WPL, int NW>
 hipError_t launch_exact(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
-                        const int32_t *qz, uint16_t *y, int M, int K, int N, int G, bool il,
+                        const int32_t *qz, uint16_t *y, int M, int K, int N, int G, int il,
                         hipStream_t s) {
     constexpr int TN = 16 * WPL;
     hipLaunchKernelGGL((exact_kernel<WPL, NW>), dim3((N + TN - 1) / TN), dim3(NW * 64),
                        (size_t)NW * M * TN * sizeof(float), s, x,
                        reinterpret_cast<const uint32_t *>(qw), sc,
-                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G, il ? 1 : 0);
+                       reinterpret_cast<const uint32_t *>(qz), y, M, K, N, G, il);
     return hipGetLastError();
 }
 
 // Fused gate/up: 8 words per lane (4 gate + 4 up columns), all live rows, X
 // staged in LDS; the shape must fit stream_kernel.
-template <int NW, int D, bool IL>
+template <int NW, int D, int IL>
 hipError_t launch_gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                           hipStream_t s) {
@@ -1089,7 +1099,7 @@ hipError_t launch_gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *
 }
 
 // Fused gate/up launcher for one layout (awq_gemv_gate_up*.hip instantiate it).
-template <bool IL>
+template <int IL>
 hipError_t gate_up_layout(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                                  const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
                                  hipStream_t s) {
@@ -1111,22 +1121,22 @@ hipError_t gate_up_layout(const uint16_t *x, const int32_t *qweight, const uint1
 }
 
 // One instantiated family of launchers per translation unit (arguments as
-// launch_stream's): the staged kernel on canonical words (name) and on
-// interleaved ones (name_il); the folded and exact kernels take the layout as
-// an argument.
+// launch_stream's): the staged kernel on canonical words (name), on interleaved
+// ones (name_il) and on blocked ones (name_blk); the folded and exact kernels
+// take the layout as an argument.
 using Launcher = hipError_t(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                             const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                             hipStream_t s);
 using LayoutLauncher = hipError_t(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                                   const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
-                                  bool il, hipStream_t s);
-Launcher gate_up, gate_up_il;
-Launcher stream_m_w2_d2, stream_m_w2_d2_il;
-Launcher stream_m_w4_d2, stream_m_w4_d2_il;
-Launcher stream_m_w4_d1, stream_m_w4_d1_il;
-Launcher prog_w2, prog_w2_il;
-Launcher prog_w4, prog_w4_il;
-Launcher prog_w8, prog_w8_il;
+                                  int il, hipStream_t s);
+Launcher gate_up, gate_up_il, gate_up_blk;
+Launcher stream_m_w2_d2, stream_m_w2_d2_il, stream_m_w2_d2_blk;
+Launcher stream_m_w4_d2, stream_m_w4_d2_il, stream_m_w4_d2_blk;
+Launcher stream_m_w4_d1, stream_m_w4_d1_il, stream_m_w4_d1_blk;
+Launcher prog_w2, prog_w2_il, prog_w2_blk;
+Launcher prog_w4, prog_w4_il, prog_w4_blk;
+Launcher prog_w8, prog_w8_il, prog_w8_blk;
 LayoutLauncher fold_w2_s16;
 LayoutLauncher fold_w4_s16;
 LayoutLauncher fold_w4_s8;

@@ -54,7 +54,7 @@ hipError_t scratch_address(void **out) {
 
 hipError_t launch_gemm_splitk_static(const uint16_t *x, const int32_t *qweight,
                                      const uint16_t *scales, const int32_t *qzeros, uint16_t *y,
-                                     int M, int K, int N, int G, int splits, bool il, hipStream_t s) {
+                                     int M, int K, int N, int G, int splits, int il, hipStream_t s) {
     if (gemm_splitk_workspace(M, N, splits) > kStaticScratchBytes) return hipErrorInvalidValue;
     void *ws = nullptr;
     const hipError_t e = scratch_address(&ws);

@@ -66,7 +66,9 @@ dequant_kernel(const uint32_t *__restrict__ qweight, const uint16_t *__restrict_
         const int r = (int)(t / n4);
         const int n = (int)(t % n4) * 4;
         const int g = (8 * r) / G;
-        const uint4 q = *reinterpret_cast<const uint4 *>(qweight + (size_t)r * N + n);
+        const bool blk = il == 2;   // il: the qweight layout (nonzero: interleaved nibbles)
+        const uint4 q = *reinterpret_cast<const uint4 *>(qweight + (size_t)r * q_pitch(blk, N) +
+                                                          q_col(blk, n, K / 8));
         const uint2 s = *reinterpret_cast<const uint2 *>(scales + (size_t)g * N + n);
         const uint32_t zw = qzeros ? qzeros[(size_t)g * (N / 8) + n / 8] >> (4 * (n % 8))
                                    : 0x8888u;
@@ -115,40 +117,51 @@ hipError_t launch_pack_zeros(const uint8_t *zeros, int32_t *qzeros, int groups, 
 }
 
 hipError_t launch_dequant(const int32_t *qweight, const uint16_t *scales, const int32_t *qzeros,
-                          uint16_t *w, int K, int N, int G, bool il, hipStream_t s) {
+                          uint16_t *w, int K, int N, int G, int il, hipStream_t s) {
     hipLaunchKernelGGL(dequant_kernel, dim3(grid_for((long long)(K / 8) * (N / 4))), dim3(256), 0,
                        s, reinterpret_cast<const uint32_t *>(qweight), scales,
-                       reinterpret_cast<const uint32_t *>(qzeros), w, K, N, G, il ? 1 : 0);
+                       reinterpret_cast<const uint32_t *>(qzeros), w, K, N, G, il);
     return hipGetLastError();
 }
 
-// Canonical <-> interleaved packed words: the nibble permutation of each word
-// (a byte swap and a nibble swap, see interleave_word), 16 bytes per thread.
+// Packed words from one layout to another: four words (packed row r, columns
+// n .. n + 3) per thread, read where layout `from` keeps them and written where
+// `to` does (q_col, q_pitch: the blocked layout moves words, the others keep
+// them in place), each word's nibbles permuted between the canonical and the
+// interleaved order when the two differ (interleave_word: a byte swap and a
+// nibble swap).  With src == dst the positions must agree (the caller checks),
+// and each thread then reads and writes only its own four words.
 __global__ void __launch_bounds__(256)
-repack_kernel(const uint4 *src, uint4 *dst, long long quads, int to_il) {   // src may equal dst
-    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < quads; i += (long long)gridDim.x * 256) {
-        uint4 v = src[i];
-        if (to_il) {
+repack_kernel(const uint32_t *src, uint32_t *dst, int K, int N, int from, int to) {
+    const int n4 = N / 4, KR = K / 8;
+    const long long total = (long long)KR * n4;
+    const bool fblk = from == 2, tblk = to == 2;
+    const int nib = (to != 0) - (from != 0);   // +1 interleave, -1 back to canonical, 0 keep
+    for (long long t = blockIdx.x * 256LL + threadIdx.x; t < total; t += (long long)gridDim.x * 256) {
+        const int r = (int)(t / n4);
+        const int n = (int)(t % n4) * 4;
+        uint4 v = *reinterpret_cast<const uint4 *>(src + (size_t)r * q_pitch(fblk, N) +
+                                                   q_col(fblk, n, KR));
+        if (nib > 0) {
             v.x = interleave_word(v.x);
             v.y = interleave_word(v.y);
             v.z = interleave_word(v.z);
             v.w = interleave_word(v.w);
-        } else {
+        } else if (nib < 0) {
             v.x = deinterleave_word(v.x);
             v.y = deinterleave_word(v.y);
             v.z = deinterleave_word(v.z);
             v.w = deinterleave_word(v.w);
         }
-        dst[i] = v;
+        *reinterpret_cast<uint4 *>(dst + (size_t)r * q_pitch(tblk, N) + q_col(tblk, n, KR)) = v;
     }
 }
 
-hipError_t launch_repack(const int32_t *src, int32_t *dst, long long words, bool to_interleaved,
+hipError_t launch_repack(const int32_t *src, int32_t *dst, int K, int N, int from, int to,
                          hipStream_t s) {
-    const long long quads = words / 4;   // words is a multiple of 8 (K / 8 * N, N % 8 == 0)
-    hipLaunchKernelGGL(repack_kernel, dim3(grid_for(quads)), dim3(256), 0, s,
-                       reinterpret_cast<const uint4 *>(src), reinterpret_cast<uint4 *>(dst), quads,
-                       to_interleaved ? 1 : 0);
+    hipLaunchKernelGGL(repack_kernel, dim3(grid_for((long long)(K / 8) * (N / 4))), dim3(256), 0, s,
+                       reinterpret_cast<const uint32_t *>(src), reinterpret_cast<uint32_t *>(dst),
+                       K, N, from, to);
     return hipGetLastError();
 }
 

@@ -426,7 +426,7 @@ hipError_t launch_scale_search(const uint16_t *x, int M, const uint16_t *w, int 
         // the migrated weight fp16(c W) is formed row by row inside the quantizer
         if ((e = launch_quantize_migrated(w, c, q, sc, qz, K, N, G, symmetric, s)) != hipSuccess)
             return e;
-        if ((e = launch_gemm(xs, q, sc, qz, yhat, M, K, N, G, false, s)) != hipSuccess) return e;
+        if ((e = launch_gemm(xs, q, sc, qz, yhat, M, K, N, G, 0 /* canonical words */, s)) != hipSuccess) return e;
         hipLaunchKernelGGL(sqerr_kernel, dim3(kLossBlocks), dim3(256), 0, s, yref, yhat, mn, part);
         hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, s, part, kLossBlocks, mn,
                            losses + i);
