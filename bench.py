@@ -5,8 +5,9 @@
 A step is one call of the fused layer (awq_gemv at M = 1) on the decode
 workload: the Llama-3-8B MLP gate shape, M=1, K=4096, N=14336, group 128,
 asymmetric zero points.  The layer is packed once and its words repacked
-into the library's interleaved layout (as when a checkpoint is loaded;
---layout canonical keeps awq_pack's word order); each step streams the packed
+into the library's blocked layout (as when a checkpoint is loaded; --layout
+canonical keeps awq_pack's word order, --layout interleaved the interleaved
+nibbles without the blocks); each step streams the packed
 weight, unpacks, dequantizes, multiplies,
 reduces and writes Y.  The weight is replicated into enough copies (>= 1 GiB)
 that successive steps read different copies, so every step streams from HBM
@@ -136,7 +137,7 @@ def to_dev(a):
 # kernel-private ones, interleaved or blocked (repacked once after packing, as
 # at load time).
 LAYOUT = {"canonical": 0, "interleaved": 1, "blocked": 2}
-BENCH_LAYOUT = "interleaved"
+BENCH_LAYOUT = "blocked"
 
 
 def build_layers(w, copies):
@@ -762,12 +763,13 @@ def synth_workload(name):
 
 
 def main():
+    global BENCH_LAYOUT
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
-    ap.add_argument("--layout", choices=sorted(LAYOUT), default="interleaved",
+    ap.add_argument("--layout", choices=sorted(LAYOUT), default=BENCH_LAYOUT,
                     help="qweight layout of the benchmarked layers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--ceilings", action="store_true", help="only measure the two ceilings")
@@ -780,7 +782,6 @@ def main():
     ap.add_argument("--command", action="append", default=[],
                     help="command line(s) that produced the profiled data, recorded in the summary")
     args = ap.parse_args()
-    global BENCH_LAYOUT
     BENCH_LAYOUT = args.layout
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1:], args.kind, args.command)

@@ -38,7 +38,7 @@ extern "C" {
 
 // kind 0: the decode kernel (64-column strips, X staged up front, two segments
 // in flight); kind 1: the small-batch kernel (128-column strips, X staged
-// segment by segment).  Interleaved words.  Returns a hipError_t.
+// segment by segment).  Blocked words.  Returns a hipError_t.
 int awq_timeline_gemv(int kind, const void *x, const void *qw, const void *sc, const void *qz,
                       void *y, int M, int K, int N, int G, void *stream) {
     const auto *xx = static_cast<const uint16_t *>(x);
@@ -47,18 +47,18 @@ int awq_timeline_gemv(int kind, const void *x, const void *qw, const void *sc, c
     const auto *z = static_cast<const int32_t *>(qz);
     auto *yy = static_cast<uint16_t *>(y);
     if (kind == 0)
-        return (int)awq::timeline_gemv::launch_stream_m<4, 8, 16, 2, true>(xx, q, s, z, yy, M, K, N, G,
+        return (int)awq::timeline_gemv::launch_stream_m<4, 8, 16, 2, 2>(xx, q, s, z, yy, M, K, N, G,
                                                                           as_stream(stream));
     if (kind == 1)
-        return (int)awq::timeline_gemv::launch_stream_prog<8, 8, 1, false, true>(xx, q, s, z, yy, M, K, N,
+        return (int)awq::timeline_gemv::launch_stream_prog<8, 8, 1, false, 2>(xx, q, s, z, yy, M, K, N,
                                                                                 G, as_stream(stream));
     return (int)hipErrorInvalidValue;
 }
 
-// awq_gemm's fast paths on interleaved words.  Returns a hipError_t.
+// awq_gemm's fast paths on blocked words.  Returns a hipError_t.
 int awq_timeline_gemm(const void *x, const void *qw, const void *sc, const void *qz, void *y, int M,
                       int K, int N, int G, void *stream) {
-    return (int)awq::timeline_gemm::launch_layout<true>(
+    return (int)awq::timeline_gemm::launch_layout<2>(
         static_cast<const uint16_t *>(x), static_cast<const int32_t *>(qw),
         static_cast<const uint16_t *>(sc), static_cast<const int32_t *>(qz),
         static_cast<uint16_t *>(y), M, K, N, G, as_stream(stream));

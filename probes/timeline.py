@@ -104,7 +104,7 @@ def gemv_timeline(name, kind, rows=None):
     w = synth.WORKLOADS[name]
     if rows is not None:
         w = dataclasses.replace(w, M=rows)
-    bench.BENCH_LAYOUT = "interleaved"
+    bench.BENCH_LAYOUT = "blocked"
     copies = max(2, math.ceil(bench.ROTATE_BYTES / bench.alg_bytes(w, 0)))
     layers = bench.build_layers(w, copies)
     x = bench.to_dev(synth.make_x(w.M, w.K, w.wid, w.n_outliers, w.outlier_gain))
@@ -138,7 +138,7 @@ def gemv_timeline(name, kind, rows=None):
     clock = st.median((c1[i] - c0[i]) / ((loop[i] - start[i]) * TICK_US * 1e3)
                       for i in range(len(slots)) if loop[i] > start[i])
     return [
-        f"## awq_gemv on {name}: M={w.M} K={w.K} N={w.N} G={w.G}, interleaved words, "
+        f"## awq_gemv on {name}: M={w.M} K={w.K} N={w.N} G={w.G}, blocked words, "
         f"{nwg} workgroups x {nw} waves, {copies} cold weight copies",
         f"outputs equal to the library's awq_gemv: {same}",
         f"per call (graph of 200, median of 5 replays): {per_call:.2f} us",
@@ -160,7 +160,7 @@ def gemm_timeline(name="prefill_out_proj"):
     from w4a16_group_quantized_amd import binding, synth
     lib = _lib()
     w = synth.WORKLOADS[name]
-    bench.BENCH_LAYOUT = "interleaved"
+    bench.BENCH_LAYOUT = "blocked"
     layers = bench.build_layers(w, 1)
     x = bench.to_dev(synth.make_x(w.M, w.K, w.wid, w.n_outliers, w.outlier_gain))
     y = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
@@ -190,7 +190,7 @@ def gemm_timeline(name="prefill_out_proj"):
     steps = w.K // 64
     busy = 32 * 32 * steps   # 32 MFMAs of 32 busy cycles per wave and 64-k step (128-row tiles)
     return [
-        f"## awq_gemm on {name}: M={w.M} K={w.K} N={w.N} G={w.G}, interleaved words, "
+        f"## awq_gemm on {name}: M={w.M} K={w.K} N={w.N} G={w.G}, blocked words, "
         f"{nwg} workgroups",
         f"outputs equal to the library's awq_gemm: {same}",
         f"per call (graph of 100 after 0.1 s of settling replays, median of 5): {per_call:.2f} us",
