@@ -58,8 +58,8 @@ hipError_t launch_gemm_splitk(const uint16_t *x, const int32_t *qweight, const u
                               const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G,
                               int splits, void *workspace, int il, hipStream_t s) {
     auto *part = static_cast<float *>(workspace);
-    const hipError_t e = (il == 2 ? gemm::split_blk : il ? gemm::split_il : gemm::split_canon)(x, qweight, scales, qzeros, part,
-                                                                   M, K, N, G, splits, s);
+    auto *split = il == 2 ? gemm::split_blk : il ? gemm::split_il : gemm::split_canon;
+    const hipError_t e = split(x, qweight, scales, qzeros, part, M, K, N, G, splits, s);
     if (e != hipSuccess) return e;
     const long long count = (long long)M * N;
     long long blocks = (count / 4 + 255) / 256;
@@ -76,14 +76,15 @@ bool gemm_gate_up_supported(int K, int N, int G) {
 hipError_t launch_gemm_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                                const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
                                int il, hipStream_t s) {
-    return (il == 2 ? gemm::gate_up_blk : il ? gemm::gate_up_il : gemm::gate_up_canon)(x, qweight, scales, qzeros, h, M, K, N, G,
-                                                         s);
+    auto *gate_up = il == 2 ? gemm::gate_up_blk : il ? gemm::gate_up_il : gemm::gate_up_canon;
+    return gate_up(x, qweight, scales, qzeros, h, M, K, N, G, s);
 }
 
 hipError_t launch_gemm(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                        const int32_t *qzeros, uint16_t *y, int M, int K, int N, int G, int il,
                        hipStream_t s) {
-    return (il == 2 ? gemm::plain_blk : il ? gemm::plain_il : gemm::plain_canon)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    auto *plain = il == 2 ? gemm::plain_blk : il ? gemm::plain_il : gemm::plain_canon;
+    return plain(x, qweight, scales, qzeros, y, M, K, N, G, s);
 }
 
 }  // namespace awq

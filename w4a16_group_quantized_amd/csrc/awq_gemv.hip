@@ -18,6 +18,10 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
     const int cus = device_cus();
     const long long n64 = (N + 63) / 64, n128 = (N + 127) / 128;
     const bool narrow = n64 * 2 <= cus;
+    // A family's launcher for the layer's word layout (AWQ_LAYOUT_*: 0, 1, 2).
+    auto run = [&](Launcher *canon, Launcher *inter, Launcher *blk) {
+        return (il == 2 ? blk : il ? inter : canon)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+    };
     if (M > 4) {
         // Beyond four rows X is staged segment by segment, one segment in
         // flight per wave, which takes any K.  Every workgroup reads all of X
@@ -28,23 +32,23 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
         // 15.5 us).
         const bool wide = n128 * 4 >= 3LL * cus && (M > 8 || n64 > 2LL * cus);
         if (narrow && stream_fits_prog(M, K, N, G, 2, 8, 1))
-            return (il == 2 ? prog_w2_blk : il ? prog_w2_il : prog_w2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+            return run(prog_w2, prog_w2_il, prog_w2_blk);
         if (!wide && stream_fits_prog(M, K, N, G, 4, 8, 1))
-            return (il == 2 ? prog_w4_blk : il ? prog_w4_il : prog_w4)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+            return run(prog_w4, prog_w4_il, prog_w4_blk);
         if (stream_fits_prog(M, K, N, G, 8, 8, 1))
-            return (il == 2 ? prog_w8_blk : il ? prog_w8_il : prog_w8)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+            return run(prog_w8, prog_w8_il, prog_w8_blk);
     }
     if (narrow && stream_fits(M, K, N, G, 2, 8, 16, 2))
-        return (il == 2 ? stream_m_w2_d2_blk : il ? stream_m_w2_d2_il : stream_m_w2_d2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        return run(stream_m_w2_d2, stream_m_w2_d2_il, stream_m_w2_d2_blk);
     if (stream_fits(M, K, N, G, 4, 8, 16, 2))
-        return (il == 2 ? stream_m_w4_d2_blk : il ? stream_m_w4_d2_il : stream_m_w4_d2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        return run(stream_m_w4_d2, stream_m_w4_d2_il, stream_m_w4_d2_blk);
     if (stream_fits(M, K, N, G, 4, 8, 16, 1))
-        return (il == 2 ? stream_m_w4_d1_blk : il ? stream_m_w4_d1_il : stream_m_w4_d1)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        return run(stream_m_w4_d1, stream_m_w4_d1_il, stream_m_w4_d1_blk);
     // Up to four rows with X beyond LDS: staged segment by segment as well.
     if (narrow && stream_fits_prog(M, K, N, G, 2, 8, 1))
-        return (il == 2 ? prog_w2_blk : il ? prog_w2_il : prog_w2)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        return run(prog_w2, prog_w2_il, prog_w2_blk);
     if (stream_fits_prog(M, K, N, G, 4, 8, 1))
-        return (il == 2 ? prog_w4_blk : il ? prog_w4_il : prog_w4)(x, qweight, scales, qzeros, y, M, K, N, G, s);
+        return run(prog_w4, prog_w4_il, prog_w4_blk);
     // A segment (SEGR packed rows) must sit inside one group and be whole 32-k steps.
     // Narrow layers on 32-column strips here too (14336 x 4096 at 16 rows:
     // 27.4 -> 22.1 us).

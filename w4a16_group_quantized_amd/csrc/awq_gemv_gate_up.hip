@@ -16,7 +16,8 @@ bool gemv_gate_up_supported(int M, int K, int N, int G) {
 hipError_t launch_gemv_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                                const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
                                int il, hipStream_t s) {
-    return (il == 2 ? gemv::gate_up_blk : il ? gemv::gate_up_il : gemv::gate_up)(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    auto *gate_up = il == 2 ? gemv::gate_up_blk : il ? gemv::gate_up_il : gemv::gate_up;
+    return gate_up(x, qweight, scales, qzeros, h, M, K, N, G, s);
 }
 
 }  // namespace awq
