@@ -10,9 +10,11 @@ blocks of 8 columns across the whole width (always the first and the last),
 and computes those columns.  Rows of X come from the synthetic generator.
 Each kernel variant the shapes select is covered: the decode kernel at 1 row
 and in its slot-staged form at 16 rows (X staged segment by segment), the GEMM,
-split K and the exact dequantization.  Two more cases take the largest batch (M K just
-below 2^31, a 4.3 GB X through the GEMM) and the largest fp16 W through the
-quantizer.
+split K and the exact dequantization.  The same again on blocked words, whose
+N must be a multiple of 128: N = 262016, the largest such width under 2^31 /
+K, repacked on the GPU from the seeded canonical words.  Two more cases take
+the largest batch (M K just below 2^31, a 4.3 GB X through the GEMM) and the
+largest fp16 W through the quantizer.
 """
 import numpy as np
 import pytest
@@ -43,6 +45,55 @@ def big():
     yield layer, cols, sampled
     del layer
     torch.cuda.empty_cache()
+
+
+NB = 262016   # the largest multiple of 128 with K * NB below 2^31
+
+
+@pytest.fixture(scope="module")
+def big_blocked():
+    rng = np.random.default_rng(20261204)
+    Q = rng.integers(0, 1 << 32, size=(K // 8, NB), dtype=np.uint32).view(np.int32)
+    S = rng.uniform(0.001, 0.01, size=(K // G, NB)).astype(np.float16).view(np.uint16)
+    QZ = rng.integers(0, 1 << 32, size=(K // G, NB // 8), dtype=np.uint32).view(np.int32)
+    canon = binding.Layer(torch.from_numpy(Q).cuda(), torch.from_numpy(S.view(np.float16)).cuda(),
+                          torch.from_numpy(QZ).cuda(), K, NB, G)
+    layer = binding.repack(canon, binding.LAYOUT_BLOCKED)
+    del canon
+    torch.cuda.empty_cache()
+    blocks = np.array(sorted({0, 15, 16, NB // 8 - 1} |
+                             set(rng.choice(NB // 8, 30, replace=False).tolist())))
+    cols = (8 * blocks[:, None] + np.arange(8)[None, :]).reshape(-1)
+    sampled = (np.ascontiguousarray(Q[:, cols]), np.ascontiguousarray(S[:, cols]),
+               np.ascontiguousarray(QZ[:, blocks]))
+    yield layer, cols, sampled
+    del layer
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("entry,M", [("gemv", 1), ("gemv", 16), ("gemm", 64), ("splitk", 64),
+                                     ("dequant", 0)])
+def test_largest_blocked_layer(big_blocked, entry, M):
+    layer, cols, sampled = big_blocked
+    print(f"largest blocked layer: {entry} M={M}", flush=True)
+    ci = torch.from_numpy(cols).cuda()
+    if entry == "dequant":
+        W = binding.dequant(layer)
+        torch.cuda.synchronize()
+        got = to_host_bits(W[:, ci])
+        del W
+        torch.cuda.empty_cache()
+        Qs, Ss, QZs = sampled
+        assert np.array_equal(got, oracle.load().dequant(Qs, Ss, QZs, G))
+        return
+    X = synth.make_x(M, K, 700 + M)
+    if entry == "splitk":
+        y = binding.gemm_splitk(to_dev(X), layer, 4)
+    else:
+        y = (binding.gemv if entry == "gemv" else binding.gemm)(to_dev(X), layer)
+    torch.cuda.synchronize()
+    got = to_host_bits(y[:, ci])
+    assert_y_close(got, _oracle_y(X, sampled), f"{entry} M={M} on the largest blocked layer")
 
 
 def _oracle_y(X, sampled):
