@@ -37,8 +37,9 @@ hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 extern "C" {
 
 // kind 0: the decode kernel (64-column strips, X staged up front, two segments
-// in flight); kind 1: the small-batch kernel (128-column strips, X staged
-// segment by segment).  Blocked words.  Returns a hipError_t.
+// in flight); kind 1: the small-batch kernel (128 columns per workgroup, as
+// paired strips where N is a multiple of 16; X staged segment by segment).
+// Blocked words.  Returns a hipError_t.
 int awq_timeline_gemv(int kind, const void *x, const void *qw, const void *sc, const void *qz,
                       void *y, int M, int K, int N, int G, void *stream) {
     const auto *xx = static_cast<const uint16_t *>(x);
@@ -49,9 +50,13 @@ int awq_timeline_gemv(int kind, const void *x, const void *qw, const void *sc, c
     if (kind == 0)
         return (int)awq::timeline_gemv::launch_stream_m<4, 8, 16, 2, 2>(xx, q, s, z, yy, M, K, N, G,
                                                                           as_stream(stream));
-    if (kind == 1)
-        return (int)awq::timeline_gemv::launch_stream_prog<8, 8, 1, false, 2>(xx, q, s, z, yy, M, K, N,
+    if (kind == 1) {
+        if (N % 16 == 0)   // paired strips, as the library takes them
+            return (int)awq::timeline_gemv::launch_stream_prog<8, 8, 1, 2, 2>(xx, q, s, z, yy, M, K, N,
                                                                                 G, as_stream(stream));
+        return (int)awq::timeline_gemv::launch_stream_prog<8, 8, 1, 0, 2>(xx, q, s, z, yy, M, K, N,
+                                                                            G, as_stream(stream));
+    }
     return (int)hipErrorInvalidValue;
 }
 

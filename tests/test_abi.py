@@ -154,8 +154,7 @@ def test_gate_up_validation(lib):
     assert f(FAKE, ctypes.byref(layer(N=24)), FAKE, 1, None) == 2            # I not a multiple of 8
     assert f(FAKE, ctypes.byref(layer()), FAKE, 17, None) == 4               # batch above 16
     assert f(FAKE, ctypes.byref(layer(G=32)), FAKE, 1, None) == 4            # group not a multiple of 128
-    # up to four rows X must fit LDS (beyond four it is staged segment by segment)
-    assert f(FAKE, ctypes.byref(layer(K=28672, N=64, G=128)), FAKE, 4, None) == 4
+    # (any K: X that does not fit LDS is staged segment by segment)
     assert f(FAKE, ctypes.byref(layer()), FAKE, 0, None) == 0                # empty batch
 
 

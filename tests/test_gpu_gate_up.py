@@ -45,6 +45,8 @@ def test_workload_gate_up(name, M):
     (5, 2048, 264, 128, False), (2, 384, 72, 384, True), (16, 4096, 520, 128, False),
     (11, 2048, 136, 256, True), (16, 1152, 136, 128, False), (1, 11008, 264, 128, True),
     (6, 1280, 40, 256, False), (3, 2688, 72, 128, False), (4, 1664, 40, 128, True),
+    # X beyond LDS at one row (130 KB) and at four rows (224 KB): staged segment by segment
+    (1, 66560, 8, 128, False), (4, 28672, 40, 128, True),
 ])
 def test_ragged_gate_up(M, K, I, G, sym):
     X, codes, zeros, scales = random_case(900 + M + K, M, K, 2 * I, G, sym)

@@ -95,7 +95,7 @@ const char *awq_status_string(awq_status status) {
     case AWQ_ERROR_INVALID_VALUE: return "AWQ_ERROR_INVALID_VALUE: null pointer or non-positive size";
     case AWQ_ERROR_SHAPE: return "AWQ_ERROR_SHAPE: K%8, N%8, G%8, K%G must be 0 (and N%128 in the blocked layout) and arrays below 2^31 elements";
     case AWQ_ERROR_ALIGNMENT: return "AWQ_ERROR_ALIGNMENT: tensor pointers must be 16-byte aligned";
-    case AWQ_ERROR_UNSUPPORTED: return "AWQ_ERROR_UNSUPPORTED: outside this entry point (awq_gemv takes M <= 16; awq_gemv_gate_up also needs G % 128 == 0 and X in LDS; awq_gemm_gate_up needs G % 64 == 0 and K % 256 == 0; awq_gemm_splitk needs slices of whole groups (or one group) and whole 128- or 256-k ring turns)";
+    case AWQ_ERROR_UNSUPPORTED: return "AWQ_ERROR_UNSUPPORTED: outside this entry point (awq_gemv takes M <= 16; awq_gemv_gate_up also needs G % 128 == 0; awq_gemm_gate_up needs G % 64 == 0 and K % 256 == 0; awq_gemm_splitk needs slices of whole groups (or one group) and whole 128- or 256-k ring turns)";
     case AWQ_ERROR_WORKSPACE: return "AWQ_ERROR_WORKSPACE: null, unaligned or smaller than the *_workspace_bytes query";
     case AWQ_ERROR_HIP: return "AWQ_ERROR_HIP: the HIP runtime refused the launch";
     }

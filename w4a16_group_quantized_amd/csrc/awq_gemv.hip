@@ -25,12 +25,19 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
     if (M > 4) {
         // Beyond four rows X is staged segment by segment, one segment in
         // flight per wave, which takes any K.  Every workgroup reads all of X
-        // (M K 2 bytes) beside its strip, so 128-column strips, half as many
-        // workgroups, pay where they still keep three quarters of the CUs
-        // busy and X is large (4096 x 28672 at 16 rows: 17.1 against 18.9
+        // (M K 2 bytes) beside its strip, so 128 columns per workgroup, half
+        // as many workgroups, pay where they still keep three quarters of the
+        // CUs busy and X is large (4096 x 28672 at 16 rows: 17.1 against 18.9
         // us); else 64-column strips (4096 x 14336 at 16 rows: 9.9 against
-        // 15.5 us).
-        const bool wide = n128 * 4 >= 3LL * cus && (M > 8 || n64 > 2LL * cus);
+        // 15.5 us).  Where N is a multiple of 16, those 128 columns are paired
+        // strips, 64 columns of each half of the layer (prog_w8): the same
+        // words, loads and sums, bit-identical outputs, and faster from five
+        // rows up (4096 x 28672: 8 rows 14.42 -> 12.62 us, 16 rows 15.86 ->
+        // 13.94 us; 8192 x 28672: 8 rows 24.19 -> 22.40 us, 16 rows 28.24 ->
+        // 23.78 us; at one to four rows, and as two 32-column strips with
+        // 8-byte loads, they are not).
+        const bool pair = N % 16 == 0 && n128 * 4 >= 3LL * cus;
+        const bool wide = pair || (n128 * 4 >= 3LL * cus && (M > 8 || n64 > 2LL * cus));
         if (narrow && stream_fits_prog(M, K, N, G, 2, 8, 1))
             return run(prog_w2, prog_w2_il, prog_w2_blk);
         if (!wide && stream_fits_prog(M, K, N, G, 4, 8, 1))

@@ -6,11 +6,10 @@ namespace awq {
 bool gemv_gate_up_supported(int M, int K, int N, int G) {
     using namespace gemv;
     if (M < 1 || M > 16 || N % 16 != 0) return false;
-    if (M > 4 && ((stream_even(K, 8, 16, 2) && stream_fits_prog(M, K, N, G, 8, 8, 2)) ||
-                  stream_fits_prog(M, K, N, G, 8, 8, 1)))
+    if (stream_fits_prog(M, K, N, G, 8, 8, 1))
         return true;   // X staged segment by segment: any K
-    return stream_fits(M, K, N, G, 8, 8, 16, 2) || stream_fits(M, K, N, G, 8, 8, 16, 1) ||
-           stream_fits(M, K, N, G, 8, 2, 16, 1) || stream_fits(M, K, N, G, 8, 1, 16, 1);
+    return stream_fits(M, K, N, G, 8, 8, 16, 1) || stream_fits(M, K, N, G, 8, 2, 16, 1) ||
+           stream_fits(M, K, N, G, 8, 1, 16, 1);
 }
 
 hipError_t launch_gemv_gate_up(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,

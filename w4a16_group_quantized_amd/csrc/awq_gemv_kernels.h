@@ -441,9 +441,11 @@ constexpr size_t kLdsMax = 160 * 1024;
 
 // XCH: 16-byte chunks of X each lane stages (the largest wave's slice,
 // M * ceil(segments / NW) * SEGR chunks, is at most 64 * XCH).
-// GU (fused gate/up): the layer's N columns are [gate | up]; a lane's WPL words
+// GU 1 (fused gate/up): the layer's N columns are [gate | up]; a lane's WPL words
 // are WPL / 2 gate columns and the same WPL / 2 columns of the up half, and the
-// output is h = fp16(SiLU(gate) * up), N / 2 columns wide.
+// output is h = fp16(SiLU(gate) * up), N / 2 columns wide.  GU 2 (paired
+// strips, a plain layer with N a multiple of 16): the same loads, a workgroup
+// taking a strip of each half of the columns, and the plain output y.
 // XS > 0 stages X progressively: the XS chunks per lane of a segment's slice
 // of X (M * SEGR <= 64 * XS) are loaded with the segment's weights and staged
 // just before the segment is multiplied, instead of the whole slice up front.
@@ -460,7 +462,7 @@ constexpr size_t kLdsMax = 160 * 1024;
 // nseg % NW waves take one segment more, and the loads ahead are guarded by
 // the wave's own count (a uniform branch).  The even case keeps the
 // unconditional pipeline.
-template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false,
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, int GU = 0,
           int XS = 0, bool UNEV = false, int IL = 0>
 __global__ void __launch_bounds__(NW * 64)
 stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
@@ -753,7 +755,7 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
             for (int i = 0; i < WPL; ++i) red[(wave * M + m) * TN + WPL * c16 + i] = acc[i][v];
     }
     __syncthreads();
-    if constexpr (GU) {
+    if constexpr (GU == 1) {
         for (int idx = threadIdx.x; idx < M * TO; idx += NW * 64) {
             const int m = idx / TO;
             const int c = idx % TO;
@@ -765,6 +767,25 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
                 us += red[(w * M + m) * TN + slot + WO];
             }
             if (n0 + c < NO) Y[(size_t)m * NO + n0 + c] = as_u16((half_t)(silu(gs) * us));
+        }
+    } else if constexpr (GU == 2) {
+        // Paired strips: slot c of the first half is column n0 + c, of the
+        // second half column NO + n0 + c; each is summed over the waves in the
+        // same order as an unpaired strip's.
+        for (int idx = threadIdx.x; idx < M * TO; idx += NW * 64) {
+            const int m = idx / TO;
+            const int c = idx % TO;
+            const int slot = WPL * (c / WO) + c % WO;
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                s1 += red[(w * M + m) * TN + slot];
+                s2 += red[(w * M + m) * TN + slot + WO];
+            }
+            if (n0 + c < NO) {
+                Y[(size_t)m * N + n0 + c] = as_u16((half_t)s1);
+                Y[(size_t)m * N + NO + n0 + c] = as_u16((half_t)s2);
+            }
         }
     } else {
         for (int idx = threadIdx.x; idx < M * TN; idx += NW * 64) {
@@ -807,7 +828,7 @@ inline size_t stream_lds_prog(int M, int K, int WPL, int NW, int SEGR) {
     return staged > red ? staged : red;
 }
 
-template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, bool GU = false,
+template <int WPL, int NW, int SEGR, int D, int VR, bool SYM, bool GRP1, int XCH, int GU = 0,
           int XS = 0, int IL = 0>
 hipError_t launch_stream(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                          const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
@@ -863,28 +884,28 @@ inline bool stream_fits_prog(int M, int K, int N, int G, int WPL, int NW, int D)
     return stream_lds_prog(M, K, WPL, NW, 16) <= kLdsMax;
 }
 
-template <int WPL, int NW, int SEGR, int D, int VR, int XCH, int IL>
+template <int WPL, int NW, int SEGR, int D, int VR, int XCH, int IL, int GU = 0>
 hipError_t launch_stream_sg(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                             const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                             hipStream_t s) {
     const bool grp1 = G == 8 * SEGR;
     if (qz == nullptr)
-        return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, true, true, XCH, false, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s)
-                    : launch_stream<WPL, NW, SEGR, D, VR, true, false, XCH, false, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s);
-    return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, false, true, XCH, false, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s)
-                : launch_stream<WPL, NW, SEGR, D, VR, false, false, XCH, false, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+        return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, true, true, XCH, GU, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s)
+                    : launch_stream<WPL, NW, SEGR, D, VR, true, false, XCH, GU, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    return grp1 ? launch_stream<WPL, NW, SEGR, D, VR, false, true, XCH, GU, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s)
+                : launch_stream<WPL, NW, SEGR, D, VR, false, false, XCH, GU, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
-template <int WPL, int NW, int SEGR, int D, int VR, int IL>
+template <int WPL, int NW, int SEGR, int D, int VR, int IL, int GU = 0>
 hipError_t launch_stream_x(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                            const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                            hipStream_t s) {
     const int chunks_w = M * ((K / 8 / SEGR + NW - 1) / NW) * SEGR;   // the largest wave's
-    if (chunks_w <= 64) return launch_stream_sg<WPL, NW, SEGR, D, VR, 1, IL>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (chunks_w <= 128) return launch_stream_sg<WPL, NW, SEGR, D, VR, 2, IL>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (chunks_w <= 256) return launch_stream_sg<WPL, NW, SEGR, D, VR, 4, IL>(x, qw, sc, qz, y, M, K, N, G, s);
-    if (chunks_w <= 512) return launch_stream_sg<WPL, NW, SEGR, D, VR, 8, IL>(x, qw, sc, qz, y, M, K, N, G, s);
-    return launch_stream_sg<WPL, NW, SEGR, D, VR, kStageChunks, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (chunks_w <= 64) return launch_stream_sg<WPL, NW, SEGR, D, VR, 1, IL, GU>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (chunks_w <= 128) return launch_stream_sg<WPL, NW, SEGR, D, VR, 2, IL, GU>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (chunks_w <= 256) return launch_stream_sg<WPL, NW, SEGR, D, VR, 4, IL, GU>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (chunks_w <= 512) return launch_stream_sg<WPL, NW, SEGR, D, VR, 8, IL, GU>(x, qw, sc, qz, y, M, K, N, G, s);
+    return launch_stream_sg<WPL, NW, SEGR, D, VR, kStageChunks, IL, GU>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
 // Compute units of the current device (queried once per process).
@@ -901,7 +922,7 @@ inline int device_cus() {
 
 // Beyond four rows (all four C rows of a lane live), X staged progressively:
 // XS = ceil(M * 16 / 64) chunks per lane per 16-row segment.
-template <int WPL, int NW, int D, bool GU, int XS, int IL>
+template <int WPL, int NW, int D, int GU, int XS, int IL>
 hipError_t launch_stream_prog_xs(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                                  const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                                  hipStream_t s) {
@@ -913,7 +934,7 @@ hipError_t launch_stream_prog_xs(const uint16_t *x, const int32_t *qw, const uin
 #undef AWQ_PROG
 }
 
-template <int WPL, int NW, int D, bool GU, int IL>
+template <int WPL, int NW, int D, int GU, int IL>
 hipError_t launch_stream_prog(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                               const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                               hipStream_t s) {
@@ -923,14 +944,14 @@ hipError_t launch_stream_prog(const uint16_t *x, const int32_t *qw, const uint16
     return launch_stream_prog_xs<WPL, NW, D, GU, 4, IL>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
-template <int WPL, int NW, int SEGR, int D, int IL>
+template <int WPL, int NW, int SEGR, int D, int IL, int GU = 0>
 hipError_t launch_stream_m(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                            const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                            hipStream_t s) {
     switch (live_rows(M)) {
-    case 1: return launch_stream_x<WPL, NW, SEGR, D, 1, IL>(x, qw, sc, qz, y, M, K, N, G, s);
-    case 2: return launch_stream_x<WPL, NW, SEGR, D, 2, IL>(x, qw, sc, qz, y, M, K, N, G, s);
-    default: return launch_stream_x<WPL, NW, SEGR, D, 4, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    case 1: return launch_stream_x<WPL, NW, SEGR, D, 1, IL, GU>(x, qw, sc, qz, y, M, K, N, G, s);
+    case 2: return launch_stream_x<WPL, NW, SEGR, D, 2, IL, GU>(x, qw, sc, qz, y, M, K, N, G, s);
+    default: return launch_stream_x<WPL, NW, SEGR, D, 4, IL, GU>(x, qw, sc, qz, y, M, K, N, G, s);
     }
 }
 
@@ -1078,13 +1099,17 @@ hipError_t launch_exact(const uint16_t *x, const int32_t *qw, const uint16_t *sc
     return hipGetLastError();
 }
 
-// Fused gate/up: 8 words per lane (4 gate + 4 up columns), all live rows, X
-// staged in LDS; the shape must fit stream_kernel.
+// Fused gate/up: 8 words per lane (4 gate + 4 up columns), all live rows.  X
+// staged segment by segment (prog), or in LDS before the loop (one row, where
+// it fits).  The shape must fit stream_kernel.  Depth 1 throughout: on the 4096 x 28672
+// [gate | up] layer, against depth 2 and X staged up front up to four rows,
+// 1 row 13.07 -> 12.47 us, 2 rows 13.46 -> 12.05, 4 rows 16.28 -> 12.40,
+// 8 rows 14.94 -> 12.81, 16 rows 16.03 -> 13.73-13.93.
 template <int NW, int D, int IL>
-hipError_t launch_gate_up(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
+hipError_t launch_gate_up(bool prog, const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                           const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                           hipStream_t s) {
-    if (M > 4) return launch_stream_prog<8, NW, D, true, IL>(x, qw, sc, qz, y, M, K, N, G, s);
+    if (prog) return launch_stream_prog<8, NW, D, 1, IL>(x, qw, sc, qz, y, M, K, N, G, s);
     const bool sym = qz == nullptr, grp1 = G == 8 * 16;
     const bool big = M * ((K / 128 + NW - 1) / NW) * 16 > 128;   // the largest wave's chunks
 #define AWQ_GU(SYMV, GRPV, XCHV) \
@@ -1103,20 +1128,17 @@ template <int IL>
 hipError_t gate_up_layout(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                                  const int32_t *qzeros, uint16_t *h, int M, int K, int N, int G,
                                  hipStream_t s) {
-        if (M > 4) {   // launch_gate_up stages X segment by segment beyond four rows
-        if (stream_even(K, 8, 16, 2) && stream_fits_prog(M, K, N, G, 8, 8, 2))
-            return launch_gate_up<8, 2, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
-        if (stream_fits_prog(M, K, N, G, 8, 8, 1))
-            return launch_gate_up<8, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
-    }
-    if (stream_fits(M, K, N, G, 8, 8, 16, 2))
-        return launch_gate_up<8, 2, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+    // One row: X staged up front where it fits LDS.  Otherwise, and for more
+    // rows, segment by segment, which takes any K.
+    const bool up_front = M == 1 && stream_fits(M, K, N, G, 8, 8, 16, 1);
+    if (!up_front && stream_fits_prog(M, K, N, G, 8, 8, 1))
+        return launch_gate_up<8, 1, IL>(true, x, qweight, scales, qzeros, h, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 8, 8, 16, 1))
-        return launch_gate_up<8, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+        return launch_gate_up<8, 1, IL>(M > 1, x, qweight, scales, qzeros, h, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 8, 2, 16, 1))
-        return launch_gate_up<2, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+        return launch_gate_up<2, 1, IL>(M > 1, x, qweight, scales, qzeros, h, M, K, N, G, s);
     if (stream_fits(M, K, N, G, 8, 1, 16, 1))
-        return launch_gate_up<1, 1, IL>(x, qweight, scales, qzeros, h, M, K, N, G, s);
+        return launch_gate_up<1, 1, IL>(M > 1, x, qweight, scales, qzeros, h, M, K, N, G, s);
     return hipErrorNotSupported;
 }
 

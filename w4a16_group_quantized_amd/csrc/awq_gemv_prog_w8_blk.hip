@@ -1,4 +1,5 @@
-// Small-batch GEMV, X staged segment by segment: 128-column strips; kernel-private blocked
+// Small-batch GEMV, X staged segment by segment: 128 columns per workgroup (a 64-column
+// strip of each half of the layer where N is a multiple of 16, else one strip); kernel-private blocked
 // words.
 #include "awq_gemv_kernels.h"
 
@@ -8,7 +9,9 @@ namespace gemv {
 hipError_t prog_w8_blk(const uint16_t *x, const int32_t *qw, const uint16_t *sc,
                        const int32_t *qz, uint16_t *y, int M, int K, int N, int G,
                        hipStream_t s) {
-    return launch_stream_prog<8, 8, 1, false, 2>(x, qw, sc, qz, y, M, K, N, G, s);
+    // A strip of each half of the columns per workgroup (N a multiple of 16).
+    if (N % 16 == 0) return launch_stream_prog<8, 8, 1, 2, 2>(x, qw, sc, qz, y, M, K, N, G, s);
+    return launch_stream_prog<8, 8, 1, 0, 2>(x, qw, sc, qz, y, M, K, N, G, s);
 }
 
 }  // namespace gemv
