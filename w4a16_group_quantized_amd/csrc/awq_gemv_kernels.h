@@ -1112,6 +1112,17 @@ hipError_t launch_gate_up(bool prog, const uint16_t *x, const int32_t *qw, const
     if (prog) return launch_stream_prog<8, NW, D, 1, IL>(x, qw, sc, qz, y, M, K, N, G, s);
     const bool sym = qz == nullptr, grp1 = G == 8 * 16;
     const bool big = M * ((K / 128 + NW - 1) / NW) * 16 > 128;   // the largest wave's chunks
+    if (M == 1) {   // one live C row per lane: 12.54 -> 12.23 us at one row
+#define AWQ_GU1(SYMV, GRPV, XCHV) \
+    launch_stream<8, NW, 16, D, 1, SYMV, GRPV, XCHV, true, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s)
+        if (big) {
+            if (sym) return grp1 ? AWQ_GU1(true, true, kStageChunks) : AWQ_GU1(true, false, kStageChunks);
+            return grp1 ? AWQ_GU1(false, true, kStageChunks) : AWQ_GU1(false, false, kStageChunks);
+        }
+        if (sym) return grp1 ? AWQ_GU1(true, true, 2) : AWQ_GU1(true, false, 2);
+        return grp1 ? AWQ_GU1(false, true, 2) : AWQ_GU1(false, false, 2);
+#undef AWQ_GU1
+    }
 #define AWQ_GU(SYMV, GRPV, XCHV) \
     launch_stream<8, NW, 16, D, 4, SYMV, GRPV, XCHV, true, 0, IL>(x, qw, sc, qz, y, M, K, N, G, s)
     if (big) {
