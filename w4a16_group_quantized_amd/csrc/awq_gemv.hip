@@ -22,22 +22,29 @@ hipError_t launch_gemv(const uint16_t *x, const int32_t *qweight, const uint16_t
     auto run = [&](Launcher *canon, Launcher *inter, Launcher *blk) {
         return (il == 2 ? blk : il ? inter : canon)(x, qweight, scales, qzeros, y, M, K, N, G, s);
     };
+    // Wide layers (128 columns per workgroup still keep three quarters of the
+    // CUs busy) with N a multiple of 16, from three rows up: paired strips, 64
+    // columns of each half of the layer per workgroup, X staged segment by
+    // segment (prog_w8).  Against one 128-column strip on the same words,
+    // outputs bit-identical: 4096 x 28672 at 8 rows 14.42 -> 12.62 us (it
+    // took 64-column strips there), at 16 rows 15.86 -> 13.94 us; 8192 x
+    // 28672 at 8 rows 24.19 -> 22.40 us, at 16 rows 28.24 -> 23.78 us.  At
+    // three and four rows, against X staged up front on 64-column strips
+    // (the segment sums then come from the matrix cores): 13.65 -> 12.13 and
+    // 13.57 -> 12.76 us; 22.46 -> 21.04 and 22.55 -> 21.75 us.  At one and two
+    // rows, and as two 32-column strips with 8-byte loads, they do not pay.
+    const bool pair = N % 16 == 0 && n128 * 4 >= 3LL * cus;
+    if (M > 2 && pair && stream_fits_prog(M, K, N, G, 8, 8, 1))
+        return run(prog_w8, prog_w8_il, prog_w8_blk);
     if (M > 4) {
         // Beyond four rows X is staged segment by segment, one segment in
         // flight per wave, which takes any K.  Every workgroup reads all of X
-        // (M K 2 bytes) beside its strip, so 128 columns per workgroup, half
-        // as many workgroups, pay where they still keep three quarters of the
-        // CUs busy and X is large (4096 x 28672 at 16 rows: 17.1 against 18.9
+        // (M K 2 bytes) beside its strip, so 128-column strips, half as many
+        // workgroups, pay where they still keep three quarters of the CUs
+        // busy and X is large (4096 x 28672 at 16 rows: 17.1 against 18.9
         // us); else 64-column strips (4096 x 14336 at 16 rows: 9.9 against
-        // 15.5 us).  Where N is a multiple of 16, those 128 columns are paired
-        // strips, 64 columns of each half of the layer (prog_w8): the same
-        // words, loads and sums, bit-identical outputs, and faster from five
-        // rows up (4096 x 28672: 8 rows 14.42 -> 12.62 us, 16 rows 15.86 ->
-        // 13.94 us; 8192 x 28672: 8 rows 24.19 -> 22.40 us, 16 rows 28.24 ->
-        // 23.78 us; at one to four rows, and as two 32-column strips with
-        // 8-byte loads, they are not).
-        const bool pair = N % 16 == 0 && n128 * 4 >= 3LL * cus;
-        const bool wide = pair || (n128 * 4 >= 3LL * cus && (M > 8 || n64 > 2LL * cus));
+        // 15.5 us).
+        const bool wide = n128 * 4 >= 3LL * cus && (M > 8 || n64 > 2LL * cus);
         if (narrow && stream_fits_prog(M, K, N, G, 2, 8, 1))
             return run(prog_w2, prog_w2_il, prog_w2_blk);
         if (!wide && stream_fits_prog(M, K, N, G, 4, 8, 1))
