@@ -89,6 +89,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_F16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU, dense fp16
 METRIC = "W4A16 GEMV HBM GB/s (% of peak) at M=1; GEMM TFLOP/s (% MFMA peak) at M=2048"
 ROTATE_BYTES = 1 << 30
+# Graph replays per configuration line; the line reports their median, so that
+# one slow replay does not decide it.
+CONFIG_REPS = 5
 GEMM_SETTLE_S = 0.1            # untimed replays before an MFMA-bound timing (see time_calls)
 CALIBRATION_COPY_BYTES = 64 << 20
 PROFILE_CALLS = 20
@@ -240,8 +243,9 @@ def bench_gemv(name, steps, warmup, reps=1, hot=False, max_copies=None):
     return out
 
 
-def bench_gate_up(name, M, steps, warmup):
-    """awq_gemv_gate_up on a concatenated [gate | up] layer: h = SiLU(gate) * up."""
+def bench_gate_up(name, M, steps, warmup, reps=CONFIG_REPS):
+    """awq_gemv_gate_up on a concatenated [gate | up] layer: h = SiLU(gate) * up;
+    the median of ``reps`` replays."""
     import torch
     from w4a16_group_quantized_amd import synth
     w = synth.WORKLOADS[name]
@@ -250,13 +254,14 @@ def bench_gate_up(name, M, steps, warmup):
     X = synth.make_x(max(M, w.M), w.K, w.wid, w.n_outliers, w.outlier_gain)[:M]
     X = to_dev(np.ascontiguousarray(X))
     h = torch.empty((M, w.N // 2), dtype=torch.float16, device="cuda")
-    t = time_calls("gemv_gate_up", X, layers, h, steps, warmup)
+    t = time_calls("gemv_gate_up", X, layers, h, steps, warmup, reps)
+    t = t[1] if reps > 1 else t                                # the median
     b = alg_bytes(w, M) - 2 * M * w.N + 2 * M * (w.N // 2)   # h replaces Y
     del layers
     torch.cuda.empty_cache()
     return {"workload": name, "M": M, "K": w.K, "N": w.N, "group_size": w.G,
             "symmetric": w.symmetric, "entry": "awq_gemv_gate_up", "weight_copies": copies,
-            "us_per_call": t * 1e6, "alg_bytes": b, "gbs": b / t / 1e9,
+            "replays": reps, "us_per_call": t * 1e6, "alg_bytes": b, "gbs": b / t / 1e9,
             "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS}
 
 
@@ -490,9 +495,10 @@ def ceiling_mfma(blocks=1024, iters=4000, reps=5):
             "frac_of_peak": round(flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
 
 
-def bench_gemm(name, steps, warmup, rotate=False):
-    """awq_gemm on the workload; ``rotate`` cycles through weight copies (1 GiB)
-    as the GEMV bench does, for batches small enough to be HBM-bound."""
+def bench_gemm(name, steps, warmup, rotate=False, reps=CONFIG_REPS):
+    """awq_gemm on the workload, the median of ``reps`` replays; ``rotate``
+    cycles through weight copies (1 GiB) as the GEMV bench does, for batches
+    small enough to be HBM-bound."""
     import torch
     from w4a16_group_quantized_amd import synth
     w = synth.WORKLOADS[name]
@@ -500,13 +506,14 @@ def bench_gemm(name, steps, warmup, rotate=False):
     layers = build_layers(w, copies)
     X = to_dev(synth.make_x(w.M, w.K, w.wid, w.n_outliers, w.outlier_gain))
     y = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
-    t = time_calls("gemm", X, layers, y, steps, warmup, settle_s=GEMM_SETTLE_S)
+    t = time_calls("gemm", X, layers, y, steps, warmup, reps, settle_s=GEMM_SETTLE_S)
+    t = t[1] if reps > 1 else t                                # the median
     flops = 2.0 * w.M * w.N * w.K
     del layers
     torch.cuda.empty_cache()
     return {"workload": name, "M": w.M, "K": w.K, "N": w.N, "group_size": w.G,
             "symmetric": w.symmetric, "entry": "awq_gemm", "us_per_call": t * 1e6,
-            "weight_copies": copies,
+            "weight_copies": copies, "replays": reps,
             "tflops": flops / t / 1e12, "mfma_frac": flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS}
 
 
@@ -740,11 +747,16 @@ def committed_traffic(kind="gemv"):
 def config_line(cfg, r):
     """One configuration's figures: time per call and its fraction of the roofline
     that bounds it (HBM bytes for the GEMV entries, MFMA flops for the GEMMs)."""
+    # The median of the line's replays where it has several (the headline's
+    # own value is its first replay, the K timed calls).
+    us = r["reps"]["median_us"] if "reps" in r else r["us_per_call"]
     line = {"config": cfg, "workload": r["workload"], "entry": r["entry"], "M": r["M"], "K": r["K"],
             "N": r["N"], "group_size": r["group_size"], "symmetric": r["symmetric"],
-            "us_per_call": round(r["us_per_call"], 3)}
+            "us_per_call": round(us, 3),
+            "replays": r["reps"]["n"] if "reps" in r else r.get("replays", 1)}
     if "gbs" in r:
-        line.update(bound="hbm", gbs=round(r["gbs"], 1), frac=round(r["hbm_frac"], 4),
+        gbs = r["alg_bytes"] / (us * 1e-6) / 1e9
+        line.update(bound="hbm", gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
                     weight_copies=r["weight_copies"])
     else:
         flops = 2.0 * r["M"] * r["N"] * r["K"]
@@ -811,13 +823,13 @@ def main():
     gemm = bench_gemm("prefill_out_proj", args.steps, args.warmup)
     # Every configuration of the workload list, each on its own entry point(s).
     configs = [
-        ("cfg1", bench_gemv("tiny", args.steps, args.warmup, max_copies=2)),
+        ("cfg1", bench_gemv("tiny", args.steps, args.warmup, reps=CONFIG_REPS, max_copies=2)),
         ("cfg2", head),
-        ("cfg3", bench_gemv("gate_up_m16", args.steps, args.warmup)),
+        ("cfg3", bench_gemv("gate_up_m16", args.steps, args.warmup, reps=CONFIG_REPS)),
         ("cfg3", bench_gate_up("gate_up_m16", 16, args.steps, args.warmup)),
         ("cfg3", bench_gemm("gate_up_m16", args.steps, args.warmup, rotate=True)),
         ("cfg4", gemm),
-        ("cfg5a", bench_gemv("sym70b_m1", args.steps, args.warmup)),
+        ("cfg5a", bench_gemv("sym70b_m1", args.steps, args.warmup, reps=CONFIG_REPS)),
         ("cfg5b", bench_gemm("sym70b_m4096", max(5, args.steps // 40), 2)),
     ]
     extra = []
