@@ -269,3 +269,26 @@ def test_gemm_one_group(M, K, N, G, sym):
     y = to_host_bits(binding.gemm(to_dev(X), device_case(codes, zeros, scales, G)))
     torch.cuda.synchronize()
     assert_y_close(y, Y16, f"gemm one group M={M} K={K} N={N} sym={sym}")
+
+
+@pytest.mark.parametrize("M,K,N,G,sym,layout", [
+    # Wide layers (128 columns per workgroup keep three quarters of the CUs busy) from three
+    # rows up: paired strips, 64 columns of each half.  N / 2 not a multiple of 64 leaves a
+    # ragged last strip in each half (canonical and interleaved words); blocked words need
+    # N % 128 == 0.  An odd segment count per wave (K = 1280) takes the guarded pipeline.
+    (3, 1024, 24592, 128, False, binding.LAYOUT_CANONICAL),
+    (5, 1024, 24592, 256, True, binding.LAYOUT_INTERLEAVED),
+    (8, 3072, 24592, 1024, True, binding.LAYOUT_CANONICAL),
+    (12, 1280, 24592, 128, False, binding.LAYOUT_CANONICAL),
+    (16, 2048, 24592, 128, False, binding.LAYOUT_INTERLEAVED),
+    (16, 1024, 24704, 128, False, binding.LAYOUT_BLOCKED),
+])
+def test_paired_strips_parity(M, K, N, G, sym, layout):
+    X, codes, zeros, scales = random_case(3100 + M + K + G, M, K, N, G, sym)
+    _, Y16 = oracle_case(X, codes, zeros, scales, G)
+    layer = device_case(codes, zeros, scales, G)
+    if layout != binding.LAYOUT_CANONICAL:
+        layer = binding.repack(layer, layout)
+    y = to_host_bits(binding.gemv(to_dev(X), layer))
+    torch.cuda.synchronize()
+    assert_y_close(y, Y16, f"gemv paired M={M} K={K} N={N} G={G} sym={sym} layout={layout}")
