@@ -28,11 +28,14 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contrac
 
 
 def build(source: str = SOURCE, out: str = LIBRARY) -> str:
-    """Compile ``source`` with gcc into the shared library ``out``."""
+    """Compile ``source`` with gcc into the shared library ``out``.  The object is
+    written under a name of this process's own and renamed into place, so that
+    processes building at once (parallel test workers) never share a file."""
     include = os.path.dirname(os.path.abspath(SOURCE))
-    cmd = ["gcc", *CFLAGS, "-I", include, source, "-o", out + ".tmp", "-lm"]
+    tmp = f"{out}.tmp{os.getpid():x}"
+    cmd = ["gcc", *CFLAGS, "-I", include, source, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(out + ".tmp", out)
+    os.replace(tmp, out)
     return out
 
 
