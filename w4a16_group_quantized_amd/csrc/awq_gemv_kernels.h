@@ -434,6 +434,11 @@ __device__ __forceinline__ Scales<WPL> join(const Scales<WPL / 2> &a, const Scal
 // SiLU in fp32: t / (1 + e^-t); far below zero the quotient is a signed zero.
 __device__ __forceinline__ float silu(float t) { return t / (1.0f + __expf(-t)); }
 
+// Whether the segment-by-segment kernel gives its reduction buffer LDS of its
+// own (beside the X slots, instead of over them): 128 columns per workgroup
+// and more than 8 rows.
+__host__ __device__ __forceinline__ bool sep_reduction(int M, int WPL) { return WPL == 8 && M > 8; }
+
 // Chunks of staged X per lane, at most.
 constexpr int kStageChunks = 16;
 // LDS of one workgroup, at most (gfx950: 160 KB per workgroup).
@@ -509,7 +514,15 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     uint4 *xs = lds + wave * (M * XR);
     float2 *tabs = reinterpret_cast<float2 *>(lds + NW * M * XR);
     float2 *tab = tabs + wave * (M * tper);
-    float *red = reinterpret_cast<float *>(lds);
+    // Slot mode with a large reduction buffer (128 columns per workgroup, more
+    // than 8 rows; stream_lds_prog sizes LDS the same way): the buffer lies after
+    // the slots, so that a wave writes its partial sums as soon as its own loop
+    // ends, with no barrier before.  16 rows of 4096 x 28672, two runs: 13.67-13.98
+    // -> 13.50-13.53 us (awq_gemv), 13.83-13.89 -> 13.51-13.58 us (fused
+    // gate/up); of 8192 x 28672: 23.47 -> 23.22 us.  At 4 to 16 rows on 64-column
+    // strips, and at 4 rows on 128 columns, it cost 0.3-1.8%.
+    const bool own_red = SLOT && sep_reduction(M, WPL);
+    float *red = reinterpret_cast<float *>(own_red ? lds + NW * M * XR : lds);
 
     const int xrow = c16 < M ? c16 : M - 1;      // A row of this lane (clamped)
     constexpr bool BLK = blocked_layout(IL);
@@ -745,7 +758,9 @@ stream_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ Q,
     AWQ_TL_STAMP(tl_loop);
     AWQ_TL_CLOCK(tc_loop);
     // C layout of the 16x16 MFMA: lane (kb, c16) holds rows 4 kb + v of column c16.
-    __syncthreads();   // every wave is done with the staged X and the tables
+    // Every wave is done with the staged X and the tables (not needed where the
+    // reduction buffer has LDS of its own).
+    if (!own_red) __syncthreads();
     AWQ_TL_STAMP(tl_red);
 #pragma unroll
     for (int v = 0; v < VR; ++v) {
@@ -825,6 +840,7 @@ inline size_t stream_lds_prog(int M, int K, int WPL, int NW, int SEGR) {
     (void)K;   // one segment's slot per wave, whatever K; no tables
     const size_t staged = (size_t)NW * M * SEGR * 16;
     const size_t red = (size_t)NW * M * 16 * WPL * 4;
+    if (sep_reduction(M, WPL)) return staged + red;   // side by side
     return staged > red ? staged : red;
 }
 
